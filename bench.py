@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Throughput of the rollout-guided FP4 rounding path on one MI355X.
+
+Workload: the deeper-half capture sweep -- 20 captured layers (of 40), each
+one bf16 site of 262144 x 2048 (64 trajectories x 4096 tokens), Gaussian with
+0.1% outlier channels x100, x_train = x_roll + N(0, (0.02|x_roll|)^2),
+grad ~ N(0, 1).  All 20 layers' inputs are generated on the GPU and resident
+in HBM (distinct 1 GiB buffers, far larger than the 256 MB last-level cache)
+before timing starts.
+
+One step = for every layer, in order: tensor scale (amax pass), capture
+(scale bytes + parity bit-plane), guided fake-quant forward (y + clip mask),
+plain RNE fake-quant forward (y + clip mask), STE backward.  Every kernel is
+bracketed by HIP events on the stream it runs on; the step's wall time is
+taken between device synchronizations.
+
+Prints one JSON line (last line of stdout).  ``value`` is the algorithmic
+bytes of the whole step divided by its wall time, in GB/s; per-kernel GB/s,
+Gelem/s and the fraction of the 8 TB/s HBM peak are reported beside it, with
+the CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GB/s and Gelem/s for capture + guided fakequant fwd/bwd; % of HBM peak"
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD specification
+LAYERS, TOTAL_LAYERS = 20, 40
+ROWS, COLS = 262144, 2048
+# Algorithmic bytes per element each kernel must move (reads + writes).
+BYTES_PER_ELEM = {
+    "tensor_scale": 2.0,                       # read x
+    "capture": 2.0 + 1 / 8 + 1 / 16,           # read x; write bits + scale bytes
+    "guided_fwd": 2.0 + 1 / 8 + 1 / 16 + 2.0 + 1 / 8,  # read x, bits, scales; write y, mask
+    "rne_fwd": 2.0 + 1 / 16 + 2.0 + 1 / 8,     # read x, scales; write y, mask
+    "ste_bwd": 2.0 + 1 / 8 + 2.0,              # read grad, mask; write grad_in
+}
+KERNELS = list(BYTES_PER_ELEM)
+CPU_SHARE = 16           # host cores a one-GPU machine grants
+CPU_BUDGET_S = 12.0      # wall-clock budget of the CPU oracle leg
+CHUNK_ROWS = 128
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------
+# CPU oracle leg (runs in worker processes started before the GPU is touched)
+# ----------------------------------------------------------------------------
+
+def _oracle_chunk(args):
+    import numpy as np
+    import oracle
+    xr, xt, g, ts = args
+    t0 = time.perf_counter()
+    oracle.tensor_scale(xr)                      # the amax pass over this chunk
+    cap = oracle.capture(xr, ts)
+    gd = oracle.guided_fwd(xt, cap["scales"], ts, cap["bits"])
+    rn = oracle.rne_fwd(xt, cap["scales"], ts)
+    gin = oracle.ste_bwd(g, gd["mask"], xt.size)
+    dt = time.perf_counter() - t0
+    return dt, {"scales": cap["scales"], "bits": cap["bits"], "y_g": gd["y"], "mask_g": gd["mask"],
+                "y_r": rn["y"], "mask_r": rn["mask"], "gin": gin}
+
+
+def make_pool():
+    import multiprocessing as mp
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(cores, CPU_SHARE))
+    ctx = mp.get_context("forkserver")
+    pool = ctx.Pool(cores)
+    pool.map(_noop, range(cores))   # start every worker now, before any GPU call
+    return pool, cores
+
+
+def _noop(_):
+    import numpy  # noqa: F401
+    import oracle  # noqa: F401
+    return 0
+
+
+# ----------------------------------------------------------------------------
+# GPU leg
+# ----------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--layers", type=int, default=LAYERS, help=argparse.SUPPRESS)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this library's path runs on a single MI355X and has no "
+              "multi-GPU mode (see the sharding paragraph of DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    pool, cores = (None, 0) if args.no_cpu_baseline else make_pool()
+
+    import numpy as np
+    import torch
+
+    import fp4_rollout_guided_amd as tr
+    import workloads
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    L = args.layers
+    n = ROWS * COLS
+    log(f"generating {L} layers of {ROWS}x{COLS} bf16 on {torch.cuda.get_device_name(dev)}")
+    layers = []
+    for l in range(L):
+        d = workloads.cfg3_layer(dev, l)
+        d["scales"] = torch.empty(n // 16, dtype=torch.uint8, device=dev)
+        d["bits"] = torch.empty(n // 8, dtype=torch.uint8, device=dev)
+        d["ts"] = torch.empty(1, dtype=torch.float32, device=dev)
+        layers.append(d)
+    y_g = torch.empty(ROWS, COLS, dtype=torch.bfloat16, device=dev)
+    y_r = torch.empty_like(y_g)
+    gin = torch.empty_like(y_g)
+    mask_g = torch.empty(n // 8, dtype=torch.uint8, device=dev)
+    mask_r = torch.empty_like(mask_g)
+    ws = torch.empty(tr.lib.trace_tensor_scale_workspace_bytes(n), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(events=None):
+        for li, d in enumerate(layers):
+            def mark(k, i):
+                if events is not None:
+                    events[k][li][i].record(stream)
+            mark("tensor_scale", 0)
+            tr.tensor_scale(d["x_roll"], out=d["ts"], workspace=ws)
+            mark("tensor_scale", 1)
+            mark("capture", 0)
+            tr.capture(d["x_roll"], d["ts"], scales=d["scales"], bits=d["bits"])
+            mark("capture", 1)
+            mark("guided_fwd", 0)
+            tr.guided_fakequant_fwd(d["x_train"], d["scales"], d["ts"], d["bits"], y=y_g, mask=mask_g)
+            mark("guided_fwd", 1)
+            mark("rne_fwd", 0)
+            tr.rne_fakequant_fwd(d["x_train"], d["scales"], d["ts"], y=y_r, mask=mask_r)
+            mark("rne_fwd", 1)
+            mark("ste_bwd", 0)
+            tr.ste_bwd(d["grad"], mask_g, grad_in=gin)
+            mark("ste_bwd", 1)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    per_kernel_ms = {k: 0.0 for k in KERNELS}
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev = {k: [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(L)] for k in KERNELS}
+        step(ev)
+        stream.synchronize()
+        for k in KERNELS:
+            per_kernel_ms[k] += sum(ev[k][li][0].elapsed_time(ev[k][li][1]) for li in range(L))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1e3 * wall / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step")
+
+    launches = args.steps * L
+    bytes_step = L * n * sum(BYTES_PER_ELEM.values())
+    value = bytes_step / (ms_per_step * 1e-3) / 1e9
+    kernels = {}
+    for k in KERNELS:
+        avg_ms = per_kernel_ms[k] / launches
+        gbs = BYTES_PER_ELEM[k] * n / (avg_ms * 1e-3) / 1e9
+        kernels[k] = {"avg_us": round(avg_ms * 1e3, 2), "GB_s": round(gbs, 1),
+                      "Gelem_s": round(n / (avg_ms * 1e-3) / 1e9, 2),
+                      "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                      "bytes_per_launch": int(BYTES_PER_ELEM[k] * n)}
+    dominant = max(KERNELS, key=lambda k: per_kernel_ms[k])
+    dk = kernels[dominant]
+
+    cache = {
+        "compact_bytes_20_layers": L * (n // 8 + n // 16),
+        "full_nvfp4_bytes_40_layers": TOTAL_LAYERS * (n // 2 + n // 16),
+    }
+    cache["ratio"] = round(cache["full_nvfp4_bytes_40_layers"] / cache["compact_bytes_20_layers"], 4)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"deeper-half capture sweep: {L} of {TOTAL_LAYERS} layers, one {ROWS}x{COLS} "
+                               f"bf16 site per layer (64 trajectories x 4096 tokens), Gaussian with 0.1% outlier "
+                               f"channels x100",
+                   "layers": L, "rows": ROWS, "cols": COLS, "elements_per_step": L * n,
+                   "step": "tensor_scale + capture + guided_fwd + rne_fwd + ste_bwd per layer"},
+        "gelem_per_s": round(L * n / (ms_per_step * 1e-3) / 1e9, 3),
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "kernels": kernels,
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": dk["GB_s"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": dk["frac_hbm_peak"], "traffic": read_traffic(dominant)},
+        "cache": cache,
+        "cpu_baseline": None,
+    }
+
+    if pool is not None:
+        result["cpu_baseline"] = cpu_leg(pool, cores, layers[0], n, y_g, mask_g, y_r, mask_r, gin, np, torch, tr)
+        pool.close()
+        pool.join()
+    print(json.dumps(result), flush=True)
+
+
+def read_traffic(kernel):
+    """HBM traffic per launch from the committed counter summary, or None
+    when there is none for this kernel or the kernel source changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_cfg3.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    src = os.path.join(ROOT, "fp4_rollout_guided_amd", "csrc", "kernels.hip")
+    with open(src, "rb") as fh:
+        digest = hashlib.sha256(fh.read()).hexdigest()
+    if kv.get("kernels_hip_sha256") != digest or "traffic_bytes_per_launch" not in kv:
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+def cpu_leg(pool, cores, d0, n, y_g, mask_g, y_r, mask_r, gin, np, torch, tr):
+    """Oracle on rows of layer 0 (its outputs recomputed on the GPU for
+    those rows are compared bit for bit), within CPU_BUDGET_S of wall time."""
+    import oracle
+    from tests.gpu_util import to_np_u16, to_np_u8
+    # layer-0 outputs of the last step are still in y_g/... for the last layer only;
+    # recompute layer 0 so that the GPU outputs of the sampled rows are at hand
+    tr.tensor_scale(d0["x_roll"], out=d0["ts"])
+    tr.capture(d0["x_roll"], d0["ts"], scales=d0["scales"], bits=d0["bits"])
+    tr.guided_fakequant_fwd(d0["x_train"], d0["scales"], d0["ts"], d0["bits"], y=y_g, mask=mask_g)
+    tr.rne_fakequant_fwd(d0["x_train"], d0["scales"], d0["ts"], y=y_r, mask=mask_r)
+    tr.ste_bwd(d0["grad"], mask_g, grad_in=gin)
+    torch.cuda.synchronize()
+    ts_gpu = np.float32(d0["ts"].item())
+    xr_all = to_np_u16(d0["x_roll"])
+    ts_oracle = oracle.tensor_scale(xr_all)
+    ts_match = bool(np.float32(ts_oracle).view(np.uint32) == ts_gpu.view(np.uint32))
+    del xr_all
+
+    per = CHUNK_ROWS * COLS
+    done_rows, busy, exact = 0, 0.0, ts_match
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < CPU_BUDGET_S and done_rows + cores * CHUNK_ROWS <= ROWS:
+        lo, hi = done_rows, done_rows + cores * CHUNK_ROWS
+        sl = slice(lo * COLS, hi * COLS)
+        xr = to_np_u16(d0["x_roll"].view(-1)[sl])
+        xt = to_np_u16(d0["x_train"].view(-1)[sl])
+        g = to_np_u16(d0["grad"].view(-1)[sl])
+        tasks = [(xr[i * per:(i + 1) * per], xt[i * per:(i + 1) * per], g[i * per:(i + 1) * per], ts_oracle)
+                 for i in range(cores)]
+        res = pool.map(_oracle_chunk, tasks)
+        busy += sum(r[0] for r in res)
+        want = {k: np.concatenate([r[1][k] for r in res]) for k in res[0][1]}
+        got = {
+            "scales": to_np_u8(d0["scales"][lo * COLS // 16:hi * COLS // 16]),
+            "bits": to_np_u8(d0["bits"][lo * COLS // 8:hi * COLS // 8]),
+            "y_g": to_np_u16(y_g.view(-1)[sl]), "mask_g": to_np_u8(mask_g[lo * COLS // 8:hi * COLS // 8]),
+            "y_r": to_np_u16(y_r.view(-1)[sl]), "mask_r": to_np_u8(mask_r[lo * COLS // 8:hi * COLS // 8]),
+            "gin": to_np_u16(gin.view(-1)[sl]),
+        }
+        exact = exact and all(np.array_equal(got[k], want[k]) for k in want)
+        done_rows = hi
+    wall = time.perf_counter() - t0
+    elems = done_rows * COLS
+    eps = elems / wall
+    bpe = sum(BYTES_PER_ELEM.values())
+    log(f"cpu oracle: {elems} elements in {wall:.2f} s on {cores} processes; bit-exact={exact}")
+    return {"value": round(eps * bpe / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "elem_per_s": round(eps, 1),
+            "sample": f"rows 0..{done_rows} of layer 0 ({elems} elements) through the whole step, "
+                      f"tensor scale of the full layer; {cores} worker processes, "
+                      f"{busy:.1f} s of CPU time in {wall:.1f} s wall",
+            "sample_bit_exact_vs_gpu": exact}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,207 @@
+"""Python binding for libtrace (rollout-guided FP4 rounding on MI355X).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+``libtrace.so`` (built by ``python -m fp4_rollout_guided_amd.build``).  PyTorch
+supplies device memory and the current stream.  There is no CPU fallback:
+importing this package fails if the library has not been built.
+
+Functions mirror the C ABI in ``include/trace.h``:
+
+    tensor_scale(x)                                  -> ts (fp32[1])
+    capture(x_roll, ts, want_codes=False)            -> (scales, bits, codes)
+    guided_fakequant_fwd(x_train, scales, ts, bits)  -> (y, mask, qcodes)
+    rne_fakequant_fwd(x_train, scales, ts)           -> (y, mask, qcodes)
+    ste_bwd(grad_out, mask)                          -> grad_in
+
+and ``GuidedFakeQuant`` wraps the forward/backward pair as an autograd
+function.
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "TraceError", "LIB_PATH", "lib", "abi_version", "tensor_scale", "capture",
+    "guided_fakequant_fwd", "rne_fakequant_fwd", "ste_bwd", "GuidedFakeQuant",
+    "STATUS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtrace.so")
+
+STATUS = {0: "TRACE_OK", 1: "TRACE_E_NULL", 2: "TRACE_E_SHAPE", 3: "TRACE_E_ALIGN",
+          4: "TRACE_E_ALIAS", 5: "TRACE_E_HIP"}
+
+
+class TraceError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        msg = lib.trace_status_string(status).decode()
+        if status == 5:
+            msg += f" (hipError_t {lib.trace_last_hip_error()})"
+        super().__init__(f"{what}: {msg}")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m fp4_rollout_guided_amd.build` "
+            "(libtrace has no CPU fallback)")
+    L = ctypes.CDLL(LIB_PATH)
+    p, i64, st, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    sig = {
+        "trace_abi_version": ([], ctypes.c_int),
+        "trace_status_string": ([st], ctypes.c_char_p),
+        "trace_last_hip_error": ([], ctypes.c_int),
+        "trace_tensor_scale_workspace_bytes": ([i64], sz),
+        "trace_tensor_scale": ([p, i64, p, sz, p, p], st),
+        "trace_capture": ([p, i64, i64, p, p, p, p, p], st),
+        "trace_guided_fakequant_fwd": ([p, i64, i64, p, p, p, p, p, p, p], st),
+        "trace_rne_fakequant_fwd": ([p, i64, i64, p, p, p, p, p, p], st),
+        "trace_ste_bwd": ([p, p, i64, p, p], st),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    return L
+
+
+lib = _load()
+
+
+def abi_version() -> int:
+    return lib.trace_abi_version()
+
+
+# --------------------------------------------------------------------------
+# marshalling helpers
+# --------------------------------------------------------------------------
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _bf16(t, name):
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name} must be bf16 (or its raw 16-bit pattern), got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _rows_cols(t):
+    cols = t.shape[-1] if t.dim() > 0 else 1
+    rows = t.numel() // cols if cols else 0
+    return rows, cols
+
+
+def _u8(n, like, out, name):
+    if out is None:
+        return torch.empty(n, dtype=torch.uint8, device=like.device)
+    if out.dtype != torch.uint8 or out.numel() < n or not out.is_contiguous() or out.device != like.device:
+        raise ValueError(f"{name} must be a contiguous uint8 device tensor of at least {n} bytes")
+    return out
+
+
+def _check(status, what):
+    if status != 0:
+        raise TraceError(status, what)
+
+
+# --------------------------------------------------------------------------
+# entry points
+# --------------------------------------------------------------------------
+
+def tensor_scale(x, out=None, workspace=None):
+    """ts = fl32(max|x| / 2688) as a float32[1] device tensor."""
+    _bf16(x, "x")
+    n = x.numel()
+    need = lib.trace_tensor_scale_workspace_bytes(n)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=x.device)
+    _check(lib.trace_tensor_scale(_ptr(x), n, _ptr(workspace), workspace.numel(), _ptr(out), _stream(x)),
+           "trace_tensor_scale")
+    return out
+
+
+def capture(x_roll, ts, want_codes=False, scales=None, bits=None, codes=None):
+    """Compact rollout record of one site tensor: (scales u8[n/16],
+    bits u8[n/8], codes u8[n/2] or None)."""
+    _bf16(x_roll, "x_roll")
+    rows, cols = _rows_cols(x_roll)
+    n = rows * cols
+    scales = _u8(n // 16, x_roll, scales, "scales")
+    bits = _u8(n // 8, x_roll, bits, "bits")
+    if want_codes or codes is not None:
+        codes = _u8(n // 2, x_roll, codes, "codes")
+    _check(lib.trace_capture(_ptr(x_roll), rows, cols, _ptr(ts), _ptr(scales), _ptr(bits), _ptr(codes),
+                             _stream(x_roll)), "trace_capture")
+    return scales, bits, codes
+
+
+def _fwd(guided, x, scales, ts, bits, y, mask, want_codes, qcodes):
+    _bf16(x, "x_train")
+    rows, cols = _rows_cols(x)
+    n = rows * cols
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _bf16(y, "y")
+    mask = _u8(n // 8, x, mask, "mask")
+    if want_codes or qcodes is not None:
+        qcodes = _u8(n // 2, x, qcodes, "qcodes")
+    if guided:
+        st = lib.trace_guided_fakequant_fwd(_ptr(x), rows, cols, _ptr(scales), _ptr(ts), _ptr(bits), _ptr(y),
+                                            _ptr(mask), _ptr(qcodes), _stream(x))
+    else:
+        st = lib.trace_rne_fakequant_fwd(_ptr(x), rows, cols, _ptr(scales), _ptr(ts), _ptr(y), _ptr(mask),
+                                         _ptr(qcodes), _stream(x))
+    _check(st, "trace_guided_fakequant_fwd" if guided else "trace_rne_fakequant_fwd")
+    return y, mask, qcodes
+
+
+def guided_fakequant_fwd(x_train, scales, ts, bits, y=None, mask=None, want_codes=False, qcodes=None):
+    """Rollout-guided fake-quant forward: (y bf16, mask u8[n/8], qcodes)."""
+    return _fwd(True, x_train, scales, ts, bits, y, mask, want_codes, qcodes)
+
+
+def rne_fakequant_fwd(x_train, scales, ts, y=None, mask=None, want_codes=False, qcodes=None):
+    """Plain round-to-nearest-even fake-quant forward: (y, mask, qcodes)."""
+    return _fwd(False, x_train, scales, ts, None, y, mask, want_codes, qcodes)
+
+
+def ste_bwd(grad_out, mask, grad_in=None):
+    """Straight-through estimator backward: grad_out where mask is set."""
+    _bf16(grad_out, "grad_out")
+    if grad_in is None:
+        grad_in = torch.empty_like(grad_out)
+    else:
+        _bf16(grad_in, "grad_in")
+    _check(lib.trace_ste_bwd(_ptr(grad_out), _ptr(mask), grad_out.numel(), _ptr(grad_in), _stream(grad_out)),
+           "trace_ste_bwd")
+    return grad_in
+
+
+class GuidedFakeQuant(torch.autograd.Function):
+    """y = s * q* in the forward, straight-through (clip-masked) gradient in
+    the backward; the rollout record (scales, ts, bits) is not differentiated."""
+
+    @staticmethod
+    def forward(ctx, x_train, scales, ts, bits):
+        y, mask, _ = guided_fakequant_fwd(x_train.contiguous(), scales, ts, bits)
+        ctx.save_for_backward(mask)
+        return y
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        (mask,) = ctx.saved_tensors
+        return ste_bwd(grad_out.contiguous(), mask), None, None, None

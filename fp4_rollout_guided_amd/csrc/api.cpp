@@ -1,0 +1,156 @@
+// C ABI of libtrace: argument validation and dispatch to the HIP launchers.
+// Validation happens before any HIP call, so a rejected call enqueues
+// nothing.  See include/trace.h for the contract of each entry point.
+#include "trace.h"
+
+#include <hip/hip_runtime.h>
+
+#include "launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+struct Range {
+  uintptr_t lo;
+  uint64_t len;
+};
+
+bool overlaps(Range a, Range b) {
+  if (a.len == 0 || b.len == 0) return false;
+  return a.lo < b.lo + b.len && b.lo < a.lo + a.len;
+}
+
+Range rng(const void* p, uint64_t len) { return Range{reinterpret_cast<uintptr_t>(p), len}; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// n = rows * cols with cols % 16 == 0 and 2n bytes addressable.
+trace_status site_size(int64_t rows, int64_t cols, uint64_t* n_out) {
+  if (rows < 0 || cols < 0 || (cols % 16) != 0) return TRACE_E_SHAPE;
+  int64_t n = 0;
+  if (__builtin_mul_overflow(rows, cols, &n) || n > (INT64_MAX / 4)) return TRACE_E_SHAPE;
+  *n_out = (uint64_t)n;
+  return TRACE_OK;
+}
+
+trace_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return TRACE_OK;
+  g_last_hip_error = (int)e;
+  return TRACE_E_HIP;
+}
+
+// Outputs must not overlap any input nor each other; `inplace_ok` lists an
+// (output, input) pair that may coincide exactly.
+trace_status check_alias(const Range* outs, int nout, const Range* ins, int nin, int inplace_out = -1,
+                         int inplace_in = -1) {
+  for (int i = 0; i < nout; ++i) {
+    for (int j = 0; j < nin; ++j) {
+      if (i == inplace_out && j == inplace_in && outs[i].lo == ins[j].lo && outs[i].len == ins[j].len)
+        continue;
+      if (overlaps(outs[i], ins[j])) return TRACE_E_ALIAS;
+    }
+    for (int k = i + 1; k < nout; ++k)
+      if (overlaps(outs[i], outs[k])) return TRACE_E_ALIAS;
+  }
+  return TRACE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int trace_abi_version(void) { return TRACE_ABI_VERSION; }
+
+const char* trace_status_string(trace_status s) {
+  switch (s) {
+    case TRACE_OK: return "TRACE_OK";
+    case TRACE_E_NULL: return "TRACE_E_NULL: a required pointer is NULL";
+    case TRACE_E_SHAPE: return "TRACE_E_SHAPE: bad size (negative, cols % 16 != 0, overflow, or workspace too small)";
+    case TRACE_E_ALIGN: return "TRACE_E_ALIGN: misaligned pointer";
+    case TRACE_E_ALIAS: return "TRACE_E_ALIAS: an output overlaps an input or another output";
+    case TRACE_E_HIP: return "TRACE_E_HIP: HIP runtime or launch failure";
+    default: return "TRACE: unknown status";
+  }
+}
+
+int trace_last_hip_error(void) { return g_last_hip_error; }
+
+size_t trace_tensor_scale_workspace_bytes(int64_t n) {
+  if (n < 0) return 0;
+  return (size_t)trace_host::amax_partial_count((uint64_t)n / 16) * sizeof(uint32_t);
+}
+
+trace_status trace_tensor_scale(const uint16_t* x, int64_t n, void* workspace, size_t workspace_bytes,
+                                float* ts_out, void* stream) {
+  if (!x || !workspace || !ts_out) return TRACE_E_NULL;
+  if (n < 0 || (n % 16) != 0 || n > (INT64_MAX / 4)) return TRACE_E_SHAPE;
+  if (workspace_bytes < trace_tensor_scale_workspace_bytes(n)) return TRACE_E_SHAPE;
+  if (!aligned(x, 16) || !aligned(workspace, 4) || !aligned(ts_out, 4)) return TRACE_E_ALIGN;
+  const uint64_t un = (uint64_t)n;
+  const Range outs[2] = {rng(workspace, trace_tensor_scale_workspace_bytes(n)), rng(ts_out, 4)};
+  const Range ins[1] = {rng(x, 2 * un)};
+  if (trace_status st = check_alias(outs, 2, ins, 1)) return st;
+  return hip_status(trace_host::launch_tensor_scale(x, un / 16, static_cast<uint32_t*>(workspace), ts_out,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
+trace_status trace_capture(const uint16_t* x_roll, int64_t rows, int64_t cols, const float* ts,
+                           uint8_t* scales, uint8_t* bits, uint8_t* codes, void* stream) {
+  if (!x_roll || !ts || !scales || !bits) return TRACE_E_NULL;
+  uint64_t n = 0;
+  if (trace_status st = site_size(rows, cols, &n)) return st;
+  if (!aligned(x_roll, 16) || !aligned(ts, 4) || !aligned(bits, 2) || (codes && !aligned(codes, 8)))
+    return TRACE_E_ALIGN;
+  const Range outs[3] = {rng(scales, n / 16), rng(bits, n / 8), rng(codes, codes ? n / 2 : 0)};
+  const Range ins[2] = {rng(x_roll, 2 * n), rng(ts, 4)};
+  if (trace_status st = check_alias(outs, 3, ins, 2)) return st;
+  if (n == 0) return TRACE_OK;
+  return hip_status(trace_host::launch_capture(x_roll, n / 16, ts, scales, bits, codes,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+static trace_status fakequant(bool guided, const uint16_t* x, int64_t rows, int64_t cols,
+                              const uint8_t* scales, const float* ts, const uint8_t* bits, uint16_t* y,
+                              uint8_t* mask, uint8_t* qcodes, void* stream) {
+  if (!x || !scales || !ts || (guided && !bits) || !y || !mask) return TRACE_E_NULL;
+  uint64_t n = 0;
+  if (trace_status st = site_size(rows, cols, &n)) return st;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ts, 4) || !aligned(mask, 2) ||
+      (guided && !aligned(bits, 2)) || (qcodes && !aligned(qcodes, 8)))
+    return TRACE_E_ALIGN;
+  const Range outs[3] = {rng(y, 2 * n), rng(mask, n / 8), rng(qcodes, qcodes ? n / 2 : 0)};
+  const Range ins[4] = {rng(x, 2 * n), rng(scales, n / 16), rng(ts, 4), rng(bits, guided ? n / 8 : 0)};
+  if (trace_status st = check_alias(outs, 3, ins, 4, /*inplace_out=*/0, /*inplace_in=*/0)) return st;
+  if (n == 0) return TRACE_OK;
+  return hip_status(trace_host::launch_fakequant(guided, x, n / 16, scales, ts, bits, y, mask, qcodes,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+trace_status trace_guided_fakequant_fwd(const uint16_t* x_train, int64_t rows, int64_t cols,
+                                        const uint8_t* scales, const float* ts, const uint8_t* bits,
+                                        uint16_t* y, uint8_t* mask, uint8_t* qcodes, void* stream) {
+  return fakequant(true, x_train, rows, cols, scales, ts, bits, y, mask, qcodes, stream);
+}
+
+trace_status trace_rne_fakequant_fwd(const uint16_t* x_train, int64_t rows, int64_t cols,
+                                     const uint8_t* scales, const float* ts, uint16_t* y, uint8_t* mask,
+                                     uint8_t* qcodes, void* stream) {
+  return fakequant(false, x_train, rows, cols, scales, ts, nullptr, y, mask, qcodes, stream);
+}
+
+trace_status trace_ste_bwd(const uint16_t* grad_out, const uint8_t* mask, int64_t n, uint16_t* grad_in,
+                           void* stream) {
+  if (!grad_out || !mask || !grad_in) return TRACE_E_NULL;
+  if (n < 0 || (n % 16) != 0 || n > (INT64_MAX / 4)) return TRACE_E_SHAPE;
+  if (!aligned(grad_out, 16) || !aligned(grad_in, 16) || !aligned(mask, 2)) return TRACE_E_ALIGN;
+  const uint64_t un = (uint64_t)n;
+  const Range outs[1] = {rng(grad_in, 2 * un)};
+  const Range ins[2] = {rng(grad_out, 2 * un), rng(mask, un / 8)};
+  if (trace_status st = check_alias(outs, 1, ins, 2, 0, 0)) return st;
+  if (n == 0) return TRACE_OK;
+  return hip_status(trace_host::launch_ste_bwd(grad_out, mask, un / 16, grad_in,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

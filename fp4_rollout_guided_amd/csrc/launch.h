@@ -1,0 +1,25 @@
+// Internal host-side launchers (not part of the C ABI).  Arguments have been
+// validated by api.cpp; sizes are in 16-element blocks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace trace_host {
+
+// Upper bound on amax partial workgroups (and on workspace words).
+constexpr uint32_t kAmaxMaxGroups = 2048;
+
+uint32_t amax_partial_count(uint64_t nblocks);
+
+hipError_t launch_tensor_scale(const uint16_t* x, uint64_t nblocks, uint32_t* partial, float* ts_out,
+                               hipStream_t stream);
+hipError_t launch_capture(const uint16_t* x, uint64_t nblocks, const float* ts, uint8_t* scales,
+                          uint8_t* bits, uint8_t* codes, hipStream_t stream);
+hipError_t launch_fakequant(bool guided, const uint16_t* x, uint64_t nblocks, const uint8_t* scales,
+                            const float* ts, const uint8_t* bits, uint16_t* y, uint8_t* mask,
+                            uint8_t* qcodes, hipStream_t stream);
+hipError_t launch_ste_bwd(const uint16_t* g, const uint8_t* mask, uint64_t nblocks, uint16_t* gin,
+                          hipStream_t stream);
+
+}  // namespace trace_host

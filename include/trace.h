@@ -1,0 +1,183 @@
+/*
+ * libtrace -- rollout-guided FP4 rounding (TRACE) for MI355X (gfx950).
+ *
+ * C ABI of the data-parallel hot path of TRACE's rollout-guided rounding as
+ * described in the rcap.io post "TRACE: Rollout-Guided Quantization-Aware
+ * Training for FP4" (2026-10-06):
+ *
+ *   rollout side  -- quantize each captured activation / KV site to NVFP4 and
+ *                    keep a compact record: one mantissa bit per element plus
+ *                    the scale metadata (bandwidth paragraph; the capture half
+ *                    of the pseudo-code listing);
+ *   training side -- recompute z = clip(x_train / s, -6, 6) with the cached
+ *                    rollout scale, bracket z between two adjacent FP4
+ *                    codewords, keep the one the cached bit points at, and
+ *                    return s * q* through a straight-through estimator
+ *                    (rollout-guided rounding paragraph; the QAT half of the
+ *                    listing).
+ *
+ * NVFP4 parameters (the pages name the format, not its parameters): blocks of
+ * 16 consecutive elements along the last dimension, one OCP E4M3FN scale byte
+ * per block, one IEEE fp32 tensor scale ts = amax / (6 * 448), and E2M1
+ * codewords {0, 0.5, 1, 1.5, 2, 3, 4, 6} with sign, reached by
+ * round-to-nearest-even.
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ * - Tensors are flat, row-major, and live in device memory (hipMalloc'd or
+ *   allocated by a framework on the same device).  bf16 values are passed as
+ *   raw uint16_t bit patterns.  A site tensor of rows x cols elements needs
+ *   cols % 16 == 0; blocks never cross rows.
+ * - Record layout (the rollout -> trainer cache contract):
+ *     scales : uint8_t[n/16], one E4M3FN byte per block, in block order;
+ *     bits   : uint8_t[n/8], bit k of byte j is the parity bit of element
+ *              8*j + k (bit 0 of its E2M1 code = parity of its signed grid
+ *              index, the "one mantissa bit");
+ *     codes  : uint8_t[n/2], optional full 4-bit codes (sign << 3 | index),
+ *              element 2*j in the low nibble of byte j;
+ *     ts     : one IEEE fp32 tensor scale, in device memory.
+ *   The caller indexes records by [trajectory, token, site]; one call handles
+ *   one site tensor.
+ * - Ownership: the caller owns every buffer.  The library allocates nothing,
+ *   frees nothing, never synchronizes, and keeps no state between calls
+ *   other than a thread-local copy of the last HIP error code.  It is safe to
+ *   call from several host threads.
+ * - Asynchrony: all device work is enqueued on `stream` (a hipStream_t; NULL
+ *   is the default stream).  Outputs are valid once that stream reaches the
+ *   point of the call.
+ * - Errors: entry points return a trace_status.  Arguments are validated
+ *   before any HIP call; on a validation error nothing is enqueued.
+ *   n == 0 is a successful no-op (trace_tensor_scale then writes ts = 0).
+ * - Alignment: bf16 tensors need 16-byte alignment, bit-planes and masks
+ *   2-byte alignment, code arrays 8-byte alignment; scale bytes have none.
+ * - Aliasing: outputs must not overlap inputs, except exact in-place use
+ *   where an entry point allows it.
+ */
+#ifndef LIBTRACE_TRACE_H
+#define LIBTRACE_TRACE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TRACE_ABI_VERSION 1
+
+#if defined(__GNUC__)
+#define TRACE_API __attribute__((visibility("default")))
+#else
+#define TRACE_API
+#endif
+
+typedef int trace_status;
+enum {
+  TRACE_OK = 0,
+  TRACE_E_NULL = 1,  /* a required pointer is NULL                          */
+  TRACE_E_SHAPE = 2, /* negative size, cols % 16 != 0, size overflow,
+                        or a workspace that is too small                    */
+  TRACE_E_ALIGN = 3, /* a pointer is not aligned as stated above            */
+  TRACE_E_ALIAS = 4, /* an output overlaps an input or another output       */
+  TRACE_E_HIP = 5    /* a HIP runtime call or kernel launch failed;
+                        trace_last_hip_error() returns its hipError_t       */
+};
+
+/* TRACE_ABI_VERSION of the built library. */
+TRACE_API int trace_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+TRACE_API const char* trace_status_string(trace_status status);
+
+/* hipError_t of the most recent TRACE_E_HIP returned on this host thread,
+ * 0 if none. */
+TRACE_API int trace_last_hip_error(void);
+
+/*
+ * Tensor scale of a rollout site tensor (NVFP4 second-level scale; "scale
+ * metadata" in the bandwidth paragraph, scale_roll in the listing):
+ *   ts = fl32(amax / 2688),  amax = max |x[i]| over the n elements, NaN
+ *   ignored, 0 for n == 0 or an all-NaN tensor.
+ *   x         : bf16[n] (device), n >= 0, n % 16 == 0.
+ *   workspace : device scratch of at least
+ *               trace_tensor_scale_workspace_bytes(n) bytes, 4-byte aligned,
+ *               caller-owned; its contents are not preserved.
+ *   ts_out    : one fp32 (device), written on `stream`.
+ * The result is exact (a maximum and one correctly rounded division), so it
+ * does not depend on the launch geometry.
+ */
+TRACE_API size_t trace_tensor_scale_workspace_bytes(int64_t n);
+TRACE_API trace_status trace_tensor_scale(const uint16_t* x, int64_t n, void* workspace,
+                                size_t workspace_bytes, float* ts_out,
+                                void* stream);
+
+/*
+ * Rollout-side capture (fp4_quantize and low_bits(q_roll, b=1) in the
+ * listing; the compact cache of the bandwidth paragraph).  Per 16-element
+ * block b:
+ *   amax_b = max |x| over the block (NaN ignored);
+ *   scales[b] = E4M3FN_RNE_saturating(fl32(fl32(amax_b / 6) / ts)), 0 when ts
+ *               is 0 or not finite;
+ *   s = fl32(E4M3FN(scales[b]) * ts).
+ * Per element: z = fl32(x / s); idx = E2M1 round-to-nearest-even index of
+ * min(|z|, 6) (ties to the even index); code = sign(z) << 3 | idx;
+ * bit = idx & 1.  In a block whose s is not a positive finite number, every
+ * code is a zero with the input's sign.  NaN elements give code 0.
+ *   x_roll : bf16[rows*cols] (device); ts : one fp32 (device), usually from
+ *            trace_tensor_scale.
+ *   scales : uint8[n/16], bits : uint8[n/8], codes : uint8[n/2] or NULL.
+ */
+TRACE_API trace_status trace_capture(const uint16_t* x_roll, int64_t rows, int64_t cols,
+                           const float* ts, uint8_t* scales, uint8_t* bits,
+                           uint8_t* codes, void* stream);
+
+/*
+ * Training-side rollout-guided fake-quant forward (the QAT half of the
+ * listing; rollout-guided rounding paragraph).  With the cached rollout
+ * record (scales, ts, bits) of the same site:
+ *   s = fl32(E4M3FN(scales[b]) * ts);  zr = fl32(x_train / s);
+ *   mask = |zr| <= 6;  z = clip(zr, -6, 6);
+ *   lo, hi = the E2M1 magnitudes enclosing |z| (equal when |z| is one);
+ *   m = |z| if lo == hi, else the one of lo, hi whose index parity is the
+ *       cached bit;  q* = copysign(m, z);  y = bf16_RNE(fl32(s * q*)).
+ * Zero-scale blocks (s not a positive finite number; any scale byte >= 0x7F)
+ * give y = +-0 with the input's sign and mask 0; NaN inputs give y = +0 and
+ * mask 0.
+ *   x_train : bf16[rows*cols]; scales/ts/bits : the capture record;
+ *   y       : bf16[n]; may be exactly x_train (in place);
+ *   mask    : uint8[n/8], clip mask for trace_ste_bwd (bit layout as bits);
+ *   qcodes  : uint8[n/2] codes of q*, or NULL.
+ */
+TRACE_API trace_status trace_guided_fakequant_fwd(const uint16_t* x_train, int64_t rows,
+                                        int64_t cols, const uint8_t* scales,
+                                        const float* ts, const uint8_t* bits,
+                                        uint16_t* y, uint8_t* mask,
+                                        uint8_t* qcodes, void* stream);
+
+/*
+ * Plain round-to-nearest-even fake-quant forward on the same scales, the
+ * vanilla-QAT baseline the post compares against ("instead of standard
+ * round-to-nearest"): as trace_guided_fakequant_fwd with m = the E2M1
+ * magnitude nearest to |z|, ties to the even index.  Same arguments minus
+ * `bits`; y may be exactly x_train.
+ */
+TRACE_API trace_status trace_rne_fakequant_fwd(const uint16_t* x_train, int64_t rows,
+                                     int64_t cols, const uint8_t* scales,
+                                     const float* ts, uint16_t* y,
+                                     uint8_t* mask, uint8_t* qcodes,
+                                     void* stream);
+
+/*
+ * Straight-through-estimator backward (straight_through_estimator in the
+ * listing): grad_in[i] = mask bit i ? grad_out[i] : +0.0 (0x0000).
+ *   grad_out, grad_in : bf16[n]; grad_in may be exactly grad_out;
+ *   mask : uint8[n/8] from a fake-quant forward; n % 16 == 0.
+ */
+TRACE_API trace_status trace_ste_bwd(const uint16_t* grad_out, const uint8_t* mask,
+                           int64_t n, uint16_t* grad_in, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBTRACE_TRACE_H */

@@ -1,0 +1,149 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry
+point declared in include/trace.h, and rejects bad arguments before making
+any HIP call (the fake device addresses below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp4_rollout_guided_amd as tr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+L = tr.lib
+A = 0x7F0000000000          # fake, 256-byte aligned "device" addresses
+OK, E_NULL, E_SHAPE, E_ALIGN, E_ALIAS = 0, 1, 2, 3, 4
+
+
+def P(v):
+    return ctypes.c_void_p(v)
+
+
+def declared_symbols():
+    with open(os.path.join(ROOT, "include", "trace.h")) as fh:
+        text = fh.read()
+    return sorted(set(re.findall(r"TRACE_API\s+[\w\s\*]+?\b(trace_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_symbols()
+    assert len(names) >= 9
+    raw = ctypes.CDLL(tr.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_version_and_status_strings():
+    assert tr.abi_version() == 1
+    for code in range(6):
+        assert L.trace_status_string(code).decode().startswith("TRACE")
+    assert b"unknown" in L.trace_status_string(99)
+    assert L.trace_last_hip_error() == 0
+
+
+def test_workspace_size():
+    assert L.trace_tensor_scale_workspace_bytes(0) == 4
+    assert L.trace_tensor_scale_workspace_bytes(16) == 4
+    assert L.trace_tensor_scale_workspace_bytes(4096 * 2) == 8
+    big = L.trace_tensor_scale_workspace_bytes(1 << 34)
+    assert 4 <= big <= 4 * 4096
+
+
+def test_tensor_scale_validation():
+    f = L.trace_tensor_scale
+    ws = L.trace_tensor_scale_workspace_bytes(4096)
+    assert f(None, 4096, P(A + 0x100000), ws, P(A + 0x200000), None) == E_NULL
+    assert f(P(A), 4096, None, ws, P(A + 0x200000), None) == E_NULL
+    assert f(P(A), 4096, P(A + 0x100000), ws, None, None) == E_NULL
+    assert f(P(A), -16, P(A + 0x100000), ws, P(A + 0x200000), None) == E_SHAPE
+    assert f(P(A), 4095, P(A + 0x100000), ws, P(A + 0x200000), None) == E_SHAPE
+    assert f(P(A), 1 << 20, P(A + 0x100000), 3, P(A + 0x200000), None) == E_SHAPE
+    assert f(P(A + 2), 4096, P(A + 0x100000), ws, P(A + 0x200000), None) == E_ALIGN
+    assert f(P(A), 4096, P(A + 0x100001), ws, P(A + 0x200000), None) == E_ALIGN
+    assert f(P(A), 4096, P(A + 0x100000), ws, P(A + 0x200002), None) == E_ALIGN
+    # ts_out inside x
+    assert f(P(A), 4096, P(A + 0x100000), ws, P(A + 64), None) == E_ALIAS
+
+
+def test_capture_validation():
+    f = L.trace_capture
+    x, ts, sc, bt, cd = A, A + 0x100000, A + 0x200000, A + 0x300000, A + 0x400000
+    assert f(None, 4, 32, P(ts), P(sc), P(bt), None, None) == E_NULL
+    assert f(P(x), 4, 32, None, P(sc), P(bt), None, None) == E_NULL
+    assert f(P(x), 4, 32, P(ts), None, P(bt), None, None) == E_NULL
+    assert f(P(x), 4, 32, P(ts), P(sc), None, None, None) == E_NULL
+    assert f(P(x), 4, 24, P(ts), P(sc), P(bt), None, None) == E_SHAPE
+    assert f(P(x), -1, 32, P(ts), P(sc), P(bt), None, None) == E_SHAPE
+    assert f(P(x), 1 << 62, 1 << 4, P(ts), P(sc), P(bt), None, None) == E_SHAPE
+    assert f(P(x + 8), 4, 32, P(ts), P(sc), P(bt), None, None) == E_ALIGN
+    assert f(P(x), 4, 32, P(ts), P(sc), P(bt + 1), None, None) == E_ALIGN
+    assert f(P(x), 4, 32, P(ts), P(sc), P(bt), P(cd + 4), None) == E_ALIGN
+    assert f(P(x), 4, 32, P(ts), P(x + 16), P(bt), None, None) == E_ALIAS      # scales inside x
+    assert f(P(x), 4, 32, P(ts), P(sc), P(sc + 4), None, None) == E_ALIAS     # bits over scales
+    assert f(P(x), 4, 32, P(ts), P(sc), P(bt), P(bt + 8), None) == E_ALIAS    # codes over bits
+    assert f(P(x), 4, 32, P(sc + 4), P(sc), P(bt), None, None) == E_ALIAS     # scales over ts
+    # empty tensors are a no-op that makes no HIP call
+    assert f(P(x), 0, 32, P(ts), P(sc), P(bt), None, None) == OK
+    assert f(P(x), 7, 0, P(ts), P(sc), P(bt), None, None) == OK
+
+
+@pytest.mark.parametrize("guided", [True, False])
+def test_fakequant_validation(guided):
+    x, sc, ts, bt, y, mk, qc = (A, A + 0x100000, A + 0x200000, A + 0x300000, A + 0x400000,
+                                A + 0x500000, A + 0x600000)
+
+    def call(x=x, rows=4, cols=32, sc=sc, ts=ts, bt=bt, y=y, mk=mk, qc=None):
+        args = [P(x) if x is not None else None, rows, cols, P(sc) if sc is not None else None,
+                P(ts) if ts is not None else None]
+        if guided:
+            args.append(P(bt) if bt is not None else None)
+        args += [P(y) if y is not None else None, P(mk) if mk is not None else None,
+                 P(qc) if qc is not None else None, None]
+        fn = L.trace_guided_fakequant_fwd if guided else L.trace_rne_fakequant_fwd
+        return fn(*args)
+
+    assert call(x=None) == E_NULL
+    assert call(sc=None) == E_NULL
+    assert call(ts=None) == E_NULL
+    assert call(y=None) == E_NULL
+    assert call(mk=None) == E_NULL
+    if guided:
+        assert call(bt=None) == E_NULL
+        assert call(bt=bt + 1) == E_ALIGN
+    assert call(cols=40) == E_SHAPE
+    assert call(rows=-2) == E_SHAPE
+    assert call(x=x + 4) == E_ALIGN
+    assert call(y=y + 8) == E_ALIGN
+    assert call(mk=mk + 1) == E_ALIGN
+    assert call(qc=qc + 2) == E_ALIGN
+    assert call(y=x + 32) == E_ALIAS          # partial overlap with x
+    assert call(mk=sc) == E_ALIAS             # mask over scales
+    assert call(qc=y + 64) == E_ALIAS         # qcodes inside y
+    assert call(mk=y + 16) == E_ALIAS
+    assert call(rows=0) == OK
+    assert call(rows=0, y=x) == OK            # exact in-place is allowed
+
+
+def test_ste_validation():
+    f = L.trace_ste_bwd
+    g, m, gi = A, A + 0x100000, A + 0x200000
+    assert f(None, P(m), 64, P(gi), None) == E_NULL
+    assert f(P(g), None, 64, P(gi), None) == E_NULL
+    assert f(P(g), P(m), 64, None, None) == E_NULL
+    assert f(P(g), P(m), 60, P(gi), None) == E_SHAPE
+    assert f(P(g), P(m), -16, P(gi), None) == E_SHAPE
+    assert f(P(g + 2), P(m), 64, P(gi), None) == E_ALIGN
+    assert f(P(g), P(m + 1), 64, P(gi), None) == E_ALIGN
+    assert f(P(g), P(m), 64, P(g + 16), None) == E_ALIAS
+    assert f(P(g), P(m), 64, P(m - 32), None) == E_ALIAS
+    assert f(P(g), P(m), 0, P(gi), None) == OK
+    assert f(P(g), P(m), 0, P(g), None) == OK
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    x = torch.zeros(4, 32, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        tr.capture(x, torch.zeros(1))
+    with pytest.raises(TypeError):
+        tr.ste_bwd(torch.zeros(32), torch.zeros(4, dtype=torch.uint8))
