@@ -83,7 +83,7 @@ size_t trace_tensor_scale_workspace_bytes(int64_t n) {
 
 trace_status trace_tensor_scale(const uint16_t* x, int64_t n, void* workspace, size_t workspace_bytes,
                                 float* ts_out, void* stream) {
-  if (!x || !workspace || !ts_out) return TRACE_E_NULL;
+  if (!workspace || !ts_out || (n > 0 && !x)) return TRACE_E_NULL;
   if (n < 0 || (n % 16) != 0 || n > (INT64_MAX / 4)) return TRACE_E_SHAPE;
   if (workspace_bytes < trace_tensor_scale_workspace_bytes(n)) return TRACE_E_SHAPE;
   if (!aligned(x, 16) || !aligned(workspace, 4) || !aligned(ts_out, 4)) return TRACE_E_ALIGN;
@@ -97,15 +97,15 @@ trace_status trace_tensor_scale(const uint16_t* x, int64_t n, void* workspace, s
 
 trace_status trace_capture(const uint16_t* x_roll, int64_t rows, int64_t cols, const float* ts,
                            uint8_t* scales, uint8_t* bits, uint8_t* codes, void* stream) {
-  if (!x_roll || !ts || !scales || !bits) return TRACE_E_NULL;
   uint64_t n = 0;
   if (trace_status st = site_size(rows, cols, &n)) return st;
+  if (n == 0) return TRACE_OK;
+  if (!x_roll || !ts || !scales || !bits) return TRACE_E_NULL;
   if (!aligned(x_roll, 16) || !aligned(ts, 4) || !aligned(bits, 2) || (codes && !aligned(codes, 8)))
     return TRACE_E_ALIGN;
   const Range outs[3] = {rng(scales, n / 16), rng(bits, n / 8), rng(codes, codes ? n / 2 : 0)};
   const Range ins[2] = {rng(x_roll, 2 * n), rng(ts, 4)};
   if (trace_status st = check_alias(outs, 3, ins, 2)) return st;
-  if (n == 0) return TRACE_OK;
   return hip_status(trace_host::launch_capture(x_roll, n / 16, ts, scales, bits, codes,
                                                static_cast<hipStream_t>(stream)));
 }
@@ -113,16 +113,16 @@ trace_status trace_capture(const uint16_t* x_roll, int64_t rows, int64_t cols, c
 static trace_status fakequant(bool guided, const uint16_t* x, int64_t rows, int64_t cols,
                               const uint8_t* scales, const float* ts, const uint8_t* bits, uint16_t* y,
                               uint8_t* mask, uint8_t* qcodes, void* stream) {
-  if (!x || !scales || !ts || (guided && !bits) || !y || !mask) return TRACE_E_NULL;
   uint64_t n = 0;
   if (trace_status st = site_size(rows, cols, &n)) return st;
+  if (n == 0) return TRACE_OK;
+  if (!x || !scales || !ts || (guided && !bits) || !y || !mask) return TRACE_E_NULL;
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ts, 4) || !aligned(mask, 2) ||
       (guided && !aligned(bits, 2)) || (qcodes && !aligned(qcodes, 8)))
     return TRACE_E_ALIGN;
   const Range outs[3] = {rng(y, 2 * n), rng(mask, n / 8), rng(qcodes, qcodes ? n / 2 : 0)};
   const Range ins[4] = {rng(x, 2 * n), rng(scales, n / 16), rng(ts, 4), rng(bits, guided ? n / 8 : 0)};
   if (trace_status st = check_alias(outs, 3, ins, 4, /*inplace_out=*/0, /*inplace_in=*/0)) return st;
-  if (n == 0) return TRACE_OK;
   return hip_status(trace_host::launch_fakequant(guided, x, n / 16, scales, ts, bits, y, mask, qcodes,
                                                  static_cast<hipStream_t>(stream)));
 }
@@ -141,14 +141,14 @@ trace_status trace_rne_fakequant_fwd(const uint16_t* x_train, int64_t rows, int6
 
 trace_status trace_ste_bwd(const uint16_t* grad_out, const uint8_t* mask, int64_t n, uint16_t* grad_in,
                            void* stream) {
-  if (!grad_out || !mask || !grad_in) return TRACE_E_NULL;
   if (n < 0 || (n % 16) != 0 || n > (INT64_MAX / 4)) return TRACE_E_SHAPE;
+  if (n == 0) return TRACE_OK;
+  if (!grad_out || !mask || !grad_in) return TRACE_E_NULL;
   if (!aligned(grad_out, 16) || !aligned(grad_in, 16) || !aligned(mask, 2)) return TRACE_E_ALIGN;
   const uint64_t un = (uint64_t)n;
   const Range outs[1] = {rng(grad_in, 2 * un)};
   const Range ins[2] = {rng(grad_out, 2 * un), rng(mask, un / 8)};
   if (trace_status st = check_alias(outs, 1, ins, 2, 0, 0)) return st;
-  if (n == 0) return TRACE_OK;
   return hip_status(trace_host::launch_ste_bwd(grad_out, mask, un / 16, grad_in,
                                                static_cast<hipStream_t>(stream)));
 }

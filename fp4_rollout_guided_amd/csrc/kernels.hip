@@ -5,8 +5,19 @@
 // contiguous bytes of bf16 (two 128-bit loads), its scale byte, and 16 bits of
 // every bit-plane (one 16-bit store).  Blocks never span lanes, so the block
 // amax needs no cross-lane traffic and every output byte has one writer.  A
-// 256-lane workgroup covers 4096 consecutive elements: its bit-plane, mask and
-// scale stores are whole 128-byte lines.
+// 256-lane workgroup covers 4096 consecutive elements per iteration, so its
+// bit-plane, mask and scale stores are whole 128-byte lines.  Workgroups loop
+// over the tensor (a grid of at most kMaxGroups workgroups), which amortizes
+// the per-workgroup scale table built in LDS.
+//
+// Every kernel has an exact fast path and an exact fallback.  The fast path
+// computes each quotient x / s with a double-word reciprocal and one
+// remainder correction (4 VALU ops, correctly rounded when the operands are in
+// range, see div_fast), and lets gfx950's FP4 / FP8 conversion instructions do
+// the grid rounding (their rounding was checked exhaustively against the
+// format definitions).  A lane whose block holds a NaN, an infinity, a
+// subnormal quotient, or a scale outside the fast range runs the fallback,
+// which evaluates the definitions directly with IEEE division.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -16,6 +27,13 @@
 namespace trace_dev {
 
 constexpr int kThreads = 256;
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// v_cmp_class mask: signalling/quiet NaN, +-infinity, +-subnormal.
+constexpr int kBadClass = 0x001 | 0x002 | 0x004 | 0x200 | 0x010 | 0x080;
 
 __device__ __forceinline__ void load_block(const uint4* __restrict__ x, uint64_t b, uint32_t (&w)[8]) {
   const uint4 v0 = x[2 * b];
@@ -30,10 +48,216 @@ __device__ __forceinline__ void store_block(uint4* __restrict__ y, uint64_t b, c
 }
 
 // ---------------------------------------------------------------------------
+// exact helpers of the fast path
+// ---------------------------------------------------------------------------
+
+// Decoded block scale of one E4M3FN byte under tensor scale ts, with the
+// reciprocals the fast division needs:
+//   rhi = RN(1/s)                       (the Markstein correction step),
+//   dhi = RD(1/s), dlo = RN((1 - s*dhi) * dhi) >= 0   (the first approximation;
+//        both parts non-negative, so x*dhi + x*dlo carries the sign of x even
+//        when x is a signed zero).
+// 1 - s*dhi is exact because dhi is within one ulp of 1/s.  Scales outside
+// [2^-96, 2^16] get dhi = NaN, so every quotient of the block is flagged and
+// the exact fallback runs.  Zero-scale bytes get s = 1, rhi = dhi = dlo = 0,
+// which maps every finite x to a zero of its own sign; rhi == 0 marks them.
+struct alignas(16) ScaleEntry {
+  float s, rhi, dhi, dlo;
+};
+
+__device__ __forceinline__ ScaleEntry make_scale_entry(uint32_t byte, float ts) {
+  const float s = e4m3_decode(byte) * ts;
+  if (s > 0.f && s <= 3.40282347e38f) {
+    const float rhi = 1.0f / s;
+    const float res = __builtin_fmaf(-s, rhi, 1.0f);  // exact: 1 - s*rhi
+    const float dhi = res < 0.f ? __uint_as_float(__float_as_uint(rhi) - 1u) : rhi;
+    const float dlo = __builtin_fmaf(-s, dhi, 1.0f) * dhi;
+    const bool fast = (s >= 0x1p-96f) && (s <= 0x1p16f);
+    return ScaleEntry{s, rhi, fast ? dhi : __uint_as_float(0x7fc00000u), dlo};
+  }
+  return ScaleEntry{1.f, 0.f, 0.f, 0.f};
+}
+
+// fl32(x / s).  q1 = RN(x*dhi + RN(x*dlo)) is within 0.5 ulp + 2^-23 ulp of
+// x/s, hence faithful; r = s*q1 - x is then exact and RN(q1 - r*rhi) with
+// rhi = RN(1/s) is the correctly rounded quotient (Markstein's theorem).
+// Preconditions: s in [2^-96, 2^16] (else dhi is NaN) and q1 normal or zero;
+// a subnormal, infinite or NaN q1 sets `bad`.  A zero quotient keeps the
+// sign of x.
+__device__ __forceinline__ float div_fast(float x, const ScaleEntry& e, bool& bad) {
+  const float q1 = __builtin_fmaf(x, e.dhi, x * e.dlo);
+  bad |= __builtin_amdgcn_class(q1, kBadClass);
+  const float r = __builtin_fmaf(q1, e.s, -x);
+  return __builtin_fmaf(-r, e.rhi, q1);
+}
+
+// The same with compile-time/uniform operands: fl32(a / d) for a >= 2^-100.
+__device__ __forceinline__ float div_fast_u(float a, float d, float rhi, float rlo) {
+  const float q1 = __builtin_fmaf(a, rhi, a * rlo);
+  const float r = __builtin_fmaf(q1, d, -a);
+  return __builtin_fmaf(-r, rhi, q1);
+}
+
+// Toward-zero E2M1 codes of two values into byte SEL of acc: the stochastic-
+// rounding conversion with a zero random operand truncates.  Issued as inline
+// asm with acc tied to the destination: the compiler's builtin for this
+// instruction does not keep the other bytes of the destination (the
+// round-to-nearest builtin does).
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4_rtz_at(uint32_t acc, float a, float b) {
+  const f32x2 v = {a, b};
+  asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, 0, 1.0 op_sel:[0,0,%2,%3]"
+      : "+v"(acc)
+      : "v"(v), "n"(SEL & 1), "n"(SEL >> 1));
+  return acc;
+}
+
+// E2M1 codes (sign << 3 | index) of two values, written into byte `sel` of
+// `acc`: round to nearest even (saturating at 6) or toward zero.
+#define FP4_RNE(acc, a, b, sel) __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((acc), (a), (b), 1.0f, (sel))
+#define FP4_RTZ(acc, a, b, sel) fp4_rtz_at<(sel)>((acc), (a), (b))
+// Codes of the even (off = 0) or odd (off = 1) elements of a 16-value block,
+// nibble k holding element 2k + off.  The byte selector must be a literal.
+#define FP4_PACK8(CVT, dst, v, off)                 \
+  do {                                              \
+    dst = CVT(dst, (v)[0 + (off)], (v)[2 + (off)], 0);   \
+    dst = CVT(dst, (v)[4 + (off)], (v)[6 + (off)], 1);   \
+    dst = CVT(dst, (v)[8 + (off)], (v)[10 + (off)], 2);  \
+    dst = CVT(dst, (v)[12 + (off)], (v)[14 + (off)], 3); \
+  } while (0)
+
+// Bit 0 of the 16 nibbles of E (elements 0,2,..,14) and O (1,3,..,15),
+// gathered into a 16-bit word in element order.
+__device__ __forceinline__ uint32_t gather_parity(uint32_t E, uint32_t O) {
+  const uint32_t X = ((O << 1) & 0x22222222u) | (E & ~0x22222222u);
+  const uint32_t Y = ((X >> 2) & 0x0C0C0C0Cu) | (X & ~0x0C0C0C0Cu);
+  const uint32_t Z = ((Y >> 4) & 0x00F000F0u) | (Y & ~0x00F000F0u);
+  return __builtin_amdgcn_perm(Z, Z, 0x0C0C0200u);
+}
+
+// Inverse of gather_parity: bit j of a 16-bit word W to bit 0 of nibble j/2
+// of the result (even j) or bit 1 of that nibble (odd j); other bits junk.
+__device__ __forceinline__ uint32_t spread_bits(uint32_t W) {
+  const uint32_t Z = __builtin_amdgcn_perm(W, W, 0x0C010C00u);
+  const uint32_t Y = ((Z << 4) & 0x0F000F00u) | (Z & ~0x0F000F00u);
+  return ((Y << 2) & 0x30303030u) | (Y & ~0x30303030u);
+}
+
+// y for elements 4K..4K+3 from byte K of the even / odd code dwords:
+// bf16_RNE(fl32(s * q)) with q the decoded codeword (sign included).
+template <int K>
+__device__ __forceinline__ void decode_scaled_pair(uint32_t QE, uint32_t QO, float s, uint32_t (&out)[8]) {
+  const f32x2 ge = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(QE, 1.0f, K);  // elements 4K, 4K+2
+  const f32x2 go = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(QO, 1.0f, K);  // elements 4K+1, 4K+3
+  const bf16x2 p0 = __builtin_convertvector((f32x2){s * ge.x, s * go.x}, bf16x2);
+  const bf16x2 p1 = __builtin_convertvector((f32x2){s * ge.y, s * go.y}, bf16x2);
+  __builtin_memcpy(&out[2 * K], &p0, 4);
+  __builtin_memcpy(&out[2 * K + 1], &p1, 4);
+}
+
+// Element-order nibble codes from the even/odd nibble dwords.
+__device__ __forceinline__ void interleave_codes(uint32_t E, uint32_t O, uint32_t& c0, uint32_t& c1) {
+  c0 = 0; c1 = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t ce = (E >> (4 * k)) & 15u, co = (O >> (4 * k)) & 15u;
+    const uint32_t pair = ce | (co << 4);
+    if (k < 4) c0 |= pair << (8 * k); else c1 |= pair << (8 * (k - 4));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// exact fallbacks: the definitions evaluated directly (IEEE division)
+// ---------------------------------------------------------------------------
+
+// These run only for the rare lanes the fast path rejects, so they favour a
+// small register footprint (one element at a time, 16-bit accesses) over
+// speed.  In-place use (y == x) is safe: each element is read before it is
+// written and the fast path stored nothing for the lane.
+__device__ __noinline__ void capture_block_exact(const uint4* __restrict__ x4, uint64_t b, float ts,
+                                                 uint8_t* __restrict__ scales, uint16_t* __restrict__ bits,
+                                                 uint2* __restrict__ codes) {
+  const uint16_t* x = reinterpret_cast<const uint16_t*>(x4) + 16 * b;
+  float amax = 0.f;
+#pragma unroll 1
+  for (int j = 0; j < kBlock; ++j) {
+    const float a = fabsf(__uint_as_float((uint32_t)x[j] << 16));
+    if (a > amax) amax = a;  // NaN compares false: ignored
+  }
+  uint32_t sb = 0;
+  if (ts > 0.f && ts <= 3.40282347e38f) sb = e4m3_encode_sat((amax / 6.f) / ts);
+  const float s = e4m3_decode(sb) * ts;
+  const bool valid = s > 0.f && s <= 3.40282347e38f;
+  uint32_t bitword = 0;
+  uint64_t cw = 0;
+#pragma unroll 1
+  for (int j = 0; j < kBlock; ++j) {
+    const float xv = __uint_as_float((uint32_t)x[j] << 16);
+    uint32_t sign = __float_as_uint(xv) >> 31;
+    uint32_t idx = 0;
+    if (is_nan_f(xv)) {
+      sign = 0;
+    } else if (valid) {
+      idx = e2m1_rne_index(fminf(fabsf(xv / s), 6.f));
+    }
+    bitword |= (idx & 1u) << j;
+    cw |= (uint64_t)((sign << 3) | idx) << (4 * j);
+  }
+  scales[b] = (uint8_t)sb;
+  bits[b] = (uint16_t)bitword;
+  if (codes) codes[b] = make_uint2((uint32_t)cw, (uint32_t)(cw >> 32));
+}
+
+__device__ __noinline__ void fakequant_block_exact(bool guided, const uint4* __restrict__ x4, uint64_t b,
+                                                   uint32_t sbyte, float ts, uint32_t cached,
+                                                   uint4* __restrict__ y4, uint16_t* __restrict__ mask,
+                                                   uint2* __restrict__ qcodes) {
+  const float s = e4m3_decode(sbyte) * ts;
+  const bool valid = s > 0.f && s <= 3.40282347e38f;
+  const uint16_t* x = reinterpret_cast<const uint16_t*>(x4) + 16 * b;
+  uint16_t* y = reinterpret_cast<uint16_t*>(y4) + 16 * b;
+  uint32_t maskword = 0;
+  uint64_t cw = 0;
+#pragma unroll 1
+  for (int j = 0; j < kBlock; ++j) {
+    const float xv = __uint_as_float((uint32_t)x[j] << 16);
+    uint32_t sign = __float_as_uint(xv) >> 31;
+    uint32_t idx = 0, mk = 0;
+    float yv;
+    if (is_nan_f(xv)) {
+      sign = 0;
+      yv = 0.f;
+    } else if (!valid) {
+      yv = sign ? -0.f : 0.f;
+    } else {
+      const float zr = xv / s;
+      mk = fabsf(zr) <= 6.f ? 1u : 0u;
+      const float a = fminf(fabsf(zr), 6.f);
+      if (guided) {
+        const uint32_t lo = e2m1_floor_index(a);
+        const bool exact = (a == e2m1_mag(lo));
+        idx = (exact || ((lo & 1u) == ((cached >> j) & 1u))) ? lo : lo + 1;
+      } else {
+        idx = e2m1_rne_index(a);
+      }
+      const float q = e2m1_mag(idx);
+      yv = s * (sign ? -q : q);
+    }
+    maskword |= mk << j;
+    y[j] = (uint16_t)bf16_rne_bits(yv);
+    cw |= (uint64_t)((sign << 3) | idx) << (4 * j);
+  }
+  mask[b] = (uint16_t)maskword;
+  if (qcodes) qcodes[b] = make_uint2((uint32_t)cw, (uint32_t)(cw >> 32));
+}
+
+// ---------------------------------------------------------------------------
 // tensor amax: per-workgroup maxima of the bf16 magnitude bits (NaN excluded),
-// then one workgroup folds them and forms ts = fl32(amax / 2688).
-// Integer maxima over magnitude bits order non-NaN bf16 values exactly as
-// their absolute values.
+// then one workgroup folds them and forms ts = fl32(amax / 2688).  Integer
+// maxima over magnitude bits order non-NaN bf16 values as their absolute
+// values do.  NaN halves (magnitude > 0x7f80) are mapped below every other
+// value: m + 0x7f stays below 0x8000 exactly for non-NaN halves, so a signed
+// 16-bit maximum of m + 0x7f ignores NaN.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
@@ -53,23 +277,29 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v) {
   return v;
 }
 
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
 __global__ __launch_bounds__(kThreads) void amax_partial_kernel(const uint4* __restrict__ x,
                                                                 uint64_t nblocks,
                                                                 uint32_t* __restrict__ partial) {
-  uint32_t best = 0;
+  s16x2 best = {0, 0};  // holds max(m + 0x7f) over non-NaN halves, >= 0x7f once any was seen
   const uint64_t stride = (uint64_t)gridDim.x * kThreads;
   for (uint64_t b = (uint64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks; b += stride) {
     uint32_t w[8];
     load_block(x, b, w);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const uint32_t lo = w[k] & 0x7fffu, hi = (w[k] >> 16) & 0x7fffu;
-      if (lo <= 0x7f80u) best = max(best, lo);
-      if (hi <= 0x7f80u) best = max(best, hi);
+      const uint32_t m = (w[k] & 0x7fff7fffu) + 0x007f007fu;  // no carry between halves
+      s16x2 v;
+      __builtin_memcpy(&v, &m, 4);
+      best = __builtin_elementwise_max(best, v);
     }
   }
-  best = block_max_u32(best);
-  if (threadIdx.x == 0) partial[blockIdx.x] = best;
+  const int lo = best.x, hi = best.y;
+  const int m = lo > hi ? lo : hi;
+  uint32_t r = m > 0x7f ? (uint32_t)(m - 0x7f) : 0u;
+  r = block_max_u32(r);
+  if (threadIdx.x == 0) partial[blockIdx.x] = r;
 }
 
 __global__ __launch_bounds__(kThreads) void amax_finalize_kernel(const uint32_t* __restrict__ partial,
@@ -88,46 +318,72 @@ __global__ __launch_bounds__(kThreads) void capture_kernel(const uint4* __restri
                                                            uint8_t* __restrict__ scales,
                                                            uint16_t* __restrict__ bits,
                                                            uint2* __restrict__ codes) {
-  const uint64_t b = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (b >= nblocks) return;
+  __shared__ ScaleEntry tab[256];
   const float ts = *ts_ptr;
-  uint32_t w[8];
-  load_block(x, b, w);
+  tab[threadIdx.x] = make_scale_entry(threadIdx.x, ts);
+  __syncthreads();
 
-  float amax = 0.f;
-#pragma unroll
-  for (int j = 0; j < kBlock; ++j) {
-    const float a = fabsf(block_elem(w, j));
-    if (a > amax) amax = a;  // NaN compares false: ignored
-  }
-  uint32_t sb = 0;
-  if (ts > 0.f && ts <= 3.40282347e38f) sb = e4m3_encode_sat((amax / 6.f) / ts);
-  const float s = e4m3_decode(sb) * ts;
-  const bool valid = s > 0.f && s <= 3.40282347e38f;
+  const bool ts_valid = ts > 0.f && ts <= 3.40282347e38f;
+  const bool ts_slow = ts_valid && !(ts >= 0x1p-100f && ts <= 0x1p100f);
+  const float rthi = 1.0f / (ts_valid ? ts : 1.f);
+  const float rtlo = __builtin_fmaf(-(ts_valid ? ts : 1.f), rthi, 1.0f) * rthi;
+  const float lim = 512.f * ts;                    // v1 beyond lim gives v > 448: saturates
+  const float r6hi = 1.0f / 6.0f;
+  const float r6lo = __builtin_fmaf(-6.0f, r6hi, 1.0f) * r6hi;
 
-  uint32_t bitword = 0, c0 = 0, c1 = 0;
+  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+  for (uint64_t b = (uint64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks; b += stride) {
+    uint32_t w[8];
+    load_block(x, b, w);
+
+    // block amax on packed bf16 magnitudes
+    u16x2 mx;
+    {
+      uint32_t m0 = w[0] & 0x7fff7fffu;
+      __builtin_memcpy(&mx, &m0, 4);
 #pragma unroll
-  for (int j = 0; j < kBlock; ++j) {
-    const float xv = block_elem(w, j);
-    uint32_t sign = __float_as_uint(xv) >> 31;
-    uint32_t idx = 0;
-    if (is_nan_f(xv)) {
-      sign = 0;
-    } else if (valid) {
-      const float z = xv / s;
-      idx = e2m1_rne_index(fminf(fabsf(z), 6.f));
+      for (int k = 1; k < 8; ++k) {
+        const uint32_t mk = w[k] & 0x7fff7fffu;
+        u16x2 v;
+        __builtin_memcpy(&v, &mk, 4);
+        mx = __builtin_elementwise_max(mx, v);
+      }
     }
-    bitword |= (idx & 1u) << j;
-    const uint32_t code = (sign << 3) | idx;
-    if (j < 8) c0 |= code << (4 * j); else c1 |= code << (4 * (j - 8));
+    const uint32_t amax_bits = mx.x > mx.y ? mx.x : mx.y;
+    const float amax = __uint_as_float(amax_bits << 16);
+    // a zero block, or amax >= 2^-100 (bf16 bits 0x0d80) keeps the two divisions exact
+    bool bad = ts_slow || (amax_bits - 1u) < 0x0d7fu;
+
+    const float v1 = __builtin_amdgcn_fmed3f(div_fast_u(amax, 6.0f, r6hi, r6lo), 0.f, lim);
+    const float v = div_fast_u(v1, ts, rthi, rtlo);
+    uint32_t sb = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(v, 0.f, 448.f), 0.f, 0, false);
+    sb = ts_valid ? sb : 0u;
+
+    const ScaleEntry e = tab[sb];
+
+    float q[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) q[j] = div_fast(block_elem(w, j), e, bad);
+
+    uint32_t E = 0, O = 0;
+    FP4_PACK8(FP4_RNE, E, q, 0);
+    FP4_PACK8(FP4_RNE, O, q, 1);
+    if (bad) {
+      capture_block_exact(x, b, ts, scales, bits, codes);
+    } else {
+      scales[b] = (uint8_t)sb;
+      bits[b] = (uint16_t)gather_parity(E, O);
+      if (codes) {
+        uint32_t c0, c1;
+        interleave_codes(E, O, c0, c1);
+        codes[b] = make_uint2(c0, c1);
+      }
+    }
   }
-  scales[b] = (uint8_t)sb;
-  bits[b] = (uint16_t)bitword;
-  if (codes) codes[b] = make_uint2(c0, c1);
 }
 
 // ---------------------------------------------------------------------------
-// fake-quant forward (guided or plain RNE) and STE backward
+// fake-quant forward (guided or plain RNE)
 // ---------------------------------------------------------------------------
 template <bool kGuided>
 __global__ __launch_bounds__(kThreads) void fakequant_kernel(const uint4* __restrict__ x, uint64_t nblocks,
@@ -137,68 +393,99 @@ __global__ __launch_bounds__(kThreads) void fakequant_kernel(const uint4* __rest
                                                              uint4* __restrict__ y,
                                                              uint16_t* __restrict__ mask,
                                                              uint2* __restrict__ qcodes) {
-  const uint64_t b = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (b >= nblocks) return;
+  __shared__ ScaleEntry tab[256];
   const float ts = *ts_ptr;
-  const float s = e4m3_decode(scales[b]) * ts;
-  const bool valid = s > 0.f && s <= 3.40282347e38f;
-  const uint32_t cached = kGuided ? (uint32_t)bits[b] : 0u;
-  uint32_t w[8];
-  load_block(x, b, w);
+  tab[threadIdx.x] = make_scale_entry(threadIdx.x, ts);
+  __syncthreads();
 
-  uint32_t out[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  uint32_t maskword = 0, c0 = 0, c1 = 0;
+  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+  for (uint64_t b = (uint64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks; b += stride) {
+    const uint32_t sbyte = scales[b];
+    const uint32_t cached = kGuided ? (uint32_t)bits[b] : 0u;
+    uint32_t w[8];
+    load_block(x, b, w);
+    const ScaleEntry e = tab[sbyte];
+    bool bad = false;
+
+    float q[16];
 #pragma unroll
-  for (int j = 0; j < kBlock; ++j) {
-    const float xv = block_elem(w, j);
-    uint32_t sign = __float_as_uint(xv) >> 31;
-    uint32_t idx = 0, mk = 0;
-    float yv;
-    if (is_nan_f(xv)) {
-      sign = 0;
-      yv = 0.f;
-    } else if (!valid) {
-      yv = sign ? -0.f : 0.f;
+    for (int j = 0; j < 16; ++j) q[j] = div_fast(block_elem(w, j), e, bad);
+
+    // clip mask: sign bit of 6 - |q| is set exactly when |q| > 6
+    uint32_t clip = 0;
+#pragma unroll
+    for (int j = 15; j >= 0; --j)
+      clip = __builtin_amdgcn_alignbit(clip, __float_as_uint(6.0f - fabsf(q[j])), 31);
+    const uint32_t maskword = (e.rhi != 0.f) ? (~clip & 0xffffu) : 0u;
+
+    float qc[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) qc[j] = __builtin_amdgcn_fmed3f(q[j], -6.0f, 6.0f);
+
+    uint32_t QE = 0, QO = 0;
+    if (kGuided) {
+      // floor codes of q and of its predecessor toward zero: equal exactly when
+      // q lies strictly inside a bracket, so the upper endpoint is floor + 1
+      float pv[16];  // predecessors toward zero (a NaN for +-0, whose floor code differs)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) pv[j] = __uint_as_float(__float_as_uint(qc[j]) - 1u);
+      uint32_t FE = 0, FO = 0, PE = 0, PO = 0;
+      FP4_PACK8(FP4_RTZ, FE, qc, 0);
+      FP4_PACK8(FP4_RTZ, FO, qc, 1);
+      FP4_PACK8(FP4_RTZ, PE, pv, 0);
+      FP4_PACK8(FP4_RTZ, PO, pv, 1);
+      const uint32_t C = spread_bits(cached);  // bit 0 / bit 1 of nibble k: cached bit of 2k / 2k+1
+      uint32_t t = FE ^ PE;
+      t |= t >> 2;
+      t |= t >> 1;
+      QE = FE + (~t & (FE ^ C) & 0x11111111u);
+      t = FO ^ PO;
+      t |= t >> 2;
+      t |= t >> 1;
+      QO = FO + (~t & (FO ^ (C >> 1)) & 0x11111111u);
     } else {
-      const float zr = xv / s;
-      mk = fabsf(zr) <= 6.f ? 1u : 0u;
-      const float a = fminf(fabsf(zr), 6.f);
-      if (kGuided) {
-        const uint32_t lo = e2m1_floor_index(a);
-        const bool exact = (a == e2m1_mag(lo));
-        const uint32_t c = (cached >> j) & 1u;
-        idx = (exact || ((lo & 1u) == c)) ? lo : lo + 1;
-      } else {
-        idx = e2m1_rne_index(a);
-      }
-      const float q = e2m1_mag(idx);
-      yv = s * (sign ? -q : q);
+      FP4_PACK8(FP4_RNE, QE, qc, 0);
+      FP4_PACK8(FP4_RNE, QO, qc, 1);
     }
-    maskword |= mk << j;
-    out[j >> 1] |= bf16_rne_bits(yv) << (16 * (j & 1));
-    const uint32_t code = (sign << 3) | idx;
-    if (j < 8) c0 |= code << (4 * j); else c1 |= code << (4 * (j - 8));
+
+    if (bad) {
+      fakequant_block_exact(kGuided, x, b, sbyte, ts, cached, y, mask, qcodes);
+    } else {
+      uint32_t out[8];
+      decode_scaled_pair<0>(QE, QO, e.s, out);
+      decode_scaled_pair<1>(QE, QO, e.s, out);
+      decode_scaled_pair<2>(QE, QO, e.s, out);
+      decode_scaled_pair<3>(QE, QO, e.s, out);
+      store_block(y, b, out);
+      mask[b] = (uint16_t)maskword;
+      if (qcodes) {
+        uint32_t c0, c1;
+        interleave_codes(QE, QO, c0, c1);
+        qcodes[b] = make_uint2(c0, c1);
+      }
+    }
   }
-  store_block(y, b, out);
-  mask[b] = (uint16_t)maskword;
-  if (qcodes) qcodes[b] = make_uint2(c0, c1);
 }
 
+// ---------------------------------------------------------------------------
+// STE backward
+// ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void ste_bwd_kernel(const uint4* __restrict__ g, uint64_t nblocks,
                                                            const uint16_t* __restrict__ mask,
                                                            uint4* __restrict__ gin) {
-  const uint64_t b = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (b >= nblocks) return;
-  const uint32_t m = mask[b];
-  uint32_t w[8];
-  load_block(g, b, w);
+  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+  for (uint64_t b = (uint64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks; b += stride) {
+    const uint32_t m = mask[b];
+    uint32_t w[8];
+    load_block(g, b, w);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const uint32_t keep = (((m >> (2 * k)) & 1u) ? 0x0000ffffu : 0u) |
-                          (((m >> (2 * k + 1)) & 1u) ? 0xffff0000u : 0u);
-    w[k] &= keep;
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t keep = (((m >> (2 * k)) & 1u) ? 0x0000ffffu : 0u) |
+                            (((m >> (2 * k + 1)) & 1u) ? 0xffff0000u : 0u);
+      w[k] &= keep;
+    }
+    store_block(gin, b, w);
   }
-  store_block(gin, b, w);
 }
 
 }  // namespace trace_dev
@@ -210,7 +497,10 @@ namespace trace_host {
 
 using namespace trace_dev;
 
-static unsigned grid_for(uint64_t nblocks) { return (unsigned)((nblocks + kThreads - 1) / kThreads); }
+static unsigned grid_for(uint64_t nblocks) {
+  const uint64_t g = (nblocks + kThreads - 1) / kThreads;
+  return (unsigned)(g < kMaxGroups ? g : kMaxGroups);
+}
 
 uint32_t amax_partial_count(uint64_t nblocks) {
   const uint64_t g = (nblocks + kThreads - 1) / kThreads;

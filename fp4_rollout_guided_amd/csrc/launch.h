@@ -9,6 +9,9 @@ namespace trace_host {
 
 // Upper bound on amax partial workgroups (and on workspace words).
 constexpr uint32_t kAmaxMaxGroups = 2048;
+// Upper bound on the grid of the streaming kernels; their workgroups loop
+// over the tensor.
+constexpr uint32_t kMaxGroups = 2048;
 
 uint32_t amax_partial_count(uint64_t nblocks);
 

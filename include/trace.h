@@ -47,7 +47,8 @@
  *   point of the call.
  * - Errors: entry points return a trace_status.  Arguments are validated
  *   before any HIP call; on a validation error nothing is enqueued.
- *   n == 0 is a successful no-op (trace_tensor_scale then writes ts = 0).
+ *   n == 0 is a successful no-op that enqueues nothing and accepts NULL data
+ *   pointers (trace_tensor_scale still writes ts = 0 to ts_out).
  * - Alignment: bf16 tensors need 16-byte alignment, bit-planes and masks
  *   2-byte alignment, code arrays 8-byte alignment; scale bytes have none.
  * - Aliasing: outputs must not overlap inputs, except exact in-place use

@@ -82,9 +82,11 @@ def test_capture_validation():
     assert f(P(x), 4, 32, P(ts), P(sc), P(sc + 4), None, None) == E_ALIAS     # bits over scales
     assert f(P(x), 4, 32, P(ts), P(sc), P(bt), P(bt + 8), None) == E_ALIAS    # codes over bits
     assert f(P(x), 4, 32, P(sc + 4), P(sc), P(bt), None, None) == E_ALIAS     # scales over ts
-    # empty tensors are a no-op that makes no HIP call
+    # empty tensors are a no-op that makes no HIP call and accepts NULL buffers
     assert f(P(x), 0, 32, P(ts), P(sc), P(bt), None, None) == OK
     assert f(P(x), 7, 0, P(ts), P(sc), P(bt), None, None) == OK
+    assert f(None, 0, 32, None, None, None, None, None) == OK
+    assert f(None, 0, 24, None, None, None, None, None) == E_SHAPE
 
 
 @pytest.mark.parametrize("guided", [True, False])
@@ -121,6 +123,7 @@ def test_fakequant_validation(guided):
     assert call(qc=y + 64) == E_ALIAS         # qcodes inside y
     assert call(mk=y + 16) == E_ALIAS
     assert call(rows=0) == OK
+    assert call(rows=0, x=None, y=None, mk=None, sc=None) == OK
     assert call(rows=0, y=x) == OK            # exact in-place is allowed
 
 
@@ -138,6 +141,7 @@ def test_ste_validation():
     assert f(P(g), P(m), 64, P(m - 32), None) == E_ALIAS
     assert f(P(g), P(m), 0, P(gi), None) == OK
     assert f(P(g), P(m), 0, P(g), None) == OK
+    assert f(None, None, 0, None, None) == OK
 
 
 def test_binding_refuses_host_tensors():
