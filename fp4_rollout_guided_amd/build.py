@@ -4,7 +4,9 @@
 
 Flags that matter for exactness: no FP contraction (every fused multiply-add
 in the kernels is written out), correctly rounded fp32 division, fp32
-denormals kept, no fast-math.  Packed-fp32 instructions are disabled.
+denormals kept, no fast-math.  Packed-fp32 instructions are disabled.  SLP
+vectorization is off: it turns the per-element flag tests into vector-of-bool
+packing code.
 """
 import os
 import shutil
@@ -30,6 +32,7 @@ FLAGS = [
     "-fno-fast-math",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-fno-gpu-flush-denormals-to-zero",
+    "-fno-slp-vectorize",
     "-Wall",
     "-Wno-unused-command-line-argument",
 ]

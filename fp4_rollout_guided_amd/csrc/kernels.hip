@@ -6,9 +6,9 @@
 // every bit-plane (one 16-bit store).  Blocks never span lanes, so the block
 // amax needs no cross-lane traffic and every output byte has one writer.  A
 // 256-lane workgroup covers 4096 consecutive elements per iteration, so its
-// bit-plane, mask and scale stores are whole 128-byte lines.  Workgroups loop
-// over the tensor (a grid of at most kMaxGroups workgroups), which amortizes
-// the per-workgroup scale table built in LDS.
+// bit-plane, mask and scale stores are whole 128-byte lines.  The grid covers
+// the tensor once (one tile per workgroup); the kernels keep a grid-stride
+// loop only for grids larger than the launch limit.
 //
 // Every kernel has an exact fast path and an exact fallback.  The fast path
 // computes each quotient x / s with a double-word reciprocal and one
@@ -32,8 +32,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-// v_cmp_class mask: signalling/quiet NaN, +-infinity, +-subnormal.
-constexpr int kBadClass = 0x001 | 0x002 | 0x004 | 0x200 | 0x010 | 0x080;
+// v_cmp_class mask: signalling/quiet NaN and +-infinity.
+constexpr int kBadClass = 0x001 | 0x002 | 0x004 | 0x200;
 
 __device__ __forceinline__ void load_block(const uint4* __restrict__ x, uint64_t b, uint32_t (&w)[8]) {
   const uint4 v0 = x[2 * b];
@@ -81,12 +81,18 @@ __device__ __forceinline__ ScaleEntry make_scale_entry(uint32_t byte, float ts) 
 // fl32(x / s).  q1 = RN(x*dhi + RN(x*dlo)) is within 0.5 ulp + 2^-23 ulp of
 // x/s, hence faithful; r = s*q1 - x is then exact and RN(q1 - r*rhi) with
 // rhi = RN(1/s) is the correctly rounded quotient (Markstein's theorem).
-// Preconditions: s in [2^-96, 2^16] (else dhi is NaN) and q1 normal or zero;
-// a subnormal, infinite or NaN q1 sets `bad`.  A zero quotient keeps the
-// sign of x.
+// This holds whenever the quotient can reach a rounding decision of the
+// E2M1 grid (|x/s| >= 2^-3 with s >= 2^-96 puts x above 2^-99, where the
+// remainder is representable).  Below that, a remainder that falls into the
+// subnormal range perturbs q by at most 2^-150 / s, i.e. by a relative
+// 2^-17 of |x/s| for every nonzero bf16 x when s <= 2^16: q keeps the sign
+// of x, stays nonzero, and stays below every decision threshold.  A zero x
+// gives a zero of the same sign.  NaN or infinite x, and quotients too large
+// for binary32, make q1 NaN or infinite; the caller flags those.
+template <bool kCheck>
 __device__ __forceinline__ float div_fast(float x, const ScaleEntry& e, bool& bad) {
   const float q1 = __builtin_fmaf(x, e.dhi, x * e.dlo);
-  bad |= __builtin_amdgcn_class(q1, kBadClass);
+  if (kCheck) bad |= __builtin_amdgcn_class(q1, kBadClass);
   const float r = __builtin_fmaf(q1, e.s, -x);
   return __builtin_fmaf(-r, e.rhi, q1);
 }
@@ -318,11 +324,7 @@ __global__ __launch_bounds__(kThreads) void capture_kernel(const uint4* __restri
                                                            uint8_t* __restrict__ scales,
                                                            uint16_t* __restrict__ bits,
                                                            uint2* __restrict__ codes) {
-  __shared__ ScaleEntry tab[256];
   const float ts = *ts_ptr;
-  tab[threadIdx.x] = make_scale_entry(threadIdx.x, ts);
-  __syncthreads();
-
   const bool ts_valid = ts > 0.f && ts <= 3.40282347e38f;
   const bool ts_slow = ts_valid && !(ts >= 0x1p-100f && ts <= 0x1p100f);
   const float rthi = 1.0f / (ts_valid ? ts : 1.f);
@@ -351,19 +353,21 @@ __global__ __launch_bounds__(kThreads) void capture_kernel(const uint4* __restri
     }
     const uint32_t amax_bits = mx.x > mx.y ? mx.x : mx.y;
     const float amax = __uint_as_float(amax_bits << 16);
-    // a zero block, or amax >= 2^-100 (bf16 bits 0x0d80) keeps the two divisions exact
-    bool bad = ts_slow || (amax_bits - 1u) < 0x0d7fu;
+    // a zero block, or amax >= 2^-100 (bf16 bits 0x0d80) keeps the two divisions
+    // exact; a NaN or infinite element shows as amax_bits >= 0x7f80
+    bool bad = ts_slow || (amax_bits - 1u) < 0x0d7fu || amax_bits >= 0x7f80u;
 
     const float v1 = __builtin_amdgcn_fmed3f(div_fast_u(amax, 6.0f, r6hi, r6lo), 0.f, lim);
     const float v = div_fast_u(v1, ts, rthi, rtlo);
     uint32_t sb = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(v, 0.f, 448.f), 0.f, 0, false);
     sb = ts_valid ? sb : 0u;
 
-    const ScaleEntry e = tab[sb];
+    const ScaleEntry e = make_scale_entry(sb, ts);
+    bad |= !(e.dhi == e.dhi);  // scale outside the fast range
 
     float q[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) q[j] = div_fast(block_elem(w, j), e, bad);
+    for (int j = 0; j < 16; ++j) q[j] = div_fast<false>(block_elem(w, j), e, bad);
 
     uint32_t E = 0, O = 0;
     FP4_PACK8(FP4_RNE, E, q, 0);
@@ -393,23 +397,19 @@ __global__ __launch_bounds__(kThreads) void fakequant_kernel(const uint4* __rest
                                                              uint4* __restrict__ y,
                                                              uint16_t* __restrict__ mask,
                                                              uint2* __restrict__ qcodes) {
-  __shared__ ScaleEntry tab[256];
   const float ts = *ts_ptr;
-  tab[threadIdx.x] = make_scale_entry(threadIdx.x, ts);
-  __syncthreads();
-
   const uint64_t stride = (uint64_t)gridDim.x * kThreads;
   for (uint64_t b = (uint64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks; b += stride) {
     const uint32_t sbyte = scales[b];
     const uint32_t cached = kGuided ? (uint32_t)bits[b] : 0u;
     uint32_t w[8];
     load_block(x, b, w);
-    const ScaleEntry e = tab[sbyte];
-    bool bad = false;
+    const ScaleEntry e = make_scale_entry(sbyte, ts);
+    bool bad = false;  // set by a NaN / infinite quotient, or a scale outside the fast range (dhi NaN)
 
     float q[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) q[j] = div_fast(block_elem(w, j), e, bad);
+    for (int j = 0; j < 16; ++j) q[j] = div_fast<true>(block_elem(w, j), e, bad);
 
     // clip mask: sign bit of 6 - |q| is set exactly when |q| > 6
     uint32_t clip = 0;

@@ -9,9 +9,14 @@ namespace trace_host {
 
 // Upper bound on amax partial workgroups (and on workspace words).
 constexpr uint32_t kAmaxMaxGroups = 2048;
-// Upper bound on the grid of the streaming kernels; their workgroups loop
-// over the tensor.
-constexpr uint32_t kMaxGroups = 2048;
+// Upper bound on the grid of the streaming kernels (one 4096-element tile per
+// workgroup below it; workgroups loop over the tensor beyond it).  A grid
+// that covers the tensor once streams faster than a persistent grid, whose
+// loop makes each tile's loads wait behind the previous tile's stores.
+#ifndef TRACE_MAX_GROUPS
+#define TRACE_MAX_GROUPS (1u << 30)
+#endif
+constexpr uint32_t kMaxGroups = TRACE_MAX_GROUPS;
 
 uint32_t amax_partial_count(uint64_t nblocks);
 

@@ -119,7 +119,7 @@ def test_tensor_scale_cases(device):
     assert out.item() == 0.0
 
 
-@pytest.mark.parametrize("ts", [1.0, 0.0123456, 3.0e-39, 1.0e30, 2.0 ** -100])
+@pytest.mark.parametrize("ts", [1.0, 0.0123456, 3.0e-39, 1.0e30, 2.0 ** -100, 146.0, 2.0 ** -90])
 def test_fwd_exhaustive_bf16_by_scale_byte(device, ts):
     """Every bf16 pattern as x_train under every scale byte (0x00..0xFF),
     for guided (random cached bits) and RNE forward."""
@@ -167,6 +167,38 @@ def test_capture_exhaustive_block_amax(device, ts):
     want = oracle.capture(xr, tsf, with_codes=True)
     assert_same({"scales": to_np_u8(scales), "bits": to_np_u8(bits), "codes": to_np_u8(codes)}, want,
                 ctx=f"capture ts={ts}")
+
+
+@pytest.mark.parametrize("ts", [1.0, 146.0, 2.0 ** -88, 0.0123456])
+def test_tiny_elements_beside_large_ones(device, ts):
+    """Blocks holding one large element (setting the block scale anywhere in
+    the E4M3 range) and otherwise bf16 subnormals, tiny normals, signed zeros
+    and small values: capture codes and guided / RNE outputs keep the sign
+    and the zero-ness of every tiny quotient."""
+    import fp4_rollout_guided_amd as tr
+    _say("case tiny elements ts", ts)
+    rng = np.random.default_rng(77)
+    tsf = np.float32(ts)
+    dec = F.E4M3FN_VALUES[1:0x7F]
+    big = np.repeat(6.0 * dec * float(tsf), 64)
+    nb = big.size
+    tiny_pool = np.concatenate([
+        F.bf16_to_f32(np.arange(1, 0x80, dtype=np.uint16)).astype(np.float64),      # subnormals
+        2.0 ** rng.uniform(-126, -96, 400),                                           # tiny normals
+        np.array([0.0, -0.0]),
+        rng.standard_normal(200) * float(tsf)])
+    rest = rng.choice(tiny_pool, size=(nb, 15)) * np.where(rng.random((nb, 15)) < 0.5, -1, 1)
+    blocks = np.concatenate([big[:, None] * np.where(rng.random((nb, 1)) < 0.5, -1, 1), rest], axis=1)
+    xr = _bf16_np(blocks.reshape(-1))
+    xt = xr.copy()
+    flip = rng.random(xt.size) < 0.3
+    xt[flip] = _bf16_np(F.bf16_to_f32(xt[flip]) * (1 + 0.3 * rng.standard_normal(flip.sum())))
+    g = _bf16_np(rng.standard_normal(xr.size))
+    shape = (nb, 16)
+    got = gpu_path(from_np_u16(xr, device, shape), from_np_u16(xt, device, shape), from_np_u16(g, device, shape),
+                   ts=torch.tensor([tsf], dtype=torch.float32, device=device))
+    want = oracle_path(xr, xt, g, ts=tsf)
+    assert_same(got, want, ctx=f"tiny ts={ts}")
 
 
 def test_in_place_and_guard_bytes(device):
