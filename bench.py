@@ -101,6 +101,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--layers", type=int, default=LAYERS, help=argparse.SUPPRESS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB bf16 device copy (reference kernel for HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -108,6 +110,9 @@ def main():
               "multi-GPU mode (see the sharding paragraph of DESIGN.md). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     pool, cores = (None, 0) if args.no_cpu_baseline else make_pool()
 
     import numpy as np
@@ -228,6 +233,27 @@ def main():
         pool.close()
         pool.join()
     print(json.dumps(result), flush=True)
+
+
+def calibrate_copy():
+    """A plain copy of ROWS x COLS bf16 (1 GiB read, 1 GiB written), three
+    times: the counter reading of a kernel whose HBM bytes are known."""
+    import torch
+    dev = torch.device("cuda", 0)
+    src = torch.randn(ROWS, COLS, device=dev).to(torch.bfloat16)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(3):
+        dst.copy_(src)
+    ev[1].record()
+    torch.cuda.synchronize()
+    us = ev[0].elapsed_time(ev[1]) * 1e3 / 3
+    nbytes = src.numel() * 2
+    log(f"copy {nbytes} B read + {nbytes} B written: {us:.1f} us per copy, {2 * nbytes / us / 1e3:.1f} GB/s")
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "avg_us": round(us, 2),
+                      "GB_s": round(2 * nbytes / us / 1e3, 1)}), flush=True)
 
 
 def read_traffic(kernel):

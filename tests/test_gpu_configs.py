@@ -1,0 +1,138 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark uses (one call per site tensor), against the oracle on sampled
+rows (the first row, random rows and the last rows, which include the ragged
+tail of the large-hidden workload).  The tensor scale of every site is
+checked over the whole tensor.  Where a workload is built around rollout /
+training agreement, the oracle's mismatch statistics on the sample are
+checked against what the rule guarantees (straddle sites are recovered,
+two-codeword mismatches fall back to RNE) and printed."""
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.gpu_util import assert_same, oracle_path, to_np_u16, to_np_u8
+from tests.workload_place import oracle_block_scales, place_kv, place_near_midpoints
+
+pytestmark = pytest.mark.gpu
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _gpu_full(x_roll, x_train, grad):
+    import fp4_rollout_guided_amd as tr
+    ts = tr.tensor_scale(x_roll)
+    sc, bt, cd = tr.capture(x_roll, ts, want_codes=True)
+    yg, mg, qg = tr.guided_fakequant_fwd(x_train, sc, ts, bt, want_codes=True)
+    yr, mr, qr = tr.rne_fakequant_fwd(x_train, sc, ts, want_codes=True)
+    gin = tr.ste_bwd(grad, mg)
+    torch.cuda.synchronize()
+    return {"ts": ts, "scales": sc, "bits": bt, "codes": cd, "y_g": yg, "mask_g": mg, "q_g": qg,
+            "y_r": yr, "mask_r": mr, "q_r": qr, "gin": gin}
+
+
+def _rows(rows, k, seed):
+    rng = np.random.default_rng(seed)
+    pick = set(rng.choice(rows, size=min(k, rows), replace=False).tolist())
+    pick.update([0, rows - 1, rows - 2, rows - 37 if rows > 37 else 0])
+    return np.array(sorted(pick))
+
+
+def _gather(t, idx, per_row, u16=False):
+    v = t.reshape(-1, per_row)[torch.from_numpy(idx).to(t.device)]
+    return to_np_u16(v) if u16 else to_np_u8(v)
+
+
+def check_site(name, x_roll, x_train, grad, k_rows=128, seed=0):
+    rows, cols = x_roll.shape[0], x_roll.numel() // x_roll.shape[0]
+    _say(f"case {name}: {tuple(x_roll.shape)} ({x_roll.numel()} elements), {k_rows} sampled rows")
+    got = _gpu_full(x_roll, x_train, grad)
+    xr_all = to_np_u16(x_roll)
+    ts = oracle.tensor_scale(xr_all)
+    del xr_all
+    assert got["ts"].cpu().numpy().view(np.uint32)[0] == np.float32(ts).view(np.uint32), name
+    idx = _rows(rows, k_rows, seed)
+    xr = _gather(x_roll.view(torch.int16), idx, cols, True)
+    xt = _gather(x_train.view(torch.int16), idx, cols, True)
+    g = _gather(grad.view(torch.int16), idx, cols, True)
+    want = oracle_path(xr, xt, g, ts=ts)
+    per = {"scales": cols // 16, "bits": cols // 8, "codes": cols // 2, "mask_g": cols // 8, "q_g": cols // 2,
+           "mask_r": cols // 8, "q_r": cols // 2}
+    sampled = {k: _gather(got[k], idx, n) for k, n in per.items()}
+    for k in ("y_g", "y_r", "gin"):
+        sampled[k] = _gather(got[k].view(torch.int16), idx, cols, True)
+    assert_same(sampled, want, keys=list(per) + ["y_g", "y_r", "gin"], ctx=name)
+    st = oracle.mismatch_stats(xt, want["scales"], ts, want["codes"], want["bits"])
+    _say(f"  {name}: sample {st['n']} sites, mismatched {st['mismatched']}, straddle {st['straddle']}, "
+         f"crossed {st['crossed']}, recovered {st['recovered']}, violations {st['violations']}, "
+         f"hist {st['hist'][:4]}")
+    # full tensor: where x_train == x_roll, guided == RNE (identical inputs give identical codes)
+    same = (x_train.view(torch.int16) == x_roll.view(torch.int16)).reshape(-1)
+    if bool(same.any()):
+        yg = got["y_g"].view(torch.int16).reshape(-1)
+        yr = got["y_r"].view(torch.int16).reshape(-1)
+        assert bool((yg[same] == yr[same]).all()), name
+    return st
+
+
+def test_workload0_full_compare(device):
+    """1024 x 2048: every element against the oracle."""
+    d = workloads.cfg0(device)
+    _say("case workload 0 full")
+    from tests.gpu_util import gpu_path
+    got = gpu_path(d["x_roll"], d["x_train"], d["grad"])
+    want = oracle_path(to_np_u16(d["x_roll"]), to_np_u16(d["x_train"]), to_np_u16(d["grad"]))
+    assert_same(got, want, ctx="workload 0")
+
+
+def test_workload1_moe_layer(device):
+    with open(os.path.join(HERE, "golden", "cfg1_sigma.json")) as fh:
+        sigma = json.load(fh)["sigma"]
+    sites = workloads.cfg1(device, sigma)
+    total = {"n": 0, "straddle": 0}
+    for i, (name, d) in enumerate(sites.items()):
+        st = check_site(f"workload 1 {name}", d["x_roll"], d["x_train"], d["grad"], seed=10 + i)
+        total["n"] += st["n"]
+        total["straddle"] += st["straddle"]
+        assert st["recovered"] >= st["straddle"]
+    rate = total["straddle"] / total["n"]
+    _say(f"  workload 1 straddle rate on the samples: {rate:.4f}")
+    assert 0.02 < rate < 0.04
+
+
+@pytest.mark.parametrize("which", ["k", "v"])
+def test_workload2_kv_cache(device, which):
+    x_roll = workloads.cfg2_rollout(device, which)
+    _, s_block = oracle_block_scales(x_roll)
+    x_train = place_kv(x_roll, which, s_block)
+    grad = workloads.grad_for(x_roll.shape, device, 2, which)
+    shape2d = (x_roll.shape[0], x_roll.shape[1] * x_roll.shape[2])
+    st = check_site(f"workload 2 {which}", x_roll.reshape(shape2d), x_train.reshape(shape2d), grad.reshape(shape2d),
+                    k_rows=256, seed=20)
+    assert st["recovered"] >= st["straddle"]
+    # all mismatches on the sample are the placed one- and two-codeword moves
+    assert st["hist"][1] > 0 and sum(st["hist"][4:]) == 0
+
+
+@pytest.mark.parametrize("layer", [0, 19])
+def test_workload3_deeper_half_layer(device, layer):
+    d = workloads.cfg3_layer(device, layer)
+    st = check_site(f"workload 3 layer {layer}", d["x_roll"], d["x_train"], d["grad"], seed=30 + layer)
+    assert st["recovered"] >= st["straddle"]
+
+
+def test_workload4_large_hidden_ragged(device):
+    x_roll = workloads.cfg4_rollout(device)
+    _, s_block = oracle_block_scales(x_roll)
+    x_train = place_near_midpoints(x_roll, s_block)
+    grad = workloads.grad_for(x_roll.shape, device, 4)
+    st = check_site("workload 4", x_roll, x_train, grad, k_rows=96, seed=40)
+    assert st["recovered"] >= st["straddle"]
