@@ -12,7 +12,9 @@ One step = for every layer, in order: tensor scale (amax pass), capture
 (scale bytes + parity bit-plane), guided fake-quant forward (y + clip mask),
 plain RNE fake-quant forward (y + clip mask), STE backward.  Every kernel is
 bracketed by HIP events on the stream it runs on; the step's wall time is
-taken between device synchronizations.
+taken between device synchronizations.  After the timed steps, a separate
+pass times the rows beyond the hot path (capture with full 4-bit codes and
+the full-information forward) and reports them under ``next_rows``.
 
 Prints one JSON line (last line of stdout).  ``value`` is the algorithmic
 bytes of the whole step divided by its wall time, in GB/s; per-kernel GB/s,
@@ -43,6 +45,11 @@ BYTES_PER_ELEM = {
     "ste_bwd": 2.0 + 1 / 8 + 2.0,              # read grad, mask; write grad_in
 }
 KERNELS = list(BYTES_PER_ELEM)
+# Rows beyond the hot path, timed in a separate pass after the step.
+NEXT_BYTES_PER_ELEM = {
+    "capture_codes": 2.0 + 1 / 8 + 1 / 16 + 1 / 2,        # capture that also writes the 4-bit codes
+    "full_info_fwd": 2.0 + 1 / 16 + 1 / 2 + 2.0 + 1 / 8,  # read x, scales, codes; write y, mask
+}
 CPU_SHARE = 16           # host cores a one-GPU machine grants
 CPU_BUDGET_S = 12.0      # wall-clock budget of the CPU oracle leg
 CHUNK_ROWS = 128
@@ -195,6 +202,31 @@ def main():
     dominant = max(KERNELS, key=lambda k: per_kernel_ms[k])
     dk = kernels[dominant]
 
+    # rows beyond the hot path: capture with full codes, then the full-information forward
+    codes = torch.empty(n // 2, dtype=torch.uint8, device=dev)
+    next_ms = {k: 0.0 for k in NEXT_BYTES_PER_ELEM}
+    next_steps = max(1, min(args.steps, 3))
+    for it in range(next_steps + 1):
+        ev = {k: [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(L)] for k in NEXT_BYTES_PER_ELEM}
+        for li, d in enumerate(layers):
+            ev["capture_codes"][li][0].record(stream)
+            tr.capture(d["x_roll"], d["ts"], scales=d["scales"], bits=d["bits"], codes=codes)
+            ev["capture_codes"][li][1].record(stream)
+            ev["full_info_fwd"][li][0].record(stream)
+            tr.full_info_fakequant_fwd(d["x_train"], d["scales"], d["ts"], codes, y=y_g, mask=mask_g)
+            ev["full_info_fwd"][li][1].record(stream)
+        stream.synchronize()
+        if it > 0:  # the first pass warms up
+            for k in NEXT_BYTES_PER_ELEM:
+                next_ms[k] += sum(ev[k][li][0].elapsed_time(ev[k][li][1]) for li in range(L))
+    next_rows = {}
+    for k, bpe in NEXT_BYTES_PER_ELEM.items():
+        avg_ms = next_ms[k] / (next_steps * L)
+        gbs = bpe * n / (avg_ms * 1e-3) / 1e9
+        next_rows[k] = {"avg_us": round(avg_ms * 1e3, 2), "GB_s": round(gbs, 1),
+                        "Gelem_s": round(n / (avg_ms * 1e-3) / 1e9, 2), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                        "bytes_per_launch": int(bpe * n)}
+
     cache = {
         "compact_bytes_20_layers": L * (n // 8 + n // 16),
         "full_nvfp4_bytes_40_layers": TOTAL_LAYERS * (n // 2 + n // 16),
@@ -222,6 +254,7 @@ def main():
         "gelem_per_s": round(L * n / (ms_per_step * 1e-3) / 1e9, 3),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "kernels": kernels,
+        "next_rows": next_rows,
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": dk["GB_s"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": dk["frac_hbm_peak"], "traffic": read_traffic(dominant)},
         "cache": cache,

@@ -11,6 +11,7 @@ Functions mirror the C ABI in ``include/trace.h``:
     capture(x_roll, ts, want_codes=False)            -> (scales, bits, codes)
     guided_fakequant_fwd(x_train, scales, ts, bits)  -> (y, mask, qcodes)
     rne_fakequant_fwd(x_train, scales, ts)           -> (y, mask, qcodes)
+    full_info_fakequant_fwd(x_train, scales, ts, codes) -> (y, mask, qcodes)
     ste_bwd(grad_out, mask)                          -> grad_in
 
 and ``GuidedFakeQuant`` wraps the forward/backward pair as an autograd
@@ -23,7 +24,7 @@ import torch
 
 __all__ = [
     "TraceError", "LIB_PATH", "lib", "abi_version", "tensor_scale", "capture",
-    "guided_fakequant_fwd", "rne_fakequant_fwd", "ste_bwd", "GuidedFakeQuant",
+    "guided_fakequant_fwd", "rne_fakequant_fwd", "full_info_fakequant_fwd", "ste_bwd", "GuidedFakeQuant",
     "STATUS",
 ]
 
@@ -58,6 +59,7 @@ def _load():
         "trace_capture": ([p, i64, i64, p, p, p, p, p], st),
         "trace_guided_fakequant_fwd": ([p, i64, i64, p, p, p, p, p, p, p], st),
         "trace_rne_fakequant_fwd": ([p, i64, i64, p, p, p, p, p, p], st),
+        "trace_full_info_fakequant_fwd": ([p, i64, i64, p, p, p, p, p, p, p], st),
         "trace_ste_bwd": ([p, p, i64, p, p], st),
     }
     for name, (args, res) in sig.items():
@@ -148,7 +150,7 @@ def capture(x_roll, ts, want_codes=False, scales=None, bits=None, codes=None):
     return scales, bits, codes
 
 
-def _fwd(guided, x, scales, ts, bits, y, mask, want_codes, qcodes):
+def _fwd(mode, x, scales, ts, side, y, mask, want_codes, qcodes):
     _bf16(x, "x_train")
     rows, cols = _rows_cols(x)
     n = rows * cols
@@ -159,24 +161,33 @@ def _fwd(guided, x, scales, ts, bits, y, mask, want_codes, qcodes):
     mask = _u8(n // 8, x, mask, "mask")
     if want_codes or qcodes is not None:
         qcodes = _u8(n // 2, x, qcodes, "qcodes")
-    if guided:
-        st = lib.trace_guided_fakequant_fwd(_ptr(x), rows, cols, _ptr(scales), _ptr(ts), _ptr(bits), _ptr(y),
+    if mode == "guided":
+        st = lib.trace_guided_fakequant_fwd(_ptr(x), rows, cols, _ptr(scales), _ptr(ts), _ptr(side), _ptr(y),
                                             _ptr(mask), _ptr(qcodes), _stream(x))
+    elif mode == "full":
+        st = lib.trace_full_info_fakequant_fwd(_ptr(x), rows, cols, _ptr(scales), _ptr(ts), _ptr(side), _ptr(y),
+                                               _ptr(mask), _ptr(qcodes), _stream(x))
     else:
         st = lib.trace_rne_fakequant_fwd(_ptr(x), rows, cols, _ptr(scales), _ptr(ts), _ptr(y), _ptr(mask),
                                          _ptr(qcodes), _stream(x))
-    _check(st, "trace_guided_fakequant_fwd" if guided else "trace_rne_fakequant_fwd")
+    _check(st, {"guided": "trace_guided_fakequant_fwd", "full": "trace_full_info_fakequant_fwd",
+                "rne": "trace_rne_fakequant_fwd"}[mode])
     return y, mask, qcodes
 
 
 def guided_fakequant_fwd(x_train, scales, ts, bits, y=None, mask=None, want_codes=False, qcodes=None):
     """Rollout-guided fake-quant forward: (y bf16, mask u8[n/8], qcodes)."""
-    return _fwd(True, x_train, scales, ts, bits, y, mask, want_codes, qcodes)
+    return _fwd("guided", x_train, scales, ts, bits, y, mask, want_codes, qcodes)
 
 
 def rne_fakequant_fwd(x_train, scales, ts, y=None, mask=None, want_codes=False, qcodes=None):
     """Plain round-to-nearest-even fake-quant forward: (y, mask, qcodes)."""
-    return _fwd(False, x_train, scales, ts, None, y, mask, want_codes, qcodes)
+    return _fwd("rne", x_train, scales, ts, None, y, mask, want_codes, qcodes)
+
+
+def full_info_fakequant_fwd(x_train, scales, ts, codes, y=None, mask=None, want_codes=False, qcodes=None):
+    """Full-information guided forward from the rollout's 4-bit codes: (y, mask, qcodes)."""
+    return _fwd("full", x_train, scales, ts, codes, y, mask, want_codes, qcodes)
 
 
 def ste_bwd(grad_out, mask, grad_in=None):

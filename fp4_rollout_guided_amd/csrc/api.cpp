@@ -110,33 +110,43 @@ trace_status trace_capture(const uint16_t* x_roll, int64_t rows, int64_t cols, c
                                                static_cast<hipStream_t>(stream)));
 }
 
-static trace_status fakequant(bool guided, const uint16_t* x, int64_t rows, int64_t cols,
-                              const uint8_t* scales, const float* ts, const uint8_t* bits, uint16_t* y,
-                              uint8_t* mask, uint8_t* qcodes, void* stream) {
+// mode 0: RNE; 1: guided (side = bit-plane, n/8 bytes, 2-byte aligned);
+// 2: full information (side = codes, n/2 bytes, 8-byte aligned).
+static trace_status fakequant(int mode, const uint16_t* x, int64_t rows, int64_t cols, const uint8_t* scales,
+                              const float* ts, const uint8_t* side, uint16_t* y, uint8_t* mask, uint8_t* qcodes,
+                              void* stream) {
   uint64_t n = 0;
   if (trace_status st = site_size(rows, cols, &n)) return st;
   if (n == 0) return TRACE_OK;
-  if (!x || !scales || !ts || (guided && !bits) || !y || !mask) return TRACE_E_NULL;
+  if (!x || !scales || !ts || (mode != 0 && !side) || !y || !mask) return TRACE_E_NULL;
+  const uint64_t side_len = mode == 1 ? n / 8 : (mode == 2 ? n / 2 : 0);
+  const uintptr_t side_align = mode == 2 ? 8 : 2;
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ts, 4) || !aligned(mask, 2) ||
-      (guided && !aligned(bits, 2)) || (qcodes && !aligned(qcodes, 8)))
+      (mode != 0 && !aligned(side, side_align)) || (qcodes && !aligned(qcodes, 8)))
     return TRACE_E_ALIGN;
   const Range outs[3] = {rng(y, 2 * n), rng(mask, n / 8), rng(qcodes, qcodes ? n / 2 : 0)};
-  const Range ins[4] = {rng(x, 2 * n), rng(scales, n / 16), rng(ts, 4), rng(bits, guided ? n / 8 : 0)};
+  const Range ins[4] = {rng(x, 2 * n), rng(scales, n / 16), rng(ts, 4), rng(side, side_len)};
   if (trace_status st = check_alias(outs, 3, ins, 4, /*inplace_out=*/0, /*inplace_in=*/0)) return st;
-  return hip_status(trace_host::launch_fakequant(guided, x, n / 16, scales, ts, bits, y, mask, qcodes,
+  return hip_status(trace_host::launch_fakequant(mode, x, n / 16, scales, ts, side, y, mask, qcodes,
                                                  static_cast<hipStream_t>(stream)));
 }
 
 trace_status trace_guided_fakequant_fwd(const uint16_t* x_train, int64_t rows, int64_t cols,
                                         const uint8_t* scales, const float* ts, const uint8_t* bits,
                                         uint16_t* y, uint8_t* mask, uint8_t* qcodes, void* stream) {
-  return fakequant(true, x_train, rows, cols, scales, ts, bits, y, mask, qcodes, stream);
+  return fakequant(1, x_train, rows, cols, scales, ts, bits, y, mask, qcodes, stream);
 }
 
 trace_status trace_rne_fakequant_fwd(const uint16_t* x_train, int64_t rows, int64_t cols,
                                      const uint8_t* scales, const float* ts, uint16_t* y, uint8_t* mask,
                                      uint8_t* qcodes, void* stream) {
-  return fakequant(false, x_train, rows, cols, scales, ts, nullptr, y, mask, qcodes, stream);
+  return fakequant(0, x_train, rows, cols, scales, ts, nullptr, y, mask, qcodes, stream);
+}
+
+trace_status trace_full_info_fakequant_fwd(const uint16_t* x_train, int64_t rows, int64_t cols,
+                                           const uint8_t* scales, const float* ts, const uint8_t* codes,
+                                           uint16_t* y, uint8_t* mask, uint8_t* qcodes, void* stream) {
+  return fakequant(2, x_train, rows, cols, scales, ts, codes, y, mask, qcodes, stream);
 }
 
 trace_status trace_ste_bwd(const uint16_t* grad_out, const uint8_t* mask, int64_t n, uint16_t* grad_in,

@@ -214,8 +214,11 @@ __device__ __noinline__ void capture_block_exact(const uint4* __restrict__ x4, u
   if (codes) codes[b] = make_uint2((uint32_t)cw, (uint32_t)(cw >> 32));
 }
 
-__device__ __noinline__ void fakequant_block_exact(bool guided, const uint4* __restrict__ x4, uint64_t b,
+// mode: 0 = RNE, 1 = guided by the cached bit (cached = 16-bit word),
+// 2 = full information (rollout codes in roll_lo / roll_hi, element order).
+__device__ __noinline__ void fakequant_block_exact(int mode, const uint4* __restrict__ x4, uint64_t b,
                                                    uint32_t sbyte, float ts, uint32_t cached,
+                                                   uint32_t roll_lo, uint32_t roll_hi,
                                                    uint4* __restrict__ y4, uint16_t* __restrict__ mask,
                                                    uint2* __restrict__ qcodes) {
   const float s = e4m3_decode(sbyte) * ts;
@@ -239,10 +242,17 @@ __device__ __noinline__ void fakequant_block_exact(bool guided, const uint4* __r
       const float zr = xv / s;
       mk = fabsf(zr) <= 6.f ? 1u : 0u;
       const float a = fminf(fabsf(zr), 6.f);
-      if (guided) {
+      if (mode == 1) {
         const uint32_t lo = e2m1_floor_index(a);
         const bool exact = (a == e2m1_mag(lo));
         idx = (exact || ((lo & 1u) == ((cached >> j) & 1u))) ? lo : lo + 1;
+      } else if (mode == 2) {
+        // endpoint nearest to the rollout codeword: the upper one exactly when
+        // the rollout code has z's sign and a larger magnitude index
+        const uint32_t lo = e2m1_floor_index(a);
+        const bool exact = (a == e2m1_mag(lo));
+        const uint32_t rc = ((j < 8 ? roll_lo : roll_hi) >> (4 * (j & 7))) & 15u;
+        idx = (!exact && (rc >> 3) == sign && (rc & 7u) > lo) ? lo + 1 : lo;
       } else {
         idx = e2m1_rne_index(a);
       }
@@ -285,20 +295,29 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v) {
 
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 
+// The amax and STE kernels have no block structure, so their loads are fully
+// coalesced: a 4096-element tile is 512 128-bit vectors and lane t takes
+// vectors t and t + 256 (every load instruction covers 1 KiB contiguous).
 __global__ __launch_bounds__(kThreads) void amax_partial_kernel(const uint4* __restrict__ x,
                                                                 uint64_t nblocks,
                                                                 uint32_t* __restrict__ partial) {
   s16x2 best = {0, 0};  // holds max(m + 0x7f) over non-NaN halves, >= 0x7f once any was seen
-  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
-  for (uint64_t b = (uint64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks; b += stride) {
-    uint32_t w[8];
-    load_block(x, b, w);
+  const uint64_t nvec = 2 * nblocks;
+  for (uint64_t tile = blockIdx.x; tile * 512 < nvec; tile += gridDim.x) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const uint32_t m = (w[k] & 0x7fff7fffu) + 0x007f007fu;  // no carry between halves
-      s16x2 v;
-      __builtin_memcpy(&v, &m, 4);
-      best = __builtin_elementwise_max(best, v);
+    for (int h = 0; h < 2; ++h) {
+      const uint64_t i = tile * 512 + 256 * h + threadIdx.x;
+      if (i < nvec) {
+        const uint4 v = x[i];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t m = (w[k] & 0x7fff7fffu) + 0x007f007fu;  // no carry between halves
+          s16x2 vv;
+          __builtin_memcpy(&vv, &m, 4);
+          best = __builtin_elementwise_max(best, vv);
+        }
+      }
     }
   }
   const int lo = best.x, hi = best.y;
@@ -389,11 +408,39 @@ __global__ __launch_bounds__(kThreads) void capture_kernel(const uint4* __restri
 // ---------------------------------------------------------------------------
 // fake-quant forward (guided or plain RNE)
 // ---------------------------------------------------------------------------
-template <bool kGuided>
+// De-interleave element-order nibble codes (c0: elements 0..7, c1: 8..15)
+// into even-element and odd-element nibble dwords.
+__device__ __forceinline__ void split_codes(uint32_t c0, uint32_t c1, uint32_t& E, uint32_t& O) {
+  uint32_t e0 = c0 & 0x0F0F0F0Fu, e1 = c1 & 0x0F0F0F0Fu;
+  uint32_t o0 = (c0 >> 4) & 0x0F0F0F0Fu, o1 = (c1 >> 4) & 0x0F0F0F0Fu;
+  e0 = (e0 | (e0 >> 4)) & 0x00FF00FFu;  // bytes 0, 2 hold nibble pairs
+  e1 = (e1 | (e1 >> 4)) & 0x00FF00FFu;
+  o0 = (o0 | (o0 >> 4)) & 0x00FF00FFu;
+  o1 = (o1 | (o1 >> 4)) & 0x00FF00FFu;
+  E = __builtin_amdgcn_perm(e1, e0, 0x06040200u);
+  O = __builtin_amdgcn_perm(o1, o0, 0x06040200u);
+}
+
+// Codes of q* for the full-information rule from the floor codes F, the
+// predecessor floor codes P (equal to F exactly when q is inside a bracket)
+// and the rollout codes R, all packed 8 per dword: the upper endpoint F + 1
+// is taken when q is inside a bracket and the rollout code has the same sign
+// as F and a larger magnitude index.
+__device__ __forceinline__ uint32_t full_info_select(uint32_t F, uint32_t P, uint32_t R) {
+  uint32_t t = F ^ P;
+  t |= t >> 2;
+  t |= t >> 1;                                                    // bit 0 per nibble: exact
+  const uint32_t gt = ((R | 0x88888888u) - (F & 0x77777777u) - 0x11111111u) & 0x88888888u;  // r_idx > f_idx
+  const uint32_t same = ~(R ^ F) & 0x88888888u;
+  return F + ((gt & same) >> 3 & ~t & 0x11111111u);
+}
+
+template <int kMode>  // 0 = RNE, 1 = guided by the cached bit, 2 = full information
 __global__ __launch_bounds__(kThreads) void fakequant_kernel(const uint4* __restrict__ x, uint64_t nblocks,
                                                              const uint8_t* __restrict__ scales,
                                                              const float* __restrict__ ts_ptr,
                                                              const uint16_t* __restrict__ bits,
+                                                             const uint2* __restrict__ rcodes,
                                                              uint4* __restrict__ y,
                                                              uint16_t* __restrict__ mask,
                                                              uint2* __restrict__ qcodes) {
@@ -401,7 +448,8 @@ __global__ __launch_bounds__(kThreads) void fakequant_kernel(const uint4* __rest
   const uint64_t stride = (uint64_t)gridDim.x * kThreads;
   for (uint64_t b = (uint64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks; b += stride) {
     const uint32_t sbyte = scales[b];
-    const uint32_t cached = kGuided ? (uint32_t)bits[b] : 0u;
+    const uint32_t cached = kMode == 1 ? (uint32_t)bits[b] : 0u;
+    const uint2 roll = kMode == 2 ? rcodes[b] : make_uint2(0u, 0u);
     uint32_t w[8];
     load_block(x, b, w);
     const ScaleEntry e = make_scale_entry(sbyte, ts);
@@ -423,7 +471,7 @@ __global__ __launch_bounds__(kThreads) void fakequant_kernel(const uint4* __rest
     for (int j = 0; j < 16; ++j) qc[j] = __builtin_amdgcn_fmed3f(q[j], -6.0f, 6.0f);
 
     uint32_t QE = 0, QO = 0;
-    if (kGuided) {
+    if (kMode != 0) {
       // floor codes of q and of its predecessor toward zero: equal exactly when
       // q lies strictly inside a bracket, so the upper endpoint is floor + 1
       float pv[16];  // predecessors toward zero (a NaN for +-0, whose floor code differs)
@@ -434,22 +482,29 @@ __global__ __launch_bounds__(kThreads) void fakequant_kernel(const uint4* __rest
       FP4_PACK8(FP4_RTZ, FO, qc, 1);
       FP4_PACK8(FP4_RTZ, PE, pv, 0);
       FP4_PACK8(FP4_RTZ, PO, pv, 1);
-      const uint32_t C = spread_bits(cached);  // bit 0 / bit 1 of nibble k: cached bit of 2k / 2k+1
-      uint32_t t = FE ^ PE;
-      t |= t >> 2;
-      t |= t >> 1;
-      QE = FE + (~t & (FE ^ C) & 0x11111111u);
-      t = FO ^ PO;
-      t |= t >> 2;
-      t |= t >> 1;
-      QO = FO + (~t & (FO ^ (C >> 1)) & 0x11111111u);
+      if (kMode == 1) {
+        const uint32_t C = spread_bits(cached);  // bit 0 / bit 1 of nibble k: cached bit of 2k / 2k+1
+        uint32_t t = FE ^ PE;
+        t |= t >> 2;
+        t |= t >> 1;
+        QE = FE + (~t & (FE ^ C) & 0x11111111u);
+        t = FO ^ PO;
+        t |= t >> 2;
+        t |= t >> 1;
+        QO = FO + (~t & (FO ^ (C >> 1)) & 0x11111111u);
+      } else {
+        uint32_t RE, RO;
+        split_codes(roll.x, roll.y, RE, RO);
+        QE = full_info_select(FE, PE, RE);
+        QO = full_info_select(FO, PO, RO);
+      }
     } else {
       FP4_PACK8(FP4_RNE, QE, qc, 0);
       FP4_PACK8(FP4_RNE, QO, qc, 1);
     }
 
     if (bad) {
-      fakequant_block_exact(kGuided, x, b, sbyte, ts, cached, y, mask, qcodes);
+      fakequant_block_exact(kMode, x, b, sbyte, ts, cached, roll.x, roll.y, y, mask, qcodes);
     } else {
       uint32_t out[8];
       decode_scaled_pair<0>(QE, QO, e.s, out);
@@ -471,20 +526,30 @@ __global__ __launch_bounds__(kThreads) void fakequant_kernel(const uint4* __rest
 // STE backward
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void ste_bwd_kernel(const uint4* __restrict__ g, uint64_t nblocks,
-                                                           const uint16_t* __restrict__ mask,
+                                                           const uint16_t* __restrict__ mask16,
                                                            uint4* __restrict__ gin) {
-  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
-  for (uint64_t b = (uint64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks; b += stride) {
-    const uint32_t m = mask[b];
-    uint32_t w[8];
-    load_block(g, b, w);
+  // coalesced like the amax kernel; vector i holds elements 8i..8i+7, whose
+  // mask bits are byte i of the mask
+  const uint8_t* mask = reinterpret_cast<const uint8_t*>(mask16);
+  const uint64_t nvec = 2 * nblocks;
+  const uint64_t stride = (uint64_t)gridDim.x * 512;
+  for (uint64_t base = (uint64_t)blockIdx.x * 512 + threadIdx.x; base < nvec; base += stride) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const uint32_t keep = (((m >> (2 * k)) & 1u) ? 0x0000ffffu : 0u) |
-                            (((m >> (2 * k + 1)) & 1u) ? 0xffff0000u : 0u);
-      w[k] &= keep;
+    for (int h = 0; h < 2; ++h) {
+      const uint64_t i = base + 256 * h;
+      if (i < nvec) {
+        const uint32_t m = mask[i];
+        const uint4 v = g[i];
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t keep = (((m >> (2 * k)) & 1u) ? 0x0000ffffu : 0u) |
+                                (((m >> (2 * k + 1)) & 1u) ? 0xffff0000u : 0u);
+          w[k] &= keep;
+        }
+        gin[i] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
     }
-    store_block(gin, b, w);
   }
 }
 
@@ -526,19 +591,23 @@ hipError_t launch_capture(const uint16_t* x, uint64_t nblocks, const float* ts, 
   return hipGetLastError();
 }
 
-hipError_t launch_fakequant(bool guided, const uint16_t* x, uint64_t nblocks, const uint8_t* scales,
-                            const float* ts, const uint8_t* bits, uint16_t* y, uint8_t* mask,
+hipError_t launch_fakequant(int mode, const uint16_t* x, uint64_t nblocks, const uint8_t* scales,
+                            const float* ts, const uint8_t* side, uint16_t* y, uint8_t* mask,
                             uint8_t* qcodes, hipStream_t stream) {
-  if (guided)
-    hipLaunchKernelGGL(fakequant_kernel<true>, dim3(grid_for(nblocks)), dim3(kThreads), 0, stream,
-                       reinterpret_cast<const uint4*>(x), nblocks, scales, ts,
-                       reinterpret_cast<const uint16_t*>(bits), reinterpret_cast<uint4*>(y),
-                       reinterpret_cast<uint16_t*>(mask), reinterpret_cast<uint2*>(qcodes));
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  uint4* yv = reinterpret_cast<uint4*>(y);
+  uint16_t* mv = reinterpret_cast<uint16_t*>(mask);
+  uint2* qv = reinterpret_cast<uint2*>(qcodes);
+  const dim3 grid(grid_for(nblocks)), block(kThreads);
+  if (mode == 1)
+    hipLaunchKernelGGL(fakequant_kernel<1>, grid, block, 0, stream, xv, nblocks, scales, ts,
+                       reinterpret_cast<const uint16_t*>(side), static_cast<const uint2*>(nullptr), yv, mv, qv);
+  else if (mode == 2)
+    hipLaunchKernelGGL(fakequant_kernel<2>, grid, block, 0, stream, xv, nblocks, scales, ts,
+                       static_cast<const uint16_t*>(nullptr), reinterpret_cast<const uint2*>(side), yv, mv, qv);
   else
-    hipLaunchKernelGGL(fakequant_kernel<false>, dim3(grid_for(nblocks)), dim3(kThreads), 0, stream,
-                       reinterpret_cast<const uint4*>(x), nblocks, scales, ts,
-                       static_cast<const uint16_t*>(nullptr), reinterpret_cast<uint4*>(y),
-                       reinterpret_cast<uint16_t*>(mask), reinterpret_cast<uint2*>(qcodes));
+    hipLaunchKernelGGL(fakequant_kernel<0>, grid, block, 0, stream, xv, nblocks, scales, ts,
+                       static_cast<const uint16_t*>(nullptr), static_cast<const uint2*>(nullptr), yv, mv, qv);
   return hipGetLastError();
 }
 

@@ -24,8 +24,10 @@ hipError_t launch_tensor_scale(const uint16_t* x, uint64_t nblocks, uint32_t* pa
                                hipStream_t stream);
 hipError_t launch_capture(const uint16_t* x, uint64_t nblocks, const float* ts, uint8_t* scales,
                           uint8_t* bits, uint8_t* codes, hipStream_t stream);
-hipError_t launch_fakequant(bool guided, const uint16_t* x, uint64_t nblocks, const uint8_t* scales,
-                            const float* ts, const uint8_t* bits, uint16_t* y, uint8_t* mask,
+// mode 0: RNE; 1: guided, side = bit-plane (u8[n/8]); 2: full information,
+// side = rollout codes (u8[n/2]).
+hipError_t launch_fakequant(int mode, const uint16_t* x, uint64_t nblocks, const uint8_t* scales,
+                            const float* ts, const uint8_t* side, uint16_t* y, uint8_t* mask,
                             uint8_t* qcodes, hipStream_t stream);
 hipError_t launch_ste_bwd(const uint16_t* g, const uint8_t* mask, uint64_t nblocks, uint16_t* gin,
                           hipStream_t stream);

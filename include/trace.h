@@ -169,6 +169,24 @@ TRACE_API trace_status trace_rne_fakequant_fwd(const uint16_t* x_train, int64_t 
                                      void* stream);
 
 /*
+ * Full-information guided fake-quant forward: the ablation reference that
+ * caches the whole 4-bit rollout code instead of one bit (rcap.io post,
+ * Ablations bullet; the rollout-guided rounding paragraph's rule with the
+ * rollout codeword known).  As trace_guided_fakequant_fwd, except
+ *   m = |z| if lo == hi, else the one of lo, hi whose signed value is nearest
+ *       to the rollout's signed codeword (no ties are possible).
+ * This choice is never farther from the rollout value than round-to-nearest.
+ *   codes : uint8[n/2] rollout codes from trace_capture (element 2j in the
+ *           low nibble of byte j), 8-byte aligned.
+ * Other arguments, aliasing and errors as trace_guided_fakequant_fwd.
+ */
+TRACE_API trace_status trace_full_info_fakequant_fwd(const uint16_t* x_train, int64_t rows,
+                                                     int64_t cols, const uint8_t* scales,
+                                                     const float* ts, const uint8_t* codes,
+                                                     uint16_t* y, uint8_t* mask,
+                                                     uint8_t* qcodes, void* stream);
+
+/*
  * Straight-through-estimator backward (straight_through_estimator in the
  * listing): grad_in[i] = mask bit i ? grad_out[i] : +0.0 (0x0000).
  *   grad_out, grad_in : bf16[n]; grad_in may be exactly grad_out;

@@ -27,6 +27,8 @@ def gpu_path(x_roll, x_train, grad, ts=None, want_codes=True):
     scales, bits, codes = tr.capture(x_roll, ts_gpu, want_codes=want_codes)
     y_g, m_g, q_g = tr.guided_fakequant_fwd(x_train, scales, ts_gpu, bits, want_codes=True)
     y_r, m_r, q_r = tr.rne_fakequant_fwd(x_train, scales, ts_gpu, want_codes=True)
+    if want_codes:
+        y_f, m_f, q_f = tr.full_info_fakequant_fwd(x_train, scales, ts_gpu, codes, want_codes=True)
     gin = tr.ste_bwd(grad, m_g)
     torch.cuda.synchronize()
     out = {
@@ -38,6 +40,7 @@ def gpu_path(x_roll, x_train, grad, ts=None, want_codes=True):
     }
     if want_codes:
         out["codes"] = to_np_u8(codes)
+        out.update({"y_f": to_np_u16(y_f), "mask_f": to_np_u8(m_f), "q_f": to_np_u8(q_f)})
     return out
 
 
@@ -56,6 +59,8 @@ def oracle_path(xr, xt, g, ts=None, want_codes=True):
     }
     if want_codes:
         out["codes"] = cap["codes"]
+        fi = oracle.full_info_fwd(xt, cap["scales"], ts, cap["codes"])
+        out.update({"y_f": fi["y"], "mask_f": fi["mask"], "q_f": fi["codes"]})
     return out
 
 

@@ -27,7 +27,7 @@ def declared_symbols():
 
 def test_every_declared_symbol_is_exported():
     names = declared_symbols()
-    assert len(names) >= 9
+    assert len(names) >= 10
     raw = ctypes.CDLL(tr.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -89,8 +89,9 @@ def test_capture_validation():
     assert f(None, 0, 24, None, None, None, None, None) == E_SHAPE
 
 
-@pytest.mark.parametrize("guided", [True, False])
-def test_fakequant_validation(guided):
+@pytest.mark.parametrize("mode", ["guided", "rne", "full"])
+def test_fakequant_validation(mode):
+    guided = mode != "rne"
     x, sc, ts, bt, y, mk, qc = (A, A + 0x100000, A + 0x200000, A + 0x300000, A + 0x400000,
                                 A + 0x500000, A + 0x600000)
 
@@ -101,7 +102,8 @@ def test_fakequant_validation(guided):
             args.append(P(bt) if bt is not None else None)
         args += [P(y) if y is not None else None, P(mk) if mk is not None else None,
                  P(qc) if qc is not None else None, None]
-        fn = L.trace_guided_fakequant_fwd if guided else L.trace_rne_fakequant_fwd
+        fn = {"guided": L.trace_guided_fakequant_fwd, "rne": L.trace_rne_fakequant_fwd,
+              "full": L.trace_full_info_fakequant_fwd}[mode]
         return fn(*args)
 
     assert call(x=None) == E_NULL
@@ -112,6 +114,9 @@ def test_fakequant_validation(guided):
     if guided:
         assert call(bt=None) == E_NULL
         assert call(bt=bt + 1) == E_ALIGN
+    if mode == "full":
+        assert call(bt=bt + 2) == E_ALIGN          # codes need 8-byte alignment
+        assert call(bt=y + 64) == E_ALIAS         # codes inside y
     assert call(cols=40) == E_SHAPE
     assert call(rows=-2) == E_SHAPE
     assert call(x=x + 4) == E_ALIGN

@@ -33,10 +33,11 @@ def _gpu_full(x_roll, x_train, grad):
     sc, bt, cd = tr.capture(x_roll, ts, want_codes=True)
     yg, mg, qg = tr.guided_fakequant_fwd(x_train, sc, ts, bt, want_codes=True)
     yr, mr, qr = tr.rne_fakequant_fwd(x_train, sc, ts, want_codes=True)
+    yf, mf, qf = tr.full_info_fakequant_fwd(x_train, sc, ts, cd, want_codes=True)
     gin = tr.ste_bwd(grad, mg)
     torch.cuda.synchronize()
     return {"ts": ts, "scales": sc, "bits": bt, "codes": cd, "y_g": yg, "mask_g": mg, "q_g": qg,
-            "y_r": yr, "mask_r": mr, "q_r": qr, "gin": gin}
+            "y_r": yr, "mask_r": mr, "q_r": qr, "y_f": yf, "mask_f": mf, "q_f": qf, "gin": gin}
 
 
 def _rows(rows, k, seed):
@@ -65,11 +66,11 @@ def check_site(name, x_roll, x_train, grad, k_rows=128, seed=0):
     g = _gather(grad.view(torch.int16), idx, cols, True)
     want = oracle_path(xr, xt, g, ts=ts)
     per = {"scales": cols // 16, "bits": cols // 8, "codes": cols // 2, "mask_g": cols // 8, "q_g": cols // 2,
-           "mask_r": cols // 8, "q_r": cols // 2}
+           "mask_r": cols // 8, "q_r": cols // 2, "mask_f": cols // 8, "q_f": cols // 2}
     sampled = {k: _gather(got[k], idx, n) for k, n in per.items()}
-    for k in ("y_g", "y_r", "gin"):
+    for k in ("y_g", "y_r", "y_f", "gin"):
         sampled[k] = _gather(got[k].view(torch.int16), idx, cols, True)
-    assert_same(sampled, want, keys=list(per) + ["y_g", "y_r", "gin"], ctx=name)
+    assert_same(sampled, want, keys=list(per) + ["y_g", "y_r", "y_f", "gin"], ctx=name)
     st = oracle.mismatch_stats(xt, want["scales"], ts, want["codes"], want["bits"])
     _say(f"  {name}: sample {st['n']} sites, mismatched {st['mismatched']}, straddle {st['straddle']}, "
          f"crossed {st['crossed']}, recovered {st['recovered']}, violations {st['violations']}, "

@@ -122,7 +122,8 @@ def test_tensor_scale_cases(device):
 @pytest.mark.parametrize("ts", [1.0, 0.0123456, 3.0e-39, 1.0e30, 2.0 ** -100, 146.0, 2.0 ** -90])
 def test_fwd_exhaustive_bf16_by_scale_byte(device, ts):
     """Every bf16 pattern as x_train under every scale byte (0x00..0xFF),
-    for guided (random cached bits) and RNE forward."""
+    for guided (random cached bits), RNE and full-information (random
+    rollout codes) forward."""
     import fp4_rollout_guided_amd as tr
     _say("case exhaustive fwd ts", ts)
     pats = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
@@ -138,10 +139,15 @@ def test_fwd_exhaustive_bf16_by_scale_byte(device, ts):
     yg, mg, qg = tr.guided_fakequant_fwd(xd, sd, tsd, bd, want_codes=True)
     yr, mr, qr = tr.rne_fakequant_fwd(xd, sd, tsd, want_codes=True)
     torch.cuda.synchronize()
+    roll = rng.integers(0, 256, size=x.size // 2, dtype=np.uint8)   # every rollout code, both nibbles
+    yf, mf, qf = tr.full_info_fakequant_fwd(xd, sd, tsd, torch.from_numpy(roll).to(device), want_codes=True)
+    torch.cuda.synchronize()
     wg = oracle.guided_fwd(x, scales, tsf, bits)
     wr = oracle.rne_fwd(x, scales, tsf)
+    wf = oracle.full_info_fwd(x, scales, tsf, roll)
     assert_same({"y": to_np_u16(yg), "mask": to_np_u8(mg), "codes": to_np_u8(qg)}, wg, ctx=f"guided ts={ts}")
     assert_same({"y": to_np_u16(yr), "mask": to_np_u8(mr), "codes": to_np_u8(qr)}, wr, ctx=f"rne ts={ts}")
+    assert_same({"y": to_np_u16(yf), "mask": to_np_u8(mf), "codes": to_np_u8(qf)}, wf, ctx=f"full ts={ts}")
 
 
 @pytest.mark.parametrize("ts", [1.0, 0.0123456, 7.5e-37, 1.0e30])
