@@ -1,7 +1,7 @@
 """Python binding for libtrace (rollout-guided FP4 rounding on MI355X).
 
 Argument marshalling only: every step of the path runs in the HIP kernels of
-``libtrace.so`` (built by ``python -m fp4_rollout_guided_amd.build``).  PyTorch
+``libtrace.so`` (built by ``python fp4_rollout_guided_amd/build.py``).  PyTorch
 supplies device memory and the current stream.  There is no CPU fallback:
 importing this package fails if the library has not been built.
 
@@ -12,6 +12,7 @@ Functions mirror the C ABI in ``include/trace.h``:
     guided_fakequant_fwd(x_train, scales, ts, bits)  -> (y, mask, qcodes)
     rne_fakequant_fwd(x_train, scales, ts)           -> (y, mask, qcodes)
     full_info_fakequant_fwd(x_train, scales, ts, codes) -> (y, mask, qcodes)
+    gather_records(bits, scales, codes, cols, row_index) -> (bits, scales, codes)
     ste_bwd(grad_out, mask)                          -> grad_in
 
 and ``GuidedFakeQuant`` wraps the forward/backward pair as an autograd
@@ -24,7 +25,8 @@ import torch
 
 __all__ = [
     "TraceError", "LIB_PATH", "lib", "abi_version", "tensor_scale", "capture",
-    "guided_fakequant_fwd", "rne_fakequant_fwd", "full_info_fakequant_fwd", "ste_bwd", "GuidedFakeQuant",
+    "guided_fakequant_fwd", "rne_fakequant_fwd", "full_info_fakequant_fwd", "ste_bwd", "gather_records",
+    "GuidedFakeQuant",
     "STATUS",
 ]
 
@@ -46,7 +48,7 @@ class TraceError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m fp4_rollout_guided_amd.build` "
+            f"{LIB_PATH} is missing: build it with `python fp4_rollout_guided_amd/build.py` "
             "(libtrace has no CPU fallback)")
     L = ctypes.CDLL(LIB_PATH)
     p, i64, st, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
@@ -61,6 +63,7 @@ def _load():
         "trace_rne_fakequant_fwd": ([p, i64, i64, p, p, p, p, p, p], st),
         "trace_full_info_fakequant_fwd": ([p, i64, i64, p, p, p, p, p, p, p], st),
         "trace_ste_bwd": ([p, p, i64, p, p], st),
+        "trace_gather_records": ([p, p, p, i64, i64, p, i64, p, p, p, p], st),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -200,6 +203,23 @@ def ste_bwd(grad_out, mask, grad_in=None):
     _check(lib.trace_ste_bwd(_ptr(grad_out), _ptr(mask), grad_out.numel(), _ptr(grad_in), _stream(grad_out)),
            "trace_ste_bwd")
     return grad_in
+
+
+def gather_records(bits, scales, codes, cols, row_index):
+    """Records in the trainer's row order: row r of the result is source row
+    row_index[r] (int64 device tensor); out-of-range indices give zero rows."""
+    if not row_index.is_cuda or row_index.dtype != torch.int64 or not row_index.is_contiguous():
+        raise ValueError("row_index must be a contiguous int64 device tensor")
+    src_rows = scales.numel() * 16 // cols if cols else 0
+    dst_rows = row_index.numel()
+    n = dst_rows * cols
+    bits_d = torch.empty(n // 8, dtype=torch.uint8, device=bits.device)
+    scales_d = torch.empty(n // 16, dtype=torch.uint8, device=bits.device)
+    codes_d = torch.empty(n // 2, dtype=torch.uint8, device=bits.device) if codes is not None else None
+    _check(lib.trace_gather_records(_ptr(bits), _ptr(scales), _ptr(codes), src_rows, cols, _ptr(row_index),
+                                    dst_rows, _ptr(bits_d), _ptr(scales_d), _ptr(codes_d), _stream(bits)),
+           "trace_gather_records")
+    return bits_d, scales_d, codes_d
 
 
 class GuidedFakeQuant(torch.autograd.Function):

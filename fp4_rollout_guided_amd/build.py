@@ -1,6 +1,8 @@
 """Build libtrace.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
 
-    python -m fp4_rollout_guided_amd.build
+    python fp4_rollout_guided_amd/build.py
+
+(run as a script: importing the package would load the library first)
 
 Flags that matter for exactness: no FP contraction (every fused multiply-add
 in the kernels is written out), correctly rounded fp32 division, fp32

@@ -163,4 +163,27 @@ trace_status trace_ste_bwd(const uint16_t* grad_out, const uint8_t* mask, int64_
                                                static_cast<hipStream_t>(stream)));
 }
 
+trace_status trace_gather_records(const uint8_t* bits_src, const uint8_t* scales_src, const uint8_t* codes_src,
+                                  int64_t src_rows, int64_t cols, const int64_t* row_index, int64_t dst_rows,
+                                  uint8_t* bits_dst, uint8_t* scales_dst, uint8_t* codes_dst, void* stream) {
+  uint64_t n_src = 0, n_dst = 0;
+  if (trace_status st = site_size(src_rows, cols, &n_src)) return st;
+  if (trace_status st = site_size(dst_rows, cols, &n_dst)) return st;
+  if (n_dst == 0) return TRACE_OK;
+  // codes are gathered iff codes_dst is given; an empty source needs no pointers
+  if (codes_src && !codes_dst) return TRACE_E_NULL;
+  if (!row_index || !bits_dst || !scales_dst || (n_src > 0 && (!bits_src || !scales_src || (codes_dst && !codes_src))))
+    return TRACE_E_NULL;
+  if (!aligned(row_index, 8) || !aligned(bits_dst, 2) || (bits_src && !aligned(bits_src, 2)) ||
+      (codes_dst && (!aligned(codes_dst, 8) || (codes_src && !aligned(codes_src, 8)))))
+    return TRACE_E_ALIGN;
+  const Range outs[3] = {rng(bits_dst, n_dst / 8), rng(scales_dst, n_dst / 16), rng(codes_dst, codes_dst ? n_dst / 2 : 0)};
+  const Range ins[4] = {rng(bits_src, n_src / 8), rng(scales_src, n_src / 16), rng(codes_src, codes_src ? n_src / 2 : 0),
+                        rng(row_index, 8 * (uint64_t)dst_rows)};
+  if (trace_status st = check_alias(outs, 3, ins, 4)) return st;
+  return hip_status(trace_host::launch_gather_records(bits_src, scales_src, codes_src, (uint64_t)src_rows,
+                                                      (uint64_t)cols, row_index, (uint64_t)dst_rows, bits_dst,
+                                                      scales_dst, codes_dst, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

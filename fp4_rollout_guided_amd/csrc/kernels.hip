@@ -553,6 +553,30 @@ __global__ __launch_bounds__(kThreads) void ste_bwd_kernel(const uint4* __restri
   }
 }
 
+// ---------------------------------------------------------------------------
+// record gather (trainer-side readback): destination row r <- source row
+// row_index[r]; one lane copies one block's record (16 plane bits, the scale
+// byte, and 8 bytes of codes when present); an index outside [0, src_rows)
+// writes a zero record (zero-scale blocks).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void gather_records_kernel(
+    const uint16_t* __restrict__ bits_src, const uint8_t* __restrict__ scales_src,
+    const uint2* __restrict__ codes_src, uint64_t src_rows, uint64_t blocks_per_row,
+    const int64_t* __restrict__ row_index, uint64_t dst_rows, uint16_t* __restrict__ bits_dst,
+    uint8_t* __restrict__ scales_dst, uint2* __restrict__ codes_dst) {
+  for (uint64_t r = blockIdx.x; r < dst_rows; r += gridDim.x) {
+    const int64_t src = row_index[r];
+    const bool ok = src >= 0 && (uint64_t)src < src_rows;
+    const uint64_t sbase = ok ? (uint64_t)src * blocks_per_row : 0;
+    const uint64_t dbase = r * blocks_per_row;
+    for (uint64_t c = threadIdx.x; c < blocks_per_row; c += kThreads) {
+      bits_dst[dbase + c] = ok ? bits_src[sbase + c] : (uint16_t)0;
+      scales_dst[dbase + c] = ok ? scales_src[sbase + c] : (uint8_t)0;
+      if (codes_dst) codes_dst[dbase + c] = ok ? codes_src[sbase + c] : make_uint2(0u, 0u);
+    }
+  }
+}
+
 }  // namespace trace_dev
 
 // ---------------------------------------------------------------------------
@@ -616,6 +640,17 @@ hipError_t launch_ste_bwd(const uint16_t* g, const uint8_t* mask, uint64_t nbloc
   hipLaunchKernelGGL(ste_bwd_kernel, dim3(grid_for(nblocks)), dim3(kThreads), 0, stream,
                      reinterpret_cast<const uint4*>(g), nblocks,
                      reinterpret_cast<const uint16_t*>(mask), reinterpret_cast<uint4*>(gin));
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_records(const uint8_t* bits_src, const uint8_t* scales_src, const uint8_t* codes_src,
+                                 uint64_t src_rows, uint64_t cols, const int64_t* row_index, uint64_t dst_rows,
+                                 uint8_t* bits_dst, uint8_t* scales_dst, uint8_t* codes_dst, hipStream_t stream) {
+  const unsigned grid = (unsigned)(dst_rows < kMaxGroups ? dst_rows : kMaxGroups);
+  hipLaunchKernelGGL(gather_records_kernel, dim3(grid), dim3(kThreads), 0, stream,
+                     reinterpret_cast<const uint16_t*>(bits_src), scales_src,
+                     reinterpret_cast<const uint2*>(codes_src), src_rows, cols / 16, row_index, dst_rows,
+                     reinterpret_cast<uint16_t*>(bits_dst), scales_dst, reinterpret_cast<uint2*>(codes_dst));
   return hipGetLastError();
 }
 

@@ -12,11 +12,15 @@ constexpr uint32_t kAmaxMaxGroups = 2048;
 // Upper bound on the grid of the streaming kernels (one 4096-element tile per
 // workgroup below it; workgroups loop over the tensor beyond it).  A grid
 // that covers the tensor once streams faster than a persistent grid, whose
-// loop makes each tile's loads wait behind the previous tile's stores.
+// loop makes each tile's loads wait behind the previous tile's stores.  A
+// dispatch counts at most 2^32 - 1 work-items per dimension, so 256-thread
+// workgroups cap the grid below 2^24; 2^22 groups cover 2^34 elements (32 GiB
+// of bf16) in one pass.
 #ifndef TRACE_MAX_GROUPS
-#define TRACE_MAX_GROUPS (1u << 30)
+#define TRACE_MAX_GROUPS (1u << 22)
 #endif
 constexpr uint32_t kMaxGroups = TRACE_MAX_GROUPS;
+static_assert((uint64_t)TRACE_MAX_GROUPS * 256 <= 0xffffffffull, "grid exceeds 2^32 - 1 work-items");
 
 uint32_t amax_partial_count(uint64_t nblocks);
 
@@ -29,6 +33,9 @@ hipError_t launch_capture(const uint16_t* x, uint64_t nblocks, const float* ts, 
 hipError_t launch_fakequant(int mode, const uint16_t* x, uint64_t nblocks, const uint8_t* scales,
                             const float* ts, const uint8_t* side, uint16_t* y, uint8_t* mask,
                             uint8_t* qcodes, hipStream_t stream);
+hipError_t launch_gather_records(const uint8_t* bits_src, const uint8_t* scales_src, const uint8_t* codes_src,
+                                 uint64_t src_rows, uint64_t cols, const int64_t* row_index, uint64_t dst_rows,
+                                 uint8_t* bits_dst, uint8_t* scales_dst, uint8_t* codes_dst, hipStream_t stream);
 hipError_t launch_ste_bwd(const uint16_t* g, const uint8_t* mask, uint64_t nblocks, uint16_t* gin,
                           hipStream_t stream);
 

@@ -195,6 +195,29 @@ TRACE_API trace_status trace_full_info_fakequant_fwd(const uint16_t* x_train, in
 TRACE_API trace_status trace_ste_bwd(const uint16_t* grad_out, const uint8_t* mask,
                            int64_t n, uint16_t* grad_in, void* stream);
 
+/*
+ * Trainer-side readback of compact records: the training engine reads the
+ * rollout's per-site records back in its own row order (rcap.io post,
+ * limitations list: a cache tier holds the records and the trainer reads
+ * them back).  Destination row r receives source row row_index[r] of the
+ * bit-plane, the scale bytes and, when both code pointers are given, the
+ * 4-bit codes.  A row index outside [0, src_rows) produces an all-zero row:
+ * scale byte 0, i.e. zero-scale blocks for the trainer.
+ *   bits_src u8[src_rows*cols/8] (2-byte aligned), scales_src
+ *   u8[src_rows*cols/16], codes_src u8[src_rows*cols/2] (8-byte aligned);
+ *   the source pointers may be NULL when src_rows == 0;
+ *   row_index int64[dst_rows] in device memory, 8-byte aligned;
+ *   bits_dst, scales_dst, codes_dst sized for dst_rows (same alignments).
+ *   Codes are gathered iff codes_dst is non-NULL; codes_src without
+ *   codes_dst is TRACE_E_NULL.  cols % 16 == 0.  Outputs must not overlap
+ *   inputs (no in-place gather).  dst_rows == 0 is a no-op.
+ */
+TRACE_API trace_status trace_gather_records(const uint8_t* bits_src, const uint8_t* scales_src,
+                                            const uint8_t* codes_src, int64_t src_rows, int64_t cols,
+                                            const int64_t* row_index, int64_t dst_rows,
+                                            uint8_t* bits_dst, uint8_t* scales_dst,
+                                            uint8_t* codes_dst, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -49,6 +49,7 @@ from .trace import (
     compact_cache_bytes,
     decode_scales,
     full_info_fwd,
+    gather_records,
     guided_fwd,
     mismatch_stats,
     pack_bits,
@@ -64,7 +65,7 @@ __all__ = [
     "E2M1_MAGNITUDES", "E4M3FN_MAX", "bf16_to_f32", "e2m1_bracket",
     "e2m1_rne_index", "e4m3fn_decode", "e4m3fn_encode_rne_sat",
     "f32_to_bf16_rne", "BLOCK", "TENSOR_SCALE_DIVISOR", "block_scales",
-    "capture", "compact_cache_bytes", "decode_scales", "full_info_fwd",
+    "capture", "compact_cache_bytes", "decode_scales", "full_info_fwd", "gather_records",
     "guided_fwd", "mismatch_stats", "pack_bits", "pack_nibbles", "rne_fwd",
     "ste_bwd", "tensor_scale", "unpack_bits", "unpack_nibbles",
 ]

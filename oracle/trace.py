@@ -265,6 +265,30 @@ def ste_bwd(grad_bits, mask_bytes, n: int) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# trainer-side readback (the post's remark that the training engine must
+# read the rollout records back): records in the trainer's row order
+# --------------------------------------------------------------------------
+
+def gather_records(record, row_index, src_rows: int, cols: int) -> dict:
+    """Row gather of a compact record: destination row r is source row
+    ``row_index[r]`` of every plane (bits: cols/8 bytes per row, scales:
+    cols/16, codes: cols/2).  An index outside [0, src_rows) gives an
+    all-zero row, i.e. zero-scale blocks."""
+    per_row = {"bits": cols // 8, "scales": cols // BLOCK, "codes": cols // 2}
+    idx = np.asarray(row_index, dtype=np.int64).reshape(-1)
+    ok = (idx >= 0) & (idx < src_rows)
+    out = {}
+    for name, plane in record.items():
+        if plane is None:
+            continue
+        src = np.asarray(plane, dtype=np.uint8).reshape(src_rows, per_row[name])
+        dst = np.zeros((idx.size, per_row[name]), dtype=np.uint8)
+        dst[ok] = src[idx[ok]]
+        out[name] = dst.reshape(-1)
+    return out
+
+
+# --------------------------------------------------------------------------
 # diagnostics and accounting
 # --------------------------------------------------------------------------
 

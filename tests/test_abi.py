@@ -156,3 +156,36 @@ def test_binding_refuses_host_tensors():
         tr.capture(x, torch.zeros(1))
     with pytest.raises(TypeError):
         tr.ste_bwd(torch.zeros(32), torch.zeros(4, dtype=torch.uint8))
+
+
+def test_gather_records_validation():
+    f = L.trace_gather_records
+    bs, ss, cs, idx, bd, sd, cd = (A, A + 0x100000, A + 0x200000, A + 0x300000, A + 0x400000, A + 0x500000,
+                                   A + 0x600000)
+
+    def call(bs=bs, ss=ss, cs=None, src_rows=8, cols=64, idx=idx, dst_rows=5, bd=bd, sd=sd, cd=None):
+        q = lambda v: P(v) if v is not None else None
+        return f(q(bs), q(ss), q(cs), src_rows, cols, q(idx), dst_rows, q(bd), q(sd), q(cd), None)
+
+    assert call(idx=None) == E_NULL
+    assert call(bd=None) == E_NULL
+    assert call(cs=cs) == E_NULL          # codes source without a destination
+    assert call(cd=cd) == E_NULL          # codes destination without a source
+    assert call(cols=40) == E_SHAPE
+    assert call(dst_rows=-1) == E_SHAPE
+    assert call(idx=idx + 4) == E_ALIGN
+    assert call(bd=bd + 1) == E_ALIGN
+    assert call(cs=cs, cd=cd + 4) == E_ALIGN
+    assert call(bd=bs + 8) == E_ALIAS     # destination over source plane
+    assert call(sd=idx + 8) == E_ALIAS    # destination over the index array
+    assert call(dst_rows=0) == OK
+
+
+def test_build_script_loads_without_the_library():
+    """build() must work on a fresh tree (no libtrace.so yet): the build
+    script is loaded by path and does not import the binding."""
+    import subprocess, sys, os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import sys, __graft_entry__ as g; m = g._build_module(); "
+            "assert 'fp4_rollout_guided_amd' not in sys.modules; assert m.LIB.endswith('libtrace.so')")
+    subprocess.run([sys.executable, "-c", code], cwd=root, check=True)

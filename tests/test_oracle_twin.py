@@ -207,3 +207,29 @@ def test_ste_bwd_against_mask_definition():
     out = oracle.ste_bwd(g, np.packbits(m, bitorder="little"), n)
     for i in range(n):
         assert out[i] == (g[i] if m[i] else 0)
+
+
+def test_gather_records_against_row_loop():
+    """Pinned against a plain per-row, per-byte loop over the definition."""
+    rng = np.random.default_rng(12)
+    src_rows, cols, dst_rows = 9, 64, 13
+    rec = {"bits": rng.integers(0, 256, src_rows * cols // 8, dtype=np.uint8),
+           "scales": rng.integers(0, 127, src_rows * cols // 16, dtype=np.uint8),
+           "codes": rng.integers(0, 256, src_rows * cols // 2, dtype=np.uint8)}
+    idx = rng.integers(-3, src_rows + 3, dst_rows)
+    out = oracle.gather_records(rec, idx, src_rows, cols)
+    for name, per in (("bits", cols // 8), ("scales", cols // 16), ("codes", cols // 2)):
+        for r in range(dst_rows):
+            for k in range(per):
+                want = rec[name][idx[r] * per + k] if 0 <= idx[r] < src_rows else 0
+                assert out[name][r * per + k] == want
+    # a gathered record drives the trainer exactly like the rows it came from
+    xr = F.f32_to_bf16_rne(rng.standard_normal(src_rows * cols).astype(np.float32))
+    ts = oracle.tensor_scale(xr)
+    cap = oracle.capture(xr, ts)
+    perm = rng.permutation(src_rows)
+    g = oracle.gather_records({"bits": cap["bits"], "scales": cap["scales"]}, perm, src_rows, cols)
+    xt = xr.reshape(src_rows, cols)[perm].reshape(-1)
+    a = oracle.guided_fwd(xt, g["scales"], ts, g["bits"])
+    b = oracle.guided_fwd(xr, cap["scales"], ts, cap["bits"])
+    assert np.array_equal(a["y"], b["y"].reshape(src_rows, cols)[perm].reshape(-1))
