@@ -50,6 +50,11 @@ from .trace import (
     decode_scales,
     full_info_fwd,
     gather_records,
+    grouped_capture,
+    grouped_full_info_fwd,
+    grouped_guided_fwd,
+    grouped_rne_fwd,
+    grouped_tensor_scale,
     guided_fwd,
     mismatch_stats,
     pack_bits,
@@ -66,6 +71,8 @@ __all__ = [
     "e2m1_rne_index", "e4m3fn_decode", "e4m3fn_encode_rne_sat",
     "f32_to_bf16_rne", "BLOCK", "TENSOR_SCALE_DIVISOR", "block_scales",
     "capture", "compact_cache_bytes", "decode_scales", "full_info_fwd", "gather_records",
+    "grouped_capture", "grouped_full_info_fwd", "grouped_guided_fwd", "grouped_rne_fwd",
+    "grouped_tensor_scale",
     "guided_fwd", "mismatch_stats", "pack_bits", "pack_nibbles", "rne_fwd",
     "ste_bwd", "tensor_scale", "unpack_bits", "unpack_nibbles",
 ]

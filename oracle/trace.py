@@ -289,6 +289,64 @@ def gather_records(record, row_index, src_rows: int, cols: int) -> dict:
 
 
 # --------------------------------------------------------------------------
+# per-expert tensor scales for packed MoE rows: the routed-expert sites hold
+# the rows of every expert back to back, and each expert's rows form their
+# own tensor (its own amax and tensor scale)
+# --------------------------------------------------------------------------
+
+def _group_slices(offsets, rows: int):
+    """Row ranges of the groups: group g is rows [offsets[g], offsets[g+1]).
+    The offsets must start at 0, end at ``rows`` and never decrease."""
+    off = [int(v) for v in np.asarray(offsets, dtype=np.int64).reshape(-1)]
+    if len(off) < 2 or off[0] != 0 or off[-1] != rows or any(b < a for a, b in zip(off, off[1:])):
+        raise ValueError("group offsets must run from 0 to rows without decreasing")
+    return [(off[g], off[g + 1]) for g in range(len(off) - 1)]
+
+
+def grouped_tensor_scale(x_bits, rows: int, cols: int, offsets) -> np.ndarray:
+    """One tensor scale per group of rows (fp32[groups]): the tensor scale
+    of the group's rows taken as a tensor of their own (0 for an empty
+    group)."""
+    x = np.asarray(x_bits, dtype=np.uint16).reshape(rows, cols)
+    return np.array([tensor_scale(x[a:b]) for a, b in _group_slices(offsets, rows)], dtype=np.float32)
+
+
+def _per_group(fn, rows, cols, offsets, ts, planes):
+    """Apply ``fn(group's planes..., ts[g])`` to each group's rows and join
+    the results in row order.  ``planes`` maps a name to (array, bytes per
+    row)."""
+    parts = []
+    ts = np.asarray(ts, dtype=np.float32).reshape(-1)
+    for g, (a, b) in enumerate(_group_slices(offsets, rows)):
+        args = [np.asarray(arr).reshape(rows, per_row)[a:b].reshape(-1) for arr, per_row in planes]
+        parts.append(fn(*args, ts[g]))
+    keys = [k for k in parts[0] if parts[0][k] is not None] if parts else []
+    return {k: np.concatenate([p[k] for p in parts]) for k in keys}
+
+
+def grouped_capture(x_bits, rows: int, cols: int, offsets, ts, with_codes: bool = False) -> dict:
+    """``capture`` of each group's rows with that group's tensor scale."""
+    return _per_group(lambda x, t: capture(x, t, with_codes), rows, cols, offsets, ts, [(x_bits, cols)])
+
+
+def grouped_guided_fwd(x_bits, rows: int, cols: int, offsets, scale_bytes, ts, bits) -> dict:
+    """``guided_fwd`` of each group's rows with that group's tensor scale."""
+    return _per_group(lambda x, sb, c, t: guided_fwd(x, sb, t, c), rows, cols, offsets, ts,
+                      [(x_bits, cols), (scale_bytes, cols // BLOCK), (bits, cols // 8)])
+
+
+def grouped_rne_fwd(x_bits, rows: int, cols: int, offsets, scale_bytes, ts) -> dict:
+    """``rne_fwd`` of each group's rows with that group's tensor scale."""
+    return _per_group(rne_fwd, rows, cols, offsets, ts, [(x_bits, cols), (scale_bytes, cols // BLOCK)])
+
+
+def grouped_full_info_fwd(x_bits, rows: int, cols: int, offsets, scale_bytes, ts, roll_codes) -> dict:
+    """``full_info_fwd`` of each group's rows with that group's tensor scale."""
+    return _per_group(lambda x, sb, rc, t: full_info_fwd(x, sb, t, rc), rows, cols, offsets, ts,
+                      [(x_bits, cols), (scale_bytes, cols // BLOCK), (roll_codes, cols // 2)])
+
+
+# --------------------------------------------------------------------------
 # diagnostics and accounting
 # --------------------------------------------------------------------------
 

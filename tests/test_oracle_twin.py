@@ -233,3 +233,53 @@ def test_gather_records_against_row_loop():
     a = oracle.guided_fwd(xt, g["scales"], ts, g["bits"])
     b = oracle.guided_fwd(xr, cap["scales"], ts, cap["bits"])
     assert np.array_equal(a["y"], b["y"].reshape(src_rows, cols)[perm].reshape(-1))
+
+
+def test_grouped_path_matches_exact_twin():
+    """Per-expert tensor scales: every group of rows (one empty) gets its own
+    amax and tensor scale; capture and all three forwards of each row use its
+    group's scale.  Checked element by element against the exact twin."""
+    rng = np.random.default_rng(21)
+    rows, cols = 7, 32
+    offsets = [0, 2, 2, 5, 7]
+    mags = [1.0, 40.0, 1e-3, 7.0]  # a different range per group
+    vals = np.zeros((rows, cols))
+    for g, (a, b) in enumerate(zip(offsets, offsets[1:])):
+        vals[a:b] = rng.standard_t(4, (b - a, cols)) * mags[g]
+    vals[3, 5] = np.nan
+    xr = _bf16(vals.reshape(-1))
+    xt = _bf16(F.bf16_to_f32(xr) * (1 + 0.05 * rng.standard_normal(xr.size)))
+    ts = oracle.grouped_tensor_scale(xr, rows, cols, offsets)
+    cap = oracle.grouped_capture(xr, rows, cols, offsets, ts, with_codes=True)
+    gd = oracle.grouped_guided_fwd(xt, rows, cols, offsets, cap["scales"], ts, cap["bits"])
+    rn = oracle.grouped_rne_fwd(xt, rows, cols, offsets, cap["scales"], ts)
+    fi = oracle.grouped_full_info_fwd(xt, rows, cols, offsets, cap["scales"], ts, cap["codes"])
+
+    fr, ft = F.bf16_to_f32(xr), F.bf16_to_f32(xt)
+    roll = oracle.unpack_nibbles(cap["codes"], xr.size)
+    bits = oracle.unpack_bits(cap["bits"], xr.size)
+    for g, (a, b) in enumerate(zip(offsets, offsets[1:])):
+        want_ts = twin_tensor_scale(list(fr[a * cols:b * cols])) if b > a else 0.0
+        assert np.float32(ts[g]) == np.float32(want_ts), (g, ts[g], want_ts)
+        for r in range(a, b):
+            for blk in range(cols // 16):
+                i0 = r * cols + blk * 16
+                byte = twin_block_byte(list(fr[i0:i0 + 16]), np.float32(want_ts))
+                assert cap["scales"][i0 // 16] == byte, (r, blk)
+                s = twin_scale(byte, np.float32(want_ts))
+                for i in range(i0, i0 + 16):
+                    code, _, _ = twin_element(fr[i], s, "rne")
+                    assert roll[i] == code and bits[i] == (code & 1), i
+                    for out, rule, kw in ((gd, "guided", {"c": int(bits[i])}), (rn, "rne", {}),
+                                          (fi, "full", {"roll_code": int(roll[i])})):
+                        c2, m2, y2 = twin_element(ft[i], s, rule, **kw)
+                        assert oracle.unpack_nibbles(out["codes"], xr.size)[i] == c2, (rule, i)
+                        assert oracle.unpack_bits(out["mask"], xr.size)[i] == m2, (rule, i)
+                        assert out["y"][i] == _bf16([y2])[0], (rule, i)
+
+
+def test_grouped_offsets_are_validated():
+    x = np.zeros(64, np.uint16)
+    for bad in ([0, 3, 2, 4], [1, 4], [0, 3], [0]):
+        with pytest.raises(ValueError):
+            oracle.grouped_tensor_scale(x, 4, 16, bad)
