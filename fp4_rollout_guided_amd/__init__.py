@@ -13,6 +13,10 @@ Functions mirror the C ABI in ``include/trace.h``:
     rne_fakequant_fwd(x_train, scales, ts)           -> (y, mask, qcodes)
     full_info_fakequant_fwd(x_train, scales, ts, codes) -> (y, mask, qcodes)
     gather_records(bits, scales, codes, cols, row_index) -> (bits, scales, codes)
+    grouped_tensor_scale(x, offsets)                 -> ts (fp32[groups])
+    grouped_capture / grouped_guided_fakequant_fwd / grouped_rne_fakequant_fwd /
+    grouped_full_info_fakequant_fwd: as above, with one tensor scale per group
+    of rows (per-expert scales of packed MoE rows; offsets int64[groups + 1])
     ste_bwd(grad_out, mask)                          -> grad_in
 
 and ``GuidedFakeQuant`` wraps the forward/backward pair as an autograd
@@ -26,6 +30,8 @@ import torch
 __all__ = [
     "TraceError", "LIB_PATH", "lib", "abi_version", "tensor_scale", "capture",
     "guided_fakequant_fwd", "rne_fakequant_fwd", "full_info_fakequant_fwd", "ste_bwd", "gather_records",
+    "grouped_tensor_scale", "grouped_capture", "grouped_guided_fakequant_fwd", "grouped_rne_fakequant_fwd",
+    "grouped_full_info_fakequant_fwd",
     "GuidedFakeQuant",
     "STATUS",
 ]
@@ -64,6 +70,12 @@ def _load():
         "trace_full_info_fakequant_fwd": ([p, i64, i64, p, p, p, p, p, p, p], st),
         "trace_ste_bwd": ([p, p, i64, p, p], st),
         "trace_gather_records": ([p, p, p, i64, i64, p, i64, p, p, p, p], st),
+        "trace_grouped_tensor_scale_workspace_bytes": ([i64], sz),
+        "trace_grouped_tensor_scale": ([p, i64, i64, p, i64, p, sz, p, p], st),
+        "trace_grouped_capture": ([p, i64, i64, p, i64, p, p, p, p, p], st),
+        "trace_grouped_guided_fakequant_fwd": ([p, i64, i64, p, i64, p, p, p, p, p, p, p], st),
+        "trace_grouped_rne_fakequant_fwd": ([p, i64, i64, p, i64, p, p, p, p, p, p], st),
+        "trace_grouped_full_info_fakequant_fwd": ([p, i64, i64, p, i64, p, p, p, p, p, p, p], st),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -220,6 +232,88 @@ def gather_records(bits, scales, codes, cols, row_index):
                                     dst_rows, _ptr(bits_d), _ptr(scales_d), _ptr(codes_d), _stream(bits)),
            "trace_gather_records")
     return bits_d, scales_d, codes_d
+
+
+def _offsets(offsets, rows):
+    if not offsets.is_cuda or offsets.dtype != torch.int64 or not offsets.is_contiguous() or offsets.dim() != 1:
+        raise ValueError("offsets must be a contiguous 1-D int64 device tensor of groups + 1 entries")
+    groups = offsets.numel() - 1
+    if groups < 1:
+        raise ValueError("at least one group is required")
+    return groups
+
+
+def grouped_tensor_scale(x, offsets, out=None, workspace=None):
+    """One tensor scale per group of rows: ts[g] = fl32(amax over rows
+    [offsets[g], offsets[g+1]) / 2688), as a float32[groups] device tensor."""
+    _bf16(x, "x")
+    rows, cols = _rows_cols(x)
+    groups = _offsets(offsets, rows)
+    need = lib.trace_grouped_tensor_scale_workspace_bytes(rows)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty(groups, dtype=torch.float32, device=x.device)
+    _check(lib.trace_grouped_tensor_scale(_ptr(x), rows, cols, _ptr(offsets), groups, _ptr(workspace),
+                                          workspace.numel(), _ptr(out), _stream(x)), "trace_grouped_tensor_scale")
+    return out
+
+
+def grouped_capture(x_roll, offsets, ts, want_codes=False, scales=None, bits=None, codes=None):
+    """``capture`` with ts[group of the row] as each row's tensor scale."""
+    _bf16(x_roll, "x_roll")
+    rows, cols = _rows_cols(x_roll)
+    groups = _offsets(offsets, rows)
+    n = rows * cols
+    scales = _u8(n // 16, x_roll, scales, "scales")
+    bits = _u8(n // 8, x_roll, bits, "bits")
+    if want_codes or codes is not None:
+        codes = _u8(n // 2, x_roll, codes, "codes")
+    _check(lib.trace_grouped_capture(_ptr(x_roll), rows, cols, _ptr(offsets), groups, _ptr(ts), _ptr(scales),
+                                     _ptr(bits), _ptr(codes), _stream(x_roll)), "trace_grouped_capture")
+    return scales, bits, codes
+
+
+def _grouped_fwd(mode, x, offsets, scales, ts, side, y, mask, want_codes, qcodes):
+    _bf16(x, "x_train")
+    rows, cols = _rows_cols(x)
+    groups = _offsets(offsets, rows)
+    n = rows * cols
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _bf16(y, "y")
+    mask = _u8(n // 8, x, mask, "mask")
+    if want_codes or qcodes is not None:
+        qcodes = _u8(n // 2, x, qcodes, "qcodes")
+    head = (_ptr(x), rows, cols, _ptr(offsets), groups, _ptr(scales), _ptr(ts))
+    tail = (_ptr(y), _ptr(mask), _ptr(qcodes), _stream(x))
+    if mode == "guided":
+        st, name = lib.trace_grouped_guided_fakequant_fwd(*head, _ptr(side), *tail), "trace_grouped_guided_fakequant_fwd"
+    elif mode == "full":
+        st, name = (lib.trace_grouped_full_info_fakequant_fwd(*head, _ptr(side), *tail),
+                    "trace_grouped_full_info_fakequant_fwd")
+    else:
+        st, name = lib.trace_grouped_rne_fakequant_fwd(*head, *tail), "trace_grouped_rne_fakequant_fwd"
+    _check(st, name)
+    return y, mask, qcodes
+
+
+def grouped_guided_fakequant_fwd(x_train, offsets, scales, ts, bits, y=None, mask=None, want_codes=False,
+                                 qcodes=None):
+    """``guided_fakequant_fwd`` with one tensor scale per group of rows."""
+    return _grouped_fwd("guided", x_train, offsets, scales, ts, bits, y, mask, want_codes, qcodes)
+
+
+def grouped_rne_fakequant_fwd(x_train, offsets, scales, ts, y=None, mask=None, want_codes=False, qcodes=None):
+    """``rne_fakequant_fwd`` with one tensor scale per group of rows."""
+    return _grouped_fwd("rne", x_train, offsets, scales, ts, None, y, mask, want_codes, qcodes)
+
+
+def grouped_full_info_fakequant_fwd(x_train, offsets, scales, ts, codes, y=None, mask=None, want_codes=False,
+                                    qcodes=None):
+    """``full_info_fakequant_fwd`` with one tensor scale per group of rows."""
+    return _grouped_fwd("full", x_train, offsets, scales, ts, codes, y, mask, want_codes, qcodes)
 
 
 class GuidedFakeQuant(torch.autograd.Function):

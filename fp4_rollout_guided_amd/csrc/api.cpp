@@ -95,28 +95,58 @@ trace_status trace_tensor_scale(const uint16_t* x, int64_t n, void* workspace, s
                                                     static_cast<hipStream_t>(stream)));
 }
 
-trace_status trace_capture(const uint16_t* x_roll, int64_t rows, int64_t cols, const float* ts,
-                           uint8_t* scales, uint8_t* bits, uint8_t* codes, void* stream) {
+// Row groups of a grouped call: 1 <= groups <= kMaxRowGroups and an
+// 8-byte-aligned offsets array of groups + 1 entries.  Fills *spec.
+trace_status group_spec(const int64_t* offsets, int64_t groups, int64_t rows, int64_t cols,
+                        trace_host::GroupSpec* spec) {
+  if (!offsets) return TRACE_E_NULL;
+  if (groups < 1 || groups > (int64_t)trace_host::kMaxRowGroups) return TRACE_E_SHAPE;
+  if (!aligned(offsets, 8)) return TRACE_E_ALIGN;
+  *spec = trace_host::GroupSpec{offsets, (uint64_t)groups, (uint64_t)rows, (uint64_t)cols};
+  return TRACE_OK;
+}
+
+static trace_status capture(const uint16_t* x_roll, int64_t rows, int64_t cols, const int64_t* offsets,
+                            int64_t groups, bool grouped, const float* ts, uint8_t* scales, uint8_t* bits,
+                            uint8_t* codes, void* stream) {
   uint64_t n = 0;
   if (trace_status st = site_size(rows, cols, &n)) return st;
+  trace_host::GroupSpec spec{};
+  if (grouped)
+    if (trace_status st = group_spec(offsets, groups, rows, cols, &spec)) return st;
   if (n == 0) return TRACE_OK;
   if (!x_roll || !ts || !scales || !bits) return TRACE_E_NULL;
   if (!aligned(x_roll, 16) || !aligned(ts, 4) || !aligned(bits, 2) || (codes && !aligned(codes, 8)))
     return TRACE_E_ALIGN;
+  const uint64_t ts_len = 4 * (grouped ? spec.count : 1);
   const Range outs[3] = {rng(scales, n / 16), rng(bits, n / 8), rng(codes, codes ? n / 2 : 0)};
-  const Range ins[2] = {rng(x_roll, 2 * n), rng(ts, 4)};
-  if (trace_status st = check_alias(outs, 3, ins, 2)) return st;
-  return hip_status(trace_host::launch_capture(x_roll, n / 16, ts, scales, bits, codes,
+  const Range ins[3] = {rng(x_roll, 2 * n), rng(ts, ts_len), rng(offsets, grouped ? 8 * (spec.count + 1) : 0)};
+  if (trace_status st = check_alias(outs, 3, ins, 3)) return st;
+  return hip_status(trace_host::launch_capture(x_roll, n / 16, ts, grouped ? &spec : nullptr, scales, bits, codes,
                                                static_cast<hipStream_t>(stream)));
+}
+
+trace_status trace_capture(const uint16_t* x_roll, int64_t rows, int64_t cols, const float* ts,
+                           uint8_t* scales, uint8_t* bits, uint8_t* codes, void* stream) {
+  return capture(x_roll, rows, cols, nullptr, 0, false, ts, scales, bits, codes, stream);
+}
+
+trace_status trace_grouped_capture(const uint16_t* x_roll, int64_t rows, int64_t cols, const int64_t* offsets,
+                                   int64_t groups, const float* ts, uint8_t* scales, uint8_t* bits,
+                                   uint8_t* codes, void* stream) {
+  return capture(x_roll, rows, cols, offsets, groups, true, ts, scales, bits, codes, stream);
 }
 
 // mode 0: RNE; 1: guided (side = bit-plane, n/8 bytes, 2-byte aligned);
 // 2: full information (side = codes, n/2 bytes, 8-byte aligned).
-static trace_status fakequant(int mode, const uint16_t* x, int64_t rows, int64_t cols, const uint8_t* scales,
-                              const float* ts, const uint8_t* side, uint16_t* y, uint8_t* mask, uint8_t* qcodes,
-                              void* stream) {
+static trace_status fakequant(int mode, const uint16_t* x, int64_t rows, int64_t cols, const int64_t* offsets,
+                              int64_t groups, bool grouped, const uint8_t* scales, const float* ts,
+                              const uint8_t* side, uint16_t* y, uint8_t* mask, uint8_t* qcodes, void* stream) {
   uint64_t n = 0;
   if (trace_status st = site_size(rows, cols, &n)) return st;
+  trace_host::GroupSpec spec{};
+  if (grouped)
+    if (trace_status st = group_spec(offsets, groups, rows, cols, &spec)) return st;
   if (n == 0) return TRACE_OK;
   if (!x || !scales || !ts || (mode != 0 && !side) || !y || !mask) return TRACE_E_NULL;
   const uint64_t side_len = mode == 1 ? n / 8 : (mode == 2 ? n / 2 : 0);
@@ -124,29 +154,74 @@ static trace_status fakequant(int mode, const uint16_t* x, int64_t rows, int64_t
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ts, 4) || !aligned(mask, 2) ||
       (mode != 0 && !aligned(side, side_align)) || (qcodes && !aligned(qcodes, 8)))
     return TRACE_E_ALIGN;
+  const uint64_t ts_len = 4 * (grouped ? spec.count : 1);
   const Range outs[3] = {rng(y, 2 * n), rng(mask, n / 8), rng(qcodes, qcodes ? n / 2 : 0)};
-  const Range ins[4] = {rng(x, 2 * n), rng(scales, n / 16), rng(ts, 4), rng(side, side_len)};
-  if (trace_status st = check_alias(outs, 3, ins, 4, /*inplace_out=*/0, /*inplace_in=*/0)) return st;
-  return hip_status(trace_host::launch_fakequant(mode, x, n / 16, scales, ts, side, y, mask, qcodes,
-                                                 static_cast<hipStream_t>(stream)));
+  const Range ins[5] = {rng(x, 2 * n), rng(scales, n / 16), rng(ts, ts_len), rng(side, side_len),
+                        rng(offsets, grouped ? 8 * (spec.count + 1) : 0)};
+  if (trace_status st = check_alias(outs, 3, ins, 5, /*inplace_out=*/0, /*inplace_in=*/0)) return st;
+  return hip_status(trace_host::launch_fakequant(mode, x, n / 16, scales, ts, grouped ? &spec : nullptr, side, y,
+                                                 mask, qcodes, static_cast<hipStream_t>(stream)));
 }
 
 trace_status trace_guided_fakequant_fwd(const uint16_t* x_train, int64_t rows, int64_t cols,
                                         const uint8_t* scales, const float* ts, const uint8_t* bits,
                                         uint16_t* y, uint8_t* mask, uint8_t* qcodes, void* stream) {
-  return fakequant(1, x_train, rows, cols, scales, ts, bits, y, mask, qcodes, stream);
+  return fakequant(1, x_train, rows, cols, nullptr, 0, false, scales, ts, bits, y, mask, qcodes, stream);
 }
 
 trace_status trace_rne_fakequant_fwd(const uint16_t* x_train, int64_t rows, int64_t cols,
                                      const uint8_t* scales, const float* ts, uint16_t* y, uint8_t* mask,
                                      uint8_t* qcodes, void* stream) {
-  return fakequant(0, x_train, rows, cols, scales, ts, nullptr, y, mask, qcodes, stream);
+  return fakequant(0, x_train, rows, cols, nullptr, 0, false, scales, ts, nullptr, y, mask, qcodes, stream);
 }
 
 trace_status trace_full_info_fakequant_fwd(const uint16_t* x_train, int64_t rows, int64_t cols,
                                            const uint8_t* scales, const float* ts, const uint8_t* codes,
                                            uint16_t* y, uint8_t* mask, uint8_t* qcodes, void* stream) {
-  return fakequant(2, x_train, rows, cols, scales, ts, codes, y, mask, qcodes, stream);
+  return fakequant(2, x_train, rows, cols, nullptr, 0, false, scales, ts, codes, y, mask, qcodes, stream);
+}
+
+trace_status trace_grouped_guided_fakequant_fwd(const uint16_t* x_train, int64_t rows, int64_t cols,
+                                                const int64_t* offsets, int64_t groups, const uint8_t* scales,
+                                                const float* ts, const uint8_t* bits, uint16_t* y, uint8_t* mask,
+                                                uint8_t* qcodes, void* stream) {
+  return fakequant(1, x_train, rows, cols, offsets, groups, true, scales, ts, bits, y, mask, qcodes, stream);
+}
+
+trace_status trace_grouped_rne_fakequant_fwd(const uint16_t* x_train, int64_t rows, int64_t cols,
+                                             const int64_t* offsets, int64_t groups, const uint8_t* scales,
+                                             const float* ts, uint16_t* y, uint8_t* mask, uint8_t* qcodes,
+                                             void* stream) {
+  return fakequant(0, x_train, rows, cols, offsets, groups, true, scales, ts, nullptr, y, mask, qcodes, stream);
+}
+
+trace_status trace_grouped_full_info_fakequant_fwd(const uint16_t* x_train, int64_t rows, int64_t cols,
+                                                   const int64_t* offsets, int64_t groups, const uint8_t* scales,
+                                                   const float* ts, const uint8_t* codes, uint16_t* y,
+                                                   uint8_t* mask, uint8_t* qcodes, void* stream) {
+  return fakequant(2, x_train, rows, cols, offsets, groups, true, scales, ts, codes, y, mask, qcodes, stream);
+}
+
+size_t trace_grouped_tensor_scale_workspace_bytes(int64_t rows) {
+  if (rows < 0) return 0;
+  return (size_t)rows * sizeof(uint32_t);
+}
+
+trace_status trace_grouped_tensor_scale(const uint16_t* x, int64_t rows, int64_t cols, const int64_t* offsets,
+                                        int64_t groups, void* workspace, size_t workspace_bytes, float* ts_out,
+                                        void* stream) {
+  uint64_t n = 0;
+  if (trace_status st = site_size(rows, cols, &n)) return st;
+  trace_host::GroupSpec spec{};
+  if (trace_status st = group_spec(offsets, groups, rows, cols, &spec)) return st;
+  if (!ts_out || (rows > 0 && !workspace) || (n > 0 && !x)) return TRACE_E_NULL;
+  if (workspace_bytes < trace_grouped_tensor_scale_workspace_bytes(rows)) return TRACE_E_SHAPE;
+  if (!aligned(x, 16) || !aligned(workspace, 4) || !aligned(ts_out, 4)) return TRACE_E_ALIGN;
+  const Range outs[2] = {rng(workspace, trace_grouped_tensor_scale_workspace_bytes(rows)), rng(ts_out, 4 * spec.count)};
+  const Range ins[2] = {rng(x, 2 * n), rng(offsets, 8 * (spec.count + 1))};
+  if (trace_status st = check_alias(outs, 2, ins, 2)) return st;
+  return hip_status(trace_host::launch_grouped_tensor_scale(x, spec, static_cast<uint32_t*>(workspace), ts_out,
+                                                            static_cast<hipStream_t>(stream)));
 }
 
 trace_status trace_ste_bwd(const uint16_t* grad_out, const uint8_t* mask, int64_t n, uint16_t* grad_in,

@@ -1,5 +1,6 @@
-// libtrace kernels for gfx950: tensor amax, capture, guided / RNE fake-quant
-// forward and STE backward.
+// libtrace kernels for gfx950: tensor amax, capture, guided / RNE /
+// full-information fake-quant forward, STE backward, per-expert (row-group)
+// variants of the tensor scale, capture and forwards, and the record gather.
 //
 // Work decomposition: one lane owns one 16-element NVFP4 block, i.e. 32
 // contiguous bytes of bf16 (two 128-bit loads), its scale byte, and 16 bits of
@@ -336,24 +337,116 @@ __global__ __launch_bounds__(kThreads) void amax_finalize_kernel(const uint32_t*
 }
 
 // ---------------------------------------------------------------------------
+// row groups (per-expert tensor scales of packed MoE rows): group g holds
+// rows [off[g], off[g+1]).  Offsets are clamped to [0, rows] when read, so
+// any offsets array (even a decreasing one) keeps every access in bounds;
+// only nondecreasing offsets give a meaningful assignment.
+// ---------------------------------------------------------------------------
+struct RowGroups {
+  const int64_t* off;  // int64[count + 1]; entries 1..count-1 are read by the block lookup
+  uint32_t count;
+  uint64_t rows;
+  uint64_t bpr;        // 16-element blocks per row
+};
+
+__device__ __forceinline__ uint64_t group_row(const RowGroups& G, uint32_t g) {
+  const int64_t o = G.off[g];
+  return o < 0 ? 0 : ((uint64_t)o > G.rows ? G.rows : (uint64_t)o);
+}
+
+// Group of block b: a wave-uniform binary search from the wave's first active
+// block (scalar loads), then a per-lane walk over the group starts that fall
+// inside the wave's span (none in the common case).
+__device__ __forceinline__ uint32_t group_of_block(const RowGroups& G, uint64_t b) {
+  const uint32_t b0lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t b0hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint64_t b0 = ((uint64_t)b0hi << 32) | b0lo;
+  uint32_t lo = 0, hi = G.count;
+  while (hi - lo > 1) {
+    const uint32_t mid = (lo + hi) >> 1;
+    if (group_row(G, mid) * G.bpr <= b0) lo = mid; else hi = mid;
+  }
+  uint32_t g = lo;
+  while (g + 1 < G.count && group_row(G, g + 1) * G.bpr <= b) ++g;
+  return g;
+}
+
+// Grouped tensor scale, pass 1: the magnitude-bit maximum of every row (NaN
+// excluded as in amax_partial_kernel); one wave per row.
+__global__ __launch_bounds__(kThreads) void row_amax_kernel(const uint4* __restrict__ x, uint64_t rows,
+                                                            uint64_t vec_per_row,
+                                                            uint32_t* __restrict__ row_amax) {
+  const uint32_t lane = threadIdx.x & 63;
+  for (uint64_t r = (uint64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); r < rows;
+       r += (uint64_t)gridDim.x * (kThreads / 64)) {
+    s16x2 best = {0, 0};
+    for (uint64_t c = lane; c < vec_per_row; c += 64) {
+      const uint4 v = x[r * vec_per_row + c];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t m = (w[k] & 0x7fff7fffu) + 0x007f007fu;
+        s16x2 vv;
+        __builtin_memcpy(&vv, &m, 4);
+        best = __builtin_elementwise_max(best, vv);
+      }
+    }
+    const int lo = best.x, hi = best.y;
+    const int m = lo > hi ? lo : hi;
+    const uint32_t rmax = wave_max_u32(m > 0x7f ? (uint32_t)(m - 0x7f) : 0u);
+    if (lane == 0) row_amax[r] = rmax;
+  }
+}
+
+// Grouped tensor scale, pass 2: one workgroup per group folds its rows' maxima.
+__global__ __launch_bounds__(kThreads) void group_amax_finalize_kernel(const uint32_t* __restrict__ row_amax,
+                                                                       RowGroups G, float* __restrict__ ts_out) {
+  const uint32_t g = blockIdx.x;
+  const uint64_t r0 = g == 0 ? 0 : group_row(G, g);
+  const uint64_t r1 = g + 1 == G.count ? G.rows : group_row(G, g + 1);
+  uint32_t best = 0;
+  for (uint64_t r = r0 + threadIdx.x; r < r1; r += kThreads) best = max(best, row_amax[r]);
+  best = block_max_u32(best);
+  if (threadIdx.x == 0) ts_out[g] = __uint_as_float(best << 16) / kTensorDiv;
+}
+
+// ---------------------------------------------------------------------------
 // capture
 // ---------------------------------------------------------------------------
+// Per-tensor-scale constants of the capture: validity, the range in which the
+// block-scale divisions are exact on the fast path, 1/ts as a double word,
+// and the v1 bound beyond which the scale byte saturates.
+struct CaptureScale {
+  float ts, rthi, rtlo, lim;
+  bool valid, slow;
+};
+
+__device__ __forceinline__ CaptureScale capture_scale(float ts) {
+  CaptureScale c;
+  c.ts = ts;
+  c.valid = ts > 0.f && ts <= 3.40282347e38f;
+  c.slow = c.valid && !(ts >= 0x1p-100f && ts <= 0x1p100f);
+  c.rthi = 1.0f / (c.valid ? ts : 1.f);
+  c.rtlo = __builtin_fmaf(-(c.valid ? ts : 1.f), c.rthi, 1.0f) * c.rthi;
+  c.lim = 512.f * ts;  // v1 beyond lim gives v > 448: saturates
+  return c;
+}
+
+template <bool kGrouped>
 __global__ __launch_bounds__(kThreads) void capture_kernel(const uint4* __restrict__ x, uint64_t nblocks,
-                                                           const float* __restrict__ ts_ptr,
+                                                           const float* __restrict__ ts_ptr, RowGroups groups,
                                                            uint8_t* __restrict__ scales,
                                                            uint16_t* __restrict__ bits,
                                                            uint2* __restrict__ codes) {
-  const float ts = *ts_ptr;
-  const bool ts_valid = ts > 0.f && ts <= 3.40282347e38f;
-  const bool ts_slow = ts_valid && !(ts >= 0x1p-100f && ts <= 0x1p100f);
-  const float rthi = 1.0f / (ts_valid ? ts : 1.f);
-  const float rtlo = __builtin_fmaf(-(ts_valid ? ts : 1.f), rthi, 1.0f) * rthi;
-  const float lim = 512.f * ts;                    // v1 beyond lim gives v > 448: saturates
+  CaptureScale cs;
+  if (!kGrouped) cs = capture_scale(*ts_ptr);
   const float r6hi = 1.0f / 6.0f;
   const float r6lo = __builtin_fmaf(-6.0f, r6hi, 1.0f) * r6hi;
 
   const uint64_t stride = (uint64_t)gridDim.x * kThreads;
   for (uint64_t b = (uint64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks; b += stride) {
+    if (kGrouped) cs = capture_scale(ts_ptr[group_of_block(groups, b)]);
+    const float ts = cs.ts;
     uint32_t w[8];
     load_block(x, b, w);
 
@@ -374,12 +467,12 @@ __global__ __launch_bounds__(kThreads) void capture_kernel(const uint4* __restri
     const float amax = __uint_as_float(amax_bits << 16);
     // a zero block, or amax >= 2^-100 (bf16 bits 0x0d80) keeps the two divisions
     // exact; a NaN or infinite element shows as amax_bits >= 0x7f80
-    bool bad = ts_slow || (amax_bits - 1u) < 0x0d7fu || amax_bits >= 0x7f80u;
+    bool bad = cs.slow || (amax_bits - 1u) < 0x0d7fu || amax_bits >= 0x7f80u;
 
-    const float v1 = __builtin_amdgcn_fmed3f(div_fast_u(amax, 6.0f, r6hi, r6lo), 0.f, lim);
-    const float v = div_fast_u(v1, ts, rthi, rtlo);
+    const float v1 = __builtin_amdgcn_fmed3f(div_fast_u(amax, 6.0f, r6hi, r6lo), 0.f, cs.lim);
+    const float v = div_fast_u(v1, ts, cs.rthi, cs.rtlo);
     uint32_t sb = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(v, 0.f, 448.f), 0.f, 0, false);
-    sb = ts_valid ? sb : 0u;
+    sb = cs.valid ? sb : 0u;
 
     const ScaleEntry e = make_scale_entry(sb, ts);
     bad |= !(e.dhi == e.dhi);  // scale outside the fast range
@@ -435,18 +528,19 @@ __device__ __forceinline__ uint32_t full_info_select(uint32_t F, uint32_t P, uin
   return F + ((gt & same) >> 3 & ~t & 0x11111111u);
 }
 
-template <int kMode>  // 0 = RNE, 1 = guided by the cached bit, 2 = full information
+template <int kMode, bool kGrouped>  // mode 0 = RNE, 1 = guided by the cached bit, 2 = full information
 __global__ __launch_bounds__(kThreads) void fakequant_kernel(const uint4* __restrict__ x, uint64_t nblocks,
                                                              const uint8_t* __restrict__ scales,
-                                                             const float* __restrict__ ts_ptr,
+                                                             const float* __restrict__ ts_ptr, RowGroups groups,
                                                              const uint16_t* __restrict__ bits,
                                                              const uint2* __restrict__ rcodes,
                                                              uint4* __restrict__ y,
                                                              uint16_t* __restrict__ mask,
                                                              uint2* __restrict__ qcodes) {
-  const float ts = *ts_ptr;
+  const float ts_uniform = kGrouped ? 0.f : *ts_ptr;
   const uint64_t stride = (uint64_t)gridDim.x * kThreads;
   for (uint64_t b = (uint64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks; b += stride) {
+    const float ts = kGrouped ? ts_ptr[group_of_block(groups, b)] : ts_uniform;
     const uint32_t sbyte = scales[b];
     const uint32_t cached = kMode == 1 ? (uint32_t)bits[b] : 0u;
     const uint2 roll = kMode == 2 ? rcodes[b] : make_uint2(0u, 0u);
@@ -607,31 +701,63 @@ hipError_t launch_tensor_scale(const uint16_t* x, uint64_t nblocks, uint32_t* pa
   return hipGetLastError();
 }
 
-hipError_t launch_capture(const uint16_t* x, uint64_t nblocks, const float* ts, uint8_t* scales,
-                          uint8_t* bits, uint8_t* codes, hipStream_t stream) {
-  hipLaunchKernelGGL(capture_kernel, dim3(grid_for(nblocks)), dim3(kThreads), 0, stream,
-                     reinterpret_cast<const uint4*>(x), nblocks, ts, scales,
-                     reinterpret_cast<uint16_t*>(bits), reinterpret_cast<uint2*>(codes));
+static RowGroups row_groups(const GroupSpec& g) {
+  return RowGroups{g.offsets, (uint32_t)g.count, g.rows, g.cols / 16};
+}
+
+hipError_t launch_grouped_tensor_scale(const uint16_t* x, const GroupSpec& g, uint32_t* row_amax, float* ts_out,
+                                       hipStream_t stream) {
+  const uint64_t rows_per_group = kThreads / 64;
+  const uint64_t wg = (g.rows + rows_per_group - 1) / rows_per_group;
+  if (g.rows > 0)  // every row gets its word, also rows of zero width
+    hipLaunchKernelGGL(row_amax_kernel, dim3((unsigned)(wg < kMaxGroups ? wg : kMaxGroups)), dim3(kThreads), 0,
+                       stream, reinterpret_cast<const uint4*>(x), g.rows, g.cols / 8, row_amax);
+  hipLaunchKernelGGL(group_amax_finalize_kernel, dim3((unsigned)g.count), dim3(kThreads), 0, stream, row_amax,
+                     row_groups(g), ts_out);
   return hipGetLastError();
 }
 
+hipError_t launch_capture(const uint16_t* x, uint64_t nblocks, const float* ts, const GroupSpec* g,
+                          uint8_t* scales, uint8_t* bits, uint8_t* codes, hipStream_t stream) {
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  uint16_t* bv = reinterpret_cast<uint16_t*>(bits);
+  uint2* cv = reinterpret_cast<uint2*>(codes);
+  if (g)
+    hipLaunchKernelGGL(capture_kernel<true>, dim3(grid_for(nblocks)), dim3(kThreads), 0, stream, xv, nblocks, ts,
+                       row_groups(*g), scales, bv, cv);
+  else
+    hipLaunchKernelGGL(capture_kernel<false>, dim3(grid_for(nblocks)), dim3(kThreads), 0, stream, xv, nblocks,
+                       ts, RowGroups{}, scales, bv, cv);
+  return hipGetLastError();
+}
+
+template <bool kGrouped>
+static void launch_fakequant_t(int mode, const uint4* xv, uint64_t nblocks, const uint8_t* scales,
+                               const float* ts, const RowGroups& rg, const uint8_t* side, uint4* yv, uint16_t* mv,
+                               uint2* qv, hipStream_t stream) {
+  const dim3 grid(grid_for(nblocks)), block(kThreads);
+  if (mode == 1)
+    hipLaunchKernelGGL((fakequant_kernel<1, kGrouped>), grid, block, 0, stream, xv, nblocks, scales, ts, rg,
+                       reinterpret_cast<const uint16_t*>(side), static_cast<const uint2*>(nullptr), yv, mv, qv);
+  else if (mode == 2)
+    hipLaunchKernelGGL((fakequant_kernel<2, kGrouped>), grid, block, 0, stream, xv, nblocks, scales, ts, rg,
+                       static_cast<const uint16_t*>(nullptr), reinterpret_cast<const uint2*>(side), yv, mv, qv);
+  else
+    hipLaunchKernelGGL((fakequant_kernel<0, kGrouped>), grid, block, 0, stream, xv, nblocks, scales, ts, rg,
+                       static_cast<const uint16_t*>(nullptr), static_cast<const uint2*>(nullptr), yv, mv, qv);
+}
+
 hipError_t launch_fakequant(int mode, const uint16_t* x, uint64_t nblocks, const uint8_t* scales,
-                            const float* ts, const uint8_t* side, uint16_t* y, uint8_t* mask,
+                            const float* ts, const GroupSpec* g, const uint8_t* side, uint16_t* y, uint8_t* mask,
                             uint8_t* qcodes, hipStream_t stream) {
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   uint4* yv = reinterpret_cast<uint4*>(y);
   uint16_t* mv = reinterpret_cast<uint16_t*>(mask);
   uint2* qv = reinterpret_cast<uint2*>(qcodes);
-  const dim3 grid(grid_for(nblocks)), block(kThreads);
-  if (mode == 1)
-    hipLaunchKernelGGL(fakequant_kernel<1>, grid, block, 0, stream, xv, nblocks, scales, ts,
-                       reinterpret_cast<const uint16_t*>(side), static_cast<const uint2*>(nullptr), yv, mv, qv);
-  else if (mode == 2)
-    hipLaunchKernelGGL(fakequant_kernel<2>, grid, block, 0, stream, xv, nblocks, scales, ts,
-                       static_cast<const uint16_t*>(nullptr), reinterpret_cast<const uint2*>(side), yv, mv, qv);
+  if (g)
+    launch_fakequant_t<true>(mode, xv, nblocks, scales, ts, row_groups(*g), side, yv, mv, qv, stream);
   else
-    hipLaunchKernelGGL(fakequant_kernel<0>, grid, block, 0, stream, xv, nblocks, scales, ts,
-                       static_cast<const uint16_t*>(nullptr), static_cast<const uint2*>(nullptr), yv, mv, qv);
+    launch_fakequant_t<false>(mode, xv, nblocks, scales, ts, RowGroups{}, side, yv, mv, qv, stream);
   return hipGetLastError();
 }
 

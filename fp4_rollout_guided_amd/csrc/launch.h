@@ -22,16 +22,30 @@ constexpr uint32_t kAmaxMaxGroups = 2048;
 constexpr uint32_t kMaxGroups = TRACE_MAX_GROUPS;
 static_assert((uint64_t)TRACE_MAX_GROUPS * 256 <= 0xffffffffull, "grid exceeds 2^32 - 1 work-items");
 
+// Row groups with one tensor scale each: group g holds rows
+// [offsets[g], offsets[g+1]) of a rows x cols site tensor (device int64[count + 1]).
+constexpr uint32_t kMaxRowGroups = 1u << 20;
+struct GroupSpec {
+  const int64_t* offsets;
+  uint64_t count;
+  uint64_t rows;
+  uint64_t cols;
+};
+
 uint32_t amax_partial_count(uint64_t nblocks);
 
 hipError_t launch_tensor_scale(const uint16_t* x, uint64_t nblocks, uint32_t* partial, float* ts_out,
                                hipStream_t stream);
-hipError_t launch_capture(const uint16_t* x, uint64_t nblocks, const float* ts, uint8_t* scales,
-                          uint8_t* bits, uint8_t* codes, hipStream_t stream);
+// row_amax: u32[rows] workspace; ts_out: fp32[count]
+hipError_t launch_grouped_tensor_scale(const uint16_t* x, const GroupSpec& g, uint32_t* row_amax, float* ts_out,
+                                       hipStream_t stream);
+// g == nullptr: one tensor scale ts[0]; otherwise ts[group of the row]
+hipError_t launch_capture(const uint16_t* x, uint64_t nblocks, const float* ts, const GroupSpec* g,
+                          uint8_t* scales, uint8_t* bits, uint8_t* codes, hipStream_t stream);
 // mode 0: RNE; 1: guided, side = bit-plane (u8[n/8]); 2: full information,
 // side = rollout codes (u8[n/2]).
 hipError_t launch_fakequant(int mode, const uint16_t* x, uint64_t nblocks, const uint8_t* scales,
-                            const float* ts, const uint8_t* side, uint16_t* y, uint8_t* mask,
+                            const float* ts, const GroupSpec* g, const uint8_t* side, uint16_t* y, uint8_t* mask,
                             uint8_t* qcodes, hipStream_t stream);
 hipError_t launch_gather_records(const uint8_t* bits_src, const uint8_t* scales_src, const uint8_t* codes_src,
                                  uint64_t src_rows, uint64_t cols, const int64_t* row_index, uint64_t dst_rows,

@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define TRACE_ABI_VERSION 1
+#define TRACE_ABI_VERSION 2
 
 #if defined(__GNUC__)
 #define TRACE_API __attribute__((visibility("default")))
@@ -217,6 +217,60 @@ TRACE_API trace_status trace_gather_records(const uint8_t* bits_src, const uint8
                                             const int64_t* row_index, int64_t dst_rows,
                                             uint8_t* bits_dst, uint8_t* scales_dst,
                                             uint8_t* codes_dst, void* stream);
+
+/*
+ * Per-expert tensor scales for packed MoE rows.  Only the routed experts (and
+ * the KV cache) run in FP4 (rcap.io post, limitations list), and a
+ * routed-expert site holds the rows of every expert back to back.  Reading
+ * taken here: each expert's rows form a tensor of their own, with their own
+ * amax and tensor scale, as a grouped FP4 GEMM quantizes them.  Group g holds
+ * rows [offsets[g], offsets[g+1]) of the rows x cols site tensor.
+ *   offsets : int64[groups + 1] in device memory, 8-byte aligned,
+ *             offsets[0] = 0, offsets[groups] = rows, nondecreasing (empty
+ *             groups allowed); 1 <= groups <= 2^20.  The library does not
+ *             read the offsets on the host: offsets that break these rules
+ *             still keep every access in bounds (values are clamped to
+ *             [0, rows]) but assign rows to groups in an unspecified way.
+ *   ts      : fp32[groups] in device memory, one tensor scale per group.
+ * Every other argument, the record layout, aliasing (offsets and ts are
+ * inputs) and the error rules are those of the ungrouped entry point.
+ */
+
+/* ts_out[g] = fl32(amax over the rows of group g / 2688); 0 for an empty
+ * group.  workspace: trace_grouped_tensor_scale_workspace_bytes(rows) bytes
+ * of device scratch (one word per row), 4-byte aligned; rows == 0 accepts a
+ * NULL workspace and still writes ts_out. */
+TRACE_API size_t trace_grouped_tensor_scale_workspace_bytes(int64_t rows);
+TRACE_API trace_status trace_grouped_tensor_scale(const uint16_t* x, int64_t rows, int64_t cols,
+                                                  const int64_t* offsets, int64_t groups,
+                                                  void* workspace, size_t workspace_bytes,
+                                                  float* ts_out, void* stream);
+
+/* trace_capture with ts[group of the row] as each row's tensor scale. */
+TRACE_API trace_status trace_grouped_capture(const uint16_t* x_roll, int64_t rows, int64_t cols,
+                                             const int64_t* offsets, int64_t groups,
+                                             const float* ts, uint8_t* scales, uint8_t* bits,
+                                             uint8_t* codes, void* stream);
+
+/* The three forwards with ts[group of the row]. */
+TRACE_API trace_status trace_grouped_guided_fakequant_fwd(const uint16_t* x_train, int64_t rows,
+                                                          int64_t cols, const int64_t* offsets,
+                                                          int64_t groups, const uint8_t* scales,
+                                                          const float* ts, const uint8_t* bits,
+                                                          uint16_t* y, uint8_t* mask,
+                                                          uint8_t* qcodes, void* stream);
+TRACE_API trace_status trace_grouped_rne_fakequant_fwd(const uint16_t* x_train, int64_t rows,
+                                                       int64_t cols, const int64_t* offsets,
+                                                       int64_t groups, const uint8_t* scales,
+                                                       const float* ts, uint16_t* y,
+                                                       uint8_t* mask, uint8_t* qcodes,
+                                                       void* stream);
+TRACE_API trace_status trace_grouped_full_info_fakequant_fwd(const uint16_t* x_train, int64_t rows,
+                                                             int64_t cols, const int64_t* offsets,
+                                                             int64_t groups, const uint8_t* scales,
+                                                             const float* ts, const uint8_t* codes,
+                                                             uint16_t* y, uint8_t* mask,
+                                                             uint8_t* qcodes, void* stream);
 
 #ifdef __cplusplus
 }

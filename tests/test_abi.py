@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert tr.abi_version() == 1
+    assert tr.abi_version() == 2
     for code in range(6):
         assert L.trace_status_string(code).decode().startswith("TRACE")
     assert b"unknown" in L.trace_status_string(99)
@@ -189,3 +189,35 @@ def test_build_script_loads_without_the_library():
     code = ("import sys, __graft_entry__ as g; m = g._build_module(); "
             "assert 'fp4_rollout_guided_amd' not in sys.modules; assert m.LIB.endswith('libtrace.so')")
     subprocess.run([sys.executable, "-c", code], cwd=root, check=True)
+
+
+def test_grouped_validation():
+    x, off, ts, sc, bi, cd, y, mk = (A + k * 0x1000000 for k in range(8))
+    cap = L.trace_grouped_capture
+    assert cap(P(x), 64, 32, None, 4, P(ts), P(sc), P(bi), None, None) == E_NULL
+    assert cap(P(x), 64, 32, P(off), 0, P(ts), P(sc), P(bi), None, None) == E_SHAPE
+    assert cap(P(x), 64, 32, P(off), (1 << 20) + 1, P(ts), P(sc), P(bi), None, None) == E_SHAPE
+    assert cap(P(x), 64, 32, P(off + 4), 4, P(ts), P(sc), P(bi), None, None) == E_ALIGN
+    assert cap(P(x), 64, 40, P(off), 4, P(ts), P(sc), P(bi), None, None) == E_SHAPE
+    assert cap(P(x), 0, 32, P(off), 4, P(ts), P(sc), P(bi), None, None) == OK
+    assert cap(P(x), 0, 32, P(off), 0, P(ts), P(sc), P(bi), None, None) == E_SHAPE  # groups checked first
+    # outputs over the ts array or the offsets are aliasing errors
+    assert cap(P(x), 64, 32, P(off), 4, P(ts), P(ts), P(bi), None, None) == E_ALIAS
+    assert cap(P(x), 64, 32, P(off), 4, P(ts), P(sc), P(off + 8), None, None) == E_ALIAS
+    for fn, side in ((L.trace_grouped_guided_fakequant_fwd, P(bi)), (L.trace_grouped_full_info_fakequant_fwd, P(cd))):
+        assert fn(P(x), 64, 32, None, 4, P(sc), P(ts), side, P(y), P(mk), None, None) == E_NULL
+        assert fn(P(x), 64, 32, P(off), 4, P(sc), P(ts), None, P(y), P(mk), None, None) == E_NULL
+        assert fn(P(x), 64, 32, P(off), -1, P(sc), P(ts), side, P(y), P(mk), None, None) == E_SHAPE
+        assert fn(P(x), 64, 32, P(off), 4, P(sc), P(ts), side, P(ts), P(mk), None, None) == E_ALIAS
+        assert fn(P(x), 64, 32, P(off), 4, P(sc), P(ts), side, P(y), P(off + 16), None, None) == E_ALIAS
+    rne = L.trace_grouped_rne_fakequant_fwd
+    assert rne(P(x), 64, 32, P(off), 4, P(sc), P(ts), P(y + 2), P(mk), None, None) == E_ALIGN
+    ts_fn = L.trace_grouped_tensor_scale
+    ws = L.trace_grouped_tensor_scale_workspace_bytes(64)
+    assert ws == 256 and L.trace_grouped_tensor_scale_workspace_bytes(0) == 0
+    assert ts_fn(P(x), 64, 32, P(off), 4, P(A + 0x9000000), ws - 4, P(ts), None) == E_SHAPE
+    assert ts_fn(P(x), 64, 32, P(off), 4, None, ws, P(ts), None) == E_NULL
+    assert ts_fn(P(x), 64, 32, P(off), 4, P(A + 0x9000000), ws, None, None) == E_NULL
+    assert ts_fn(P(x), 64, 32, P(off), 4, P(A + 0x9000000), ws, P(ts + 2), None) == E_ALIGN
+    assert ts_fn(P(x), 64, 32, P(off), 4, P(x + 64), ws, P(ts), None) == E_ALIAS
+    assert ts_fn(P(x), 64, 32, P(off), 4, P(A + 0x9000000), ws, P(off + 24), None) == E_ALIAS

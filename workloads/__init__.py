@@ -132,6 +132,14 @@ def moe_routing(device):
     return tokens[order], experts[order]
 
 
+def moe_expert_offsets(expert_of_row):
+    """Row offsets of the expert groups of packed rows sorted by expert:
+    int64[experts + 1], group e = rows [off[e], off[e+1]) (empty experts give
+    empty groups)."""
+    counts = torch.bincount(expert_of_row, minlength=MOE_EXPERTS)
+    return torch.cat([torch.zeros(1, dtype=torch.int64, device=counts.device), torch.cumsum(counts, 0)])
+
+
 def cfg1(device, sigma, sites=None):
     """Dict site -> {x_roll, x_train, grad} for the MoE layer sites."""
     sites = sites or list(SHAPES[1])
