@@ -14,7 +14,10 @@ plain RNE fake-quant forward (y + clip mask), STE backward.  Every kernel is
 bracketed by HIP events on the stream it runs on; the step's wall time is
 taken between device synchronizations.  After the timed steps, a separate
 pass times the rows beyond the hot path (capture with full 4-bit codes and
-the full-information forward) and reports them under ``next_rows``.
+the full-information forward) and reports them under ``next_rows``; another
+times the per-expert (grouped) tensor scale, capture and guided forward and
+the record gather on the packed routed-expert site of the MoE layer workload
+(``moe_expert_site``).
 
 Prints one JSON line (last line of stdout).  ``value`` is the algorithmic
 bytes of the whole step divided by its wall time, in GB/s; per-kernel GB/s,
@@ -49,6 +52,14 @@ KERNELS = list(BYTES_PER_ELEM)
 NEXT_BYTES_PER_ELEM = {
     "capture_codes": 2.0 + 1 / 8 + 1 / 16 + 1 / 2,        # capture that also writes the 4-bit codes
     "full_info_fwd": 2.0 + 1 / 16 + 1 / 2 + 2.0 + 1 / 8,  # read x, scales, codes; write y, mask
+}
+# Per-expert rows on the packed routed-expert site of the MoE layer workload
+# (131072 x 2048, rows grouped by 128 experts), timed in their own pass.
+MOE_BYTES_PER_ELEM = {
+    "grouped_tensor_scale": 2.0,                                   # read x (+ one word per row)
+    "grouped_capture": 2.0 + 1 / 8 + 1 / 16,
+    "grouped_guided_fwd": 2.0 + 1 / 8 + 1 / 16 + 2.0 + 1 / 8,
+    "gather_records": 2 * (1 / 8 + 1 / 16),                        # read + write bits and scale bytes
 }
 CPU_SHARE = 16           # host cores a one-GPU machine grants
 CPU_BUDGET_S = 12.0      # wall-clock budget of the CPU oracle leg
@@ -227,6 +238,8 @@ def main():
                         "Gelem_s": round(n / (avg_ms * 1e-3) / 1e9, 2), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                         "bytes_per_launch": int(bpe * n)}
 
+    moe = moe_rows(tr, workloads, torch, dev, stream, layers, next_steps)
+
     cache = {
         "compact_bytes_20_layers": L * (n // 8 + n // 16),
         "full_nvfp4_bytes_40_layers": TOTAL_LAYERS * (n // 2 + n // 16),
@@ -255,6 +268,7 @@ def main():
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "kernels": kernels,
         "next_rows": next_rows,
+        "moe_expert_site": moe,
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": dk["GB_s"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": dk["frac_hbm_peak"], "traffic": read_traffic(dominant)},
         "cache": cache,
@@ -266,6 +280,55 @@ def main():
         pool.close()
         pool.join()
     print(json.dumps(result), flush=True)
+
+
+def moe_rows(tr, workloads, torch, dev, stream, layers, reps):
+    """Per-expert tensor scales on the packed routed-expert site, and the
+    trainer-side gather of its records into a shuffled row order."""
+    sigma = 0.02
+    d = workloads.cfg1(dev, sigma, sites=["expert_in"])["expert_in"]
+    _, experts = workloads.moe_routing(dev)
+    offsets = workloads.moe_expert_offsets(experts)
+    x_roll, x_train = d["x_roll"], d["x_train"]
+    rows, cols = x_roll.shape
+    n = rows * cols
+    perm = torch.randperm(rows, generator=workloads.generator(dev, "trainer order"), device=dev)
+    groups = offsets.numel() - 1
+    ts = torch.empty(groups, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(4, tr.lib.trace_grouped_tensor_scale_workspace_bytes(rows)), dtype=torch.uint8, device=dev)
+    scales = torch.empty(n // 16, dtype=torch.uint8, device=dev)
+    bits = torch.empty(n // 8, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x_train)
+    mask = torch.empty(n // 8, dtype=torch.uint8, device=dev)
+    ms = {k: 0.0 for k in MOE_BYTES_PER_ELEM}
+    for it in range(reps + 1):
+        ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(2)] for k in MOE_BYTES_PER_ELEM}
+        ev["grouped_tensor_scale"][0].record(stream)
+        tr.grouped_tensor_scale(x_roll, offsets, out=ts, workspace=ws)
+        ev["grouped_tensor_scale"][1].record(stream)
+        ev["grouped_capture"][0].record(stream)
+        tr.grouped_capture(x_roll, offsets, ts, scales=scales, bits=bits)
+        ev["grouped_capture"][1].record(stream)
+        ev["grouped_guided_fwd"][0].record(stream)
+        tr.grouped_guided_fakequant_fwd(x_train, offsets, scales, ts, bits, y=y, mask=mask)
+        ev["grouped_guided_fwd"][1].record(stream)
+        ev["gather_records"][0].record(stream)
+        tr.gather_records(bits, scales, None, cols, perm)
+        ev["gather_records"][1].record(stream)
+        stream.synchronize()
+        if it > 0:
+            for k in MOE_BYTES_PER_ELEM:
+                ms[k] += ev[k][0].elapsed_time(ev[k][1])
+    out = {"site": f"routed-expert input {rows}x{cols} bf16, rows grouped by {groups} experts "
+                   f"(top-8 of 128 routing of 16384 tokens), Student-t(4)", "kernels": {}}
+    for k, bpe in MOE_BYTES_PER_ELEM.items():
+        avg = ms[k] / reps
+        gbs = bpe * n / (avg * 1e-3) / 1e9
+        out["kernels"][k] = {"avg_us": round(avg * 1e3, 2), "GB_s": round(gbs, 1),
+                             "Gelem_s": round(n / (avg * 1e-3) / 1e9, 2), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                             "bytes_per_launch": int(bpe * n)}
+    del d, x_roll, x_train, y
+    return out
 
 
 def calibrate_copy():

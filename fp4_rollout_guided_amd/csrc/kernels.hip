@@ -343,10 +343,11 @@ __global__ __launch_bounds__(kThreads) void amax_finalize_kernel(const uint32_t*
 // only nondecreasing offsets give a meaningful assignment.
 // ---------------------------------------------------------------------------
 struct RowGroups {
-  const int64_t* off;  // int64[count + 1]; entries 1..count-1 are read by the block lookup
+  const int64_t* off;  // int64[count + 1]
   uint32_t count;
   uint64_t rows;
   uint64_t bpr;        // 16-element blocks per row
+  float per_block;     // count / blocks: the group a block would fall in if all groups were equal
 };
 
 __device__ __forceinline__ uint64_t group_row(const RowGroups& G, uint32_t g) {
@@ -354,22 +355,76 @@ __device__ __forceinline__ uint64_t group_row(const RowGroups& G, uint32_t g) {
   return o < 0 ? 0 : ((uint64_t)o > G.rows ? G.rows : (uint64_t)o);
 }
 
-// Group of block b: a wave-uniform binary search from the wave's first active
-// block (scalar loads), then a per-lane walk over the group starts that fall
-// inside the wave's span (none in the common case).
-__device__ __forceinline__ uint32_t group_of_block(const RowGroups& G, uint64_t b) {
+// Start of group g in blocks, with group 0 starting at 0 and group count
+// (one past the last) at infinity.
+__device__ __forceinline__ uint64_t group_start(const RowGroups& G, uint32_t g) {
+  if (g == 0) return 0;
+  if (g >= G.count) return ~0ull;
+  return group_row(G, g) * G.bpr;
+}
+
+// Tensor scale of block b's group.  The group of the wave's first active
+// block is found wave-uniformly with scalar loads: first from a guess that
+// assumes equal groups, checked against a window of three groups whose
+// starts and scales are fetched in one round of independent loads (enough
+// for balanced expert loads); otherwise by binary search.  Lanes past the
+// next group start (a group boundary inside the wave's span, rare) walk on
+// with per-lane loads.
+__device__ __forceinline__ float group_tensor_scale(const RowGroups& G, const float* __restrict__ ts, uint64_t b) {
   const uint32_t b0lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
   const uint32_t b0hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
   const uint64_t b0 = ((uint64_t)b0hi << 32) | b0lo;
-  uint32_t lo = 0, hi = G.count;
-  while (hi - lo > 1) {
-    const uint32_t mid = (lo + hi) >> 1;
-    if (group_row(G, mid) * G.bpr <= b0) lo = mid; else hi = mid;
+  const float gf = __builtin_fminf((float)b0 * G.per_block, (float)(G.count - 1));
+  const uint32_t guess = __builtin_amdgcn_readfirstlane((uint32_t)gf);
+  uint32_t lo = G.count;  // not found yet
+  float t = 0.f;
+  uint64_t next = 0;
+  if (G.count >= 3) {
+    // window: groups i, i + 1, i + 2 around the guess; offsets[i .. i + 3]
+    // and ts[i .. i + 2] are in bounds and loaded unconditionally, together
+    const uint32_t i = guess == 0 ? 0 : (guess - 1 > G.count - 3 ? G.count - 3 : guess - 1);
+    int64_t ov[4];
+    float tw[3];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ov[j] = G.off[i + j];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) tw[j] = ts[i + j];
+    uint64_t st[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t o = ov[j];
+      const uint64_t row = o < 0 ? 0 : ((uint64_t)o > G.rows ? G.rows : (uint64_t)o);
+      st[j] = i + j == 0 ? 0 : (i + j >= G.count ? ~0ull : row * G.bpr);
+    }
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const bool in = st[j] <= b0 && b0 < st[j + 1];
+      lo = in ? i + j : lo;
+      t = in ? tw[j] : t;
+      next = in ? st[j + 1] : next;
+    }
   }
-  uint32_t g = lo;
-  while (g + 1 < G.count && group_row(G, g + 1) * G.bpr <= b) ++g;
-  return g;
+  if (lo == G.count) {  // unbalanced groups: binary search
+    uint32_t l = 0, h = G.count;
+    while (h - l > 1) {
+      const uint32_t mid = (l + h) >> 1;
+      if (group_row(G, mid) * G.bpr <= b0) l = mid; else h = mid;
+    }
+    lo = l;
+    next = group_start(G, lo + 1);
+    t = ts[lo];
+  }
+  // readfirstlane keeps the uniform value scalar (the compiler would otherwise
+  // merge the loads with the per-lane load below into vector loads)
+  t = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(t)));
+  if (b >= next) {
+    uint32_t g = lo + 1;
+    while (g + 1 < G.count && group_row(G, g + 1) * G.bpr <= b) ++g;
+    t = ts[g];
+  }
+  return t;
 }
+
 
 // Grouped tensor scale, pass 1: the magnitude-bit maximum of every row (NaN
 // excluded as in amax_partial_kernel); one wave per row.
@@ -380,15 +435,23 @@ __global__ __launch_bounds__(kThreads) void row_amax_kernel(const uint4* __restr
   for (uint64_t r = (uint64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); r < rows;
        r += (uint64_t)gridDim.x * (kThreads / 64)) {
     s16x2 best = {0, 0};
-    for (uint64_t c = lane; c < vec_per_row; c += 64) {
-      const uint4 v = x[r * vec_per_row + c];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    for (uint64_t c0 = 0; c0 < vec_per_row; c0 += 4 * 64) {
+      uint4 v[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t m = (w[k] & 0x7fff7fffu) + 0x007f007fu;
-        s16x2 vv;
-        __builtin_memcpy(&vv, &m, 4);
-        best = __builtin_elementwise_max(best, vv);
+      for (int u = 0; u < 4; ++u) {  // four loads in flight before any is used
+        const uint64_t c = c0 + 64 * u + lane;
+        v[u] = c < vec_per_row ? x[r * vec_per_row + c] : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t m = (w[k] & 0x7fff7fffu) + 0x007f007fu;
+          s16x2 vv;
+          __builtin_memcpy(&vv, &m, 4);
+          best = __builtin_elementwise_max(best, vv);
+        }
       }
     }
     const int lo = best.x, hi = best.y;
@@ -432,69 +495,74 @@ __device__ __forceinline__ CaptureScale capture_scale(float ts) {
   return c;
 }
 
+// One block of the capture: scale byte, parity bits and (optionally) codes.
+__device__ __forceinline__ void capture_one(const uint4* __restrict__ x, uint64_t b, const uint32_t (&w)[8],
+                                            const CaptureScale& cs, float r6hi, float r6lo,
+                                            uint8_t* __restrict__ scales, uint16_t* __restrict__ bits,
+                                            uint2* __restrict__ codes) {
+  const float ts = cs.ts;
+  // block amax on packed bf16 magnitudes
+  u16x2 mx;
+  {
+    uint32_t m0 = w[0] & 0x7fff7fffu;
+    __builtin_memcpy(&mx, &m0, 4);
+#pragma unroll
+    for (int k = 1; k < 8; ++k) {
+      const uint32_t mk = w[k] & 0x7fff7fffu;
+      u16x2 v;
+      __builtin_memcpy(&v, &mk, 4);
+      mx = __builtin_elementwise_max(mx, v);
+    }
+  }
+  const uint32_t amax_bits = mx.x > mx.y ? mx.x : mx.y;
+  const float amax = __uint_as_float(amax_bits << 16);
+  // a zero block, or amax >= 2^-100 (bf16 bits 0x0d80) keeps the two divisions
+  // exact; a NaN or infinite element shows as amax_bits >= 0x7f80
+  bool bad = cs.slow || (amax_bits - 1u) < 0x0d7fu || amax_bits >= 0x7f80u;
+
+  const float v1 = __builtin_amdgcn_fmed3f(div_fast_u(amax, 6.0f, r6hi, r6lo), 0.f, cs.lim);
+  const float v = div_fast_u(v1, ts, cs.rthi, cs.rtlo);
+  uint32_t sb = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(v, 0.f, 448.f), 0.f, 0, false);
+  sb = cs.valid ? sb : 0u;
+
+  const ScaleEntry e = make_scale_entry(sb, ts);
+  bad |= !(e.dhi == e.dhi);  // scale outside the fast range
+
+  float q[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) q[j] = div_fast<false>(block_elem(w, j), e, bad);
+
+  uint32_t E = 0, O = 0;
+  FP4_PACK8(FP4_RNE, E, q, 0);
+  FP4_PACK8(FP4_RNE, O, q, 1);
+  if (bad) {
+    capture_block_exact(x, b, ts, scales, bits, codes);
+  } else {
+    scales[b] = (uint8_t)sb;
+    bits[b] = (uint16_t)gather_parity(E, O);
+    if (codes) {
+      uint32_t c0, c1;
+      interleave_codes(E, O, c0, c1);
+      codes[b] = make_uint2(c0, c1);
+    }
+  }
+}
+
 template <bool kGrouped>
 __global__ __launch_bounds__(kThreads) void capture_kernel(const uint4* __restrict__ x, uint64_t nblocks,
                                                            const float* __restrict__ ts_ptr, RowGroups groups,
                                                            uint8_t* __restrict__ scales,
                                                            uint16_t* __restrict__ bits,
                                                            uint2* __restrict__ codes) {
-  CaptureScale cs;
-  if (!kGrouped) cs = capture_scale(*ts_ptr);
   const float r6hi = 1.0f / 6.0f;
   const float r6lo = __builtin_fmaf(-6.0f, r6hi, 1.0f) * r6hi;
-
+  const CaptureScale cs0 = kGrouped ? CaptureScale{} : capture_scale(*ts_ptr);
   const uint64_t stride = (uint64_t)gridDim.x * kThreads;
   for (uint64_t b = (uint64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks; b += stride) {
-    if (kGrouped) cs = capture_scale(ts_ptr[group_of_block(groups, b)]);
-    const float ts = cs.ts;
     uint32_t w[8];
-    load_block(x, b, w);
-
-    // block amax on packed bf16 magnitudes
-    u16x2 mx;
-    {
-      uint32_t m0 = w[0] & 0x7fff7fffu;
-      __builtin_memcpy(&mx, &m0, 4);
-#pragma unroll
-      for (int k = 1; k < 8; ++k) {
-        const uint32_t mk = w[k] & 0x7fff7fffu;
-        u16x2 v;
-        __builtin_memcpy(&v, &mk, 4);
-        mx = __builtin_elementwise_max(mx, v);
-      }
-    }
-    const uint32_t amax_bits = mx.x > mx.y ? mx.x : mx.y;
-    const float amax = __uint_as_float(amax_bits << 16);
-    // a zero block, or amax >= 2^-100 (bf16 bits 0x0d80) keeps the two divisions
-    // exact; a NaN or infinite element shows as amax_bits >= 0x7f80
-    bool bad = cs.slow || (amax_bits - 1u) < 0x0d7fu || amax_bits >= 0x7f80u;
-
-    const float v1 = __builtin_amdgcn_fmed3f(div_fast_u(amax, 6.0f, r6hi, r6lo), 0.f, cs.lim);
-    const float v = div_fast_u(v1, ts, cs.rthi, cs.rtlo);
-    uint32_t sb = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(v, 0.f, 448.f), 0.f, 0, false);
-    sb = cs.valid ? sb : 0u;
-
-    const ScaleEntry e = make_scale_entry(sb, ts);
-    bad |= !(e.dhi == e.dhi);  // scale outside the fast range
-
-    float q[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) q[j] = div_fast<false>(block_elem(w, j), e, bad);
-
-    uint32_t E = 0, O = 0;
-    FP4_PACK8(FP4_RNE, E, q, 0);
-    FP4_PACK8(FP4_RNE, O, q, 1);
-    if (bad) {
-      capture_block_exact(x, b, ts, scales, bits, codes);
-    } else {
-      scales[b] = (uint8_t)sb;
-      bits[b] = (uint16_t)gather_parity(E, O);
-      if (codes) {
-        uint32_t c0, c1;
-        interleave_codes(E, O, c0, c1);
-        codes[b] = make_uint2(c0, c1);
-      }
-    }
+    load_block(x, b, w);  // issued before the group search, whose latency it hides
+    const CaptureScale cs = kGrouped ? capture_scale(group_tensor_scale(groups, ts_ptr, b)) : cs0;
+    capture_one(x, b, w, cs, r6hi, r6lo, scales, bits, codes);
   }
 }
 
@@ -528,7 +596,83 @@ __device__ __forceinline__ uint32_t full_info_select(uint32_t F, uint32_t P, uin
   return F + ((gt & same) >> 3 & ~t & 0x11111111u);
 }
 
-template <int kMode, bool kGrouped>  // mode 0 = RNE, 1 = guided by the cached bit, 2 = full information
+// One block of a fake-quant forward.
+template <int kMode>
+__device__ __forceinline__ void fakequant_one(const uint4* __restrict__ x, uint64_t b, const uint32_t (&w)[8],
+                                              uint32_t sbyte, uint32_t cached, uint2 roll, float ts,
+                                              uint4* __restrict__ y, uint16_t* __restrict__ mask,
+                                              uint2* __restrict__ qcodes) {
+  const ScaleEntry e = make_scale_entry(sbyte, ts);
+  bool bad = false;  // set by a NaN / infinite quotient, or a scale outside the fast range (dhi NaN)
+
+  float q[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) q[j] = div_fast<true>(block_elem(w, j), e, bad);
+
+  // clip mask: sign bit of 6 - |q| is set exactly when |q| > 6
+  uint32_t clip = 0;
+#pragma unroll
+  for (int j = 15; j >= 0; --j)
+    clip = __builtin_amdgcn_alignbit(clip, __float_as_uint(6.0f - fabsf(q[j])), 31);
+  const uint32_t maskword = (e.rhi != 0.f) ? (~clip & 0xffffu) : 0u;
+
+  float qc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) qc[j] = __builtin_amdgcn_fmed3f(q[j], -6.0f, 6.0f);
+
+  uint32_t QE = 0, QO = 0;
+  if (kMode != 0) {
+    // floor codes of q and of its predecessor toward zero: equal exactly when
+    // q lies strictly inside a bracket, so the upper endpoint is floor + 1
+    float pv[16];  // predecessors toward zero (a NaN for +-0, whose floor code differs)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) pv[j] = __uint_as_float(__float_as_uint(qc[j]) - 1u);
+    uint32_t FE = 0, FO = 0, PE = 0, PO = 0;
+    FP4_PACK8(FP4_RTZ, FE, qc, 0);
+    FP4_PACK8(FP4_RTZ, FO, qc, 1);
+    FP4_PACK8(FP4_RTZ, PE, pv, 0);
+    FP4_PACK8(FP4_RTZ, PO, pv, 1);
+    if (kMode == 1) {
+      const uint32_t C = spread_bits(cached);  // bit 0 / bit 1 of nibble k: cached bit of 2k / 2k+1
+      uint32_t t = FE ^ PE;
+      t |= t >> 2;
+      t |= t >> 1;
+      QE = FE + (~t & (FE ^ C) & 0x11111111u);
+      t = FO ^ PO;
+      t |= t >> 2;
+      t |= t >> 1;
+      QO = FO + (~t & (FO ^ (C >> 1)) & 0x11111111u);
+    } else {
+      uint32_t RE, RO;
+      split_codes(roll.x, roll.y, RE, RO);
+      QE = full_info_select(FE, PE, RE);
+      QO = full_info_select(FO, PO, RO);
+    }
+  } else {
+    FP4_PACK8(FP4_RNE, QE, qc, 0);
+    FP4_PACK8(FP4_RNE, QO, qc, 1);
+  }
+
+  if (bad) {
+    fakequant_block_exact(kMode, x, b, sbyte, ts, cached, roll.x, roll.y, y, mask, qcodes);
+  } else {
+    uint32_t out[8];
+    decode_scaled_pair<0>(QE, QO, e.s, out);
+    decode_scaled_pair<1>(QE, QO, e.s, out);
+    decode_scaled_pair<2>(QE, QO, e.s, out);
+    decode_scaled_pair<3>(QE, QO, e.s, out);
+    store_block(y, b, out);
+    mask[b] = (uint16_t)maskword;
+    if (qcodes) {
+      uint32_t c0, c1;
+      interleave_codes(QE, QO, c0, c1);
+      qcodes[b] = make_uint2(c0, c1);
+    }
+  }
+}
+
+// kMode: 0 = RNE, 1 = guided by the cached bit, 2 = full information.
+template <int kMode, bool kGrouped>
 __global__ __launch_bounds__(kThreads) void fakequant_kernel(const uint4* __restrict__ x, uint64_t nblocks,
                                                              const uint8_t* __restrict__ scales,
                                                              const float* __restrict__ ts_ptr, RowGroups groups,
@@ -537,82 +681,16 @@ __global__ __launch_bounds__(kThreads) void fakequant_kernel(const uint4* __rest
                                                              uint4* __restrict__ y,
                                                              uint16_t* __restrict__ mask,
                                                              uint2* __restrict__ qcodes) {
-  const float ts_uniform = kGrouped ? 0.f : *ts_ptr;
+  const float ts0 = kGrouped ? 0.f : *ts_ptr;
   const uint64_t stride = (uint64_t)gridDim.x * kThreads;
   for (uint64_t b = (uint64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks; b += stride) {
-    const float ts = kGrouped ? ts_ptr[group_of_block(groups, b)] : ts_uniform;
     const uint32_t sbyte = scales[b];
     const uint32_t cached = kMode == 1 ? (uint32_t)bits[b] : 0u;
     const uint2 roll = kMode == 2 ? rcodes[b] : make_uint2(0u, 0u);
     uint32_t w[8];
-    load_block(x, b, w);
-    const ScaleEntry e = make_scale_entry(sbyte, ts);
-    bool bad = false;  // set by a NaN / infinite quotient, or a scale outside the fast range (dhi NaN)
-
-    float q[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) q[j] = div_fast<true>(block_elem(w, j), e, bad);
-
-    // clip mask: sign bit of 6 - |q| is set exactly when |q| > 6
-    uint32_t clip = 0;
-#pragma unroll
-    for (int j = 15; j >= 0; --j)
-      clip = __builtin_amdgcn_alignbit(clip, __float_as_uint(6.0f - fabsf(q[j])), 31);
-    const uint32_t maskword = (e.rhi != 0.f) ? (~clip & 0xffffu) : 0u;
-
-    float qc[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) qc[j] = __builtin_amdgcn_fmed3f(q[j], -6.0f, 6.0f);
-
-    uint32_t QE = 0, QO = 0;
-    if (kMode != 0) {
-      // floor codes of q and of its predecessor toward zero: equal exactly when
-      // q lies strictly inside a bracket, so the upper endpoint is floor + 1
-      float pv[16];  // predecessors toward zero (a NaN for +-0, whose floor code differs)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) pv[j] = __uint_as_float(__float_as_uint(qc[j]) - 1u);
-      uint32_t FE = 0, FO = 0, PE = 0, PO = 0;
-      FP4_PACK8(FP4_RTZ, FE, qc, 0);
-      FP4_PACK8(FP4_RTZ, FO, qc, 1);
-      FP4_PACK8(FP4_RTZ, PE, pv, 0);
-      FP4_PACK8(FP4_RTZ, PO, pv, 1);
-      if (kMode == 1) {
-        const uint32_t C = spread_bits(cached);  // bit 0 / bit 1 of nibble k: cached bit of 2k / 2k+1
-        uint32_t t = FE ^ PE;
-        t |= t >> 2;
-        t |= t >> 1;
-        QE = FE + (~t & (FE ^ C) & 0x11111111u);
-        t = FO ^ PO;
-        t |= t >> 2;
-        t |= t >> 1;
-        QO = FO + (~t & (FO ^ (C >> 1)) & 0x11111111u);
-      } else {
-        uint32_t RE, RO;
-        split_codes(roll.x, roll.y, RE, RO);
-        QE = full_info_select(FE, PE, RE);
-        QO = full_info_select(FO, PO, RO);
-      }
-    } else {
-      FP4_PACK8(FP4_RNE, QE, qc, 0);
-      FP4_PACK8(FP4_RNE, QO, qc, 1);
-    }
-
-    if (bad) {
-      fakequant_block_exact(kMode, x, b, sbyte, ts, cached, roll.x, roll.y, y, mask, qcodes);
-    } else {
-      uint32_t out[8];
-      decode_scaled_pair<0>(QE, QO, e.s, out);
-      decode_scaled_pair<1>(QE, QO, e.s, out);
-      decode_scaled_pair<2>(QE, QO, e.s, out);
-      decode_scaled_pair<3>(QE, QO, e.s, out);
-      store_block(y, b, out);
-      mask[b] = (uint16_t)maskword;
-      if (qcodes) {
-        uint32_t c0, c1;
-        interleave_codes(QE, QO, c0, c1);
-        qcodes[b] = make_uint2(c0, c1);
-      }
-    }
+    load_block(x, b, w);  // all loads are issued before the group search
+    const float ts = kGrouped ? group_tensor_scale(groups, ts_ptr, b) : ts0;
+    fakequant_one<kMode>(x, b, w, sbyte, cached, roll, ts, y, mask, qcodes);
   }
 }
 
@@ -649,25 +727,33 @@ __global__ __launch_bounds__(kThreads) void ste_bwd_kernel(const uint4* __restri
 
 // ---------------------------------------------------------------------------
 // record gather (trainer-side readback): destination row r <- source row
-// row_index[r]; one lane copies one block's record (16 plane bits, the scale
-// byte, and 8 bytes of codes when present); an index outside [0, src_rows)
-// writes a zero record (zero-scale blocks).
+// row_index[r] of one record plane (bits, scale bytes or codes), moved in
+// words of type V.  A workgroup covers whole rows: with wpr words per row,
+// thread t copies word t % wpr of row t / wpr (rows_per_wg = 256 / wpr rows),
+// or, for rows of 256 words or more, one row in 256-word strides.  An index
+// outside [0, src_rows) writes a zero row (zero-scale blocks).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void gather_records_kernel(
-    const uint16_t* __restrict__ bits_src, const uint8_t* __restrict__ scales_src,
-    const uint2* __restrict__ codes_src, uint64_t src_rows, uint64_t blocks_per_row,
-    const int64_t* __restrict__ row_index, uint64_t dst_rows, uint16_t* __restrict__ bits_dst,
-    uint8_t* __restrict__ scales_dst, uint2* __restrict__ codes_dst) {
-  for (uint64_t r = blockIdx.x; r < dst_rows; r += gridDim.x) {
-    const int64_t src = row_index[r];
-    const bool ok = src >= 0 && (uint64_t)src < src_rows;
-    const uint64_t sbase = ok ? (uint64_t)src * blocks_per_row : 0;
-    const uint64_t dbase = r * blocks_per_row;
-    for (uint64_t c = threadIdx.x; c < blocks_per_row; c += kThreads) {
-      bits_dst[dbase + c] = ok ? bits_src[sbase + c] : (uint16_t)0;
-      scales_dst[dbase + c] = ok ? scales_src[sbase + c] : (uint8_t)0;
-      if (codes_dst) codes_dst[dbase + c] = ok ? codes_src[sbase + c] : make_uint2(0u, 0u);
-    }
+template <typename V>
+__device__ __forceinline__ V zero_word() {
+  V z;
+  __builtin_memset(&z, 0, sizeof(V));
+  return z;
+}
+
+template <typename V>
+__global__ __launch_bounds__(kThreads) void gather_plane_kernel(const V* __restrict__ src, V* __restrict__ dst,
+                                                                uint64_t src_rows, uint64_t dst_rows, uint32_t wpr,
+                                                                uint32_t rows_per_wg,
+                                                                const int64_t* __restrict__ row_index) {
+  const uint32_t lr = wpr >= kThreads ? 0u : threadIdx.x / wpr;
+  if (lr >= rows_per_wg) return;
+  const uint32_t w0 = threadIdx.x - lr * (wpr >= kThreads ? 0u : wpr);
+  const uint32_t wstep = wpr >= kThreads ? kThreads : wpr;
+  for (uint64_t r = (uint64_t)blockIdx.x * rows_per_wg + lr; r < dst_rows; r += (uint64_t)gridDim.x * rows_per_wg) {
+    const int64_t s = row_index[r];
+    const bool ok = s >= 0 && (uint64_t)s < src_rows;
+    for (uint32_t w = w0; w < wpr; w += wstep)
+      dst[r * wpr + w] = ok ? src[(uint64_t)s * wpr + w] : zero_word<V>();
   }
 }
 
@@ -701,8 +787,9 @@ hipError_t launch_tensor_scale(const uint16_t* x, uint64_t nblocks, uint32_t* pa
   return hipGetLastError();
 }
 
-static RowGroups row_groups(const GroupSpec& g) {
-  return RowGroups{g.offsets, (uint32_t)g.count, g.rows, g.cols / 16};
+static RowGroups row_groups(const GroupSpec& g, uint64_t nblocks = 0) {
+  return RowGroups{g.offsets, (uint32_t)g.count, g.rows, g.cols / 16,
+                   nblocks ? (float)((double)g.count / (double)nblocks) : 0.f};
 }
 
 hipError_t launch_grouped_tensor_scale(const uint16_t* x, const GroupSpec& g, uint32_t* row_amax, float* ts_out,
@@ -722,12 +809,12 @@ hipError_t launch_capture(const uint16_t* x, uint64_t nblocks, const float* ts, 
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   uint16_t* bv = reinterpret_cast<uint16_t*>(bits);
   uint2* cv = reinterpret_cast<uint2*>(codes);
+  const dim3 grid(grid_for(nblocks)), block(kThreads);
   if (g)
-    hipLaunchKernelGGL(capture_kernel<true>, dim3(grid_for(nblocks)), dim3(kThreads), 0, stream, xv, nblocks, ts,
-                       row_groups(*g), scales, bv, cv);
+    hipLaunchKernelGGL(capture_kernel<true>, grid, block, 0, stream, xv, nblocks, ts, row_groups(*g, nblocks),
+                       scales, bv, cv);
   else
-    hipLaunchKernelGGL(capture_kernel<false>, dim3(grid_for(nblocks)), dim3(kThreads), 0, stream, xv, nblocks,
-                       ts, RowGroups{}, scales, bv, cv);
+    hipLaunchKernelGGL(capture_kernel<false>, grid, block, 0, stream, xv, nblocks, ts, RowGroups{}, scales, bv, cv);
   return hipGetLastError();
 }
 
@@ -750,12 +837,13 @@ static void launch_fakequant_t(int mode, const uint4* xv, uint64_t nblocks, cons
 hipError_t launch_fakequant(int mode, const uint16_t* x, uint64_t nblocks, const uint8_t* scales,
                             const float* ts, const GroupSpec* g, const uint8_t* side, uint16_t* y, uint8_t* mask,
                             uint8_t* qcodes, hipStream_t stream) {
+  if (nblocks == 0) return hipSuccess;  // the kernels load block min(b, nblocks - 1) up front
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   uint4* yv = reinterpret_cast<uint4*>(y);
   uint16_t* mv = reinterpret_cast<uint16_t*>(mask);
   uint2* qv = reinterpret_cast<uint2*>(qcodes);
   if (g)
-    launch_fakequant_t<true>(mode, xv, nblocks, scales, ts, row_groups(*g), side, yv, mv, qv, stream);
+    launch_fakequant_t<true>(mode, xv, nblocks, scales, ts, row_groups(*g, nblocks), side, yv, mv, qv, stream);
   else
     launch_fakequant_t<false>(mode, xv, nblocks, scales, ts, RowGroups{}, side, yv, mv, qv, stream);
   return hipGetLastError();
@@ -769,14 +857,39 @@ hipError_t launch_ste_bwd(const uint16_t* g, const uint8_t* mask, uint64_t nbloc
   return hipGetLastError();
 }
 
+template <typename V>
+static void launch_gather_plane_t(const uint8_t* src, uint8_t* dst, uint64_t src_rows, uint64_t dst_rows,
+                                  uint64_t row_bytes, const int64_t* row_index, hipStream_t stream) {
+  const uint32_t wpr = (uint32_t)(row_bytes / sizeof(V));
+  const uint32_t rpw = wpr >= (uint32_t)kThreads ? 1u : (uint32_t)kThreads / wpr;
+  const uint64_t wg = (dst_rows + rpw - 1) / rpw;
+  hipLaunchKernelGGL(gather_plane_kernel<V>, dim3((unsigned)(wg < kMaxGroups ? wg : kMaxGroups)), dim3(kThreads), 0,
+                     stream, reinterpret_cast<const V*>(src), reinterpret_cast<V*>(dst), src_rows, dst_rows, wpr, rpw,
+                     row_index);
+}
+
+// The widest word that divides the row and keeps both planes aligned.
+static void launch_gather_plane(const uint8_t* src, uint8_t* dst, uint64_t src_rows, uint64_t dst_rows,
+                                uint64_t row_bytes, const int64_t* row_index, hipStream_t stream) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst) | (uintptr_t)row_bytes;
+  if ((a & 15) == 0)
+    launch_gather_plane_t<uint4>(src, dst, src_rows, dst_rows, row_bytes, row_index, stream);
+  else if ((a & 7) == 0)
+    launch_gather_plane_t<uint2>(src, dst, src_rows, dst_rows, row_bytes, row_index, stream);
+  else if ((a & 3) == 0)
+    launch_gather_plane_t<uint32_t>(src, dst, src_rows, dst_rows, row_bytes, row_index, stream);
+  else if ((a & 1) == 0)
+    launch_gather_plane_t<uint16_t>(src, dst, src_rows, dst_rows, row_bytes, row_index, stream);
+  else
+    launch_gather_plane_t<uint8_t>(src, dst, src_rows, dst_rows, row_bytes, row_index, stream);
+}
+
 hipError_t launch_gather_records(const uint8_t* bits_src, const uint8_t* scales_src, const uint8_t* codes_src,
                                  uint64_t src_rows, uint64_t cols, const int64_t* row_index, uint64_t dst_rows,
                                  uint8_t* bits_dst, uint8_t* scales_dst, uint8_t* codes_dst, hipStream_t stream) {
-  const unsigned grid = (unsigned)(dst_rows < kMaxGroups ? dst_rows : kMaxGroups);
-  hipLaunchKernelGGL(gather_records_kernel, dim3(grid), dim3(kThreads), 0, stream,
-                     reinterpret_cast<const uint16_t*>(bits_src), scales_src,
-                     reinterpret_cast<const uint2*>(codes_src), src_rows, cols / 16, row_index, dst_rows,
-                     reinterpret_cast<uint16_t*>(bits_dst), scales_dst, reinterpret_cast<uint2*>(codes_dst));
+  launch_gather_plane(bits_src, bits_dst, src_rows, dst_rows, cols / 8, row_index, stream);
+  launch_gather_plane(scales_src, scales_dst, src_rows, dst_rows, cols / 16, row_index, stream);
+  if (codes_dst) launch_gather_plane(codes_src, codes_dst, src_rows, dst_rows, cols / 2, row_index, stream);
   return hipGetLastError();
 }
 

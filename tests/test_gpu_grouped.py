@@ -43,6 +43,11 @@ CASES = [
     ("leading-empty", 129, 4112, lambda rng: np.array([0, 0, 0, 64, 64, 129, 129])),
     ("single", 1024, 2048, lambda rng: np.array([0, 1024])),
     ("many", 2000, 96, lambda rng: _partition(rng, 2000, 128, empties=10)),
+    # equal groups: the lookup's first guess lands in the group or next to it
+    ("balanced-3", 300, 32, lambda rng: np.array([0, 100, 200, 300])),
+    ("balanced-16", 1024, 64, lambda rng: np.arange(0, 1025, 64)),
+    ("near-balanced", 4096, 32, lambda rng: np.r_[0, np.arange(1, 64) * 64 + rng.integers(-40, 40, 63), 4096]),
+    ("balanced-empties", 960, 48, lambda rng: np.array([0, 0, 240, 240, 480, 720, 720, 960, 960])),
 ]
 
 
