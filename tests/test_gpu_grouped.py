@@ -46,7 +46,7 @@ CASES = [
     # equal groups: the lookup's first guess lands in the group or next to it
     ("balanced-3", 300, 32, lambda rng: np.array([0, 100, 200, 300])),
     ("balanced-16", 1024, 64, lambda rng: np.arange(0, 1025, 64)),
-    ("near-balanced", 4096, 32, lambda rng: np.r_[0, np.arange(1, 64) * 64 + rng.integers(-40, 40, 63), 4096]),
+    ("near-balanced", 4096, 32, lambda rng: np.r_[0, np.arange(1, 64) * 64 + rng.integers(-25, 25, 63), 4096]),
     ("balanced-empties", 960, 48, lambda rng: np.array([0, 0, 240, 240, 480, 720, 720, 960, 960])),
 ]
 
