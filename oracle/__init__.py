@@ -14,7 +14,8 @@ Quantization-Aware Training for FP4" (2026-10-06):
 * the training side recomputes ``z = clip(x_train / s, -6, 6)`` with the
   cached rollout scale, brackets z between two adjacent FP4 codewords and
   keeps the one the cached bit points at, with a straight-through estimator
-  around ``s * q*`` (the rollout-guided rounding paragraph and the listing).
+  around ``s * q*`` (the rollout-guided rounding paragraph and the listing);
+* the same path on MXFP4 scales (``oracle.mx``; the Ablations bullet).
 
 The pages name NVFP4 and the E2M1 grid but not the format's parameters; the
 oracle uses the NVFP4 definition: 16-element blocks along the last dimension,
@@ -40,6 +41,16 @@ from .formats import (
     e4m3fn_decode,
     e4m3fn_encode_rne_sat,
     f32_to_bf16_rne,
+)
+from .mx import (
+    MX_BLOCK,
+    e8m0_decode,
+    floor_log2,
+    mx_block_scales,
+    mx_capture,
+    mx_full_info_fwd,
+    mx_guided_fwd,
+    mx_rne_fwd,
 )
 from .trace import (
     BLOCK,
@@ -72,7 +83,8 @@ __all__ = [
     "f32_to_bf16_rne", "BLOCK", "TENSOR_SCALE_DIVISOR", "block_scales",
     "capture", "compact_cache_bytes", "decode_scales", "full_info_fwd", "gather_records",
     "grouped_capture", "grouped_full_info_fwd", "grouped_guided_fwd", "grouped_rne_fwd",
-    "grouped_tensor_scale",
+    "grouped_tensor_scale", "MX_BLOCK", "e8m0_decode", "floor_log2", "mx_block_scales", "mx_capture",
+    "mx_full_info_fwd", "mx_guided_fwd", "mx_rne_fwd",
     "guided_fwd", "mismatch_stats", "pack_bits", "pack_nibbles", "rne_fwd",
     "ste_bwd", "tensor_scale", "unpack_bits", "unpack_nibbles",
 ]

@@ -171,9 +171,15 @@ def capture(x_bits, ts, with_codes: bool = False) -> dict:
     """
     scales = block_scales(x_bits, ts)
     x, zr, _, valid = _quotients(x_bits, scales, ts)
+    return {"scales": scales, **capture_record(x, zr, valid, with_codes)}
+
+
+def capture_record(x, zr, valid, with_codes: bool) -> dict:
+    """The per-element half of the capture, given the quotients ``zr`` and
+    the per-element valid-scale flags: parity bit-plane and optional codes."""
     sign, a = _sign_and_clipped(x, zr, valid)
     idx = np.where(valid & ~np.isnan(x), e2m1_rne_index(a), 0).astype(np.uint8)
-    out = {"scales": scales, "bits": pack_bits(idx & 1)}
+    out = {"bits": pack_bits(idx & 1)}
     if with_codes:
         out["codes"] = pack_nibbles((sign.astype(np.uint8) << 3) | idx)
     return out
@@ -211,8 +217,12 @@ def guided_fwd(x_bits, scale_bytes, ts, bits) -> dict:
     (u8[n/8]) and the codes of q* (u8[n/2]).
     """
     x, zr, s, valid = _quotients(x_bits, scale_bytes, ts)
-    n = x.size
-    c = unpack_bits(bits, n)
+    return guided_rule(x, zr, s, valid, unpack_bits(bits, x.size))
+
+
+def guided_rule(x, zr, s, valid, c) -> dict:
+    """The guided rule on given quotients (per-element x, zr, s, valid) and
+    cached bits c (one 0/1 per element)."""
     sign, a = _sign_and_clipped(x, zr, valid)
     lo, hi = e2m1_bracket(a)
     pick_lo = (lo & 1) == c
@@ -227,6 +237,11 @@ def rne_fwd(x_bits, scale_bytes, ts) -> dict:
     round-to-nearest", the vanilla-QAT baseline): as ``guided_fwd`` but
     ``m`` = the E2M1 value nearest to |z|, ties to the even index."""
     x, zr, s, valid = _quotients(x_bits, scale_bytes, ts)
+    return rne_rule(x, zr, s, valid)
+
+
+def rne_rule(x, zr, s, valid) -> dict:
+    """Round-to-nearest-even on given quotients."""
     sign, a = _sign_and_clipped(x, zr, valid)
     m_idx = e2m1_rne_index(a)
     m_val = E2M1_MAGNITUDES[m_idx].astype(np.float32)
@@ -244,8 +259,13 @@ def full_info_fwd(x_bits, scale_bytes, ts, roll_codes) -> dict:
     whole 4-bit rollout code): the endpoint of z's bracket nearest to the
     rollout's signed codeword; |z| itself when z is a codeword."""
     x, zr, s, valid = _quotients(x_bits, scale_bytes, ts)
-    n = x.size
-    q_roll = _signed_values(unpack_nibbles(roll_codes, n))
+    return full_info_rule(x, zr, s, valid, unpack_nibbles(roll_codes, x.size))
+
+
+def full_info_rule(x, zr, s, valid, roll) -> dict:
+    """Full-information guidance on given quotients and rollout codes (one
+    code per element)."""
+    q_roll = _signed_values(roll)
     sign, a = _sign_and_clipped(x, zr, valid)
     lo, hi = e2m1_bracket(a)
     sgn = np.where(sign, -1.0, 1.0)
