@@ -17,6 +17,9 @@ Functions mirror the C ABI in ``include/trace.h``:
     grouped_capture / grouped_guided_fakequant_fwd / grouped_rne_fakequant_fwd /
     grouped_full_info_fakequant_fwd: as above, with one tensor scale per group
     of rows (per-expert scales of packed MoE rows; offsets int64[groups + 1])
+    mx_capture / mx_guided_fakequant_fwd / mx_rne_fakequant_fwd /
+    mx_full_info_fakequant_fwd: the MXFP4 variant (32-element blocks, E8M0
+    scales, no tensor scale)
     ste_bwd(grad_out, mask)                          -> grad_in
 
 and ``GuidedFakeQuant`` wraps the forward/backward pair as an autograd
@@ -31,7 +34,8 @@ __all__ = [
     "TraceError", "LIB_PATH", "lib", "abi_version", "tensor_scale", "capture",
     "guided_fakequant_fwd", "rne_fakequant_fwd", "full_info_fakequant_fwd", "ste_bwd", "gather_records",
     "grouped_tensor_scale", "grouped_capture", "grouped_guided_fakequant_fwd", "grouped_rne_fakequant_fwd",
-    "grouped_full_info_fakequant_fwd",
+    "grouped_full_info_fakequant_fwd", "mx_capture", "mx_guided_fakequant_fwd", "mx_rne_fakequant_fwd",
+    "mx_full_info_fakequant_fwd",
     "GuidedFakeQuant",
     "STATUS",
 ]
@@ -76,6 +80,10 @@ def _load():
         "trace_grouped_guided_fakequant_fwd": ([p, i64, i64, p, i64, p, p, p, p, p, p, p], st),
         "trace_grouped_rne_fakequant_fwd": ([p, i64, i64, p, i64, p, p, p, p, p, p], st),
         "trace_grouped_full_info_fakequant_fwd": ([p, i64, i64, p, i64, p, p, p, p, p, p, p], st),
+        "trace_mx_capture": ([p, i64, i64, p, p, p, p], st),
+        "trace_mx_guided_fakequant_fwd": ([p, i64, i64, p, p, p, p, p, p], st),
+        "trace_mx_rne_fakequant_fwd": ([p, i64, i64, p, p, p, p, p], st),
+        "trace_mx_full_info_fakequant_fwd": ([p, i64, i64, p, p, p, p, p, p], st),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -314,6 +322,60 @@ def grouped_full_info_fakequant_fwd(x_train, offsets, scales, ts, codes, y=None,
                                     qcodes=None):
     """``full_info_fakequant_fwd`` with one tensor scale per group of rows."""
     return _grouped_fwd("full", x_train, offsets, scales, ts, codes, y, mask, want_codes, qcodes)
+
+
+def mx_capture(x_roll, want_codes=False, scales=None, bits=None, codes=None):
+    """MXFP4 capture: (scales u8[n/32] E8M0, bits u8[n/8], codes u8[n/2] or None)."""
+    _bf16(x_roll, "x_roll")
+    rows, cols = _rows_cols(x_roll)
+    n = rows * cols
+    scales = _u8(n // 32, x_roll, scales, "scales")
+    bits = _u8(n // 8, x_roll, bits, "bits")
+    if want_codes or codes is not None:
+        codes = _u8(n // 2, x_roll, codes, "codes")
+    _check(lib.trace_mx_capture(_ptr(x_roll), rows, cols, _ptr(scales), _ptr(bits), _ptr(codes), _stream(x_roll)),
+           "trace_mx_capture")
+    return scales, bits, codes
+
+
+def _mx_fwd(mode, x, scales, side, y, mask, want_codes, qcodes):
+    _bf16(x, "x_train")
+    rows, cols = _rows_cols(x)
+    n = rows * cols
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _bf16(y, "y")
+    mask = _u8(n // 8, x, mask, "mask")
+    if want_codes or qcodes is not None:
+        qcodes = _u8(n // 2, x, qcodes, "qcodes")
+    tail = (_ptr(y), _ptr(mask), _ptr(qcodes), _stream(x))
+    if mode == "guided":
+        st, name = lib.trace_mx_guided_fakequant_fwd(_ptr(x), rows, cols, _ptr(scales), _ptr(side), *tail), \
+            "trace_mx_guided_fakequant_fwd"
+    elif mode == "full":
+        st, name = lib.trace_mx_full_info_fakequant_fwd(_ptr(x), rows, cols, _ptr(scales), _ptr(side), *tail), \
+            "trace_mx_full_info_fakequant_fwd"
+    else:
+        st, name = lib.trace_mx_rne_fakequant_fwd(_ptr(x), rows, cols, _ptr(scales), *tail), \
+            "trace_mx_rne_fakequant_fwd"
+    _check(st, name)
+    return y, mask, qcodes
+
+
+def mx_guided_fakequant_fwd(x_train, scales, bits, y=None, mask=None, want_codes=False, qcodes=None):
+    """Rollout-guided forward on MXFP4 scales: (y, mask, qcodes)."""
+    return _mx_fwd("guided", x_train, scales, bits, y, mask, want_codes, qcodes)
+
+
+def mx_rne_fakequant_fwd(x_train, scales, y=None, mask=None, want_codes=False, qcodes=None):
+    """Round-to-nearest-even forward on MXFP4 scales: (y, mask, qcodes)."""
+    return _mx_fwd("rne", x_train, scales, None, y, mask, want_codes, qcodes)
+
+
+def mx_full_info_fakequant_fwd(x_train, scales, codes, y=None, mask=None, want_codes=False, qcodes=None):
+    """Full-information guided forward on MXFP4 scales: (y, mask, qcodes)."""
+    return _mx_fwd("full", x_train, scales, codes, y, mask, want_codes, qcodes)
 
 
 class GuidedFakeQuant(torch.autograd.Function):

@@ -23,30 +23,10 @@
 #include <stdint.h>
 
 #include "device_math.h"
+#include "fp4_block.h"
 #include "launch.h"
 
 namespace trace_dev {
-
-constexpr int kThreads = 256;
-
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-
-// v_cmp_class mask: signalling/quiet NaN and +-infinity.
-constexpr int kBadClass = 0x001 | 0x002 | 0x004 | 0x200;
-
-__device__ __forceinline__ void load_block(const uint4* __restrict__ x, uint64_t b, uint32_t (&w)[8]) {
-  const uint4 v0 = x[2 * b];
-  const uint4 v1 = x[2 * b + 1];
-  w[0] = v0.x; w[1] = v0.y; w[2] = v0.z; w[3] = v0.w;
-  w[4] = v1.x; w[5] = v1.y; w[6] = v1.z; w[7] = v1.w;
-}
-
-__device__ __forceinline__ void store_block(uint4* __restrict__ y, uint64_t b, const uint32_t (&w)[8]) {
-  y[2 * b] = make_uint4(w[0], w[1], w[2], w[3]);
-  y[2 * b + 1] = make_uint4(w[4], w[5], w[6], w[7]);
-}
 
 // ---------------------------------------------------------------------------
 // exact helpers of the fast path
@@ -105,74 +85,6 @@ __device__ __forceinline__ float div_fast_u(float a, float d, float rhi, float r
   return __builtin_fmaf(-r, rhi, q1);
 }
 
-// Toward-zero E2M1 codes of two values into byte SEL of acc: the stochastic-
-// rounding conversion with a zero random operand truncates.  Issued as inline
-// asm with acc tied to the destination: the compiler's builtin for this
-// instruction does not keep the other bytes of the destination (the
-// round-to-nearest builtin does).
-template <int SEL>
-__device__ __forceinline__ uint32_t fp4_rtz_at(uint32_t acc, float a, float b) {
-  const f32x2 v = {a, b};
-  asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, 0, 1.0 op_sel:[0,0,%2,%3]"
-      : "+v"(acc)
-      : "v"(v), "n"(SEL & 1), "n"(SEL >> 1));
-  return acc;
-}
-
-// E2M1 codes (sign << 3 | index) of two values, written into byte `sel` of
-// `acc`: round to nearest even (saturating at 6) or toward zero.
-#define FP4_RNE(acc, a, b, sel) __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((acc), (a), (b), 1.0f, (sel))
-#define FP4_RTZ(acc, a, b, sel) fp4_rtz_at<(sel)>((acc), (a), (b))
-// Codes of the even (off = 0) or odd (off = 1) elements of a 16-value block,
-// nibble k holding element 2k + off.  The byte selector must be a literal.
-#define FP4_PACK8(CVT, dst, v, off)                 \
-  do {                                              \
-    dst = CVT(dst, (v)[0 + (off)], (v)[2 + (off)], 0);   \
-    dst = CVT(dst, (v)[4 + (off)], (v)[6 + (off)], 1);   \
-    dst = CVT(dst, (v)[8 + (off)], (v)[10 + (off)], 2);  \
-    dst = CVT(dst, (v)[12 + (off)], (v)[14 + (off)], 3); \
-  } while (0)
-
-// Bit 0 of the 16 nibbles of E (elements 0,2,..,14) and O (1,3,..,15),
-// gathered into a 16-bit word in element order.
-__device__ __forceinline__ uint32_t gather_parity(uint32_t E, uint32_t O) {
-  const uint32_t X = ((O << 1) & 0x22222222u) | (E & ~0x22222222u);
-  const uint32_t Y = ((X >> 2) & 0x0C0C0C0Cu) | (X & ~0x0C0C0C0Cu);
-  const uint32_t Z = ((Y >> 4) & 0x00F000F0u) | (Y & ~0x00F000F0u);
-  return __builtin_amdgcn_perm(Z, Z, 0x0C0C0200u);
-}
-
-// Inverse of gather_parity: bit j of a 16-bit word W to bit 0 of nibble j/2
-// of the result (even j) or bit 1 of that nibble (odd j); other bits junk.
-__device__ __forceinline__ uint32_t spread_bits(uint32_t W) {
-  const uint32_t Z = __builtin_amdgcn_perm(W, W, 0x0C010C00u);
-  const uint32_t Y = ((Z << 4) & 0x0F000F00u) | (Z & ~0x0F000F00u);
-  return ((Y << 2) & 0x30303030u) | (Y & ~0x30303030u);
-}
-
-// y for elements 4K..4K+3 from byte K of the even / odd code dwords:
-// bf16_RNE(fl32(s * q)) with q the decoded codeword (sign included).
-template <int K>
-__device__ __forceinline__ void decode_scaled_pair(uint32_t QE, uint32_t QO, float s, uint32_t (&out)[8]) {
-  const f32x2 ge = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(QE, 1.0f, K);  // elements 4K, 4K+2
-  const f32x2 go = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(QO, 1.0f, K);  // elements 4K+1, 4K+3
-  const bf16x2 p0 = __builtin_convertvector((f32x2){s * ge.x, s * go.x}, bf16x2);
-  const bf16x2 p1 = __builtin_convertvector((f32x2){s * ge.y, s * go.y}, bf16x2);
-  __builtin_memcpy(&out[2 * K], &p0, 4);
-  __builtin_memcpy(&out[2 * K + 1], &p1, 4);
-}
-
-// Element-order nibble codes from the even/odd nibble dwords.
-__device__ __forceinline__ void interleave_codes(uint32_t E, uint32_t O, uint32_t& c0, uint32_t& c1) {
-  c0 = 0; c1 = 0;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const uint32_t ce = (E >> (4 * k)) & 15u, co = (O >> (4 * k)) & 15u;
-    const uint32_t pair = ce | (co << 4);
-    if (k < 4) c0 |= pair << (8 * k); else c1 |= pair << (8 * (k - 4));
-  }
-}
-
 // ---------------------------------------------------------------------------
 // exact fallbacks: the definitions evaluated directly (IEEE division)
 // ---------------------------------------------------------------------------
@@ -199,16 +111,9 @@ __device__ __noinline__ void capture_block_exact(const uint4* __restrict__ x4, u
   uint64_t cw = 0;
 #pragma unroll 1
   for (int j = 0; j < kBlock; ++j) {
-    const float xv = __uint_as_float((uint32_t)x[j] << 16);
-    uint32_t sign = __float_as_uint(xv) >> 31;
-    uint32_t idx = 0;
-    if (is_nan_f(xv)) {
-      sign = 0;
-    } else if (valid) {
-      idx = e2m1_rne_index(fminf(fabsf(xv / s), 6.f));
-    }
-    bitword |= (idx & 1u) << j;
-    cw |= (uint64_t)((sign << 3) | idx) << (4 * j);
+    const uint32_t code = exact_capture_code(__uint_as_float((uint32_t)x[j] << 16), s, valid);
+    bitword |= (code & 1u) << j;
+    cw |= (uint64_t)code << (4 * j);
   }
   scales[b] = (uint8_t)sb;
   bits[b] = (uint16_t)bitword;
@@ -230,39 +135,13 @@ __device__ __noinline__ void fakequant_block_exact(int mode, const uint4* __rest
   uint64_t cw = 0;
 #pragma unroll 1
   for (int j = 0; j < kBlock; ++j) {
-    const float xv = __uint_as_float((uint32_t)x[j] << 16);
-    uint32_t sign = __float_as_uint(xv) >> 31;
-    uint32_t idx = 0, mk = 0;
-    float yv;
-    if (is_nan_f(xv)) {
-      sign = 0;
-      yv = 0.f;
-    } else if (!valid) {
-      yv = sign ? -0.f : 0.f;
-    } else {
-      const float zr = xv / s;
-      mk = fabsf(zr) <= 6.f ? 1u : 0u;
-      const float a = fminf(fabsf(zr), 6.f);
-      if (mode == 1) {
-        const uint32_t lo = e2m1_floor_index(a);
-        const bool exact = (a == e2m1_mag(lo));
-        idx = (exact || ((lo & 1u) == ((cached >> j) & 1u))) ? lo : lo + 1;
-      } else if (mode == 2) {
-        // endpoint nearest to the rollout codeword: the upper one exactly when
-        // the rollout code has z's sign and a larger magnitude index
-        const uint32_t lo = e2m1_floor_index(a);
-        const bool exact = (a == e2m1_mag(lo));
-        const uint32_t rc = ((j < 8 ? roll_lo : roll_hi) >> (4 * (j & 7))) & 15u;
-        idx = (!exact && (rc >> 3) == sign && (rc & 7u) > lo) ? lo + 1 : lo;
-      } else {
-        idx = e2m1_rne_index(a);
-      }
-      const float q = e2m1_mag(idx);
-      yv = s * (sign ? -q : q);
-    }
+    const uint32_t rc = ((j < 8 ? roll_lo : roll_hi) >> (4 * (j & 7))) & 15u;
+    uint32_t code, mk, ybits;
+    exact_forward_element(mode, __uint_as_float((uint32_t)x[j] << 16), s, valid, (cached >> j) & 1u, rc, code, mk,
+                          ybits);
     maskword |= mk << j;
-    y[j] = (uint16_t)bf16_rne_bits(yv);
-    cw |= (uint64_t)((sign << 3) | idx) << (4 * j);
+    y[j] = (uint16_t)ybits;
+    cw |= (uint64_t)code << (4 * j);
   }
   mask[b] = (uint16_t)maskword;
   if (qcodes) qcodes[b] = make_uint2((uint32_t)cw, (uint32_t)(cw >> 32));
@@ -569,33 +448,6 @@ __global__ __launch_bounds__(kThreads) void capture_kernel(const uint4* __restri
 // ---------------------------------------------------------------------------
 // fake-quant forward (guided or plain RNE)
 // ---------------------------------------------------------------------------
-// De-interleave element-order nibble codes (c0: elements 0..7, c1: 8..15)
-// into even-element and odd-element nibble dwords.
-__device__ __forceinline__ void split_codes(uint32_t c0, uint32_t c1, uint32_t& E, uint32_t& O) {
-  uint32_t e0 = c0 & 0x0F0F0F0Fu, e1 = c1 & 0x0F0F0F0Fu;
-  uint32_t o0 = (c0 >> 4) & 0x0F0F0F0Fu, o1 = (c1 >> 4) & 0x0F0F0F0Fu;
-  e0 = (e0 | (e0 >> 4)) & 0x00FF00FFu;  // bytes 0, 2 hold nibble pairs
-  e1 = (e1 | (e1 >> 4)) & 0x00FF00FFu;
-  o0 = (o0 | (o0 >> 4)) & 0x00FF00FFu;
-  o1 = (o1 | (o1 >> 4)) & 0x00FF00FFu;
-  E = __builtin_amdgcn_perm(e1, e0, 0x06040200u);
-  O = __builtin_amdgcn_perm(o1, o0, 0x06040200u);
-}
-
-// Codes of q* for the full-information rule from the floor codes F, the
-// predecessor floor codes P (equal to F exactly when q is inside a bracket)
-// and the rollout codes R, all packed 8 per dword: the upper endpoint F + 1
-// is taken when q is inside a bracket and the rollout code has the same sign
-// as F and a larger magnitude index.
-__device__ __forceinline__ uint32_t full_info_select(uint32_t F, uint32_t P, uint32_t R) {
-  uint32_t t = F ^ P;
-  t |= t >> 2;
-  t |= t >> 1;                                                    // bit 0 per nibble: exact
-  const uint32_t gt = ((R | 0x88888888u) - (F & 0x77777777u) - 0x11111111u) & 0x88888888u;  // r_idx > f_idx
-  const uint32_t same = ~(R ^ F) & 0x88888888u;
-  return F + ((gt & same) >> 3 & ~t & 0x11111111u);
-}
-
 // One block of a fake-quant forward.
 template <int kMode>
 __device__ __forceinline__ void fakequant_one(const uint4* __restrict__ x, uint64_t b, const uint32_t (&w)[8],
@@ -609,58 +461,15 @@ __device__ __forceinline__ void fakequant_one(const uint4* __restrict__ x, uint6
 #pragma unroll
   for (int j = 0; j < 16; ++j) q[j] = div_fast<true>(block_elem(w, j), e, bad);
 
-  // clip mask: sign bit of 6 - |q| is set exactly when |q| > 6
-  uint32_t clip = 0;
-#pragma unroll
-  for (int j = 15; j >= 0; --j)
-    clip = __builtin_amdgcn_alignbit(clip, __float_as_uint(6.0f - fabsf(q[j])), 31);
-  const uint32_t maskword = (e.rhi != 0.f) ? (~clip & 0xffffu) : 0u;
-
-  float qc[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) qc[j] = __builtin_amdgcn_fmed3f(q[j], -6.0f, 6.0f);
-
-  uint32_t QE = 0, QO = 0;
-  if (kMode != 0) {
-    // floor codes of q and of its predecessor toward zero: equal exactly when
-    // q lies strictly inside a bracket, so the upper endpoint is floor + 1
-    float pv[16];  // predecessors toward zero (a NaN for +-0, whose floor code differs)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) pv[j] = __uint_as_float(__float_as_uint(qc[j]) - 1u);
-    uint32_t FE = 0, FO = 0, PE = 0, PO = 0;
-    FP4_PACK8(FP4_RTZ, FE, qc, 0);
-    FP4_PACK8(FP4_RTZ, FO, qc, 1);
-    FP4_PACK8(FP4_RTZ, PE, pv, 0);
-    FP4_PACK8(FP4_RTZ, PO, pv, 1);
-    if (kMode == 1) {
-      const uint32_t C = spread_bits(cached);  // bit 0 / bit 1 of nibble k: cached bit of 2k / 2k+1
-      uint32_t t = FE ^ PE;
-      t |= t >> 2;
-      t |= t >> 1;
-      QE = FE + (~t & (FE ^ C) & 0x11111111u);
-      t = FO ^ PO;
-      t |= t >> 2;
-      t |= t >> 1;
-      QO = FO + (~t & (FO ^ (C >> 1)) & 0x11111111u);
-    } else {
-      uint32_t RE, RO;
-      split_codes(roll.x, roll.y, RE, RO);
-      QE = full_info_select(FE, PE, RE);
-      QO = full_info_select(FO, PO, RO);
-    }
-  } else {
-    FP4_PACK8(FP4_RNE, QE, qc, 0);
-    FP4_PACK8(FP4_RNE, QO, qc, 1);
-  }
+  uint32_t QE, QO;
+  const uint32_t keep = select_codes<kMode>(q, cached, roll, QE, QO);
+  const uint32_t maskword = (e.rhi != 0.f) ? keep : 0u;
 
   if (bad) {
     fakequant_block_exact(kMode, x, b, sbyte, ts, cached, roll.x, roll.y, y, mask, qcodes);
   } else {
     uint32_t out[8];
-    decode_scaled_pair<0>(QE, QO, e.s, out);
-    decode_scaled_pair<1>(QE, QO, e.s, out);
-    decode_scaled_pair<2>(QE, QO, e.s, out);
-    decode_scaled_pair<3>(QE, QO, e.s, out);
+    decode_block(QE, QO, e.s, out);
     store_block(y, b, out);
     mask[b] = (uint16_t)maskword;
     if (qcodes) {

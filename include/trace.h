@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define TRACE_ABI_VERSION 2
+#define TRACE_ABI_VERSION 3
 
 #if defined(__GNUC__)
 #define TRACE_API __attribute__((visibility("default")))
@@ -271,6 +271,42 @@ TRACE_API trace_status trace_grouped_full_info_fakequant_fwd(const uint16_t* x_t
                                                              const float* ts, const uint8_t* codes,
                                                              uint16_t* y, uint8_t* mask,
                                                              uint8_t* qcodes, void* stream);
+
+/*
+ * MXFP4 variant.  The post reports that the method carries over to MXFP4
+ * (rcap.io post, Ablations bullet) without giving the format's parameters;
+ * they are the OCP Microscaling Formats (MX) v1.0 specification's:
+ *   - blocks of 32 consecutive elements along the last dimension
+ *     (cols % 32 == 0);
+ *   - one E8M0 scale byte b per block, standing for s = 2^(b - 127); byte
+ *     0xFF (NaN) makes a zero-scale block;
+ *   - capture: b = 127 + clamp(floor(log2(amax)) - 2, -127, 127) with amax
+ *     the block's largest magnitude (NaN ignored; an all-zero block gets
+ *     b = 0; an infinite element counts as exponent 128, b = 253);
+ *   - elements, parity bits, codes, the three forwards, the clip mask, zero
+ *     scales and NaN handling: exactly as on the NVFP4 path above, with this
+ *     s in place of fl32(E4M3FN(byte) * ts).  There is no tensor scale.
+ * Layouts: scales uint8[n/32]; bits and mask uint8[n/8] as above but 4-byte
+ * aligned; codes and qcodes uint8[n/2], 16-byte aligned.  The STE backward
+ * (trace_ste_bwd) takes the mask unchanged.
+ */
+TRACE_API trace_status trace_mx_capture(const uint16_t* x_roll, int64_t rows, int64_t cols,
+                                        uint8_t* scales, uint8_t* bits, uint8_t* codes,
+                                        void* stream);
+TRACE_API trace_status trace_mx_guided_fakequant_fwd(const uint16_t* x_train, int64_t rows,
+                                                     int64_t cols, const uint8_t* scales,
+                                                     const uint8_t* bits, uint16_t* y,
+                                                     uint8_t* mask, uint8_t* qcodes,
+                                                     void* stream);
+TRACE_API trace_status trace_mx_rne_fakequant_fwd(const uint16_t* x_train, int64_t rows,
+                                                  int64_t cols, const uint8_t* scales,
+                                                  uint16_t* y, uint8_t* mask, uint8_t* qcodes,
+                                                  void* stream);
+TRACE_API trace_status trace_mx_full_info_fakequant_fwd(const uint16_t* x_train, int64_t rows,
+                                                        int64_t cols, const uint8_t* scales,
+                                                        const uint8_t* codes, uint16_t* y,
+                                                        uint8_t* mask, uint8_t* qcodes,
+                                                        void* stream);
 
 #ifdef __cplusplus
 }

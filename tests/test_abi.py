@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert tr.abi_version() == 2
+    assert tr.abi_version() == 3
     for code in range(6):
         assert L.trace_status_string(code).decode().startswith("TRACE")
     assert b"unknown" in L.trace_status_string(99)
@@ -221,3 +221,22 @@ def test_grouped_validation():
     assert ts_fn(P(x), 64, 32, P(off), 4, P(A + 0x9000000), ws, P(ts + 2), None) == E_ALIGN
     assert ts_fn(P(x), 64, 32, P(off), 4, P(x + 64), ws, P(ts), None) == E_ALIAS
     assert ts_fn(P(x), 64, 32, P(off), 4, P(A + 0x9000000), ws, P(off + 24), None) == E_ALIAS
+
+
+def test_mx_validation():
+    x, sc, bi, cd, y, mk = (A + k * 0x1000000 for k in range(6))
+    cap = L.trace_mx_capture
+    assert cap(P(x), 4, 48, P(sc), P(bi), None, None) == E_SHAPE      # cols % 32
+    assert cap(P(x), 4, 64, None, P(bi), None, None) == E_NULL
+    assert cap(P(x), 4, 64, P(sc), P(bi + 2), None, None) == E_ALIGN   # bits need 4 bytes
+    assert cap(P(x), 4, 64, P(sc), P(bi), P(cd + 8), None) == E_ALIGN  # codes need 16 bytes
+    assert cap(P(x), 4, 64, P(sc), P(x + 64), None, None) == E_ALIAS
+    assert cap(P(x), 0, 64, None, None, None, None) == OK
+    g = L.trace_mx_guided_fakequant_fwd
+    assert g(P(x), 4, 64, P(sc), None, P(y), P(mk), None, None) == E_NULL
+    assert g(P(x), 4, 64, P(sc), P(bi), P(y), P(mk + 2), None, None) == E_ALIGN
+    assert g(P(x), 4, 64, P(sc), P(bi), P(sc), P(mk), None, None) == E_ALIAS
+    f = L.trace_mx_full_info_fakequant_fwd
+    assert f(P(x), 4, 64, P(sc), P(cd + 8), P(y), P(mk), None, None) == E_ALIGN
+    r = L.trace_mx_rne_fakequant_fwd
+    assert r(P(x), 4, 80, P(sc), P(y), P(mk), None, None) == E_SHAPE
