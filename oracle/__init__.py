@@ -57,6 +57,7 @@ from .trace import (
     TENSOR_SCALE_DIVISOR,
     block_scales,
     capture,
+    capture_lowbits,
     compact_cache_bytes,
     decode_scales,
     full_info_fwd,
@@ -67,10 +68,13 @@ from .trace import (
     grouped_rne_fwd,
     grouped_tensor_scale,
     guided_fwd,
+    lowbits_fwd,
+    lowbits_reconstruct,
     mismatch_stats,
     pack_bits,
     pack_nibbles,
     rne_fwd,
+    signed_index,
     ste_bwd,
     tensor_scale,
     unpack_bits,
@@ -84,7 +88,8 @@ __all__ = [
     "capture", "compact_cache_bytes", "decode_scales", "full_info_fwd", "gather_records",
     "grouped_capture", "grouped_full_info_fwd", "grouped_guided_fwd", "grouped_rne_fwd",
     "grouped_tensor_scale", "MX_BLOCK", "e8m0_decode", "floor_log2", "mx_block_scales", "mx_capture",
-    "mx_full_info_fwd", "mx_guided_fwd", "mx_rne_fwd",
+    "mx_full_info_fwd", "mx_guided_fwd", "mx_rne_fwd", "capture_lowbits", "lowbits_fwd", "lowbits_reconstruct",
+    "signed_index",
     "guided_fwd", "mismatch_stats", "pack_bits", "pack_nibbles", "rne_fwd",
     "ste_bwd", "tensor_scale", "unpack_bits", "unpack_nibbles",
 ]

@@ -285,6 +285,76 @@ def ste_bwd(grad_bits, mask_bytes, n: int) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# b > 1 cached low bits (low_bits(q_roll, b) in the listing, which the post
+# runs with b = 1).  Reading: the b low bits of the codeword's signed grid
+# index in two's complement (for b = 1 the E2M1 mantissa bit); stored as b
+# bit-planes of the b = 1 layout, plane k holding bit k.  The training side
+# reconstructs the rollout codeword as the signed index with that residue
+# modulo 2^b nearest to the middle of z's bracket (within the grid's 15
+# signed indices), then takes the bracket endpoint nearest to it.  For b = 1
+# this is the guided rule, for b = 4 the full-information rule.
+# --------------------------------------------------------------------------
+
+SIGNED_INDEX_MAX = 7
+
+
+def signed_index(codes) -> np.ndarray:
+    """Signed grid index of each E2M1 code (sign << 3 | index): -7 .. 7, with
+    both zeros at 0."""
+    c = np.asarray(codes, dtype=np.uint8)
+    mag = (c & 7).astype(np.int64)
+    return np.where(c & 8, -mag, mag)
+
+
+def capture_lowbits(x_bits, ts, b: int) -> dict:
+    """Capture keeping b low bits per element: ``scales`` as ``capture`` and
+    ``planes`` (u8[b * n/8]): plane k is bit k of each element's signed grid
+    index modulo 2^b, in the bit-plane layout."""
+    if not 1 <= b <= 4:
+        raise ValueError("b must be 1..4")
+    cap = capture(x_bits, ts, with_codes=True)
+    n = np.asarray(x_bits).size
+    r = np.mod(signed_index(unpack_nibbles(cap["codes"], n)), 1 << b)
+    planes = np.concatenate([pack_bits((r >> k) & 1) for k in range(b)])
+    return {"scales": cap["scales"], "planes": planes}
+
+
+def lowbits_reconstruct(r, lo_signed, b: int) -> np.ndarray:
+    """Signed index with residue r (mod 2^b) nearest to lo_signed + 1/2, among
+    -7 .. 7 (candidates are 2^b apart, so there are no ties)."""
+    m = 1 << b
+    best = np.full(np.shape(r), 99, dtype=np.int64)
+    for cand in range(-SIGNED_INDEX_MAX, SIGNED_INDEX_MAX + 1):
+        ok = np.mod(cand, m) == r
+        closer = ok & (np.abs(2 * cand - (2 * lo_signed + 1)) < np.abs(2 * best - (2 * lo_signed + 1)))
+        best = np.where(closer, cand, best)
+    return best
+
+
+def lowbits_fwd(x_bits, scale_bytes, ts, planes, b: int) -> dict:
+    """Guided fake-quant forward from b cached low bits: z's bracket
+    (q-, q+) in signed indices (a, a + 1); the reconstructed rollout index t
+    (``lowbits_reconstruct``); q* = q+ if t >= a + 1 else q-; z itself when it
+    is a codeword.  Outputs as ``guided_fwd``."""
+    x, zr, s, valid = _quotients(x_bits, scale_bytes, ts)
+    n = x.size
+    pl = np.asarray(planes, dtype=np.uint8).reshape(b, -1)
+    r = np.zeros(n, dtype=np.int64)
+    for k in range(b):
+        r |= unpack_bits(pl[k], n).astype(np.int64) << k
+    sign, a = _sign_and_clipped(x, zr, valid)
+    lo, hi = e2m1_bracket(a)
+    # signed bracket: z >= 0: (lo, hi); z < 0: (-hi, -lo)
+    lo_signed = np.where(sign, -hi.astype(np.int64), lo.astype(np.int64))
+    t = lowbits_reconstruct(r, lo_signed, b)
+    upper = t >= lo_signed + 1
+    # magnitude of the chosen endpoint: the signed upper endpoint is hi for z >= 0, lo for z < 0
+    m_idx = np.where(lo == hi, lo, np.where(upper != sign, hi, lo)).astype(np.uint8)
+    m_val = E2M1_MAGNITUDES[m_idx].astype(np.float32)
+    return _finish(x, zr, s, valid, sign, m_idx, m_val)
+
+
+# --------------------------------------------------------------------------
 # trainer-side readback (the post's remark that the training engine must
 # read the rollout records back): records in the trainer's row order
 # --------------------------------------------------------------------------
