@@ -20,6 +20,8 @@ Functions mirror the C ABI in ``include/trace.h``:
     mx_capture / mx_guided_fakequant_fwd / mx_rne_fakequant_fwd /
     mx_full_info_fakequant_fwd: the MXFP4 variant (32-element blocks, E8M0
     scales, no tensor scale)
+    capture_lowbits(x_roll, ts, nbits)               -> (scales, planes, codes)
+    lowbits_fakequant_fwd(x_train, scales, ts, nbits, planes) -> (y, mask, qcodes)
     ste_bwd(grad_out, mask)                          -> grad_in
 
 and ``GuidedFakeQuant`` wraps the forward/backward pair as an autograd
@@ -35,7 +37,7 @@ __all__ = [
     "guided_fakequant_fwd", "rne_fakequant_fwd", "full_info_fakequant_fwd", "ste_bwd", "gather_records",
     "grouped_tensor_scale", "grouped_capture", "grouped_guided_fakequant_fwd", "grouped_rne_fakequant_fwd",
     "grouped_full_info_fakequant_fwd", "mx_capture", "mx_guided_fakequant_fwd", "mx_rne_fakequant_fwd",
-    "mx_full_info_fakequant_fwd",
+    "mx_full_info_fakequant_fwd", "capture_lowbits", "lowbits_fakequant_fwd",
     "GuidedFakeQuant",
     "STATUS",
 ]
@@ -81,6 +83,8 @@ def _load():
         "trace_grouped_rne_fakequant_fwd": ([p, i64, i64, p, i64, p, p, p, p, p, p], st),
         "trace_grouped_full_info_fakequant_fwd": ([p, i64, i64, p, i64, p, p, p, p, p, p, p], st),
         "trace_mx_capture": ([p, i64, i64, p, p, p, p], st),
+        "trace_capture_lowbits": ([p, i64, i64, p, ctypes.c_int32, p, p, p, p], st),
+        "trace_lowbits_fakequant_fwd": ([p, i64, i64, p, p, ctypes.c_int32, p, p, p, p, p], st),
         "trace_mx_guided_fakequant_fwd": ([p, i64, i64, p, p, p, p, p, p], st),
         "trace_mx_rne_fakequant_fwd": ([p, i64, i64, p, p, p, p, p], st),
         "trace_mx_full_info_fakequant_fwd": ([p, i64, i64, p, p, p, p, p, p], st),
@@ -322,6 +326,39 @@ def grouped_full_info_fakequant_fwd(x_train, offsets, scales, ts, codes, y=None,
                                     qcodes=None):
     """``full_info_fakequant_fwd`` with one tensor scale per group of rows."""
     return _grouped_fwd("full", x_train, offsets, scales, ts, codes, y, mask, want_codes, qcodes)
+
+
+def capture_lowbits(x_roll, ts, nbits, want_codes=False, scales=None, planes=None, codes=None):
+    """Capture keeping b = nbits low bits per element: (scales u8[n/16],
+    planes u8[nbits * n/8], codes or None)."""
+    _bf16(x_roll, "x_roll")
+    rows, cols = _rows_cols(x_roll)
+    n = rows * cols
+    scales = _u8(n // 16, x_roll, scales, "scales")
+    planes = _u8(nbits * (n // 8), x_roll, planes, "planes")
+    if want_codes or codes is not None:
+        codes = _u8(n // 2, x_roll, codes, "codes")
+    _check(lib.trace_capture_lowbits(_ptr(x_roll), rows, cols, _ptr(ts), nbits, _ptr(scales), _ptr(planes),
+                                     _ptr(codes), _stream(x_roll)), "trace_capture_lowbits")
+    return scales, planes, codes
+
+
+def lowbits_fakequant_fwd(x_train, scales, ts, nbits, planes, y=None, mask=None, want_codes=False, qcodes=None):
+    """Guided forward from b = nbits cached low bits: (y, mask, qcodes)."""
+    _bf16(x_train, "x_train")
+    rows, cols = _rows_cols(x_train)
+    n = rows * cols
+    if y is None:
+        y = torch.empty_like(x_train)
+    else:
+        _bf16(y, "y")
+    mask = _u8(n // 8, x_train, mask, "mask")
+    if want_codes or qcodes is not None:
+        qcodes = _u8(n // 2, x_train, qcodes, "qcodes")
+    _check(lib.trace_lowbits_fakequant_fwd(_ptr(x_train), rows, cols, _ptr(scales), _ptr(ts), nbits, _ptr(planes),
+                                           _ptr(y), _ptr(mask), _ptr(qcodes), _stream(x_train)),
+           "trace_lowbits_fakequant_fwd")
+    return y, mask, qcodes
 
 
 def mx_capture(x_roll, want_codes=False, scales=None, bits=None, codes=None):

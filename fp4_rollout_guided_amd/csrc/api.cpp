@@ -262,6 +262,45 @@ trace_status trace_gather_records(const uint8_t* bits_src, const uint8_t* scales
 }
 
 // ---------------------------------------------------------------------------
+// b cached low bits
+// ---------------------------------------------------------------------------
+
+trace_status trace_capture_lowbits(const uint16_t* x_roll, int64_t rows, int64_t cols, const float* ts,
+                                   int32_t nbits, uint8_t* scales, uint8_t* planes, uint8_t* codes, void* stream) {
+  uint64_t n = 0;
+  if (trace_status st = site_size(rows, cols, &n)) return st;
+  if (nbits < 1 || nbits > 4) return TRACE_E_SHAPE;
+  if (n == 0) return TRACE_OK;
+  if (!x_roll || !ts || !scales || !planes) return TRACE_E_NULL;
+  if (!aligned(x_roll, 16) || !aligned(ts, 4) || !aligned(planes, 2) || (codes && !aligned(codes, 8)))
+    return TRACE_E_ALIGN;
+  const Range outs[3] = {rng(scales, n / 16), rng(planes, (uint64_t)nbits * (n / 8)), rng(codes, codes ? n / 2 : 0)};
+  const Range ins[2] = {rng(x_roll, 2 * n), rng(ts, 4)};
+  if (trace_status st = check_alias(outs, 3, ins, 2)) return st;
+  return hip_status(trace_host::launch_capture(x_roll, n / 16, ts, nullptr, scales, planes, codes,
+                                               static_cast<hipStream_t>(stream), (uint32_t)nbits));
+}
+
+trace_status trace_lowbits_fakequant_fwd(const uint16_t* x_train, int64_t rows, int64_t cols, const uint8_t* scales,
+                                         const float* ts, int32_t nbits, const uint8_t* planes, uint16_t* y,
+                                         uint8_t* mask, uint8_t* qcodes, void* stream) {
+  uint64_t n = 0;
+  if (trace_status st = site_size(rows, cols, &n)) return st;
+  if (nbits < 1 || nbits > 4) return TRACE_E_SHAPE;
+  if (n == 0) return TRACE_OK;
+  if (!x_train || !scales || !ts || !planes || !y || !mask) return TRACE_E_NULL;
+  if (!aligned(x_train, 16) || !aligned(y, 16) || !aligned(ts, 4) || !aligned(mask, 2) || !aligned(planes, 2) ||
+      (qcodes && !aligned(qcodes, 8)))
+    return TRACE_E_ALIGN;
+  const Range outs[3] = {rng(y, 2 * n), rng(mask, n / 8), rng(qcodes, qcodes ? n / 2 : 0)};
+  const Range ins[4] = {rng(x_train, 2 * n), rng(scales, n / 16), rng(ts, 4),
+                        rng(planes, (uint64_t)nbits * (n / 8))};
+  if (trace_status st = check_alias(outs, 3, ins, 4, /*inplace_out=*/0, /*inplace_in=*/0)) return st;
+  return hip_status(trace_host::launch_lowbits_fakequant(x_train, n / 16, scales, ts, planes, (uint32_t)nbits, y,
+                                                         mask, qcodes, static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
 // MXFP4
 // ---------------------------------------------------------------------------
 

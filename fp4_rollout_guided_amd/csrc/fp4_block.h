@@ -130,14 +130,47 @@ __device__ __forceinline__ uint32_t full_info_select(uint32_t F, uint32_t P, uin
   return F + ((gt & same) >> 3 & ~t & 0x11111111u);
 }
 
+// Decision table of the b-low-bits rule, built on the host for one b: bit
+// (f & 3) * 16 + r of lo (f < 4) or hi (f >= 4) is set when, for z >= 0 in
+// the bracket (f, f + 1) and a rollout residue r, the reconstructed rollout
+// index is at or above f + 1.
+struct LowBitsTable {
+  uint32_t mask;   // 2^b - 1
+  uint64_t lo, hi;
+};
+
+// Codes of q* for the b-low-bits rule, 8 nibbles at a time: floor codes F,
+// predecessor floor codes P (F == P inside a bracket) and residues R (b low
+// bits of the rollout's signed grid index).  Inside a bracket the magnitude
+// steps up from f to f + 1 exactly when the table bit for (f, r') is set,
+// where r' is the residue mirrored to z >= 0 (-r mod 2^b for negative z).
+__device__ __forceinline__ uint32_t lowbits_select(uint32_t F, uint32_t P, uint32_t R, const LowBitsTable& lb) {
+  uint32_t t = F ^ P;
+  t |= t >> 2;
+  t |= t >> 1;
+  uint32_t Q = F;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t n = (F >> (4 * k)) & 15u;
+    const uint32_t sgn = n >> 3, f = n & 7u;
+    const uint32_t r = (R >> (4 * k)) & 15u;
+    const uint32_t rp = ((r ^ (0u - sgn)) + sgn) & lb.mask;  // sgn ? -r : r, modulo 2^b
+    const uint32_t up = (uint32_t)(((f < 4u) ? lb.lo : lb.hi) >> (((f & 3u) << 4) | rp)) & 1u;
+    Q += (up & ~(t >> (4 * k))) << (4 * k);
+  }
+  return Q;
+}
+
 // Codes of q* for 16 quotients q (even / odd nibble dwords QE, QO) and the
 // clip-mask bits (bit j set when |q_j| <= 6; NaN quotients are the caller's
 // to flag).  kMode 0: round to nearest even; 1: guided by the cached bits
 // (16-bit word, bit j = element j); 2: full information (rollout codes,
 // element order, in roll.x / roll.y).
+// kMode 3: b cached low bits; roll holds the residues as even / odd nibble
+// dwords and lb the decision table.
 template <int kMode>
 __device__ __forceinline__ uint32_t select_codes(const float (&q)[16], uint32_t cached, uint2 roll, uint32_t& QE,
-                                                 uint32_t& QO) {
+                                                 uint32_t& QO, const LowBitsTable& lb = LowBitsTable{}) {
   // clip mask: sign bit of 6 - |q| is set exactly when |q| > 6
   uint32_t clip = 0;
 #pragma unroll
@@ -171,17 +204,47 @@ __device__ __forceinline__ uint32_t select_codes(const float (&q)[16], uint32_t 
       t |= t >> 2;
       t |= t >> 1;
       QO = FO + (~t & (FO ^ (C >> 1)) & 0x11111111u);
-    } else {
+    } else if (kMode == 2) {
       uint32_t RE, RO;
       split_codes(roll.x, roll.y, RE, RO);
       QE = full_info_select(FE, PE, RE);
       QO = full_info_select(FO, PO, RO);
+    } else {
+      QE = lowbits_select(FE, PE, roll.x, lb);
+      QO = lowbits_select(FO, PO, roll.y, lb);
     }
   } else {
     FP4_PACK8(FP4_RNE, QE, qc, 0);
     FP4_PACK8(FP4_RNE, QO, qc, 1);
   }
   return ~clip & 0xffffu;
+}
+
+// Signed grid index of each code nibble (sign << 3 | index) as a 4-bit two's
+// complement nibble: the index, or 16 - index for negative codes (0 for -0).
+// Its low b bits are the b cached low bits.
+__device__ __forceinline__ uint32_t signed_index_nibbles(uint32_t C) {
+  const uint32_t i = C & 0x77777777u;
+  const uint32_t sgn = (C >> 3) & 0x11111111u;
+  const uint32_t m = (sgn << 4) - sgn;                       // 0xF in negative nibbles
+  const uint32_t neg = (0x88888888u - i) ^ 0x88888888u;      // (16 - i) mod 16, no borrows (i <= 7)
+  return (i & ~m) | (neg & m);
+}
+
+// Low-bit residues of 16 elements from b bit-plane words (bit j = element
+// j), as even / odd nibble dwords.
+__device__ __forceinline__ void residue_nibbles(const uint32_t (&pw)[4], uint32_t nplanes, uint32_t& RE,
+                                                uint32_t& RO) {
+  RE = 0;
+  RO = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if ((uint32_t)k < nplanes) {
+      const uint32_t sp = spread_bits(pw[k]);
+      RE |= (sp & 0x11111111u) << k;
+      RO |= ((sp >> 1) & 0x11111111u) << k;
+    }
+  }
 }
 
 // y (8 packed bf16 pairs) for 16 codes: bf16_RNE(fl32(s * q)).
@@ -207,9 +270,10 @@ __device__ __forceinline__ uint32_t exact_capture_code(float xv, float s, bool v
 
 // Forward of one element: code of q*, clip-mask bit and y bits.
 // mode 0: RNE; 1: guided by the cached bit cbit; 2: full information with
-// rollout code rc.
+// rollout code rc; 3: b cached low bits with residue rc and table lb.
 __device__ __forceinline__ void exact_forward_element(int mode, float xv, float s, bool valid, uint32_t cbit,
-                                                      uint32_t rc, uint32_t& code, uint32_t& mk, uint32_t& ybits) {
+                                                      uint32_t rc, uint32_t& code, uint32_t& mk, uint32_t& ybits,
+                                                      const LowBitsTable& lb = LowBitsTable{}) {
   uint32_t sign = __float_as_uint(xv) >> 31;
   uint32_t idx = 0;
   mk = 0;
@@ -233,6 +297,13 @@ __device__ __forceinline__ void exact_forward_element(int mode, float xv, float 
       const uint32_t lo = e2m1_floor_index(a);
       const bool exact = (a == e2m1_mag(lo));
       idx = (!exact && (rc >> 3) == sign && (rc & 7u) > lo) ? lo + 1 : lo;
+    } else if (mode == 3) {
+      // rc: residue of the rollout's signed index; the table decides the step
+      const uint32_t lo = e2m1_floor_index(a);
+      const bool exact = (a == e2m1_mag(lo));
+      const uint32_t rp = ((rc ^ (0u - sign)) + sign) & lb.mask;
+      const uint32_t up = (uint32_t)(((lo < 4u) ? lb.lo : lb.hi) >> (((lo & 3u) << 4) | rp)) & 1u;
+      idx = (!exact && up) ? lo + 1 : lo;
     } else {
       idx = e2m1_rne_index(a);
     }

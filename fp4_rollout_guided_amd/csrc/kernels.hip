@@ -93,9 +93,16 @@ __device__ __forceinline__ float div_fast_u(float a, float d, float rhi, float r
 // small register footprint (one element at a time, 16-bit accesses) over
 // speed.  In-place use (y == x) is safe: each element is read before it is
 // written and the fast path stored nothing for the lane.
+// Bit planes of the b cached low bits: plane k of block b is word
+// b + k * stride of the plane array (plane 0 is the parity plane).
+struct Planes {
+  uint32_t count;   // b
+  uint64_t stride;  // words (16-bit) per plane = blocks
+};
+
 __device__ __noinline__ void capture_block_exact(const uint4* __restrict__ x4, uint64_t b, float ts,
                                                  uint8_t* __restrict__ scales, uint16_t* __restrict__ bits,
-                                                 uint2* __restrict__ codes) {
+                                                 uint2* __restrict__ codes, Planes planes = Planes{1, 0}) {
   const uint16_t* x = reinterpret_cast<const uint16_t*>(x4) + 16 * b;
   float amax = 0.f;
 #pragma unroll 1
@@ -107,26 +114,32 @@ __device__ __noinline__ void capture_block_exact(const uint4* __restrict__ x4, u
   if (ts > 0.f && ts <= 3.40282347e38f) sb = e4m3_encode_sat((amax / 6.f) / ts);
   const float s = e4m3_decode(sb) * ts;
   const bool valid = s > 0.f && s <= 3.40282347e38f;
-  uint32_t bitword = 0;
+  uint32_t pw[4] = {0, 0, 0, 0};
   uint64_t cw = 0;
 #pragma unroll 1
   for (int j = 0; j < kBlock; ++j) {
     const uint32_t code = exact_capture_code(__uint_as_float((uint32_t)x[j] << 16), s, valid);
-    bitword |= (code & 1u) << j;
+    const uint32_t si = (code & 8u) ? ((16u - (code & 7u)) & 15u) : code;  // signed index, 4-bit two's complement
+#pragma unroll
+    for (int k = 0; k < 4; ++k) pw[k] |= ((si >> k) & 1u) << j;
     cw |= (uint64_t)code << (4 * j);
   }
   scales[b] = (uint8_t)sb;
-  bits[b] = (uint16_t)bitword;
+#pragma unroll 1
+  for (uint32_t k = 0; k < planes.count; ++k) bits[b + k * planes.stride] = (uint16_t)pw[k];
   if (codes) codes[b] = make_uint2((uint32_t)cw, (uint32_t)(cw >> 32));
 }
 
 // mode: 0 = RNE, 1 = guided by the cached bit (cached = 16-bit word),
 // 2 = full information (rollout codes in roll_lo / roll_hi, element order).
+// mode 3: b cached low bits, residues as even / odd nibble dwords in
+// roll_lo / roll_hi, decision table lb.
 __device__ __noinline__ void fakequant_block_exact(int mode, const uint4* __restrict__ x4, uint64_t b,
                                                    uint32_t sbyte, float ts, uint32_t cached,
                                                    uint32_t roll_lo, uint32_t roll_hi,
                                                    uint4* __restrict__ y4, uint16_t* __restrict__ mask,
-                                                   uint2* __restrict__ qcodes) {
+                                                   uint2* __restrict__ qcodes,
+                                                   LowBitsTable lb = LowBitsTable{}) {
   const float s = e4m3_decode(sbyte) * ts;
   const bool valid = s > 0.f && s <= 3.40282347e38f;
   const uint16_t* x = reinterpret_cast<const uint16_t*>(x4) + 16 * b;
@@ -135,10 +148,11 @@ __device__ __noinline__ void fakequant_block_exact(int mode, const uint4* __rest
   uint64_t cw = 0;
 #pragma unroll 1
   for (int j = 0; j < kBlock; ++j) {
-    const uint32_t rc = ((j < 8 ? roll_lo : roll_hi) >> (4 * (j & 7))) & 15u;
+    const uint32_t rc = mode == 3 ? (((j & 1) ? roll_hi : roll_lo) >> (4 * (j >> 1))) & 15u
+                                  : ((j < 8 ? roll_lo : roll_hi) >> (4 * (j & 7))) & 15u;
     uint32_t code, mk, ybits;
     exact_forward_element(mode, __uint_as_float((uint32_t)x[j] << 16), s, valid, (cached >> j) & 1u, rc, code, mk,
-                          ybits);
+                          ybits, lb);
     maskword |= mk << j;
     y[j] = (uint16_t)ybits;
     cw |= (uint64_t)code << (4 * j);
@@ -375,10 +389,11 @@ __device__ __forceinline__ CaptureScale capture_scale(float ts) {
 }
 
 // One block of the capture: scale byte, parity bits and (optionally) codes.
+template <bool kPlanes>
 __device__ __forceinline__ void capture_one(const uint4* __restrict__ x, uint64_t b, const uint32_t (&w)[8],
                                             const CaptureScale& cs, float r6hi, float r6lo,
                                             uint8_t* __restrict__ scales, uint16_t* __restrict__ bits,
-                                            uint2* __restrict__ codes) {
+                                            uint2* __restrict__ codes, Planes planes) {
   const float ts = cs.ts;
   // block amax on packed bf16 magnitudes
   u16x2 mx;
@@ -415,10 +430,19 @@ __device__ __forceinline__ void capture_one(const uint4* __restrict__ x, uint64_
   FP4_PACK8(FP4_RNE, E, q, 0);
   FP4_PACK8(FP4_RNE, O, q, 1);
   if (bad) {
-    capture_block_exact(x, b, ts, scales, bits, codes);
+    capture_block_exact(x, b, ts, scales, bits, codes, kPlanes ? planes : Planes{1, 0});
   } else {
     scales[b] = (uint8_t)sb;
-    bits[b] = (uint16_t)gather_parity(E, O);
+    if (kPlanes) {
+      // plane k: bit k of each element's signed grid index (two's complement)
+      const uint32_t SE = signed_index_nibbles(E), SO = signed_index_nibbles(O);
+      bits[b] = (uint16_t)gather_parity(SE, SO);
+#pragma unroll
+      for (uint32_t k = 1; k < 4; ++k)
+        if (k < planes.count) bits[b + k * planes.stride] = (uint16_t)gather_parity(SE >> k, SO >> k);
+    } else {
+      bits[b] = (uint16_t)gather_parity(E, O);
+    }
     if (codes) {
       uint32_t c0, c1;
       interleave_codes(E, O, c0, c1);
@@ -427,12 +451,12 @@ __device__ __forceinline__ void capture_one(const uint4* __restrict__ x, uint64_
   }
 }
 
-template <bool kGrouped>
+template <bool kGrouped, bool kPlanes>
 __global__ __launch_bounds__(kThreads) void capture_kernel(const uint4* __restrict__ x, uint64_t nblocks,
                                                            const float* __restrict__ ts_ptr, RowGroups groups,
                                                            uint8_t* __restrict__ scales,
                                                            uint16_t* __restrict__ bits,
-                                                           uint2* __restrict__ codes) {
+                                                           uint2* __restrict__ codes, Planes planes) {
   const float r6hi = 1.0f / 6.0f;
   const float r6lo = __builtin_fmaf(-6.0f, r6hi, 1.0f) * r6hi;
   const CaptureScale cs0 = kGrouped ? CaptureScale{} : capture_scale(*ts_ptr);
@@ -441,7 +465,7 @@ __global__ __launch_bounds__(kThreads) void capture_kernel(const uint4* __restri
     uint32_t w[8];
     load_block(x, b, w);  // issued before the group search, whose latency it hides
     const CaptureScale cs = kGrouped ? capture_scale(group_tensor_scale(groups, ts_ptr, b)) : cs0;
-    capture_one(x, b, w, cs, r6hi, r6lo, scales, bits, codes);
+    capture_one<kPlanes>(x, b, w, cs, r6hi, r6lo, scales, bits, codes, planes);
   }
 }
 
@@ -453,7 +477,8 @@ template <int kMode>
 __device__ __forceinline__ void fakequant_one(const uint4* __restrict__ x, uint64_t b, const uint32_t (&w)[8],
                                               uint32_t sbyte, uint32_t cached, uint2 roll, float ts,
                                               uint4* __restrict__ y, uint16_t* __restrict__ mask,
-                                              uint2* __restrict__ qcodes) {
+                                              uint2* __restrict__ qcodes,
+                                              const LowBitsTable& lb = LowBitsTable{}) {
   const ScaleEntry e = make_scale_entry(sbyte, ts);
   bool bad = false;  // set by a NaN / infinite quotient, or a scale outside the fast range (dhi NaN)
 
@@ -462,11 +487,11 @@ __device__ __forceinline__ void fakequant_one(const uint4* __restrict__ x, uint6
   for (int j = 0; j < 16; ++j) q[j] = div_fast<true>(block_elem(w, j), e, bad);
 
   uint32_t QE, QO;
-  const uint32_t keep = select_codes<kMode>(q, cached, roll, QE, QO);
+  const uint32_t keep = select_codes<kMode>(q, cached, roll, QE, QO, lb);
   const uint32_t maskword = (e.rhi != 0.f) ? keep : 0u;
 
   if (bad) {
-    fakequant_block_exact(kMode, x, b, sbyte, ts, cached, roll.x, roll.y, y, mask, qcodes);
+    fakequant_block_exact(kMode, x, b, sbyte, ts, cached, roll.x, roll.y, y, mask, qcodes, lb);
   } else {
     uint32_t out[8];
     decode_block(QE, QO, e.s, out);
@@ -500,6 +525,30 @@ __global__ __launch_bounds__(kThreads) void fakequant_kernel(const uint4* __rest
     load_block(x, b, w);  // all loads are issued before the group search
     const float ts = kGrouped ? group_tensor_scale(groups, ts_ptr, b) : ts0;
     fakequant_one<kMode>(x, b, w, sbyte, cached, roll, ts, y, mask, qcodes);
+  }
+}
+
+// b cached low bits (kMode 3): the residues come from b bit-planes.
+__global__ __launch_bounds__(kThreads) void lowbits_fakequant_kernel(const uint4* __restrict__ x, uint64_t nblocks,
+                                                                     const uint8_t* __restrict__ scales,
+                                                                     const float* __restrict__ ts_ptr,
+                                                                     const uint16_t* __restrict__ planes, Planes pl,
+                                                                     LowBitsTable lb, uint4* __restrict__ y,
+                                                                     uint16_t* __restrict__ mask,
+                                                                     uint2* __restrict__ qcodes) {
+  const float ts0 = *ts_ptr;
+  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+  for (uint64_t b = (uint64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks; b += stride) {
+    const uint32_t sbyte = scales[b];
+    uint32_t pw[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (uint32_t k = 0; k < 4; ++k)
+      if (k < pl.count) pw[k] = planes[b + k * pl.stride];
+    uint32_t w[8];
+    load_block(x, b, w);
+    uint32_t RE, RO;
+    residue_nibbles(pw, pl.count, RE, RO);
+    fakequant_one<3>(x, b, w, sbyte, 0u, make_uint2(RE, RO), ts0, y, mask, qcodes, lb);
   }
 }
 
@@ -614,16 +663,54 @@ hipError_t launch_grouped_tensor_scale(const uint16_t* x, const GroupSpec& g, ui
 }
 
 hipError_t launch_capture(const uint16_t* x, uint64_t nblocks, const float* ts, const GroupSpec* g,
-                          uint8_t* scales, uint8_t* bits, uint8_t* codes, hipStream_t stream) {
+                          uint8_t* scales, uint8_t* bits, uint8_t* codes, hipStream_t stream, uint32_t nplanes) {
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   uint16_t* bv = reinterpret_cast<uint16_t*>(bits);
   uint2* cv = reinterpret_cast<uint2*>(codes);
   const dim3 grid(grid_for(nblocks)), block(kThreads);
+  const Planes pl{nplanes, nblocks};
   if (g)
-    hipLaunchKernelGGL(capture_kernel<true>, grid, block, 0, stream, xv, nblocks, ts, row_groups(*g, nblocks),
-                       scales, bv, cv);
+    hipLaunchKernelGGL((capture_kernel<true, false>), grid, block, 0, stream, xv, nblocks, ts,
+                       row_groups(*g, nblocks), scales, bv, cv, pl);
+  else if (nplanes > 1)
+    hipLaunchKernelGGL((capture_kernel<false, true>), grid, block, 0, stream, xv, nblocks, ts, RowGroups{}, scales,
+                       bv, cv, pl);
   else
-    hipLaunchKernelGGL(capture_kernel<false>, grid, block, 0, stream, xv, nblocks, ts, RowGroups{}, scales, bv, cv);
+    hipLaunchKernelGGL((capture_kernel<false, false>), grid, block, 0, stream, xv, nblocks, ts, RowGroups{}, scales,
+                       bv, cv, pl);
+  return hipGetLastError();
+}
+
+// Decision table of the b-low-bits rule (see LowBitsTable): for z >= 0 in
+// the bracket (f, f + 1) and residue r, the rollout index is taken to be the
+// one with residue r (mod 2^b) nearest to f + 1/2 among -7..7 (the
+// candidates are 2^b apart, so there is no tie); the upper endpoint is
+// chosen when that index is at least f + 1.
+static LowBitsTable lowbits_table(uint32_t nbits) {
+  LowBitsTable t{(1u << nbits) - 1u, 0ull, 0ull};
+  const int m = 1 << nbits;
+  for (int f = 0; f <= 6; ++f) {
+    for (int r = 0; r < m; ++r) {
+      int best = 99;
+      for (int c = -7; c <= 7; ++c) {
+        const int res = ((c % m) + m) % m;
+        const int dc = 2 * c - (2 * f + 1), db = 2 * best - (2 * f + 1);
+        if (res == r && (dc < 0 ? -dc : dc) < (db < 0 ? -db : db)) best = c;
+      }
+      if (best >= f + 1) (f < 4 ? t.lo : t.hi) |= 1ull << (((f & 3) << 4) | r);
+    }
+  }
+  return t;
+}
+
+hipError_t launch_lowbits_fakequant(const uint16_t* x, uint64_t nblocks, const uint8_t* scales, const float* ts,
+                                    const uint8_t* planes, uint32_t nplanes, uint16_t* y, uint8_t* mask,
+                                    uint8_t* qcodes, hipStream_t stream) {
+  if (nblocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(lowbits_fakequant_kernel, dim3(grid_for(nblocks)), dim3(kThreads), 0, stream,
+                     reinterpret_cast<const uint4*>(x), nblocks, scales, ts,
+                     reinterpret_cast<const uint16_t*>(planes), Planes{nplanes, nblocks}, lowbits_table(nplanes),
+                     reinterpret_cast<uint4*>(y), reinterpret_cast<uint16_t*>(mask), reinterpret_cast<uint2*>(qcodes));
   return hipGetLastError();
 }
 

@@ -39,9 +39,16 @@ hipError_t launch_tensor_scale(const uint16_t* x, uint64_t nblocks, uint32_t* pa
 // row_amax: u32[rows] workspace; ts_out: fp32[count]
 hipError_t launch_grouped_tensor_scale(const uint16_t* x, const GroupSpec& g, uint32_t* row_amax, float* ts_out,
                                        hipStream_t stream);
-// g == nullptr: one tensor scale ts[0]; otherwise ts[group of the row]
+// g == nullptr: one tensor scale ts[0]; otherwise ts[group of the row].
+// nplanes > 1 (ungrouped only): bits holds nplanes bit-planes of n/8 bytes
+// (the b cached low bits).
 hipError_t launch_capture(const uint16_t* x, uint64_t nblocks, const float* ts, const GroupSpec* g,
-                          uint8_t* scales, uint8_t* bits, uint8_t* codes, hipStream_t stream);
+                          uint8_t* scales, uint8_t* bits, uint8_t* codes, hipStream_t stream,
+                          uint32_t nplanes = 1);
+// b = nplanes cached low bits (1..4) in nplanes bit-planes of n/8 bytes.
+hipError_t launch_lowbits_fakequant(const uint16_t* x, uint64_t nblocks, const uint8_t* scales, const float* ts,
+                                    const uint8_t* planes, uint32_t nplanes, uint16_t* y, uint8_t* mask,
+                                    uint8_t* qcodes, hipStream_t stream);
 // mode 0: RNE; 1: guided, side = bit-plane (u8[n/8]); 2: full information,
 // side = rollout codes (u8[n/2]).
 hipError_t launch_fakequant(int mode, const uint16_t* x, uint64_t nblocks, const uint8_t* scales,

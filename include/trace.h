@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define TRACE_ABI_VERSION 3
+#define TRACE_ABI_VERSION 4
 
 #if defined(__GNUC__)
 #define TRACE_API __attribute__((visibility("default")))
@@ -271,6 +271,33 @@ TRACE_API trace_status trace_grouped_full_info_fakequant_fwd(const uint16_t* x_t
                                                              const float* ts, const uint8_t* codes,
                                                              uint16_t* y, uint8_t* mask,
                                                              uint8_t* qcodes, void* stream);
+
+/*
+ * b cached low bits, b = 1..4 (low_bits(q_roll, b) in the listing, which the
+ * post runs with b = 1; the bandwidth paragraph's "one mantissa bit").
+ * Reading for b > 1: the b low bits of each codeword's signed grid index
+ * (-7..7) in two's complement; for b = 1 this is the parity bit above.  The
+ * record keeps them as b bit-planes of n/8 bytes each, back to back: plane k
+ * holds bit k, in the bit-plane layout above, so plane 0 is the b = 1 record.
+ * The training side reconstructs the rollout's signed index as the one with
+ * that residue modulo 2^b nearest to the middle of z's bracket (among the
+ * grid's 15 indices; the candidates are 2^b apart, so there is no tie) and
+ * returns the bracket endpoint nearest to it; z itself when z is a
+ * codeword.  A rollout codeword within the window of 2^b signed indices
+ * around z's bracket is recovered exactly; b = 4 is full information.
+ *   nbits  : b, 1..4 (else TRACE_E_SHAPE);
+ *   planes : uint8[b * n/8], 2-byte aligned.
+ * Other arguments, layouts, aliasing and errors as trace_capture /
+ * trace_guided_fakequant_fwd.
+ */
+TRACE_API trace_status trace_capture_lowbits(const uint16_t* x_roll, int64_t rows, int64_t cols,
+                                             const float* ts, int32_t nbits, uint8_t* scales,
+                                             uint8_t* planes, uint8_t* codes, void* stream);
+TRACE_API trace_status trace_lowbits_fakequant_fwd(const uint16_t* x_train, int64_t rows,
+                                                   int64_t cols, const uint8_t* scales,
+                                                   const float* ts, int32_t nbits,
+                                                   const uint8_t* planes, uint16_t* y,
+                                                   uint8_t* mask, uint8_t* qcodes, void* stream);
 
 /*
  * MXFP4 variant.  The post reports that the method carries over to MXFP4

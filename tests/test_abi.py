@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert tr.abi_version() == 3
+    assert tr.abi_version() == 4
     for code in range(6):
         assert L.trace_status_string(code).decode().startswith("TRACE")
     assert b"unknown" in L.trace_status_string(99)
@@ -240,3 +240,18 @@ def test_mx_validation():
     assert f(P(x), 4, 64, P(sc), P(cd + 8), P(y), P(mk), None, None) == E_ALIGN
     r = L.trace_mx_rne_fakequant_fwd
     assert r(P(x), 4, 80, P(sc), P(y), P(mk), None, None) == E_SHAPE
+
+
+def test_lowbits_validation():
+    x, ts, sc, pl, cd, y, mk = (A + k * 0x1000000 for k in range(7))
+    cap = L.trace_capture_lowbits
+    assert cap(P(x), 4, 64, P(ts), 0, P(sc), P(pl), None, None) == E_SHAPE
+    assert cap(P(x), 4, 64, P(ts), 5, P(sc), P(pl), None, None) == E_SHAPE
+    assert cap(P(x), 4, 64, P(ts), 2, P(sc), None, None, None) == E_NULL
+    assert cap(P(x), 4, 64, P(ts), 2, P(sc), P(pl + 1), None, None) == E_ALIGN
+    assert cap(P(x), 4, 64, P(ts), 3, P(pl + 64), P(pl), None, None) == E_ALIAS   # 3 * 32 bytes > 64
+    assert cap(P(x), 0, 64, P(ts), 3, None, None, None, None) == OK
+    f = L.trace_lowbits_fakequant_fwd
+    assert f(P(x), 4, 64, P(sc), P(ts), 9, P(pl), P(y), P(mk), None, None) == E_SHAPE
+    assert f(P(x), 4, 64, P(sc), P(ts), 2, None, P(y), P(mk), None, None) == E_NULL
+    assert f(P(x), 4, 64, P(sc), P(ts), 2, P(pl), P(pl + 32), P(mk), None, None) == E_ALIAS  # y over plane 1
