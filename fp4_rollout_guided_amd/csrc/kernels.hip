@@ -685,7 +685,8 @@ hipError_t launch_capture(const uint16_t* x, uint64_t nblocks, const float* ts, 
 // the bracket (f, f + 1) and residue r, the rollout index is taken to be the
 // one with residue r (mod 2^b) nearest to f + 1/2 among -7..7 (the
 // candidates are 2^b apart, so there is no tie); the upper endpoint is
-// chosen when that index is at least f + 1.
+// chosen when that index is at least f + 1.  A residue no index has (8 for
+// b = 4) leaves the bit clear: the endpoint nearer zero, for either sign.
 static LowBitsTable lowbits_table(uint32_t nbits) {
   LowBitsTable t{(1u << nbits) - 1u, 0ull, 0ull};
   const int m = 1 << nbits;
@@ -697,7 +698,7 @@ static LowBitsTable lowbits_table(uint32_t nbits) {
         const int dc = 2 * c - (2 * f + 1), db = 2 * best - (2 * f + 1);
         if (res == r && (dc < 0 ? -dc : dc) < (db < 0 ? -db : db)) best = c;
       }
-      if (best >= f + 1) (f < 4 ? t.lo : t.hi) |= 1ull << (((f & 3) << 4) | r);
+      if (best != 99 && best >= f + 1) (f < 4 ? t.lo : t.hi) |= 1ull << (((f & 3) << 4) | r);
     }
   }
   return t;

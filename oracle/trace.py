@@ -292,7 +292,9 @@ def ste_bwd(grad_bits, mask_bytes, n: int) -> np.ndarray:
 # reconstructs the rollout codeword as the signed index with that residue
 # modulo 2^b nearest to the middle of z's bracket (within the grid's 15
 # signed indices), then takes the bracket endpoint nearest to it.  For b = 1
-# this is the guided rule, for b = 4 the full-information rule.
+# this is the guided rule, for b = 4 the full-information rule.  A residue
+# no index has (8 for b = 4, which no capture writes) takes the endpoint
+# nearer zero.
 # --------------------------------------------------------------------------
 
 SIGNED_INDEX_MAX = 7
@@ -321,7 +323,8 @@ def capture_lowbits(x_bits, ts, b: int) -> dict:
 
 def lowbits_reconstruct(r, lo_signed, b: int) -> np.ndarray:
     """Signed index with residue r (mod 2^b) nearest to lo_signed + 1/2, among
-    -7 .. 7 (candidates are 2^b apart, so there are no ties)."""
+    -7 .. 7 (candidates are 2^b apart, so there are no ties); 99 where no
+    index has residue r (r = 8 for b = 4)."""
     m = 1 << b
     best = np.full(np.shape(r), 99, dtype=np.int64)
     for cand in range(-SIGNED_INDEX_MAX, SIGNED_INDEX_MAX + 1):
@@ -348,8 +351,10 @@ def lowbits_fwd(x_bits, scale_bytes, ts, planes, b: int) -> dict:
     lo_signed = np.where(sign, -hi.astype(np.int64), lo.astype(np.int64))
     t = lowbits_reconstruct(r, lo_signed, b)
     upper = t >= lo_signed + 1
-    # magnitude of the chosen endpoint: the signed upper endpoint is hi for z >= 0, lo for z < 0
-    m_idx = np.where(lo == hi, lo, np.where(upper != sign, hi, lo)).astype(np.uint8)
+    # magnitude of the chosen endpoint: the signed upper endpoint is hi for z >= 0, lo for z < 0;
+    # a residue no grid index has (8 when b = 4; no capture produces it) takes the endpoint nearer zero
+    none = t == 99
+    m_idx = np.where((lo == hi) | none, lo, np.where(upper != sign, hi, lo)).astype(np.uint8)
     m_val = E2M1_MAGNITUDES[m_idx].astype(np.float32)
     return _finish(x, zr, s, valid, sign, m_idx, m_val)
 

@@ -106,3 +106,16 @@ def test_capture_planes():
     si = np.where(res >= 8, res - 16, res)                 # two's complement back to -7..7
     codes = oracle.unpack_nibbles(cap["codes"], n)
     assert np.array_equal(si, _signed_idx(codes))
+
+
+def test_residue_without_an_index_takes_the_endpoint_nearer_zero():
+    """b = 4, residue 8: no signed index -7..7 has it (no capture writes it);
+    the reading takes the bracket endpoint nearer zero for either sign."""
+    z = np.array([0.3, -0.3, 2.4, -2.4, 5.0, -5.0, 1.0, -1.0] * 2, np.float32)
+    x = F.f32_to_bf16_rne(z)
+    scales = np.full(1, 0x38, np.uint8)
+    planes = np.concatenate([oracle.pack_bits(np.full(16, (8 >> k) & 1, np.uint8)) for k in range(4)])
+    out = oracle.lowbits_fwd(x, scales, 1.0, planes, 4)
+    got = np.abs(_signed_val(_signed_idx(oracle.unpack_nibbles(out["codes"], 16))))
+    want = np.array([0.0, 0.0, 2.0, 2.0, 4.0, 4.0, 1.0, 1.0] * 2)
+    assert np.array_equal(got, want)
