@@ -14,8 +14,9 @@ plain RNE fake-quant forward (y + clip mask), STE backward.  Every kernel is
 bracketed by HIP events on the stream it runs on; the step's wall time is
 taken between device synchronizations.  After the timed steps, a separate
 pass times the rows beyond the hot path (capture with full 4-bit codes, the
-full-information forward, and MXFP4 capture and guided forward on the same
-layers) and reports them under ``next_rows``; another
+full-information forward, MXFP4 capture and guided forward, and capture to
+and forward from b = 3 cached low bits, on the same layers) and reports them
+under ``next_rows``; another
 times the per-expert (grouped) tensor scale, capture and guided forward and
 the record gather on the packed routed-expert site of the MoE layer workload
 (``moe_expert_site``).
@@ -55,6 +56,8 @@ NEXT_BYTES_PER_ELEM = {
     "full_info_fwd": 2.0 + 1 / 16 + 1 / 2 + 2.0 + 1 / 8,  # read x, scales, codes; write y, mask
     "mx_capture": 2.0 + 1 / 8 + 1 / 32,                   # MXFP4: read x; write bits + E8M0 scale bytes
     "mx_guided_fwd": 2.0 + 1 / 8 + 1 / 32 + 2.0 + 1 / 8,  # MXFP4: read x, bits, scales; write y, mask
+    "capture_lowbits3": 2.0 + 3 / 8 + 1 / 16,             # b = 3 cached low bits: three bit-planes
+    "lowbits3_fwd": 2.0 + 3 / 8 + 1 / 16 + 2.0 + 1 / 8,   # forward from three bit-planes
 }
 # Per-expert rows on the packed routed-expert site of the MoE layer workload
 # (131072 x 2048, rows grouped by 128 experts), timed in their own pass.
@@ -220,6 +223,7 @@ def main():
     codes = torch.empty(n // 2, dtype=torch.uint8, device=dev)
     mx_scales = torch.empty(n // 32, dtype=torch.uint8, device=dev)
     mx_bits = torch.empty(n // 8, dtype=torch.uint8, device=dev)
+    planes3 = torch.empty(3 * (n // 8), dtype=torch.uint8, device=dev)
     next_ms = {k: 0.0 for k in NEXT_BYTES_PER_ELEM}
     next_steps = max(1, min(args.steps, 3))
     for it in range(next_steps + 1):
@@ -237,6 +241,12 @@ def main():
             ev["mx_guided_fwd"][li][0].record(stream)
             tr.mx_guided_fakequant_fwd(d["x_train"], mx_scales, mx_bits, y=y_g, mask=mask_g)
             ev["mx_guided_fwd"][li][1].record(stream)
+            ev["capture_lowbits3"][li][0].record(stream)
+            tr.capture_lowbits(d["x_roll"], d["ts"], 3, scales=d["scales"], planes=planes3)
+            ev["capture_lowbits3"][li][1].record(stream)
+            ev["lowbits3_fwd"][li][0].record(stream)
+            tr.lowbits_fakequant_fwd(d["x_train"], d["scales"], d["ts"], 3, planes3, y=y_g, mask=mask_g)
+            ev["lowbits3_fwd"][li][1].record(stream)
         stream.synchronize()
         if it > 0:  # the first pass warms up
             for k in NEXT_BYTES_PER_ELEM:
