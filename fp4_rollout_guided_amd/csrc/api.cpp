@@ -316,7 +316,7 @@ trace_status trace_mx_capture(const uint16_t* x_roll, int64_t rows, int64_t cols
   if (trace_status st = mx_site_size(rows, cols, &n)) return st;
   if (n == 0) return TRACE_OK;
   if (!x_roll || !scales || !bits) return TRACE_E_NULL;
-  if (!aligned(x_roll, 16) || !aligned(bits, 4) || (codes && !aligned(codes, 16))) return TRACE_E_ALIGN;
+  if (!aligned(x_roll, 16) || !aligned(bits, 2) || (codes && !aligned(codes, 8))) return TRACE_E_ALIGN;
   const Range outs[3] = {rng(scales, n / 32), rng(bits, n / 8), rng(codes, codes ? n / 2 : 0)};
   const Range ins[1] = {rng(x_roll, 2 * n)};
   if (trace_status st = check_alias(outs, 3, ins, 1)) return st;
@@ -324,8 +324,8 @@ trace_status trace_mx_capture(const uint16_t* x_roll, int64_t rows, int64_t cols
                                                   static_cast<hipStream_t>(stream)));
 }
 
-// mode 0: RNE; 1: guided (side = bit-plane, n/8 bytes, 4-byte aligned);
-// 2: full information (side = codes, n/2 bytes, 16-byte aligned).
+// mode 0: RNE; 1: guided (side = bit-plane, n/8 bytes, 2-byte aligned);
+// 2: full information (side = codes, n/2 bytes, 8-byte aligned).
 static trace_status mx_fakequant(int mode, const uint16_t* x, int64_t rows, int64_t cols, const uint8_t* scales,
                                  const uint8_t* side, uint16_t* y, uint8_t* mask, uint8_t* qcodes, void* stream) {
   uint64_t n = 0;
@@ -333,9 +333,9 @@ static trace_status mx_fakequant(int mode, const uint16_t* x, int64_t rows, int6
   if (n == 0) return TRACE_OK;
   if (!x || !scales || (mode != 0 && !side) || !y || !mask) return TRACE_E_NULL;
   const uint64_t side_len = mode == 1 ? n / 8 : (mode == 2 ? n / 2 : 0);
-  const uintptr_t side_align = mode == 2 ? 16 : 4;
-  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(mask, 4) || (mode != 0 && !aligned(side, side_align)) ||
-      (qcodes && !aligned(qcodes, 16)))
+  const uintptr_t side_align = mode == 2 ? 8 : 2;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(mask, 2) || (mode != 0 && !aligned(side, side_align)) ||
+      (qcodes && !aligned(qcodes, 8)))
     return TRACE_E_ALIGN;
   const Range outs[3] = {rng(y, 2 * n), rng(mask, n / 8), rng(qcodes, qcodes ? n / 2 : 0)};
   const Range ins[3] = {rng(x, 2 * n), rng(scales, n / 32), rng(side, side_len)};

@@ -130,35 +130,54 @@ __device__ __forceinline__ uint32_t full_info_select(uint32_t F, uint32_t P, uin
   return F + ((gt & same) >> 3 & ~t & 0x11111111u);
 }
 
-// Decision table of the b-low-bits rule, built on the host for one b: bit
-// (f & 3) * 16 + r of lo (f < 4) or hi (f >= 4) is set when, for z >= 0 in
-// the bracket (f, f + 1) and a rollout residue r, the reconstructed rollout
-// index is at or above f + 1.
-struct LowBitsTable {
-  uint32_t mask;   // 2^b - 1
-  uint64_t lo, hi;
+// The b-low-bits rule for one b.  For z >= 0 in the bracket (f, f + 1) and a
+// rollout residue r, the rollout index is reconstructed as the one with
+// residue r (mod 2^b) nearest to f + 1/2 among -7..7; the upper endpoint is
+// taken when that index is at least f + 1.  With d = (r - f) mod 2^b this is
+// exactly 1 <= d <= 2^(b-1) and d + f <= 7: offsets d above 2^(b-1) fall
+// below the bracket, and an index past 7 does not exist, so the candidate
+// 2^b lower (below the bracket) is the one taken -- or none, for the one
+// residue no index has (8 when b = 4), which then keeps the endpoint nearer
+// zero.  Negative z mirror: residue -r mod 2^b.
+struct LowBitsRule {
+  uint32_t mask;  // 2^b - 1
+  uint32_t half;  // 2^(b-1)
 };
+
+__device__ __forceinline__ bool lowbits_up(uint32_t f, uint32_t sign, uint32_t r, const LowBitsRule& lb) {
+  const uint32_t rp = ((r ^ (0u - sign)) + sign) & lb.mask;  // sign ? -r : r, modulo 2^b
+  const uint32_t d = (rp - f) & lb.mask;
+  return d >= 1u && d <= lb.half && d + f <= 7u;
+}
 
 // Codes of q* for the b-low-bits rule, 8 nibbles at a time: floor codes F,
 // predecessor floor codes P (F == P inside a bracket) and residues R (b low
 // bits of the rollout's signed grid index).  Inside a bracket the magnitude
-// steps up from f to f + 1 exactly when the table bit for (f, r') is set,
-// where r' is the residue mirrored to z >= 0 (-r mod 2^b for negative z).
-__device__ __forceinline__ uint32_t lowbits_select(uint32_t F, uint32_t P, uint32_t R, const LowBitsTable& lb) {
+// steps up from f to f + 1 when lowbits_up holds; computed on 8-bit lanes
+// (4 elements per dword, values at most 15), each comparison the carry into
+// bit 7 of a biased sum.
+__device__ __forceinline__ uint32_t lowbits_select(uint32_t F, uint32_t P, uint32_t R, const LowBitsRule& lb) {
   uint32_t t = F ^ P;
   t |= t >> 2;
   t |= t >> 1;
-  uint32_t Q = F;
+  const uint32_t mb = lb.mask * 0x01010101u;
+  const uint32_t le_half = (0x80u - (lb.half + 1u)) * 0x01010101u;
+  uint32_t up = 0;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const uint32_t n = (F >> (4 * k)) & 15u;
-    const uint32_t sgn = n >> 3, f = n & 7u;
-    const uint32_t r = (R >> (4 * k)) & 15u;
-    const uint32_t rp = ((r ^ (0u - sgn)) + sgn) & lb.mask;  // sgn ? -r : r, modulo 2^b
-    const uint32_t up = (uint32_t)(((f < 4u) ? lb.lo : lb.hi) >> (((f & 3u) << 4) | rp)) & 1u;
-    Q += (up & ~(t >> (4 * k))) << (4 * k);
+  for (int sh = 0; sh < 8; sh += 4) {
+    const uint32_t fb = (F >> sh) & 0x0F0F0F0Fu, rb = (R >> sh) & 0x0F0F0F0Fu;
+    const uint32_t sgn = (fb >> 3) & 0x01010101u;
+    const uint32_t f = fb & 0x07070707u;
+    const uint32_t sm = (sgn << 8) - sgn;                        // 0xFF in negative lanes
+    const uint32_t rneg = 0x10101010u - rb;                      // 16 - r, no borrows (r <= 15)
+    const uint32_t rp = ((rb & ~sm) | (rneg & sm)) & mb;
+    const uint32_t d = ((rp + 0x10101010u) - f) & mb;            // (r' - f) mod 2^b, no borrows
+    uint32_t u = (d + 0x7F7F7F7Fu) & 0x80808080u;               // d >= 1
+    u &= ~(d + le_half) & 0x80808080u;                           // d <= 2^(b-1)
+    u &= ~(d + f + 0x78787878u) & 0x80808080u;                   // d + f <= 7
+    up |= (u >> 7) << sh;
   }
-  return Q;
+  return F + (up & ~t & 0x11111111u);
 }
 
 // Codes of q* for 16 quotients q (even / odd nibble dwords QE, QO) and the
@@ -167,10 +186,10 @@ __device__ __forceinline__ uint32_t lowbits_select(uint32_t F, uint32_t P, uint3
 // (16-bit word, bit j = element j); 2: full information (rollout codes,
 // element order, in roll.x / roll.y).
 // kMode 3: b cached low bits; roll holds the residues as even / odd nibble
-// dwords and lb the decision table.
+// dwords and lb the rule.
 template <int kMode>
 __device__ __forceinline__ uint32_t select_codes(const float (&q)[16], uint32_t cached, uint2 roll, uint32_t& QE,
-                                                 uint32_t& QO, const LowBitsTable& lb = LowBitsTable{}) {
+                                                 uint32_t& QO, const LowBitsRule& lb = LowBitsRule{}) {
   // clip mask: sign bit of 6 - |q| is set exactly when |q| > 6
   uint32_t clip = 0;
 #pragma unroll
@@ -270,10 +289,10 @@ __device__ __forceinline__ uint32_t exact_capture_code(float xv, float s, bool v
 
 // Forward of one element: code of q*, clip-mask bit and y bits.
 // mode 0: RNE; 1: guided by the cached bit cbit; 2: full information with
-// rollout code rc; 3: b cached low bits with residue rc and table lb.
+// rollout code rc; 3: b cached low bits with residue rc and rule lb.
 __device__ __forceinline__ void exact_forward_element(int mode, float xv, float s, bool valid, uint32_t cbit,
                                                       uint32_t rc, uint32_t& code, uint32_t& mk, uint32_t& ybits,
-                                                      const LowBitsTable& lb = LowBitsTable{}) {
+                                                      const LowBitsRule& lb = LowBitsRule{}) {
   uint32_t sign = __float_as_uint(xv) >> 31;
   uint32_t idx = 0;
   mk = 0;
@@ -301,9 +320,7 @@ __device__ __forceinline__ void exact_forward_element(int mode, float xv, float 
       // rc: residue of the rollout's signed index; the table decides the step
       const uint32_t lo = e2m1_floor_index(a);
       const bool exact = (a == e2m1_mag(lo));
-      const uint32_t rp = ((rc ^ (0u - sign)) + sign) & lb.mask;
-      const uint32_t up = (uint32_t)(((lo < 4u) ? lb.lo : lb.hi) >> (((lo & 3u) << 4) | rp)) & 1u;
-      idx = (!exact && up) ? lo + 1 : lo;
+      idx = (!exact && lowbits_up(lo, sign, rc, lb)) ? lo + 1 : lo;
     } else {
       idx = e2m1_rne_index(a);
     }

@@ -133,13 +133,13 @@ __device__ __noinline__ void capture_block_exact(const uint4* __restrict__ x4, u
 // mode: 0 = RNE, 1 = guided by the cached bit (cached = 16-bit word),
 // 2 = full information (rollout codes in roll_lo / roll_hi, element order).
 // mode 3: b cached low bits, residues as even / odd nibble dwords in
-// roll_lo / roll_hi, decision table lb.
+// roll_lo / roll_hi, rule lb.
 __device__ __noinline__ void fakequant_block_exact(int mode, const uint4* __restrict__ x4, uint64_t b,
                                                    uint32_t sbyte, float ts, uint32_t cached,
                                                    uint32_t roll_lo, uint32_t roll_hi,
                                                    uint4* __restrict__ y4, uint16_t* __restrict__ mask,
                                                    uint2* __restrict__ qcodes,
-                                                   LowBitsTable lb = LowBitsTable{}) {
+                                                   LowBitsRule lb = LowBitsRule{}) {
   const float s = e4m3_decode(sbyte) * ts;
   const bool valid = s > 0.f && s <= 3.40282347e38f;
   const uint16_t* x = reinterpret_cast<const uint16_t*>(x4) + 16 * b;
@@ -478,7 +478,7 @@ __device__ __forceinline__ void fakequant_one(const uint4* __restrict__ x, uint6
                                               uint32_t sbyte, uint32_t cached, uint2 roll, float ts,
                                               uint4* __restrict__ y, uint16_t* __restrict__ mask,
                                               uint2* __restrict__ qcodes,
-                                              const LowBitsTable& lb = LowBitsTable{}) {
+                                              const LowBitsRule& lb = LowBitsRule{}) {
   const ScaleEntry e = make_scale_entry(sbyte, ts);
   bool bad = false;  // set by a NaN / infinite quotient, or a scale outside the fast range (dhi NaN)
 
@@ -533,7 +533,7 @@ __global__ __launch_bounds__(kThreads) void lowbits_fakequant_kernel(const uint4
                                                                      const uint8_t* __restrict__ scales,
                                                                      const float* __restrict__ ts_ptr,
                                                                      const uint16_t* __restrict__ planes, Planes pl,
-                                                                     LowBitsTable lb, uint4* __restrict__ y,
+                                                                     LowBitsRule lb, uint4* __restrict__ y,
                                                                      uint16_t* __restrict__ mask,
                                                                      uint2* __restrict__ qcodes) {
   const float ts0 = *ts_ptr;
@@ -681,36 +681,14 @@ hipError_t launch_capture(const uint16_t* x, uint64_t nblocks, const float* ts, 
   return hipGetLastError();
 }
 
-// Decision table of the b-low-bits rule (see LowBitsTable): for z >= 0 in
-// the bracket (f, f + 1) and residue r, the rollout index is taken to be the
-// one with residue r (mod 2^b) nearest to f + 1/2 among -7..7 (the
-// candidates are 2^b apart, so there is no tie); the upper endpoint is
-// chosen when that index is at least f + 1.  A residue no index has (8 for
-// b = 4) leaves the bit clear: the endpoint nearer zero, for either sign.
-static LowBitsTable lowbits_table(uint32_t nbits) {
-  LowBitsTable t{(1u << nbits) - 1u, 0ull, 0ull};
-  const int m = 1 << nbits;
-  for (int f = 0; f <= 6; ++f) {
-    for (int r = 0; r < m; ++r) {
-      int best = 99;
-      for (int c = -7; c <= 7; ++c) {
-        const int res = ((c % m) + m) % m;
-        const int dc = 2 * c - (2 * f + 1), db = 2 * best - (2 * f + 1);
-        if (res == r && (dc < 0 ? -dc : dc) < (db < 0 ? -db : db)) best = c;
-      }
-      if (best != 99 && best >= f + 1) (f < 4 ? t.lo : t.hi) |= 1ull << (((f & 3) << 4) | r);
-    }
-  }
-  return t;
-}
-
 hipError_t launch_lowbits_fakequant(const uint16_t* x, uint64_t nblocks, const uint8_t* scales, const float* ts,
                                     const uint8_t* planes, uint32_t nplanes, uint16_t* y, uint8_t* mask,
                                     uint8_t* qcodes, hipStream_t stream) {
   if (nblocks == 0) return hipSuccess;
   hipLaunchKernelGGL(lowbits_fakequant_kernel, dim3(grid_for(nblocks)), dim3(kThreads), 0, stream,
                      reinterpret_cast<const uint4*>(x), nblocks, scales, ts,
-                     reinterpret_cast<const uint16_t*>(planes), Planes{nplanes, nblocks}, lowbits_table(nplanes),
+                     reinterpret_cast<const uint16_t*>(planes), Planes{nplanes, nblocks},
+                     LowBitsRule{(1u << nplanes) - 1u, 1u << (nplanes - 1)},
                      reinterpret_cast<uint4*>(y), reinterpret_cast<uint16_t*>(mask), reinterpret_cast<uint2*>(qcodes));
   return hipGetLastError();
 }

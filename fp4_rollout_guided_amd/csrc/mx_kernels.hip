@@ -6,10 +6,12 @@
 // NaN), E2M1 elements.  The block scale is 2^(floor(log2(amax)) - 2) clamped
 // to E8M0's range; elements are rounded as on the NVFP4 path.
 //
-// One lane owns one 32-element block: 64 contiguous bytes of bf16 (four
-// 128-bit loads), its scale byte, one 32-bit word of every bit-plane and 16
-// bytes of codes; the block is processed as two 16-element halves with the
-// machinery of fp4_block.h.  Dividing by a power of two is a multiplication
+// A lane owns one 16-element half of a block -- the same 32 contiguous bytes
+// of bf16, 16-bit bit-plane words and 8 bytes of codes as on the NVFP4 path
+// -- and lane pairs share a block's scale: the pair exchanges its halves'
+// maxima with one DPP move.  (A lane per 32-element block was measured ~15%
+// slower: its 64-byte stride doubles the cache lines each load instruction
+// touches.)  Dividing by a power of two is a multiplication
 // by its exact inverse: x * 2^(127 - b) is the correctly rounded x / s, also
 // where it underflows, so there is no division at all.  Blocks holding a NaN
 // or an infinity, or whose quotients overflow, run the exact per-element
@@ -41,20 +43,14 @@ __device__ __forceinline__ uint32_t mx_scale_byte(uint32_t amax_bits) {
   return (e < 2u ? 2u : e) - 2u;
 }
 
-__device__ __forceinline__ void load_mx_block(const uint4* __restrict__ x, uint64_t b, uint32_t (&wa)[8],
-                                              uint32_t (&wb)[8]) {
-  load_block(x, 2 * b, wa);
-  load_block(x, 2 * b + 1, wb);
-}
-
-// Largest magnitude's bf16 bits over 32 elements, NaN excluded (a signed
+// Largest magnitude's bf16 bits over 16 elements, NaN excluded (a signed
 // 16-bit maximum of m + 0x7f puts NaN halves below every other value).
-__device__ __forceinline__ uint32_t mx_amax_bits(const uint32_t (&wa)[8], const uint32_t (&wb)[8]) {
+__device__ __forceinline__ uint32_t half_amax_bits(const uint32_t (&w)[8]) {
   typedef short s16x2_t __attribute__((ext_vector_type(2)));
   s16x2_t best = {0, 0};
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const uint32_t m = ((k < 8 ? wa[k] : wb[k - 8]) & 0x7fff7fffu) + 0x007f007fu;
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t m = (w[k] & 0x7fff7fffu) + 0x007f007fu;
     s16x2_t v;
     __builtin_memcpy(&v, &m, 4);
     best = __builtin_elementwise_max(best, v);
@@ -64,121 +60,115 @@ __device__ __forceinline__ uint32_t mx_amax_bits(const uint32_t (&wa)[8], const 
   return m > 0x7f ? (uint32_t)(m - 0x7f) : 0u;
 }
 
-// ---------------------------------------------------------------------------
-// exact fallbacks (IEEE division, one element at a time)
-// ---------------------------------------------------------------------------
-__device__ __noinline__ void mx_capture_block_exact(const uint4* __restrict__ x4, uint64_t b,
-                                                    uint8_t* __restrict__ scales, uint32_t* __restrict__ bits,
-                                                    uint4* __restrict__ codes) {
-  const uint16_t* x = reinterpret_cast<const uint16_t*>(x4) + 32 * b;
-  uint32_t amax_bits = 0;
-#pragma unroll 1
-  for (int j = 0; j < 32; ++j) {
-    const uint32_t m = x[j] & 0x7fffu;
-    if (m <= 0x7f80u && m > amax_bits) amax_bits = m;  // NaN (m > 0x7f80) ignored
-  }
-  const uint32_t sb = mx_scale_byte(amax_bits);
-  const float s = e8m0_value(sb);
-  uint32_t bitword = 0;
-  uint32_t cw[4] = {0, 0, 0, 0};
-#pragma unroll 1
-  for (int j = 0; j < 32; ++j) {
-    const uint32_t code = exact_capture_code(__uint_as_float((uint32_t)x[j] << 16), s, true);
-    bitword |= (code & 1u) << j;
-    cw[j >> 3] |= code << (4 * (j & 7));
-  }
-  scales[b] = (uint8_t)sb;
-  bits[b] = bitword;
-  if (codes) codes[b] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+// The partner lane's value (lane ^ 1): a DPP quad permutation [1, 0, 3, 2].
+__device__ __forceinline__ uint32_t pair_swap(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
 }
 
-__device__ __noinline__ void mx_fakequant_block_exact(int mode, const uint4* __restrict__ x4, uint64_t b,
-                                                      uint32_t sbyte, uint32_t cached, uint4 roll,
-                                                      uint4* __restrict__ y4, uint32_t* __restrict__ mask,
-                                                      uint4* __restrict__ qcodes) {
+// ---------------------------------------------------------------------------
+// exact fallbacks (IEEE division, one element at a time) for one lane's
+// 16-element half of a block whose scale byte is already known
+// ---------------------------------------------------------------------------
+__device__ __noinline__ void mx_capture_half_exact(const uint4* __restrict__ x4, uint64_t h, uint32_t sb,
+                                                   uint16_t* __restrict__ bits, uint2* __restrict__ codes) {
+  const uint16_t* x = reinterpret_cast<const uint16_t*>(x4) + 16 * h;
+  const float s = e8m0_value(sb);
+  uint32_t bitword = 0;
+  uint64_t cw = 0;
+#pragma unroll 1
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t code = exact_capture_code(__uint_as_float((uint32_t)x[j] << 16), s, true);
+    bitword |= (code & 1u) << j;
+    cw |= (uint64_t)code << (4 * j);
+  }
+  bits[h] = (uint16_t)bitword;
+  if (codes) codes[h] = make_uint2((uint32_t)cw, (uint32_t)(cw >> 32));
+}
+
+__device__ __noinline__ void mx_fakequant_half_exact(int mode, const uint4* __restrict__ x4, uint64_t h,
+                                                     uint32_t sbyte, uint32_t cached, uint2 roll,
+                                                     uint4* __restrict__ y4, uint16_t* __restrict__ mask,
+                                                     uint2* __restrict__ qcodes) {
   const bool valid = sbyte != 0xffu;
   const float s = valid ? e8m0_value(sbyte) : 1.f;
-  const uint16_t* x = reinterpret_cast<const uint16_t*>(x4) + 32 * b;
-  uint16_t* y = reinterpret_cast<uint16_t*>(y4) + 32 * b;
-  const uint32_t rw[4] = {roll.x, roll.y, roll.z, roll.w};
+  const uint16_t* x = reinterpret_cast<const uint16_t*>(x4) + 16 * h;
+  uint16_t* y = reinterpret_cast<uint16_t*>(y4) + 16 * h;
   uint32_t maskword = 0;
-  uint32_t cw[4] = {0, 0, 0, 0};
+  uint64_t cw = 0;
 #pragma unroll 1
-  for (int j = 0; j < 32; ++j) {
-    const uint32_t rc = (rw[j >> 3] >> (4 * (j & 7))) & 15u;
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t rc = ((j < 8 ? roll.x : roll.y) >> (4 * (j & 7))) & 15u;
     uint32_t code, mk, ybits;
     exact_forward_element(mode, __uint_as_float((uint32_t)x[j] << 16), s, valid, (cached >> j) & 1u, rc, code, mk,
                           ybits);
     maskword |= mk << j;
     y[j] = (uint16_t)ybits;
-    cw[j >> 3] |= code << (4 * (j & 7));
+    cw |= (uint64_t)code << (4 * j);
   }
-  mask[b] = maskword;
-  if (qcodes) qcodes[b] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+  mask[h] = (uint16_t)maskword;
+  if (qcodes) qcodes[h] = make_uint2((uint32_t)cw, (uint32_t)(cw >> 32));
 }
 
 // ---------------------------------------------------------------------------
-// capture
+// capture.  Lane pairs (h even, h + 1) hold one 32-element block: each lane
+// loads its 16 elements (32 contiguous bytes), the pair exchanges its
+// halves' maxima, and the even lane writes the scale byte.  The half count
+// n/16 is even, so both lanes of a pair are always active together.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void mx_capture_kernel(const uint4* __restrict__ x, uint64_t nblocks,
+__global__ __launch_bounds__(kThreads) void mx_capture_kernel(const uint4* __restrict__ x, uint64_t nhalves,
                                                               uint8_t* __restrict__ scales,
-                                                              uint32_t* __restrict__ bits,
-                                                              uint4* __restrict__ codes) {
+                                                              uint16_t* __restrict__ bits,
+                                                              uint2* __restrict__ codes) {
   const uint64_t stride = (uint64_t)gridDim.x * kThreads;
-  for (uint64_t b = (uint64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks; b += stride) {
-    uint32_t wa[8], wb[8];
-    load_mx_block(x, b, wa, wb);
-    const uint32_t sb = mx_scale_byte(mx_amax_bits(wa, wb));
+  for (uint64_t h = (uint64_t)blockIdx.x * kThreads + threadIdx.x; h < nhalves; h += stride) {
+    uint32_t w[8];
+    load_block(x, h, w);
+    const uint32_t a = half_amax_bits(w);
+    const uint32_t b = pair_swap(a);
+    const uint32_t sb = mx_scale_byte(a > b ? a : b);
     const float inv = e8m0_inverse(sb);
     bool bad = false;
     float q[16];
-    uint32_t E0 = 0, O0 = 0, E1 = 0, O1 = 0;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      q[j] = block_elem(wa, j) * inv;
+      q[j] = block_elem(w, j) * inv;
       bad |= __builtin_amdgcn_class(q[j], kBadClass);
     }
-    FP4_PACK8(FP4_RNE, E0, q, 0);
-    FP4_PACK8(FP4_RNE, O0, q, 1);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      q[j] = block_elem(wb, j) * inv;
-      bad |= __builtin_amdgcn_class(q[j], kBadClass);
-    }
-    FP4_PACK8(FP4_RNE, E1, q, 0);
-    FP4_PACK8(FP4_RNE, O1, q, 1);
+    uint32_t E = 0, O = 0;
+    FP4_PACK8(FP4_RNE, E, q, 0);
+    FP4_PACK8(FP4_RNE, O, q, 1);
+    if ((h & 1) == 0) scales[h >> 1] = (uint8_t)sb;
     if (bad) {
-      mx_capture_block_exact(x, b, scales, bits, codes);
+      mx_capture_half_exact(x, h, sb, bits, codes);
     } else {
-      scales[b] = (uint8_t)sb;
-      bits[b] = gather_parity(E0, O0) | (gather_parity(E1, O1) << 16);
+      bits[h] = (uint16_t)gather_parity(E, O);
       if (codes) {
-        uint32_t c0, c1, c2, c3;
-        interleave_codes(E0, O0, c0, c1);
-        interleave_codes(E1, O1, c2, c3);
-        codes[b] = make_uint4(c0, c1, c2, c3);
+        uint32_t c0, c1;
+        interleave_codes(E, O, c0, c1);
+        codes[h] = make_uint2(c0, c1);
       }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// fake-quant forward; kMode: 0 = RNE, 1 = guided, 2 = full information
+// fake-quant forward; kMode: 0 = RNE, 1 = guided, 2 = full information.  One
+// lane per 16-element half; both lanes of a block read its scale byte.
 // ---------------------------------------------------------------------------
 template <int kMode>
-__global__ __launch_bounds__(kThreads) void mx_fakequant_kernel(const uint4* __restrict__ x, uint64_t nblocks,
+__global__ __launch_bounds__(kThreads) void mx_fakequant_kernel(const uint4* __restrict__ x, uint64_t nhalves,
                                                                 const uint8_t* __restrict__ scales,
-                                                                const uint32_t* __restrict__ bits,
-                                                                const uint4* __restrict__ rcodes,
-                                                                uint4* __restrict__ y, uint32_t* __restrict__ mask,
-                                                                uint4* __restrict__ qcodes) {
+                                                                const uint16_t* __restrict__ bits,
+                                                                const uint2* __restrict__ rcodes,
+                                                                uint4* __restrict__ y, uint16_t* __restrict__ mask,
+                                                                uint2* __restrict__ qcodes) {
   const uint64_t stride = (uint64_t)gridDim.x * kThreads;
-  for (uint64_t b = (uint64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks; b += stride) {
-    const uint32_t sbyte = scales[b];
-    const uint32_t cached = kMode == 1 ? bits[b] : 0u;
-    const uint4 roll = kMode == 2 ? rcodes[b] : make_uint4(0u, 0u, 0u, 0u);
-    uint32_t wa[8], wb[8];
-    load_mx_block(x, b, wa, wb);
+  for (uint64_t h = (uint64_t)blockIdx.x * kThreads + threadIdx.x; h < nhalves; h += stride) {
+    const uint32_t sbyte = scales[h >> 1];
+    const uint32_t cached = kMode == 1 ? (uint32_t)bits[h] : 0u;
+    const uint2 roll = kMode == 2 ? rcodes[h] : make_uint2(0u, 0u);
+    uint32_t w[8];
+    load_block(x, h, w);
     // a NaN scale byte makes a zero-scale block: multiplying by 0 maps every
     // finite x to a zero of its own sign, decoded with s = 1
     const bool valid = sbyte != 0xffu;
@@ -186,33 +176,24 @@ __global__ __launch_bounds__(kThreads) void mx_fakequant_kernel(const uint4* __r
     const float s = valid ? e8m0_value(sbyte) : 1.f;
     bool bad = false;
     float q[16];
-    uint32_t QE0, QO0, QE1, QO1;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      q[j] = block_elem(wa, j) * inv;
+      q[j] = block_elem(w, j) * inv;
       bad |= __builtin_amdgcn_class(q[j], kBadClass);
     }
-    const uint32_t keep0 = select_codes<kMode>(q, cached & 0xffffu, make_uint2(roll.x, roll.y), QE0, QO0);
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      q[j] = block_elem(wb, j) * inv;
-      bad |= __builtin_amdgcn_class(q[j], kBadClass);
-    }
-    const uint32_t keep1 = select_codes<kMode>(q, cached >> 16, make_uint2(roll.z, roll.w), QE1, QO1);
+    uint32_t QE, QO;
+    const uint32_t keep = select_codes<kMode>(q, cached, roll, QE, QO);
     if (bad) {
-      mx_fakequant_block_exact(kMode, x, b, sbyte, cached, roll, y, mask, qcodes);
+      mx_fakequant_half_exact(kMode, x, h, sbyte, cached, roll, y, mask, qcodes);
     } else {
       uint32_t out[8];
-      decode_block(QE0, QO0, s, out);
-      store_block(y, 2 * b, out);
-      decode_block(QE1, QO1, s, out);
-      store_block(y, 2 * b + 1, out);
-      mask[b] = valid ? (keep0 | (keep1 << 16)) : 0u;
+      decode_block(QE, QO, s, out);
+      store_block(y, h, out);
+      mask[h] = (uint16_t)(valid ? keep : 0u);
       if (qcodes) {
-        uint32_t c0, c1, c2, c3;
-        interleave_codes(QE0, QO0, c0, c1);
-        interleave_codes(QE1, QO1, c2, c3);
-        qcodes[b] = make_uint4(c0, c1, c2, c3);
+        uint32_t c0, c1;
+        interleave_codes(QE, QO, c0, c1);
+        qcodes[h] = make_uint2(c0, c1);
       }
     }
   }
@@ -231,29 +212,31 @@ static unsigned mx_grid(uint64_t nblocks) {
 
 hipError_t launch_mx_capture(const uint16_t* x, uint64_t nblocks, uint8_t* scales, uint8_t* bits, uint8_t* codes,
                              hipStream_t stream) {
-  hipLaunchKernelGGL(mx_capture_kernel, dim3(mx_grid(nblocks)), dim3(kThreads), 0, stream,
-                     reinterpret_cast<const uint4*>(x), nblocks, scales, reinterpret_cast<uint32_t*>(bits),
-                     reinterpret_cast<uint4*>(codes));
+  const uint64_t nhalves = 2 * nblocks;
+  hipLaunchKernelGGL(mx_capture_kernel, dim3(mx_grid(nhalves)), dim3(kThreads), 0, stream,
+                     reinterpret_cast<const uint4*>(x), nhalves, scales, reinterpret_cast<uint16_t*>(bits),
+                     reinterpret_cast<uint2*>(codes));
   return hipGetLastError();
 }
 
 hipError_t launch_mx_fakequant(int mode, const uint16_t* x, uint64_t nblocks, const uint8_t* scales,
                                const uint8_t* side, uint16_t* y, uint8_t* mask, uint8_t* qcodes,
                                hipStream_t stream) {
+  const uint64_t nhalves = 2 * nblocks;
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   uint4* yv = reinterpret_cast<uint4*>(y);
-  uint32_t* mv = reinterpret_cast<uint32_t*>(mask);
-  uint4* qv = reinterpret_cast<uint4*>(qcodes);
-  const dim3 grid(mx_grid(nblocks)), block(kThreads);
+  uint16_t* mv = reinterpret_cast<uint16_t*>(mask);
+  uint2* qv = reinterpret_cast<uint2*>(qcodes);
+  const dim3 grid(mx_grid(nhalves)), block(kThreads);
   if (mode == 1)
-    hipLaunchKernelGGL(mx_fakequant_kernel<1>, grid, block, 0, stream, xv, nblocks, scales,
-                       reinterpret_cast<const uint32_t*>(side), static_cast<const uint4*>(nullptr), yv, mv, qv);
+    hipLaunchKernelGGL(mx_fakequant_kernel<1>, grid, block, 0, stream, xv, nhalves, scales,
+                       reinterpret_cast<const uint16_t*>(side), static_cast<const uint2*>(nullptr), yv, mv, qv);
   else if (mode == 2)
-    hipLaunchKernelGGL(mx_fakequant_kernel<2>, grid, block, 0, stream, xv, nblocks, scales,
-                       static_cast<const uint32_t*>(nullptr), reinterpret_cast<const uint4*>(side), yv, mv, qv);
+    hipLaunchKernelGGL(mx_fakequant_kernel<2>, grid, block, 0, stream, xv, nhalves, scales,
+                       static_cast<const uint16_t*>(nullptr), reinterpret_cast<const uint2*>(side), yv, mv, qv);
   else
-    hipLaunchKernelGGL(mx_fakequant_kernel<0>, grid, block, 0, stream, xv, nblocks, scales,
-                       static_cast<const uint32_t*>(nullptr), static_cast<const uint4*>(nullptr), yv, mv, qv);
+    hipLaunchKernelGGL(mx_fakequant_kernel<0>, grid, block, 0, stream, xv, nhalves, scales,
+                       static_cast<const uint16_t*>(nullptr), static_cast<const uint2*>(nullptr), yv, mv, qv);
   return hipGetLastError();
 }
 

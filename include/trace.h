@@ -313,9 +313,9 @@ TRACE_API trace_status trace_lowbits_fakequant_fwd(const uint16_t* x_train, int6
  *   - elements, parity bits, codes, the three forwards, the clip mask, zero
  *     scales and NaN handling: exactly as on the NVFP4 path above, with this
  *     s in place of fl32(E4M3FN(byte) * ts).  There is no tensor scale.
- * Layouts: scales uint8[n/32]; bits and mask uint8[n/8] as above but 4-byte
- * aligned; codes and qcodes uint8[n/2], 16-byte aligned.  The STE backward
- * (trace_ste_bwd) takes the mask unchanged.
+ * Layouts: scales uint8[n/32]; bits, mask, codes and qcodes as above (same
+ * layouts and alignments).  The STE backward (trace_ste_bwd) takes the mask
+ * unchanged.
  */
 TRACE_API trace_status trace_mx_capture(const uint16_t* x_roll, int64_t rows, int64_t cols,
                                         uint8_t* scales, uint8_t* bits, uint8_t* codes,

@@ -228,16 +228,16 @@ def test_mx_validation():
     cap = L.trace_mx_capture
     assert cap(P(x), 4, 48, P(sc), P(bi), None, None) == E_SHAPE      # cols % 32
     assert cap(P(x), 4, 64, None, P(bi), None, None) == E_NULL
-    assert cap(P(x), 4, 64, P(sc), P(bi + 2), None, None) == E_ALIGN   # bits need 4 bytes
-    assert cap(P(x), 4, 64, P(sc), P(bi), P(cd + 8), None) == E_ALIGN  # codes need 16 bytes
+    assert cap(P(x), 4, 64, P(sc), P(bi + 1), None, None) == E_ALIGN   # bits need 2 bytes
+    assert cap(P(x), 4, 64, P(sc), P(bi), P(cd + 4), None) == E_ALIGN  # codes need 8 bytes
     assert cap(P(x), 4, 64, P(sc), P(x + 64), None, None) == E_ALIAS
     assert cap(P(x), 0, 64, None, None, None, None) == OK
     g = L.trace_mx_guided_fakequant_fwd
     assert g(P(x), 4, 64, P(sc), None, P(y), P(mk), None, None) == E_NULL
-    assert g(P(x), 4, 64, P(sc), P(bi), P(y), P(mk + 2), None, None) == E_ALIGN
+    assert g(P(x), 4, 64, P(sc), P(bi), P(y), P(mk + 1), None, None) == E_ALIGN
     assert g(P(x), 4, 64, P(sc), P(bi), P(sc), P(mk), None, None) == E_ALIAS
     f = L.trace_mx_full_info_fakequant_fwd
-    assert f(P(x), 4, 64, P(sc), P(cd + 8), P(y), P(mk), None, None) == E_ALIGN
+    assert f(P(x), 4, 64, P(sc), P(cd + 4), P(y), P(mk), None, None) == E_ALIGN
     r = L.trace_mx_rne_fakequant_fwd
     assert r(P(x), 4, 80, P(sc), P(y), P(mk), None, None) == E_SHAPE
 
