@@ -33,7 +33,7 @@ import os
 import torch
 
 __all__ = [
-    "TraceError", "LIB_PATH", "lib", "abi_version", "tensor_scale", "capture",
+    "TraceError", "LIB_PATH", "SMALLGRID_LIB_PATH", "lib", "load_library", "abi_version", "tensor_scale", "capture",
     "guided_fakequant_fwd", "rne_fakequant_fwd", "full_info_fakequant_fwd", "ste_bwd", "gather_records",
     "grouped_tensor_scale", "grouped_capture", "grouped_guided_fakequant_fwd", "grouped_rne_fakequant_fwd",
     "grouped_full_info_fakequant_fwd", "mx_capture", "mx_guided_fakequant_fwd", "mx_rne_fakequant_fwd",
@@ -43,6 +43,8 @@ __all__ = [
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtrace.so")
+# the same sources with tiny grid caps, for the tests of the grid-stride paths
+SMALLGRID_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtrace_smallgrid.so")
 
 STATUS = {0: "TRACE_OK", 1: "TRACE_E_NULL", 2: "TRACE_E_SHAPE", 3: "TRACE_E_ALIGN",
           4: "TRACE_E_ALIAS", 5: "TRACE_E_HIP"}
@@ -57,12 +59,13 @@ class TraceError(RuntimeError):
         super().__init__(f"{what}: {msg}")
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
+def load_library(path):
+    """Load a libtrace build and declare its entry points' signatures."""
+    if not os.path.exists(path):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python fp4_rollout_guided_amd/build.py` "
+            f"{path} is missing: build it with `python fp4_rollout_guided_amd/build.py` "
             "(libtrace has no CPU fallback)")
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     p, i64, st, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     sig = {
         "trace_abi_version": ([], ctypes.c_int),
@@ -96,7 +99,7 @@ def _load():
     return L
 
 
-lib = _load()
+lib = load_library(LIB_PATH)
 
 
 def abi_version() -> int:

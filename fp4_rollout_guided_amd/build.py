@@ -47,24 +47,40 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: libtrace needs ROCm's hipcc to build")
 
 
+# The same sources with grids capped at 3 workgroups, so that every kernel's
+# grid-stride loop runs several iterations on test-sized tensors (the
+# production caps are reached only beyond 2^34 elements).  Loaded by the GPU
+# tests only.
+SMALLGRID_LIB = os.path.join(PKG, "libtrace_smallgrid.so")
+SMALLGRID_DEFINES = ["-DTRACE_MAX_GROUPS=3u", "-DTRACE_AMAX_MAX_GROUPS=3u"]
+
+
+def _command(out, defines=()):
+    return [hipcc(), *FLAGS, *defines, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+            *[os.path.join(CSRC, s) for s in SOURCES], "-o", out]
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source into fp4_rollout_guided_amd/libtrace.so (always
-    rebuilds) and return its path."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
-    if verbose and res.stderr.strip():
-        # the host pass does not know the packed-fp32 feature flag; that warning is expected
-        lines = [l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l and l.strip()]
-        if lines:
-            print("\n".join(lines))
-    os.replace(tmp, LIB)
+    """Compile every source into fp4_rollout_guided_amd/libtrace.so (and the
+    small-grid test build beside it), always rebuilding, and return the
+    library's path."""
+    jobs = [(LIB, _command(LIB + ".tmp")), (SMALLGRID_LIB, _command(SMALLGRID_LIB + ".tmp", SMALLGRID_DEFINES))]
+    procs = []
+    for out, cmd in jobs:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((out, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+    for out, p in procs:
+        stdout, stderr = p.communicate()
+        if p.returncode != 0:
+            sys.stderr.write(stdout + stderr)
+            raise RuntimeError(f"hipcc failed with exit code {p.returncode} building {os.path.basename(out)}")
+        if verbose and stderr.strip():
+            # the host pass does not know the packed-fp32 feature flag; that warning is expected
+            lines = [l for l in stderr.splitlines() if "packed-fp32-ops" not in l and l.strip()]
+            if lines:
+                print("\n".join(lines))
+        os.replace(out + ".tmp", out)
     return LIB
 
 

@@ -8,7 +8,10 @@
 namespace trace_host {
 
 // Upper bound on amax partial workgroups (and on workspace words).
-constexpr uint32_t kAmaxMaxGroups = 2048;
+#ifndef TRACE_AMAX_MAX_GROUPS
+#define TRACE_AMAX_MAX_GROUPS 2048u
+#endif
+constexpr uint32_t kAmaxMaxGroups = TRACE_AMAX_MAX_GROUPS;
 // Upper bound on the grid of the streaming kernels (one 4096-element tile per
 // workgroup below it; workgroups loop over the tensor beyond it).  A grid
 // that covers the tensor once streams faster than a persistent grid, whose
