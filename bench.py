@@ -24,7 +24,9 @@ the record gather on the packed routed-expert site of the MoE layer workload
 Prints one JSON line (last line of stdout).  ``value`` is the algorithmic
 bytes of the whole step divided by its wall time, in GB/s; per-kernel GB/s,
 Gelem/s and the fraction of the 8 TB/s HBM peak are reported beside it, with
-the CPU oracle timed on a bounded sample of the same workload.
+the CPU oracle timed on a bounded sample of the same workload and, under
+``practical_ceiling``, the GB/s of a plain copy, a read-only and a
+write-only stream on the same GPU (``bench_ceiling.hip``).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -296,6 +298,8 @@ def main():
         "cpu_baseline": None,
     }
 
+    result["practical_ceiling"] = practical_ceiling()
+
     if pool is not None:
         result["cpu_baseline"] = cpu_leg(pool, cores, layers[0], n, y_g, mask_g, y_r, mask_r, gin, np, torch, tr)
         pool.close()
@@ -350,6 +354,27 @@ def moe_rows(tr, workloads, torch, dev, stream, layers, reps):
                              "bytes_per_launch": int(bpe * n)}
     del d, x_roll, x_train, y
     return out
+
+
+def practical_ceiling():
+    """Plain copy / read / fill streams over 1 GiB (``bench_ceiling.hip``,
+    built into _build/), back to back, after a read-only pass and after a
+    1 GiB write: the practical ceilings for the kernels' access mixes.  Run
+    as a child process after the timed work; None if it is not built."""
+    import subprocess
+    exe = os.path.join(ROOT, "_build", "bench_ceiling")
+    if not os.path.exists(exe):
+        log("practical ceiling: _build/bench_ceiling is not built (python fp4_rollout_guided_amd/build.py)")
+        return None
+    try:
+        res = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    except subprocess.TimeoutExpired:
+        log("practical ceiling: probe timed out")
+        return None
+    if res.returncode != 0:
+        log(f"practical ceiling: probe failed ({res.returncode}): {res.stderr.strip()[-300:]}")
+        return None
+    return json.loads(res.stdout.strip().splitlines()[-1])
 
 
 def calibrate_copy():

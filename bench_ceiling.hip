@@ -1,0 +1,142 @@
+// Practical HBM ceilings of this GPU for the access mixes of the libtrace
+// kernels: a plain 128-bit copy (read + write, the layout of the STE
+// backward), a read-only stream and a write-only fill, each over 1 GiB
+// buffers with one-shot grids, plus the runtime's device-to-device copy.
+// Each is timed (median of 15 HIP-event-timed launches) in three settings:
+// back to back, after a read-only pass over another 1 GiB buffer, and after
+// a 1 GiB write to another buffer (whose dirty lines are then written back
+// while the measured kernel streams).  Prints one JSON object.
+//
+// Built by fp4_rollout_guided_amd/build.py into _build/bench_ceiling; run by
+// `python bench.py` (the "practical_ceiling" field) or on its own.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <algorithm>
+#include <vector>
+
+#define CHECK(call)                                                                  \
+  do {                                                                               \
+    hipError_t e_ = (call);                                                          \
+    if (e_ != hipSuccess) {                                                          \
+      fprintf(stderr, "%s failed: %s\n", #call, hipGetErrorString(e_));              \
+      exit(1);                                                                       \
+    }                                                                                \
+  } while (0)
+
+__global__ __launch_bounds__(256) void copy_kernel(const uint4* __restrict__ s, uint4* __restrict__ d, uint64_t n) {
+  const uint64_t base = (uint64_t)blockIdx.x * 512 + threadIdx.x;
+  uint4 v[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const uint64_t i = base + 256 * u;
+    if (i < n) v[u] = s[i];
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const uint64_t i = base + 256 * u;
+    if (i < n) d[i] = v[u];
+  }
+}
+
+__global__ __launch_bounds__(256) void read_kernel(const uint4* __restrict__ s, uint32_t* __restrict__ out,
+                                                   uint64_t n) {
+  const uint64_t base = (uint64_t)blockIdx.x * 512 + threadIdx.x;
+  uint32_t acc = 0;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const uint64_t i = base + 256 * u;
+    if (i < n) {
+      const uint4 v = s[i];
+      acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+  }
+  if (acc == 0x9e3779b9u) out[blockIdx.x] = acc;  // data-dependent store keeps the loads
+}
+
+__global__ __launch_bounds__(256) void fill_kernel(uint4* __restrict__ d, uint64_t n) {
+  const uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) d[i] = make_uint4(1u, 2u, 3u, 4u);
+}
+
+struct Buffers {
+  uint4 *src, *dst, *other;
+  uint32_t* sink;
+  uint64_t n;  // uint4 per buffer
+};
+
+enum Kind { kCopy, kRead, kFill, kMemcpy };
+
+static void launch(Kind k, const Buffers& b) {
+  const dim3 blk(256);
+  switch (k) {
+    case kCopy: hipLaunchKernelGGL(copy_kernel, dim3((unsigned)((b.n + 511) / 512)), blk, 0, 0, b.src, b.dst, b.n); break;
+    case kRead: hipLaunchKernelGGL(read_kernel, dim3((unsigned)((b.n + 511) / 512)), blk, 0, 0, b.src, b.sink, b.n); break;
+    case kFill: hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((b.n + 255) / 256)), blk, 0, 0, b.dst, b.n); break;
+    case kMemcpy: CHECK(hipMemcpyAsync(b.dst, b.src, b.n * 16, hipMemcpyDeviceToDevice, 0)); break;
+  }
+}
+
+static void prepass(int mode, const Buffers& b) {
+  if (mode == 1)
+    hipLaunchKernelGGL(read_kernel, dim3((unsigned)((b.n + 511) / 512)), dim3(256), 0, 0, b.other, b.sink, b.n);
+  if (mode == 2) hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((b.n + 255) / 256)), dim3(256), 0, 0, b.other, b.n);
+}
+
+static double median_us(Kind k, int mode, const Buffers& b) {
+  hipEvent_t e0, e1;
+  CHECK(hipEventCreate(&e0));
+  CHECK(hipEventCreate(&e1));
+  std::vector<float> t;
+  for (int r = 0; r < 16; ++r) {
+    prepass(mode, b);
+    CHECK(hipEventRecord(e0, 0));
+    launch(k, b);
+    CHECK(hipEventRecord(e1, 0));
+    CHECK(hipEventSynchronize(e1));
+    float ms = 0.f;
+    CHECK(hipEventElapsedTime(&ms, e0, e1));
+    if (r > 0) t.push_back(ms);  // the first launch warms up
+  }
+  CHECK(hipEventDestroy(e0));
+  CHECK(hipEventDestroy(e1));
+  std::sort(t.begin(), t.end());
+  return 1e3 * t[t.size() / 2];
+}
+
+int main() {
+  const uint64_t bytes = 1ull << 30;
+  Buffers b;
+  b.n = bytes / 16;
+  CHECK(hipMalloc(&b.src, bytes));
+  CHECK(hipMalloc(&b.dst, bytes));
+  CHECK(hipMalloc(&b.other, bytes));
+  CHECK(hipMalloc(&b.sink, (b.n / 512 + 1) * sizeof(uint32_t)));
+  CHECK(hipMemset(b.src, 1, bytes));
+  CHECK(hipMemset(b.dst, 2, bytes));
+  CHECK(hipMemset(b.other, 3, bytes));
+  CHECK(hipDeviceSynchronize());
+  const struct { const char* name; Kind k; double traffic; } tests[] = {
+      {"copy", kCopy, 2.0 * bytes}, {"read", kRead, 1.0 * bytes}, {"fill", kFill, 1.0 * bytes},
+      {"runtime_d2d_copy", kMemcpy, 2.0 * bytes}};
+  const char* modes[] = {"back_to_back", "after_read_pass", "after_write_pass"};
+  printf("{\"buffer_bytes\": %llu, \"peak_GB_s\": 8000", (unsigned long long)bytes);
+  for (const auto& t : tests) {
+    printf(", \"%s\": {", t.name);
+    for (int m = 0; m < 3; ++m) {
+      const double us = median_us(t.k, m, b);
+      const double gbs = t.traffic / (us * 1e-6) / 1e9;
+      printf("%s\"%s\": {\"us\": %.1f, \"GB_s\": %.1f, \"frac\": %.4f}", m ? ", " : "", modes[m], us, gbs,
+             gbs / 8000.0);
+    }
+    printf("}");
+  }
+  printf("}\n");
+  CHECK(hipFree(b.src));
+  CHECK(hipFree(b.dst));
+  CHECK(hipFree(b.other));
+  CHECK(hipFree(b.sink));
+  return 0;
+}

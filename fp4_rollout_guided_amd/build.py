@@ -60,11 +60,21 @@ def _command(out, defines=()):
             *[os.path.join(CSRC, s) for s in SOURCES], "-o", out]
 
 
+# The bench's practical-ceiling probe (plain copy / read / fill streams).
+CEILING_SRC = os.path.join(ROOT, "bench_ceiling.hip")
+CEILING_BIN = os.path.join(ROOT, "_build", "bench_ceiling")
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source into fp4_rollout_guided_amd/libtrace.so (and the
     small-grid test build beside it), always rebuilding, and return the
     library's path."""
     jobs = [(LIB, _command(LIB + ".tmp")), (SMALLGRID_LIB, _command(SMALLGRID_LIB + ".tmp", SMALLGRID_DEFINES))]
+    if os.path.exists(CEILING_SRC):
+        os.makedirs(os.path.dirname(CEILING_BIN), exist_ok=True)
+        jobs.append((CEILING_BIN, [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17",
+                                   "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                                   CEILING_SRC, "-o", CEILING_BIN + ".tmp"]))
     procs = []
     for out, cmd in jobs:
         if verbose:
