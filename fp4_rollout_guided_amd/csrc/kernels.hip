@@ -1,6 +1,8 @@
-// libtrace kernels for gfx950: tensor amax, capture, guided / RNE /
+// libtrace NVFP4 kernels for gfx950: tensor amax, capture, guided / RNE /
 // full-information fake-quant forward, STE backward, per-expert (row-group)
-// variants of the tensor scale, capture and forwards, and the record gather.
+// variants of the tensor scale, capture and forwards, capture to and forward
+// from b cached low bits, and the record gather.  The MXFP4 kernels are in
+// mx_kernels.hip; the block machinery both share is in fp4_block.h.
 //
 // Work decomposition: one lane owns one 16-element NVFP4 block, i.e. 32
 // contiguous bytes of bf16 (two 128-bit loads), its scale byte, and 16 bits of
@@ -664,6 +666,7 @@ hipError_t launch_grouped_tensor_scale(const uint16_t* x, const GroupSpec& g, ui
 
 hipError_t launch_capture(const uint16_t* x, uint64_t nblocks, const float* ts, const GroupSpec* g,
                           uint8_t* scales, uint8_t* bits, uint8_t* codes, hipStream_t stream, uint32_t nplanes) {
+  if (nblocks == 0) return hipSuccess;  // an empty grid is not a valid launch
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   uint16_t* bv = reinterpret_cast<uint16_t*>(bits);
   uint2* cv = reinterpret_cast<uint2*>(codes);
@@ -684,7 +687,7 @@ hipError_t launch_capture(const uint16_t* x, uint64_t nblocks, const float* ts, 
 hipError_t launch_lowbits_fakequant(const uint16_t* x, uint64_t nblocks, const uint8_t* scales, const float* ts,
                                     const uint8_t* planes, uint32_t nplanes, uint16_t* y, uint8_t* mask,
                                     uint8_t* qcodes, hipStream_t stream) {
-  if (nblocks == 0) return hipSuccess;
+  if (nblocks == 0) return hipSuccess;  // an empty grid is not a valid launch
   hipLaunchKernelGGL(lowbits_fakequant_kernel, dim3(grid_for(nblocks)), dim3(kThreads), 0, stream,
                      reinterpret_cast<const uint4*>(x), nblocks, scales, ts,
                      reinterpret_cast<const uint16_t*>(planes), Planes{nplanes, nblocks},
@@ -712,7 +715,7 @@ static void launch_fakequant_t(int mode, const uint4* xv, uint64_t nblocks, cons
 hipError_t launch_fakequant(int mode, const uint16_t* x, uint64_t nblocks, const uint8_t* scales,
                             const float* ts, const GroupSpec* g, const uint8_t* side, uint16_t* y, uint8_t* mask,
                             uint8_t* qcodes, hipStream_t stream) {
-  if (nblocks == 0) return hipSuccess;  // the kernels load block min(b, nblocks - 1) up front
+  if (nblocks == 0) return hipSuccess;  // an empty grid is not a valid launch
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   uint4* yv = reinterpret_cast<uint4*>(y);
   uint16_t* mv = reinterpret_cast<uint16_t*>(mask);
@@ -726,6 +729,7 @@ hipError_t launch_fakequant(int mode, const uint16_t* x, uint64_t nblocks, const
 
 hipError_t launch_ste_bwd(const uint16_t* g, const uint8_t* mask, uint64_t nblocks, uint16_t* gin,
                           hipStream_t stream) {
+  if (nblocks == 0) return hipSuccess;  // an empty grid is not a valid launch
   hipLaunchKernelGGL(ste_bwd_kernel, dim3(grid_for(nblocks)), dim3(kThreads), 0, stream,
                      reinterpret_cast<const uint4*>(g), nblocks,
                      reinterpret_cast<const uint16_t*>(mask), reinterpret_cast<uint4*>(gin));

@@ -212,6 +212,7 @@ static unsigned mx_grid(uint64_t nblocks) {
 
 hipError_t launch_mx_capture(const uint16_t* x, uint64_t nblocks, uint8_t* scales, uint8_t* bits, uint8_t* codes,
                              hipStream_t stream) {
+  if (nblocks == 0) return hipSuccess;  // an empty grid is not a valid launch
   const uint64_t nhalves = 2 * nblocks;
   hipLaunchKernelGGL(mx_capture_kernel, dim3(mx_grid(nhalves)), dim3(kThreads), 0, stream,
                      reinterpret_cast<const uint4*>(x), nhalves, scales, reinterpret_cast<uint16_t*>(bits),
@@ -222,6 +223,7 @@ hipError_t launch_mx_capture(const uint16_t* x, uint64_t nblocks, uint8_t* scale
 hipError_t launch_mx_fakequant(int mode, const uint16_t* x, uint64_t nblocks, const uint8_t* scales,
                                const uint8_t* side, uint16_t* y, uint8_t* mask, uint8_t* qcodes,
                                hipStream_t stream) {
+  if (nblocks == 0) return hipSuccess;  // an empty grid is not a valid launch
   const uint64_t nhalves = 2 * nblocks;
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   uint4* yv = reinterpret_cast<uint4*>(y);
