@@ -66,7 +66,9 @@ const char* trace_status_string(trace_status s) {
   switch (s) {
     case TRACE_OK: return "TRACE_OK";
     case TRACE_E_NULL: return "TRACE_E_NULL: a required pointer is NULL";
-    case TRACE_E_SHAPE: return "TRACE_E_SHAPE: bad size (negative, cols % 16 != 0, overflow, or workspace too small)";
+    case TRACE_E_SHAPE:
+      return "TRACE_E_SHAPE: bad size or count (negative, cols not a multiple of the block length, overflow, "
+             "group or bit count out of range, or workspace too small)";
     case TRACE_E_ALIGN: return "TRACE_E_ALIGN: misaligned pointer";
     case TRACE_E_ALIAS: return "TRACE_E_ALIAS: an output overlaps an input or another output";
     case TRACE_E_HIP: return "TRACE_E_HIP: HIP runtime or launch failure";
@@ -97,8 +99,8 @@ trace_status trace_tensor_scale(const uint16_t* x, int64_t n, void* workspace, s
 
 // Row groups of a grouped call: 1 <= groups <= kMaxRowGroups and an
 // 8-byte-aligned offsets array of groups + 1 entries.  Fills *spec.
-trace_status group_spec(const int64_t* offsets, int64_t groups, int64_t rows, int64_t cols,
-                        trace_host::GroupSpec* spec) {
+static trace_status group_spec(const int64_t* offsets, int64_t groups, int64_t rows, int64_t cols,
+                               trace_host::GroupSpec* spec) {
   if (!offsets) return TRACE_E_NULL;
   if (groups < 1 || groups > (int64_t)trace_host::kMaxRowGroups) return TRACE_E_SHAPE;
   if (!aligned(offsets, 8)) return TRACE_E_ALIGN;

@@ -76,8 +76,10 @@ typedef int trace_status;
 enum {
   TRACE_OK = 0,
   TRACE_E_NULL = 1,  /* a required pointer is NULL                          */
-  TRACE_E_SHAPE = 2, /* negative size, cols % 16 != 0, size overflow,
-                        or a workspace that is too small                    */
+  TRACE_E_SHAPE = 2, /* negative size, cols not a multiple of the block
+                        length (16; 32 for MXFP4), size overflow, a group or
+                        bit count out of range, or a workspace that is too
+                        small                                               */
   TRACE_E_ALIGN = 3, /* a pointer is not aligned as stated above            */
   TRACE_E_ALIAS = 4, /* an output overlaps an input or another output       */
   TRACE_E_HIP = 5    /* a HIP runtime call or kernel launch failed;
