@@ -411,12 +411,25 @@ def read_traffic(kernel):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    src = os.path.join(ROOT, "fp4_rollout_guided_amd", "csrc", "kernels.hip")
-    with open(src, "rb") as fh:
-        digest = hashlib.sha256(fh.read()).hexdigest()
-    if kv.get("kernels_hip_sha256") != digest or "traffic_bytes_per_launch" not in kv:
+    recorded = (kv.get("kernel_sources_sha256") or "-").split()[0]   # the digest, then the file list
+    if recorded != kernel_sources_digest() or "traffic_bytes_per_launch" not in kv:
         return None
     return float(kv["traffic_bytes_per_launch"])
+
+
+KERNEL_SOURCES = ("kernels.hip", "fp4_block.h", "device_math.h", "launch.h")
+
+
+def kernel_sources_digest():
+    """SHA-256 over the sources that make up the NVFP4 kernels' code; the
+    committed counter summaries record it, so they are ignored once any of
+    these files changes."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "fp4_rollout_guided_amd", "csrc", name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def cpu_leg(pool, cores, d0, n, y_g, mask_g, y_r, mask_r, gin, np, torch, tr):
