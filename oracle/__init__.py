@@ -15,7 +15,8 @@ Quantization-Aware Training for FP4" (2026-10-06):
   cached rollout scale, brackets z between two adjacent FP4 codewords and
   keeps the one the cached bit points at, with a straight-through estimator
   around ``s * q*`` (the rollout-guided rounding paragraph and the listing);
-* the same path on MXFP4 scales (``oracle.mx``; the Ablations bullet).
+* the same path on MXFP4 scales (``oracle.mx``) and on the FP8 activation
+  grid of the W4A8 setting (``oracle.mx8``), both from the Ablations bullet.
 
 The pages name NVFP4 and the E2M1 grid but not the format's parameters; the
 oracle uses the NVFP4 definition: 16-element blocks along the last dimension,
@@ -51,6 +52,18 @@ from .mx import (
     mx_full_info_fwd,
     mx_guided_fwd,
     mx_rne_fwd,
+)
+from .mx8 import (
+    E4M3_MAGNITUDES,
+    e4m3_bracket,
+    e4m3_rne_code,
+    e4m3_signed_values,
+    mx8_block_scales,
+    mx8_capture,
+    mx8_full_info_fwd,
+    mx8_guided_fwd,
+    mx8_mismatch_counts,
+    mx8_rne_fwd,
 )
 from .trace import (
     BLOCK,
@@ -89,7 +102,9 @@ __all__ = [
     "grouped_capture", "grouped_full_info_fwd", "grouped_guided_fwd", "grouped_rne_fwd",
     "grouped_tensor_scale", "MX_BLOCK", "e8m0_decode", "floor_log2", "mx_block_scales", "mx_capture",
     "mx_full_info_fwd", "mx_guided_fwd", "mx_rne_fwd", "capture_lowbits", "lowbits_fwd", "lowbits_reconstruct",
-    "signed_index",
+    "signed_index", "E4M3_MAGNITUDES", "e4m3_bracket", "e4m3_rne_code", "e4m3_signed_values",
+    "mx8_block_scales", "mx8_capture", "mx8_full_info_fwd", "mx8_guided_fwd", "mx8_mismatch_counts",
+    "mx8_rne_fwd",
     "guided_fwd", "mismatch_stats", "pack_bits", "pack_nibbles", "rne_fwd",
     "ste_bwd", "tensor_scale", "unpack_bits", "unpack_nibbles",
 ]

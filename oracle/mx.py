@@ -62,10 +62,12 @@ def _block_view(x_bits) -> np.ndarray:
     return x.reshape(-1, MX_BLOCK)
 
 
-def mx_block_scales(x_bits) -> np.ndarray:
-    """One E8M0 byte per 32-element block: 127 + clamp(floor(log2(amax)) - 2,
-    -127, 127); amax ignores NaN; amax = 0 gives byte 0; an infinite amax
-    counts as exponent 128."""
+def mx_block_scales(x_bits, elem_emax: int = E2M1_EMAX) -> np.ndarray:
+    """One E8M0 byte per 32-element block: 127 + clamp(floor(log2(amax)) -
+    elem_emax, -127, 127), elem_emax being the exponent of the element
+    format's largest normal (2 for E2M1; ``oracle.mx8`` passes 8 for E4M3);
+    amax ignores NaN; amax = 0 gives byte 0; an infinite amax counts as
+    exponent 128."""
     f = bf16_to_f32(_block_view(x_bits))
     a = np.abs(f)
     a = np.where(np.isnan(a), np.float32(0), a)
@@ -73,12 +75,14 @@ def mx_block_scales(x_bits) -> np.ndarray:
     pos = (amax > 0) & np.isfinite(amax)
     e = np.where(np.isinf(amax), INF_EXPONENT, 0)
     e = np.where(pos, floor_log2(np.where(pos, amax, 1)), e)
-    shared = np.clip(e - E2M1_EMAX, -E8M0_BIAS, E8M0_BIAS)
+    shared = np.clip(e - elem_emax, -E8M0_BIAS, E8M0_BIAS)
     shared = np.where(amax == 0, -E8M0_BIAS, shared)
     return (shared + E8M0_BIAS).astype(np.uint8)
 
 
-def _mx_quotients(x_bits, scale_bytes):
+def mx_quotients(x_bits, scale_bytes):
+    """Per element: x (float32), zr = fl32(x / s), s and the valid-scale
+    flag, for 32-element blocks with E8M0 scale bytes."""
     xb = _block_view(x_bits)
     x = bf16_to_f32(xb)
     s = e8m0_decode(np.asarray(scale_bytes, dtype=np.uint8))
@@ -95,23 +99,23 @@ def mx_capture(x_bits, with_codes: bool = False) -> dict:
     """MXFP4 capture: ``scales`` (E8M0, u8[n/32]), ``bits`` (u8[n/8]) and
     optional ``codes`` (u8[n/2]), element rounding as in ``trace.capture``."""
     scales = mx_block_scales(x_bits)
-    x, zr, _, valid = _mx_quotients(x_bits, scales)
+    x, zr, _, valid = mx_quotients(x_bits, scales)
     return {"scales": scales, **capture_record(x, zr, valid, with_codes)}
 
 
 def mx_guided_fwd(x_bits, scale_bytes, bits) -> dict:
     """Rollout-guided fake-quant forward on MXFP4 scales."""
-    x, zr, s, valid = _mx_quotients(x_bits, scale_bytes)
+    x, zr, s, valid = mx_quotients(x_bits, scale_bytes)
     return guided_rule(x, zr, s, valid, unpack_bits(bits, x.size))
 
 
 def mx_rne_fwd(x_bits, scale_bytes) -> dict:
     """Round-to-nearest-even fake-quant forward on MXFP4 scales."""
-    x, zr, s, valid = _mx_quotients(x_bits, scale_bytes)
+    x, zr, s, valid = mx_quotients(x_bits, scale_bytes)
     return rne_rule(x, zr, s, valid)
 
 
 def mx_full_info_fwd(x_bits, scale_bytes, roll_codes) -> dict:
     """Full-information guided forward on MXFP4 scales."""
-    x, zr, s, valid = _mx_quotients(x_bits, scale_bytes)
+    x, zr, s, valid = mx_quotients(x_bits, scale_bytes)
     return full_info_rule(x, zr, s, valid, unpack_nibbles(roll_codes, x.size))
