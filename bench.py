@@ -58,6 +58,8 @@ NEXT_BYTES_PER_ELEM = {
     "full_info_fwd": 2.0 + 1 / 16 + 1 / 2 + 2.0 + 1 / 8,  # read x, scales, codes; write y, mask
     "mx_capture": 2.0 + 1 / 8 + 1 / 32,                   # MXFP4: read x; write bits + E8M0 scale bytes
     "mx_guided_fwd": 2.0 + 1 / 8 + 1 / 32 + 2.0 + 1 / 8,  # MXFP4: read x, bits, scales; write y, mask
+    "mx8_capture": 2.0 + 1 / 8 + 1 / 32,                  # MXFP8 (E4M3): read x; write bits + E8M0 scale bytes
+    "mx8_guided_fwd": 2.0 + 1 / 8 + 1 / 32 + 2.0 + 1 / 8, # MXFP8: read x, bits, scales; write y, mask
     "capture_lowbits3": 2.0 + 3 / 8 + 1 / 16,             # b = 3 cached low bits: three bit-planes
     "lowbits3_fwd": 2.0 + 3 / 8 + 1 / 16 + 2.0 + 1 / 8,   # forward from three bit-planes
 }
@@ -221,7 +223,8 @@ def main():
     dominant = max(KERNELS, key=lambda k: per_kernel_ms[k])
     dk = kernels[dominant]
 
-    # rows beyond the hot path: capture with full codes, then the full-information forward
+    # rows beyond the hot path: capture with full codes and the full-information
+    # forward, the MXFP4 and MXFP8 variants, b = 3 cached low bits
     codes = torch.empty(n // 2, dtype=torch.uint8, device=dev)
     mx_scales = torch.empty(n // 32, dtype=torch.uint8, device=dev)
     mx_bits = torch.empty(n // 8, dtype=torch.uint8, device=dev)
@@ -243,6 +246,12 @@ def main():
             ev["mx_guided_fwd"][li][0].record(stream)
             tr.mx_guided_fakequant_fwd(d["x_train"], mx_scales, mx_bits, y=y_g, mask=mask_g)
             ev["mx_guided_fwd"][li][1].record(stream)
+            ev["mx8_capture"][li][0].record(stream)
+            tr.mx8_capture(d["x_roll"], scales=mx_scales, bits=mx_bits)
+            ev["mx8_capture"][li][1].record(stream)
+            ev["mx8_guided_fwd"][li][0].record(stream)
+            tr.mx8_guided_fakequant_fwd(d["x_train"], mx_scales, mx_bits, y=y_g, mask=mask_g)
+            ev["mx8_guided_fwd"][li][1].record(stream)
             ev["capture_lowbits3"][li][0].record(stream)
             tr.capture_lowbits(d["x_roll"], d["ts"], 3, scales=d["scales"], planes=planes3)
             ev["capture_lowbits3"][li][1].record(stream)

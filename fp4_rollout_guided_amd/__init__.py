@@ -20,6 +20,9 @@ Functions mirror the C ABI in ``include/trace.h``:
     mx_capture / mx_guided_fakequant_fwd / mx_rne_fakequant_fwd /
     mx_full_info_fakequant_fwd: the MXFP4 variant (32-element blocks, E8M0
     scales, no tensor scale)
+    mx8_capture / mx8_guided_fakequant_fwd / mx8_rne_fakequant_fwd /
+    mx8_full_info_fakequant_fwd: the MXFP8 (E4M3) activation grid of the W4A8
+    setting (32-element blocks, E8M0 scales, one code byte per element)
     capture_lowbits(x_roll, ts, nbits)               -> (scales, planes, codes)
     lowbits_fakequant_fwd(x_train, scales, ts, nbits, planes) -> (y, mask, qcodes)
     ste_bwd(grad_out, mask)                          -> grad_in
@@ -37,7 +40,8 @@ __all__ = [
     "guided_fakequant_fwd", "rne_fakequant_fwd", "full_info_fakequant_fwd", "ste_bwd", "gather_records",
     "grouped_tensor_scale", "grouped_capture", "grouped_guided_fakequant_fwd", "grouped_rne_fakequant_fwd",
     "grouped_full_info_fakequant_fwd", "mx_capture", "mx_guided_fakequant_fwd", "mx_rne_fakequant_fwd",
-    "mx_full_info_fakequant_fwd", "capture_lowbits", "lowbits_fakequant_fwd",
+    "mx_full_info_fakequant_fwd", "mx8_capture", "mx8_guided_fakequant_fwd", "mx8_rne_fakequant_fwd",
+    "mx8_full_info_fakequant_fwd", "capture_lowbits", "lowbits_fakequant_fwd",
     "GuidedFakeQuant",
     "STATUS",
 ]
@@ -91,6 +95,10 @@ def load_library(path):
         "trace_mx_guided_fakequant_fwd": ([p, i64, i64, p, p, p, p, p, p], st),
         "trace_mx_rne_fakequant_fwd": ([p, i64, i64, p, p, p, p, p], st),
         "trace_mx_full_info_fakequant_fwd": ([p, i64, i64, p, p, p, p, p, p], st),
+        "trace_mx8_capture": ([p, i64, i64, p, p, p, p], st),
+        "trace_mx8_guided_fakequant_fwd": ([p, i64, i64, p, p, p, p, p, p], st),
+        "trace_mx8_rne_fakequant_fwd": ([p, i64, i64, p, p, p, p, p], st),
+        "trace_mx8_full_info_fakequant_fwd": ([p, i64, i64, p, p, p, p, p, p], st),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -416,6 +424,61 @@ def mx_rne_fakequant_fwd(x_train, scales, y=None, mask=None, want_codes=False, q
 def mx_full_info_fakequant_fwd(x_train, scales, codes, y=None, mask=None, want_codes=False, qcodes=None):
     """Full-information guided forward on MXFP4 scales: (y, mask, qcodes)."""
     return _mx_fwd("full", x_train, scales, codes, y, mask, want_codes, qcodes)
+
+
+def mx8_capture(x_roll, want_codes=False, scales=None, bits=None, codes=None):
+    """MXFP8 capture: (scales u8[n/32] E8M0, bits u8[n/8], codes u8[n] E4M3FN or None)."""
+    _bf16(x_roll, "x_roll")
+    rows, cols = _rows_cols(x_roll)
+    n = rows * cols
+    scales = _u8(n // 32, x_roll, scales, "scales")
+    bits = _u8(n // 8, x_roll, bits, "bits")
+    if want_codes or codes is not None:
+        codes = _u8(n, x_roll, codes, "codes")
+    _check(lib.trace_mx8_capture(_ptr(x_roll), rows, cols, _ptr(scales), _ptr(bits), _ptr(codes), _stream(x_roll)),
+           "trace_mx8_capture")
+    return scales, bits, codes
+
+
+def _mx8_fwd(mode, x, scales, side, y, mask, want_codes, qcodes):
+    _bf16(x, "x_train")
+    rows, cols = _rows_cols(x)
+    n = rows * cols
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _bf16(y, "y")
+    mask = _u8(n // 8, x, mask, "mask")
+    if want_codes or qcodes is not None:
+        qcodes = _u8(n, x, qcodes, "qcodes")
+    tail = (_ptr(y), _ptr(mask), _ptr(qcodes), _stream(x))
+    if mode == "guided":
+        name = "trace_mx8_guided_fakequant_fwd"
+        st = lib.trace_mx8_guided_fakequant_fwd(_ptr(x), rows, cols, _ptr(scales), _ptr(side), *tail)
+    elif mode == "full":
+        name = "trace_mx8_full_info_fakequant_fwd"
+        st = lib.trace_mx8_full_info_fakequant_fwd(_ptr(x), rows, cols, _ptr(scales), _ptr(side), *tail)
+    else:
+        name = "trace_mx8_rne_fakequant_fwd"
+        st = lib.trace_mx8_rne_fakequant_fwd(_ptr(x), rows, cols, _ptr(scales), *tail)
+    _check(st, name)
+    return y, mask, qcodes
+
+
+def mx8_guided_fakequant_fwd(x_train, scales, bits, y=None, mask=None, want_codes=False, qcodes=None):
+    """Rollout-guided forward on the MXFP8 grid: (y, mask, qcodes u8[n])."""
+    return _mx8_fwd("guided", x_train, scales, bits, y, mask, want_codes, qcodes)
+
+
+def mx8_rne_fakequant_fwd(x_train, scales, y=None, mask=None, want_codes=False, qcodes=None):
+    """Round-to-nearest-even forward on the MXFP8 grid: (y, mask, qcodes u8[n])."""
+    return _mx8_fwd("rne", x_train, scales, None, y, mask, want_codes, qcodes)
+
+
+def mx8_full_info_fakequant_fwd(x_train, scales, codes, y=None, mask=None, want_codes=False, qcodes=None):
+    """Full-information forward on the MXFP8 grid (codes: rollout E4M3FN bytes,
+    u8[n]): (y, mask, qcodes u8[n])."""
+    return _mx8_fwd("full", x_train, scales, codes, y, mask, want_codes, qcodes)
 
 
 class GuidedFakeQuant(torch.autograd.Function):

@@ -363,4 +363,59 @@ trace_status trace_mx_full_info_fakequant_fwd(const uint16_t* x_train, int64_t r
   return mx_fakequant(2, x_train, rows, cols, scales, codes, y, mask, qcodes, stream);
 }
 
+// ---------------------------------------------------------------------------
+// MXFP8 (the W4A8 setting's FP8 activation grid)
+// ---------------------------------------------------------------------------
+
+trace_status trace_mx8_capture(const uint16_t* x_roll, int64_t rows, int64_t cols, uint8_t* scales, uint8_t* bits,
+                               uint8_t* codes, void* stream) {
+  uint64_t n = 0;
+  if (trace_status st = mx_site_size(rows, cols, &n)) return st;
+  if (n == 0) return TRACE_OK;
+  if (!x_roll || !scales || !bits) return TRACE_E_NULL;
+  if (!aligned(x_roll, 16) || !aligned(bits, 2) || (codes && !aligned(codes, 16))) return TRACE_E_ALIGN;
+  const Range outs[3] = {rng(scales, n / 32), rng(bits, n / 8), rng(codes, codes ? n : 0)};
+  const Range ins[1] = {rng(x_roll, 2 * n)};
+  if (trace_status st = check_alias(outs, 3, ins, 1)) return st;
+  return hip_status(trace_host::launch_mx8_capture(x_roll, n / 32, scales, bits, codes,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
+// mode 0: RNE; 1: guided (side = bit-plane, n/8 bytes, 2-byte aligned);
+// 2: full information (side = rollout codes, n bytes, 16-byte aligned).
+static trace_status mx8_fakequant(int mode, const uint16_t* x, int64_t rows, int64_t cols, const uint8_t* scales,
+                                  const uint8_t* side, uint16_t* y, uint8_t* mask, uint8_t* qcodes, void* stream) {
+  uint64_t n = 0;
+  if (trace_status st = mx_site_size(rows, cols, &n)) return st;
+  if (n == 0) return TRACE_OK;
+  if (!x || !scales || (mode != 0 && !side) || !y || !mask) return TRACE_E_NULL;
+  const uint64_t side_len = mode == 1 ? n / 8 : (mode == 2 ? n : 0);
+  const uintptr_t side_align = mode == 2 ? 16 : 2;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(mask, 2) || (mode != 0 && !aligned(side, side_align)) ||
+      (qcodes && !aligned(qcodes, 16)))
+    return TRACE_E_ALIGN;
+  const Range outs[3] = {rng(y, 2 * n), rng(mask, n / 8), rng(qcodes, qcodes ? n : 0)};
+  const Range ins[3] = {rng(x, 2 * n), rng(scales, n / 32), rng(side, side_len)};
+  if (trace_status st = check_alias(outs, 3, ins, 3, /*inplace_out=*/0, /*inplace_in=*/0)) return st;
+  return hip_status(trace_host::launch_mx8_fakequant(mode, x, n / 32, scales, side, y, mask, qcodes,
+                                                     static_cast<hipStream_t>(stream)));
+}
+
+trace_status trace_mx8_guided_fakequant_fwd(const uint16_t* x_train, int64_t rows, int64_t cols,
+                                            const uint8_t* scales, const uint8_t* bits, uint16_t* y, uint8_t* mask,
+                                            uint8_t* qcodes, void* stream) {
+  return mx8_fakequant(1, x_train, rows, cols, scales, bits, y, mask, qcodes, stream);
+}
+
+trace_status trace_mx8_rne_fakequant_fwd(const uint16_t* x_train, int64_t rows, int64_t cols, const uint8_t* scales,
+                                         uint16_t* y, uint8_t* mask, uint8_t* qcodes, void* stream) {
+  return mx8_fakequant(0, x_train, rows, cols, scales, nullptr, y, mask, qcodes, stream);
+}
+
+trace_status trace_mx8_full_info_fakequant_fwd(const uint16_t* x_train, int64_t rows, int64_t cols,
+                                               const uint8_t* scales, const uint8_t* codes, uint16_t* y,
+                                               uint8_t* mask, uint8_t* qcodes, void* stream) {
+  return mx8_fakequant(2, x_train, rows, cols, scales, codes, y, mask, qcodes, stream);
+}
+
 }  // extern "C"

@@ -63,6 +63,13 @@ hipError_t launch_mx_capture(const uint16_t* x, uint64_t nblocks, uint8_t* scale
 hipError_t launch_mx_fakequant(int mode, const uint16_t* x, uint64_t nblocks, const uint8_t* scales,
                                const uint8_t* side, uint16_t* y, uint8_t* mask, uint8_t* qcodes,
                                hipStream_t stream);
+// MXFP8 (E4M3 elements, 32-element blocks, E8M0 scales); sizes in 32-element
+// blocks; codes / rollout codes / qcodes: one byte per element.
+hipError_t launch_mx8_capture(const uint16_t* x, uint64_t nblocks, uint8_t* scales, uint8_t* bits, uint8_t* codes,
+                              hipStream_t stream);
+hipError_t launch_mx8_fakequant(int mode, const uint16_t* x, uint64_t nblocks, const uint8_t* scales,
+                                const uint8_t* side, uint16_t* y, uint8_t* mask, uint8_t* qcodes,
+                                hipStream_t stream);
 hipError_t launch_gather_records(const uint8_t* bits_src, const uint8_t* scales_src, const uint8_t* codes_src,
                                  uint64_t src_rows, uint64_t cols, const int64_t* row_index, uint64_t dst_rows,
                                  uint8_t* bits_dst, uint8_t* scales_dst, uint8_t* codes_dst, hipStream_t stream);

@@ -20,50 +20,11 @@
 #include <stdint.h>
 
 #include "device_math.h"
+#include "e8m0.h"
 #include "fp4_block.h"
 #include "launch.h"
 
 namespace trace_dev {
-
-// 2^(b - 127) for an E8M0 byte b in 0..254 (b = 0: the binary32 subnormal 2^-127).
-__device__ __forceinline__ float e8m0_value(uint32_t b) { return __uint_as_float(b ? (b << 23) : 0x00400000u); }
-
-// 2^(127 - b), exact for every b in 0..254 (b = 254: 2^-127).
-__device__ __forceinline__ float e8m0_inverse(uint32_t b) {
-  return __uint_as_float(b < 254u ? ((254u - b) << 23) : 0x00400000u);
-}
-
-// Scale byte of a block from its largest magnitude's bf16 bits (NaN
-// excluded): the exponent field E gives floor(log2(amax)) = E - 127 for
-// normal values; the byte 127 + clamp(E - 127 - 2, -127, 127) is then
-// max(E, 2) - 2, which also covers zero and subnormal maxima (byte 0) and an
-// infinite one (E = 255: byte 253).
-__device__ __forceinline__ uint32_t mx_scale_byte(uint32_t amax_bits) {
-  const uint32_t e = amax_bits >> 7;
-  return (e < 2u ? 2u : e) - 2u;
-}
-
-// Largest magnitude's bf16 bits over 16 elements, NaN excluded (a signed
-// 16-bit maximum of m + 0x7f puts NaN halves below every other value).
-__device__ __forceinline__ uint32_t half_amax_bits(const uint32_t (&w)[8]) {
-  typedef short s16x2_t __attribute__((ext_vector_type(2)));
-  s16x2_t best = {0, 0};
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const uint32_t m = (w[k] & 0x7fff7fffu) + 0x007f007fu;
-    s16x2_t v;
-    __builtin_memcpy(&v, &m, 4);
-    best = __builtin_elementwise_max(best, v);
-  }
-  const int lo = best.x, hi = best.y;
-  const int m = lo > hi ? lo : hi;
-  return m > 0x7f ? (uint32_t)(m - 0x7f) : 0u;
-}
-
-// The partner lane's value (lane ^ 1): a DPP quad permutation [1, 0, 3, 2].
-__device__ __forceinline__ uint32_t pair_swap(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
-}
 
 // ---------------------------------------------------------------------------
 // exact fallbacks (IEEE division, one element at a time) for one lane's
@@ -125,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void mx_capture_kernel(const uint4* __res
     load_block(x, h, w);
     const uint32_t a = half_amax_bits(w);
     const uint32_t b = pair_swap(a);
-    const uint32_t sb = mx_scale_byte(a > b ? a : b);
+    const uint32_t sb = mx_scale_byte<kE2M1Emax>(a > b ? a : b);
     const float inv = e8m0_inverse(sb);
     bool bad = false;
     float q[16];

@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define TRACE_ABI_VERSION 4
+#define TRACE_ABI_VERSION 5
 
 #if defined(__GNUC__)
 #define TRACE_API __attribute__((visibility("default")))
@@ -336,6 +336,49 @@ TRACE_API trace_status trace_mx_full_info_fakequant_fwd(const uint16_t* x_train,
                                                         const uint8_t* codes, uint16_t* y,
                                                         uint8_t* mask, uint8_t* qcodes,
                                                         void* stream);
+
+/*
+ * MXFP8 variant: the FP8 activation grid of the W4A8 setting.  The post
+ * reports that the method carries over to MXFP4 W4A8 (rcap.io post,
+ * Ablations bullet); in W4A8 the rounded activations are 8-bit.  Reading:
+ * the OCP MX v1.0 format MXFP8 with E4M3 elements:
+ *   - blocks of 32 consecutive elements along the last dimension
+ *     (cols % 32 == 0), one E8M0 scale byte b each, s = 2^(b - 127); byte
+ *     0xFF (NaN) makes a zero-scale block;
+ *   - capture: b = 127 + clamp(floor(log2(amax)) - 8, -127, 127) (8: the
+ *     exponent of E4M3's largest normal, 448), with amax as for MXFP4 (an
+ *     infinite element gives b = 247);
+ *   - elements: OCP E4M3FN bytes, sign << 7 | magnitude code; the code of
+ *     z = clip(fl32(x / s), -448, 448) rounded to nearest even; the cached
+ *     bit is the magnitude code's last bit, bit k of byte j of the
+ *     bit-plane belonging to element 8j + k;
+ *   - forwards: as on the NVFP4 path with this grid, clip bound 448 and mask
+ *     |x / s| <= 448; full information takes the bracket endpoint nearest
+ *     the rollout's signed codeword, a NaN rollout byte (0x7F / 0xFF)
+ *     counting as +-480.
+ * Layouts: scales uint8[n/32]; bits and mask uint8[n/8], 2-byte aligned;
+ * codes, rollout codes and qcodes uint8[n] (one E4M3FN byte per element,
+ * flat element order), 16-byte aligned.  Aliasing and errors as the MXFP4
+ * entry points; y may alias x_train exactly.  The STE backward
+ * (trace_ste_bwd) takes the mask unchanged.
+ */
+TRACE_API trace_status trace_mx8_capture(const uint16_t* x_roll, int64_t rows, int64_t cols,
+                                         uint8_t* scales, uint8_t* bits, uint8_t* codes,
+                                         void* stream);
+TRACE_API trace_status trace_mx8_guided_fakequant_fwd(const uint16_t* x_train, int64_t rows,
+                                                      int64_t cols, const uint8_t* scales,
+                                                      const uint8_t* bits, uint16_t* y,
+                                                      uint8_t* mask, uint8_t* qcodes,
+                                                      void* stream);
+TRACE_API trace_status trace_mx8_rne_fakequant_fwd(const uint16_t* x_train, int64_t rows,
+                                                   int64_t cols, const uint8_t* scales,
+                                                   uint16_t* y, uint8_t* mask, uint8_t* qcodes,
+                                                   void* stream);
+TRACE_API trace_status trace_mx8_full_info_fakequant_fwd(const uint16_t* x_train, int64_t rows,
+                                                         int64_t cols, const uint8_t* scales,
+                                                         const uint8_t* codes, uint16_t* y,
+                                                         uint8_t* mask, uint8_t* qcodes,
+                                                         void* stream);
 
 #ifdef __cplusplus
 }

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert tr.abi_version() == 4
+    assert tr.abi_version() == 5
     for code in range(6):
         assert L.trace_status_string(code).decode().startswith("TRACE")
     assert b"unknown" in L.trace_status_string(99)
@@ -240,6 +240,27 @@ def test_mx_validation():
     assert f(P(x), 4, 64, P(sc), P(cd + 4), P(y), P(mk), None, None) == E_ALIGN
     r = L.trace_mx_rne_fakequant_fwd
     assert r(P(x), 4, 80, P(sc), P(y), P(mk), None, None) == E_SHAPE
+
+
+def test_mx8_validation():
+    x, sc, bi, cd, y, mk = (A + k * 0x1000000 for k in range(6))
+    cap = L.trace_mx8_capture
+    assert cap(P(x), 4, 48, P(sc), P(bi), None, None) == E_SHAPE      # cols % 32
+    assert cap(P(x), 4, 64, P(sc), None, None, None) == E_NULL
+    assert cap(P(x + 8), 4, 64, P(sc), P(bi), None, None) == E_ALIGN   # bf16 needs 16 bytes
+    assert cap(P(x), 4, 64, P(sc), P(bi), P(cd + 8), None) == E_ALIGN  # codes need 16 bytes
+    assert cap(P(x), 4, 64, P(sc), P(bi), P(x + 256), None) == E_ALIAS  # 256 code bytes end at x + 512
+    assert cap(P(x), 0, 64, None, None, None, None) == OK
+    g = L.trace_mx8_guided_fakequant_fwd
+    assert g(P(x), 4, 64, P(sc), None, P(y), P(mk), None, None) == E_NULL
+    assert g(P(x), 4, 64, P(sc), P(bi), P(y), P(mk), P(cd + 8), None) == E_ALIGN
+    assert g(P(x), 4, 64, P(sc), P(bi), P(y), P(mk), P(y + 496), None) == E_ALIAS   # qcodes over y
+    f = L.trace_mx8_full_info_fakequant_fwd
+    assert f(P(x), 4, 64, P(sc), P(cd + 8), P(y), P(mk), None, None) == E_ALIGN
+    assert f(P(x), 4, 64, P(sc), P(cd), P(cd + 240), P(mk), None, None) == E_ALIAS  # y over the rollout codes
+    r = L.trace_mx8_rne_fakequant_fwd
+    assert r(P(x), 4, 80, P(sc), P(y), P(mk), None, None) == E_SHAPE
+    assert r(P(x), -1, 64, P(sc), P(y), P(mk), None, None) == E_SHAPE
 
 
 def test_lowbits_validation():

@@ -73,6 +73,13 @@ def _everything(tr, xr, xt, g, offsets, perm):
                      ("mf", lambda: tr.mx_full_info_fakequant_fwd(xt, msc, mcd, want_codes=True))):
         y, m, q = fn()
         out.update({f"y_{name}": y, f"m_{name}": m, f"q_{name}": q})
+    esc, ebt, ecd = tr.mx8_capture(xr, want_codes=True)
+    out.update(esc=esc, ebt=ebt, ecd=ecd)
+    for name, fn in (("eg", lambda: tr.mx8_guided_fakequant_fwd(xt, esc, ebt, want_codes=True)),
+                     ("er", lambda: tr.mx8_rne_fakequant_fwd(xt, esc, want_codes=True)),
+                     ("ef", lambda: tr.mx8_full_info_fakequant_fwd(xt, esc, ecd, want_codes=True))):
+        y, m, q = fn()
+        out.update({f"y_{name}": y, f"m_{name}": m, f"q_{name}": q})
     lsc, lpl, _ = tr.capture_lowbits(xr, ts, 3)
     y, m, q = tr.lowbits_fakequant_fwd(xt, lsc, ts, 3, lpl, want_codes=True)
     out.update(lsc=lsc, lpl=lpl, y_l=y, m_l=m, q_l=q)

@@ -1,4 +1,4 @@
-"""The MXFP4 and b-cached-low-bits variants at full workload sizes: the KV
+"""The MXFP4, MXFP8 and b-cached-low-bits variants at full workload sizes: the KV
 cache workload (2 x 131072 x 512) and the ragged large-hidden workload
 (65573 x 7168, half of the training values placed near codeword midpoints),
 every output on sampled rows (first, last, ragged tail, random) against the
@@ -62,6 +62,27 @@ def _mx_site(name, x_roll, x_train, k_rows, seed):
     _check(name, got, want)
 
 
+def _mx8_site(name, x_roll, x_train, k_rows, seed):
+    import fp4_rollout_guided_amd as tr
+    rows, cols = x_roll.shape
+    _say(f"case {name}: MXFP8 {rows}x{cols}")
+    sc, bt, cd = tr.mx8_capture(x_roll, want_codes=True)
+    yg, mg, qg = tr.mx8_guided_fakequant_fwd(x_train, sc, bt, want_codes=True)
+    yf, mf, qf = tr.mx8_full_info_fakequant_fwd(x_train, sc, cd, want_codes=True)
+    torch.cuda.synchronize()
+    idx = _rows(rows, k_rows, seed)
+    xr, xt = _take(x_roll, idx, cols, True), _take(x_train, idx, cols, True)
+    cap = oracle.mx8_capture(xr, with_codes=True)
+    gd = oracle.mx8_guided_fwd(xt, cap["scales"], cap["bits"])
+    fi = oracle.mx8_full_info_fwd(xt, cap["scales"], cap["codes"])
+    got = {"scales": _take(sc, idx, cols // 32), "bits": _take(bt, idx, cols // 8), "codes": _take(cd, idx, cols),
+           "y_g": _take(yg, idx, cols, True), "m_g": _take(mg, idx, cols // 8), "q_g": _take(qg, idx, cols),
+           "y_f": _take(yf, idx, cols, True), "m_f": _take(mf, idx, cols // 8), "q_f": _take(qf, idx, cols)}
+    want = {"scales": cap["scales"], "bits": cap["bits"], "codes": cap["codes"], "y_g": gd["y"], "m_g": gd["mask"],
+            "q_g": gd["codes"], "y_f": fi["y"], "m_f": fi["mask"], "q_f": fi["codes"]}
+    _check(name, got, want)
+
+
 def _lowbits_site(name, x_roll, x_train, nbits, k_rows, seed):
     import fp4_rollout_guided_amd as tr
     rows, cols = x_roll.shape
@@ -96,6 +117,10 @@ def test_mx_workload4(device, workload4):
     _mx_site("workload 4", *workload4, k_rows=96, seed=41)
 
 
+def test_mx8_workload4(device, workload4):
+    _mx8_site("workload 4", *workload4, k_rows=96, seed=47)
+
+
 @pytest.mark.parametrize("nbits", [2, 3])
 def test_lowbits_workload4(device, workload4, nbits):
     _lowbits_site("workload 4", *workload4, nbits=nbits, k_rows=96, seed=42 + nbits)
@@ -108,5 +133,6 @@ def test_variants_workload2(device, which):
     x_train = place_kv(x_roll, which, s_block)
     shape2d = (x_roll.shape[0], x_roll.shape[1] * x_roll.shape[2])
     _mx_site(f"workload 2 {which}", x_roll.reshape(shape2d), x_train.reshape(shape2d), k_rows=256, seed=21)
+    _mx8_site(f"workload 2 {which}", x_roll.reshape(shape2d), x_train.reshape(shape2d), k_rows=256, seed=23)
     _lowbits_site(f"workload 2 {which}", x_roll.reshape(shape2d), x_train.reshape(shape2d), nbits=2, k_rows=256,
                   seed=22)
