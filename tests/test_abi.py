@@ -276,3 +276,22 @@ def test_lowbits_validation():
     assert f(P(x), 4, 64, P(sc), P(ts), 9, P(pl), P(y), P(mk), None, None) == E_SHAPE
     assert f(P(x), 4, 64, P(sc), P(ts), 2, None, P(y), P(mk), None, None) == E_NULL
     assert f(P(x), 4, 64, P(sc), P(ts), 2, P(pl), P(pl + 32), P(mk), None, None) == E_ALIAS  # y over plane 1
+
+
+def test_header_is_c99_and_links(tmp_path):
+    """include/trace.h is a C header: a strict C99 translation unit that
+    includes it compiles without warnings, links against libtrace.so and
+    reads the ABI version (no GPU call)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "use_trace.c"
+    src.write_text('#include "trace.h"\n'
+                   "int main(void) { return trace_abi_version() == TRACE_ABI_VERSION ? 0 : 1; }\n")
+    exe = tmp_path / "use_trace"
+    libdir = os.path.dirname(tr.LIB_PATH)
+    subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-L", libdir, "-l:libtrace.so", f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True)
+    assert subprocess.run([str(exe)]).returncode == 0
