@@ -2,7 +2,9 @@
 benchmark uses (one call per site tensor), against the oracle on sampled
 rows (the first row, random rows and the last rows, which include the ragged
 tail of the large-hidden workload).  The tensor scale of every site is
-checked over the whole tensor.  Where a workload is built around rollout /
+checked over the whole tensor, and every element of every output against
+the whole-tensor properties of ``tests/full_props.py`` (on all 20 layers of
+the deeper-half sweep too).  Where a workload is built around rollout /
 training agreement, the oracle's mismatch statistics on the sample are
 checked against what the rule guarantees (straddle sites are recovered,
 two-codeword mismatches fall back to RNE) and printed."""
@@ -16,6 +18,7 @@ import torch
 
 import oracle
 import workloads
+from tests.full_props import check_nvfp4_outputs
 from tests.gpu_util import assert_same, oracle_path, to_np_u16, to_np_u8
 from tests.workload_place import oracle_block_scales, place_kv, place_near_midpoints
 
@@ -56,6 +59,7 @@ def check_site(name, x_roll, x_train, grad, k_rows=128, seed=0):
     rows, cols = x_roll.shape[0], x_roll.numel() // x_roll.shape[0]
     _say(f"case {name}: {tuple(x_roll.shape)} ({x_roll.numel()} elements), {k_rows} sampled rows")
     got = _gpu_full(x_roll, x_train, grad)
+    check_nvfp4_outputs(name, x_roll, x_train, grad, got["ts"], got)
     xr_all = to_np_u16(x_roll)
     ts = oracle.tensor_scale(xr_all)
     del xr_all
@@ -128,6 +132,18 @@ def test_workload3_deeper_half_layer(device, layer):
     d = workloads.cfg3_layer(device, layer)
     st = check_site(f"workload 3 layer {layer}", d["x_roll"], d["x_train"], d["grad"], seed=30 + layer)
     assert st["recovered"] >= st["straddle"]
+
+
+def test_workload3_every_layer_whole_tensor(device):
+    """All 20 layers of the deeper-half sweep, every element of every output
+    checked against the whole-tensor properties (layers 0 and 19 are also
+    compared with the oracle on sampled rows above)."""
+    for layer in range(20):
+        d = workloads.cfg3_layer(device, layer)
+        _say(f"case workload 3 layer {layer}: whole-tensor properties")
+        got = _gpu_full(d["x_roll"], d["x_train"], d["grad"])
+        check_nvfp4_outputs(f"workload 3 layer {layer}", d["x_roll"], d["x_train"], d["grad"], got["ts"], got)
+        del d, got
 
 
 def test_workload4_large_hidden_ragged(device):
