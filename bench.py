@@ -19,7 +19,8 @@ and forward from b = 3 cached low bits, on the same layers) and reports them
 under ``next_rows``; another
 times the per-expert (grouped) tensor scale, capture and guided forward and
 the record gather on the packed routed-expert site of the MoE layer workload
-(``moe_expert_site``).
+(``moe_expert_site``); a last one runs the step's kernels on the sites of
+the other workloads, cold and repeated (``other_workloads``).
 
 Prints one JSON line (last line of stdout).  ``value`` is the algorithmic
 bytes of the whole step divided by its wall time, in GB/s; per-kernel GB/s,
@@ -271,6 +272,7 @@ def main():
                         "bytes_per_launch": int(bpe * n)}
 
     moe = moe_rows(tr, workloads, torch, dev, stream, layers, next_steps)
+    other = workload_rows(tr, workloads, torch, dev, stream)
 
     cache = {
         "compact_bytes_20_layers": L * (n // 8 + n // 16),
@@ -301,6 +303,7 @@ def main():
         "kernels": kernels,
         "next_rows": next_rows,
         "moe_expert_site": moe,
+        "other_workloads": other,
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": dk["GB_s"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": dk["frac_hbm_peak"], "traffic": read_traffic(dominant)},
         "cache": cache,
@@ -314,6 +317,101 @@ def main():
         pool.close()
         pool.join()
     print(json.dumps(result), flush=True)
+
+
+def workload_rows(tr, workloads, torch, dev, stream, reps=3):
+    """The step's five kernels on each site of the other workloads (the MoE
+    layer's four sites, K and V of the KV cache, the ragged large-hidden
+    site, and the small 1024x2048 case), timed per kernel with HIP events.
+    Cold: every rep follows a 1 GiB read-only pass, which evicts the 256 MB
+    last-level cache without leaving dirty lines; warm: the same step again
+    at once (sites under 256 MB then read from the cache).  x_train follows
+    the relative-noise rule of each workload where it is one (the MoE layer:
+    its tuned sigma; elsewhere the small case's 2%): the kernels have no
+    data-dependent path on finite inputs, so where values land does not
+    change the time."""
+    import json as _json
+    with open(os.path.join(ROOT, "tests", "golden", "cfg1_sigma.json")) as fh:
+        sigma = _json.load(fh)["sigma"]
+    flush = torch.zeros(1 << 29, dtype=torch.bfloat16, device=dev)   # 1 GiB
+    flush_ts = torch.empty(1, dtype=torch.float32, device=dev)
+
+    def noisy(x, *key):
+        return workloads.relative_noise(x, 0.02, workloads.generator(dev, *key))
+
+    sites = {"small 1024x2048": {"x": workloads.cfg0(dev)}}
+    sites["MoE layer"] = workloads.cfg1(dev, sigma)
+    kv = {}
+    for which in ("k", "v"):
+        xr = workloads.cfg2_rollout(dev, which)
+        kv[which] = {"x_roll": xr, "x_train": noisy(xr, 2, which, "bench"), "grad": workloads.grad_for(xr.shape, dev, 2, which)}
+    sites["KV cache"] = kv
+    xr = workloads.cfg4_rollout(dev)
+    sites["large hidden 65573x7168"] = {"x": {"x_roll": xr, "x_train": noisy(xr, 4, "bench"),
+                                              "grad": workloads.grad_for(xr.shape, dev, 4)}}
+    bpe_step = sum(BYTES_PER_ELEM.values())
+    out = {"protocol": "cold: each of %d reps after a 1 GiB read-only pass (evicts the 256 MB last-level cache, "
+                       "leaves no dirty lines); warm: the same step again at once (small sites' inputs partly "
+                       "cache-resident, the first run's output lines still being written back); GB/s = algorithmic "
+                       "bytes of the five kernels / the sum of their HIP-event times; x_train by relative noise" % reps}
+    for wname, ws_ in sites.items():
+        tot = {"bytes": 0.0, "cold_s": 0.0, "warm_s": 0.0}
+        res = {}
+        for sname, d in ws_.items():
+            x_roll = d["x_roll"].reshape(d["x_roll"].shape[0], -1)
+            x_train = d["x_train"].reshape(x_roll.shape)
+            grad = d["grad"].reshape(x_roll.shape)
+            n = x_roll.numel()
+            ts = torch.empty(1, dtype=torch.float32, device=dev)
+            ws = torch.empty(tr.lib.trace_tensor_scale_workspace_bytes(n), dtype=torch.uint8, device=dev)
+            scales = torch.empty(n // 16, dtype=torch.uint8, device=dev)
+            bits = torch.empty(n // 8, dtype=torch.uint8, device=dev)
+            y = torch.empty_like(x_train)
+            mask = torch.empty(n // 8, dtype=torch.uint8, device=dev)
+            gin = torch.empty_like(grad)
+
+            def run(evs):
+                evs[0].record(stream)
+                tr.tensor_scale(x_roll, out=ts, workspace=ws)
+                evs[1].record(stream)
+                tr.capture(x_roll, ts, scales=scales, bits=bits)
+                evs[2].record(stream)
+                tr.guided_fakequant_fwd(x_train, scales, ts, bits, y=y, mask=mask)
+                evs[3].record(stream)
+                tr.rne_fakequant_fwd(x_train, scales, ts, y=y, mask=mask)
+                evs[4].record(stream)
+                tr.ste_bwd(grad, mask, grad_in=gin)
+                evs[5].record(stream)
+
+            def events():
+                return [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+
+            run(events())                                   # warm-up
+            cold = [0.0] * 5
+            warm = [0.0] * 5
+            for _ in range(reps):
+                tr.tensor_scale(flush, out=flush_ts)        # read-only 1 GiB pass
+                ec, ew = events(), events()
+                run(ec)
+                run(ew)
+                stream.synchronize()
+                for k in range(5):
+                    cold[k] += ec[k].elapsed_time(ec[k + 1]) / reps
+                    warm[k] += ew[k].elapsed_time(ew[k + 1]) / reps
+            nbytes = bpe_step * n
+            cs, wsec = sum(cold) * 1e-3, sum(warm) * 1e-3
+            res[sname] = {"elements": n, "cold_us": round(cs * 1e6, 1), "cold_GB_s": round(nbytes / cs / 1e9, 1),
+                          "cold_frac_hbm_peak": round(nbytes / cs / 1e9 / HBM_PEAK_GBS, 4),
+                          "warm_us": round(wsec * 1e6, 1), "warm_GB_s": round(nbytes / wsec / 1e9, 1),
+                          "cold_kernel_us": {k: round(cold[i] * 1e3, 1) for i, k in enumerate(KERNELS)}}
+            tot["bytes"] += nbytes
+            tot["cold_s"] += cs
+            tot["warm_s"] += wsec
+        out[wname] = {"sites": res, "cold_GB_s": round(tot["bytes"] / tot["cold_s"] / 1e9, 1),
+                      "warm_GB_s": round(tot["bytes"] / tot["warm_s"] / 1e9, 1)}
+        log(f"workload {wname}: cold {out[wname]['cold_GB_s']} GB/s, warm {out[wname]['warm_GB_s']} GB/s")
+    del sites, flush
+    return out
 
 
 def moe_rows(tr, workloads, torch, dev, stream, layers, reps):
@@ -490,6 +588,8 @@ def cpu_leg(pool, cores, d0, n, y_g, mask_g, y_r, mask_r, gin, np, torch, tr):
     log(f"cpu oracle: {elems} elements in {wall:.2f} s on {cores} processes; bit-exact={exact}")
     return {"value": round(eps * bpe / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "elem_per_s": round(eps, 1),
+            "one_core_value": round(elems * bpe / busy / 1e9, 4) if busy > 0 else None,
+            "one_core_elem_per_s": round(elems / busy, 1) if busy > 0 else None,
             "sample": f"rows 0..{done_rows} of layer 0 ({elems} elements) through the whole step, "
                       f"tensor scale of the full layer; {cores} worker processes, "
                       f"{busy:.1f} s of CPU time in {wall:.1f} s wall",
