@@ -10,9 +10,10 @@ before timing starts.
 
 One step = for every layer, in order: tensor scale (amax pass), capture
 (scale bytes + parity bit-plane), guided fake-quant forward (y + clip mask),
-plain RNE fake-quant forward (y + clip mask), STE backward.  Every kernel is
-bracketed by HIP events on the stream it runs on; the step's wall time is
-taken between device synchronizations.  After the timed steps, a separate
+plain RNE fake-quant forward (y + clip mask), STE backward.  A HIP event
+marker on the kernels' stream sits before the first kernel and after every
+kernel, so each kernel is timed between the markers around it; the step's
+wall time is taken between device synchronizations.  After the timed steps, a separate
 pass times the rows beyond the hot path (capture with full 4-bit codes, the
 full-information forward, MXFP4 capture and guided forward, and capture to
 and forward from b = 3 cached low bits, on the same layers) and reports them
@@ -172,39 +173,43 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
 
-    def step(events=None):
-        for li, d in enumerate(layers):
-            def mark(k, i):
-                if events is not None:
-                    events[k][li][i].record(stream)
-            mark("tensor_scale", 0)
+    def step(markers=None):
+        """One pass over all layers.  markers: None, or len(KERNELS) * L + 1
+        timing events, recorded before the first kernel and after every
+        kernel (one shared marker between consecutive kernels: a kernel's
+        duration is the time between the markers around it; two markers per
+        kernel would add a second queue barrier per launch)."""
+        it = iter(markers) if markers is not None else None
+
+        def mark():
+            if it is not None:
+                next(it).record(stream)
+        mark()
+        for d in layers:
             tr.tensor_scale(d["x_roll"], out=d["ts"], workspace=ws)
-            mark("tensor_scale", 1)
-            mark("capture", 0)
+            mark()
             tr.capture(d["x_roll"], d["ts"], scales=d["scales"], bits=d["bits"])
-            mark("capture", 1)
-            mark("guided_fwd", 0)
+            mark()
             tr.guided_fakequant_fwd(d["x_train"], d["scales"], d["ts"], d["bits"], y=y_g, mask=mask_g)
-            mark("guided_fwd", 1)
-            mark("rne_fwd", 0)
+            mark()
             tr.rne_fakequant_fwd(d["x_train"], d["scales"], d["ts"], y=y_r, mask=mask_r)
-            mark("rne_fwd", 1)
-            mark("ste_bwd", 0)
+            mark()
             tr.ste_bwd(d["grad"], mask_g, grad_in=gin)
-            mark("ste_bwd", 1)
+            mark()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     per_kernel_ms = {k: 0.0 for k in KERNELS}
+    nk = len(KERNELS)
+    markers = [torch.cuda.Event(enable_timing=True) for _ in range(nk * L + 1)]   # created once, re-recorded
     t0 = time.perf_counter()
     for s in range(args.steps):
-        ev = {k: [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(L)] for k in KERNELS}
-        step(ev)
+        step(markers)
         stream.synchronize()
-        for k in KERNELS:
-            per_kernel_ms[k] += sum(ev[k][li][0].elapsed_time(ev[k][li][1]) for li in range(L))
+        for i in range(nk * L):
+            per_kernel_ms[KERNELS[i % nk]] += markers[i].elapsed_time(markers[i + 1])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = 1e3 * wall / args.steps
