@@ -529,7 +529,7 @@ def read_traffic(kernel):
     return float(kv["traffic_bytes_per_launch"])
 
 
-KERNEL_SOURCES = ("kernels.hip", "fp4_block.h", "device_math.h", "launch.h")
+KERNEL_SOURCES = ("kernels.hip", "fp4_block.h", "device_math.h", "nvfp4_scale.h", "launch.h")
 
 
 def kernel_sources_digest():

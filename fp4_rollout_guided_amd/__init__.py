@@ -26,6 +26,7 @@ Functions mirror the C ABI in ``include/trace.h``:
     capture_lowbits(x_roll, ts, nbits)               -> (scales, planes, codes)
     lowbits_fakequant_fwd(x_train, scales, ts, nbits, planes) -> (y, mask, qcodes)
     ste_bwd(grad_out, mask)                          -> grad_in
+    mismatch_stats(x_train, scales, ts, bits, codes, stats=None) -> stats (int64[20], added to)
 
 and ``GuidedFakeQuant`` wraps the forward/backward pair as an autograd
 function.
@@ -41,7 +42,7 @@ __all__ = [
     "grouped_tensor_scale", "grouped_capture", "grouped_guided_fakequant_fwd", "grouped_rne_fakequant_fwd",
     "grouped_full_info_fakequant_fwd", "mx_capture", "mx_guided_fakequant_fwd", "mx_rne_fakequant_fwd",
     "mx_full_info_fakequant_fwd", "mx8_capture", "mx8_guided_fakequant_fwd", "mx8_rne_fakequant_fwd",
-    "mx8_full_info_fakequant_fwd", "capture_lowbits", "lowbits_fakequant_fwd",
+    "mx8_full_info_fakequant_fwd", "capture_lowbits", "lowbits_fakequant_fwd", "mismatch_stats", "STAT_FIELDS",
     "GuidedFakeQuant",
     "STATUS",
 ]
@@ -96,6 +97,7 @@ def load_library(path):
         "trace_mx_rne_fakequant_fwd": ([p, i64, i64, p, p, p, p, p], st),
         "trace_mx_full_info_fakequant_fwd": ([p, i64, i64, p, p, p, p, p, p], st),
         "trace_mx8_capture": ([p, i64, i64, p, p, p, p], st),
+        "trace_mismatch_stats": ([p, i64, i64, p, p, p, p, p, p], st),
         "trace_mx8_guided_fakequant_fwd": ([p, i64, i64, p, p, p, p, p, p], st),
         "trace_mx8_rne_fakequant_fwd": ([p, i64, i64, p, p, p, p, p], st),
         "trace_mx8_full_info_fakequant_fwd": ([p, i64, i64, p, p, p, p, p, p], st),
@@ -479,6 +481,27 @@ def mx8_full_info_fakequant_fwd(x_train, scales, codes, y=None, mask=None, want_
     """Full-information forward on the MXFP8 grid (codes: rollout E4M3FN bytes,
     u8[n]): (y, mask, qcodes u8[n])."""
     return _mx8_fwd("full", x_train, scales, codes, y, mask, want_codes, qcodes)
+
+
+# Layout of the agreement statistics: hist[0..14], then these counters.
+STAT_FIELDS = ("straddle", "crossed", "recovered", "violations", "elements")
+
+
+def mismatch_stats(x_train, scales, ts, bits, codes, stats=None):
+    """Agreement statistics of x_train's RNE / guided / full-information
+    codes with the rollout codes, ADDED to ``stats`` (an int64[20] device
+    tensor, zeroed here when not given): [0..14] histogram of signed grid
+    steps between rollout and RNE codes, then straddle, crossed, recovered,
+    violations, elements (the counts are below 2^63)."""
+    _bf16(x_train, "x_train")
+    rows, cols = _rows_cols(x_train)
+    if stats is None:
+        stats = torch.zeros(20, dtype=torch.int64, device=x_train.device)
+    elif stats.dtype != torch.int64 or stats.numel() != 20 or not stats.is_contiguous():
+        raise ValueError("stats must be a contiguous int64 tensor of 20 elements")
+    _check(lib.trace_mismatch_stats(_ptr(x_train), rows, cols, _ptr(scales), _ptr(ts), _ptr(bits), _ptr(codes),
+                                    _ptr(stats), _stream(x_train)), "trace_mismatch_stats")
+    return stats
 
 
 class GuidedFakeQuant(torch.autograd.Function):

@@ -19,7 +19,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libtrace.so")
-SOURCES = ["kernels.hip", "mx_kernels.hip", "mx8_kernels.hip", "api.cpp"]
+SOURCES = ["kernels.hip", "mx_kernels.hip", "mx8_kernels.hip", "diag_kernels.hip", "api.cpp"]
 ARCH = "gfx950"
 
 FLAGS = [

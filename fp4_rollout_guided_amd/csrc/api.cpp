@@ -364,6 +364,26 @@ trace_status trace_mx_full_info_fakequant_fwd(const uint16_t* x_train, int64_t r
 }
 
 // ---------------------------------------------------------------------------
+// agreement statistics
+// ---------------------------------------------------------------------------
+
+trace_status trace_mismatch_stats(const uint16_t* x_train, int64_t rows, int64_t cols, const uint8_t* scales,
+                                  const float* ts, const uint8_t* bits, const uint8_t* codes, uint64_t* stats,
+                                  void* stream) {
+  uint64_t n = 0;
+  if (trace_status st = site_size(rows, cols, &n)) return st;
+  if (n == 0) return TRACE_OK;
+  if (!x_train || !scales || !ts || !bits || !codes || !stats) return TRACE_E_NULL;
+  if (!aligned(x_train, 16) || !aligned(ts, 4) || !aligned(bits, 2) || !aligned(codes, 8) || !aligned(stats, 8))
+    return TRACE_E_ALIGN;
+  const Range outs[1] = {rng(stats, 20 * sizeof(uint64_t))};
+  const Range ins[5] = {rng(x_train, 2 * n), rng(scales, n / 16), rng(ts, 4), rng(bits, n / 8), rng(codes, n / 2)};
+  if (trace_status st = check_alias(outs, 1, ins, 5)) return st;
+  return hip_status(trace_host::launch_mismatch_stats(x_train, n / 16, scales, ts, bits, codes, stats,
+                                                      static_cast<hipStream_t>(stream)));
+}
+
+// ---------------------------------------------------------------------------
 // MXFP8 (the W4A8 setting's FP8 activation grid)
 // ---------------------------------------------------------------------------
 

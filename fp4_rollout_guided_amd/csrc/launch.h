@@ -73,6 +73,12 @@ hipError_t launch_mx8_fakequant(int mode, const uint16_t* x, uint64_t nblocks, c
 hipError_t launch_gather_records(const uint8_t* bits_src, const uint8_t* scales_src, const uint8_t* codes_src,
                                  uint64_t src_rows, uint64_t cols, const int64_t* row_index, uint64_t dst_rows,
                                  uint8_t* bits_dst, uint8_t* scales_dst, uint8_t* codes_dst, hipStream_t stream);
+// Agreement statistics, added to stats (uint64[20]): [0..14] elements whose
+// rollout and RNE codes are k signed grid steps apart, [15] straddles,
+// [16] crossed one-step mismatches, [17] recovered mismatches, [18] guarantee
+// violations, [19] elements.
+hipError_t launch_mismatch_stats(const uint16_t* x, uint64_t nblocks, const uint8_t* scales, const float* ts,
+                                 const uint8_t* bits, const uint8_t* codes, uint64_t* stats, hipStream_t stream);
 hipError_t launch_ste_bwd(const uint16_t* g, const uint8_t* mask, uint64_t nblocks, uint16_t* gin,
                           hipStream_t stream);
 

@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define TRACE_ABI_VERSION 5
+#define TRACE_ABI_VERSION 6
 
 #if defined(__GNUC__)
 #define TRACE_API __attribute__((visibility("default")))
@@ -300,6 +300,39 @@ TRACE_API trace_status trace_lowbits_fakequant_fwd(const uint16_t* x_train, int6
                                                    const float* ts, int32_t nbits,
                                                    const uint8_t* planes, uint16_t* y,
                                                    uint8_t* mask, uint8_t* qcodes, void* stream);
+
+/*
+ * Agreement statistics of one site tensor between the rollout's codes and
+ * the training side.  The post's premises: most mismatched sites differ by
+ * one adjacent codeword (bandwidth paragraph), a one-codeword mismatch is a
+ * value straddling a rounding midpoint (rounding-boundary paragraph), and
+ * the guided choice is never farther from the rollout codeword than plain
+ * rounding (rollout-guided rounding paragraph).  Per element, the RNE,
+ * guided and full-information codes of x_train under the rollout record
+ * (scales, ts, bits; as trace_guided_fakequant_fwd computes them) are
+ * compared with the rollout code (codes, as trace_capture writes them), and
+ * the counts are ADDED to stats (calls accumulate, e.g. over a layer sweep;
+ * zero it before the first call):
+ *   stats[k], k = 0..14 : elements whose rollout and RNE codes are k signed
+ *                         grid steps apart (k = 0: agreement);
+ *   stats[15] : straddles -- mismatches whose rollout codeword is an end of
+ *               the bracket of x_train / s;
+ *   stats[16] : crossed -- one-step mismatches that are not straddles;
+ *   stats[17] : recovered -- mismatches where the guided code is the
+ *               rollout's (equal to stats[15] when bits are the parity of
+ *               codes);
+ *   stats[18] : violations -- elements whose guided value is farther from
+ *               the rollout value than the RNE value;
+ *   stats[19] : elements counted.
+ * Arguments: x_train bf16[rows*cols] (16-byte aligned), scales uint8[n/16],
+ * ts device fp32[1], bits uint8[n/8] (2-byte aligned), codes uint8[n/2]
+ * (8-byte aligned), stats uint64[20] device (8-byte aligned, must not overlap
+ * an input).  Errors as trace_guided_fakequant_fwd; n == 0 is a no-op.
+ */
+TRACE_API trace_status trace_mismatch_stats(const uint16_t* x_train, int64_t rows, int64_t cols,
+                                            const uint8_t* scales, const float* ts,
+                                            const uint8_t* bits, const uint8_t* codes,
+                                            uint64_t* stats, void* stream);
 
 /*
  * MXFP4 variant.  The post reports that the method carries over to MXFP4

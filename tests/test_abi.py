@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert tr.abi_version() == 5
+    assert tr.abi_version() == 6
     for code in range(6):
         assert L.trace_status_string(code).decode().startswith("TRACE")
     assert b"unknown" in L.trace_status_string(99)
@@ -261,6 +261,19 @@ def test_mx8_validation():
     r = L.trace_mx8_rne_fakequant_fwd
     assert r(P(x), 4, 80, P(sc), P(y), P(mk), None, None) == E_SHAPE
     assert r(P(x), -1, 64, P(sc), P(y), P(mk), None, None) == E_SHAPE
+
+
+def test_mismatch_stats_validation():
+    x, sc, ts, bi, cd, st = (A + k * 0x1000000 for k in range(6))
+    f = L.trace_mismatch_stats
+    assert f(P(x), 4, 40, P(sc), P(ts), P(bi), P(cd), P(st), None) == E_SHAPE
+    assert f(P(x), 4, 64, P(sc), P(ts), P(bi), None, P(st), None) == E_NULL
+    assert f(P(x), 4, 64, P(sc), P(ts), P(bi), P(cd), None, None) == E_NULL
+    assert f(P(x), 4, 64, P(sc), P(ts), P(bi), P(cd), P(st + 4), None) == E_ALIGN
+    assert f(P(x), 4, 64, P(sc), P(ts), P(bi), P(cd + 4), P(st), None) == E_ALIGN
+    assert f(P(x), 4, 64, P(sc), P(ts), P(bi), P(cd), P(x + 8), None) == E_ALIAS
+    assert f(P(x), 4, 64, P(sc), P(ts), P(bi), P(cd), P(cd + 120), None) == E_ALIAS   # codes are 128 bytes
+    assert f(P(x), 0, 64, None, None, None, None, None, None) == OK
 
 
 def test_lowbits_validation():

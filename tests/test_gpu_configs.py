@@ -79,6 +79,21 @@ def check_site(name, x_roll, x_train, grad, k_rows=128, seed=0):
     _say(f"  {name}: sample {st['n']} sites, mismatched {st['mismatched']}, straddle {st['straddle']}, "
          f"crossed {st['crossed']}, recovered {st['recovered']}, violations {st['violations']}, "
          f"hist {st['hist'][:4]}")
+    # agreement statistics on the GPU: the sampled rows against the oracle's
+    # counts, then the whole tensor (every straddle recovered)
+    import fp4_rollout_guided_amd as tr
+    pick = torch.from_numpy(idx).to(x_train.device)
+    rows_t = lambda t, per: t.reshape(-1, per)[pick].contiguous()
+    g_sample = tr.mismatch_stats(rows_t(x_train.view(-1, cols), cols), rows_t(got["scales"], cols // 16), got["ts"],
+                                 rows_t(got["bits"], cols // 8), rows_t(got["codes"], cols // 2))
+    assert g_sample.cpu().numpy().tolist() == st["hist"] + [st["straddle"], st["crossed"], st["recovered"],
+                                                            st["violations"], st["n"]], name
+    full = tr.mismatch_stats(x_train.view(-1, cols), got["scales"], got["ts"], got["bits"], got["codes"])
+    full = full.cpu().numpy().tolist()
+    assert sum(full[:15]) == full[19] == rows * cols and full[17] == full[15], name
+    _say(f"  {name}: whole tensor {full[19]} sites, mismatched {full[19] - full[0]}, straddle {full[15]}, "
+         f"crossed {full[16]}, violations {full[18]}, hist {full[:4]}")
+    st["full"] = full
     # full tensor: where x_train == x_roll, guided == RNE (identical inputs give identical codes)
     same = (x_train.view(torch.int16) == x_roll.view(torch.int16)).reshape(-1)
     if bool(same.any()):
@@ -102,15 +117,20 @@ def test_workload1_moe_layer(device):
     with open(os.path.join(HERE, "golden", "cfg1_sigma.json")) as fh:
         sigma = json.load(fh)["sigma"]
     sites = workloads.cfg1(device, sigma)
-    total = {"n": 0, "straddle": 0}
+    total = {"n": 0, "straddle": 0, "full_n": 0, "full_straddle": 0}
     for i, (name, d) in enumerate(sites.items()):
         st = check_site(f"workload 1 {name}", d["x_roll"], d["x_train"], d["grad"], seed=10 + i)
         total["n"] += st["n"]
         total["straddle"] += st["straddle"]
+        total["full_n"] += st["full"][19]
+        total["full_straddle"] += st["full"][15]
         assert st["recovered"] >= st["straddle"]
     rate = total["straddle"] / total["n"]
     _say(f"  workload 1 straddle rate on the samples: {rate:.4f}")
     assert 0.02 < rate < 0.04
+    full_rate = total["full_straddle"] / total["full_n"]
+    _say(f"  workload 1 straddle rate over the whole layer: {full_rate:.4f}")
+    assert 0.02 < full_rate < 0.04
 
 
 @pytest.mark.parametrize("which", ["k", "v"])
