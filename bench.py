@@ -58,6 +58,7 @@ KERNELS = list(BYTES_PER_ELEM)
 NEXT_BYTES_PER_ELEM = {
     "capture_codes": 2.0 + 1 / 8 + 1 / 16 + 1 / 2,        # capture that also writes the 4-bit codes
     "full_info_fwd": 2.0 + 1 / 16 + 1 / 2 + 2.0 + 1 / 8,  # read x, scales, codes; write y, mask
+    "mismatch_stats": 2.0 + 1 / 16 + 1 / 8 + 1 / 2,       # agreement statistics: read x_train, scales, bits, codes
     "mx_capture": 2.0 + 1 / 8 + 1 / 32,                   # MXFP4: read x; write bits + E8M0 scale bytes
     "mx_guided_fwd": 2.0 + 1 / 8 + 1 / 32 + 2.0 + 1 / 8,  # MXFP4: read x, bits, scales; write y, mask
     "mx8_capture": 2.0 + 1 / 8 + 1 / 32,                  # MXFP8 (E4M3): read x; write bits + E8M0 scale bytes
@@ -229,12 +230,14 @@ def main():
     dominant = max(KERNELS, key=lambda k: per_kernel_ms[k])
     dk = kernels[dominant]
 
-    # rows beyond the hot path: capture with full codes and the full-information
-    # forward, the MXFP4 and MXFP8 variants, b = 3 cached low bits
+    # rows beyond the hot path: capture with full codes, the full-information
+    # forward and the agreement statistics, the MXFP4 and MXFP8 variants,
+    # b = 3 cached low bits
     codes = torch.empty(n // 2, dtype=torch.uint8, device=dev)
     mx_scales = torch.empty(n // 32, dtype=torch.uint8, device=dev)
     mx_bits = torch.empty(n // 8, dtype=torch.uint8, device=dev)
     planes3 = torch.empty(3 * (n // 8), dtype=torch.uint8, device=dev)
+    stats_acc = torch.zeros(20, dtype=torch.int64, device=dev)
     next_ms = {k: 0.0 for k in NEXT_BYTES_PER_ELEM}
     next_steps = max(1, min(args.steps, 3))
     for it in range(next_steps + 1):
@@ -246,6 +249,9 @@ def main():
             ev["full_info_fwd"][li][0].record(stream)
             tr.full_info_fakequant_fwd(d["x_train"], d["scales"], d["ts"], codes, y=y_g, mask=mask_g)
             ev["full_info_fwd"][li][1].record(stream)
+            ev["mismatch_stats"][li][0].record(stream)
+            tr.mismatch_stats(d["x_train"], d["scales"], d["ts"], d["bits"], codes, stats=stats_acc)
+            ev["mismatch_stats"][li][1].record(stream)
             ev["mx_capture"][li][0].record(stream)
             tr.mx_capture(d["x_roll"], scales=mx_scales, bits=mx_bits)
             ev["mx_capture"][li][1].record(stream)
