@@ -135,3 +135,24 @@ def test_e2m1_bracket_exhaustive_all_bf16():
     assert np.array_equal(lo == hi, on_grid)
     # nothing of the grid lies strictly inside a non-degenerate bracket
     assert np.all((hi == lo) | (hi == lo + 1))
+
+
+def test_small_decoders_against_torch_and_definitions():
+    """The oracle's byte decoders that the pins above reach only through the
+    functions using them: E4M3FN decode of arbitrary arrays (torch's cast),
+    the signed grid index of E2M1 codes (-7..7, both zeros 0) and the signed
+    E4M3 values with NaN bytes read as +-480."""
+    import torch
+    import oracle
+    b = np.arange(256, dtype=np.uint32).astype(np.uint8).reshape(16, 16)
+    want = torch.from_numpy(b.copy()).view(torch.float8_e4m3fn).double().numpy()
+    got = oracle.e4m3fn_decode(b)
+    assert got.shape == b.shape
+    assert np.array_equal(np.isnan(got), np.isnan(want)) and np.array_equal(got[~np.isnan(got)], want[~np.isnan(want)])
+    codes = np.arange(16, dtype=np.uint8)
+    assert oracle.signed_index(codes).tolist() == [0, 1, 2, 3, 4, 5, 6, 7, 0, -1, -2, -3, -4, -5, -6, -7]
+    v = oracle.e4m3_signed_values(np.arange(256, dtype=np.uint32).astype(np.uint8))
+    dec = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    finite = ~np.isnan(dec)
+    assert np.array_equal(v[finite], dec[finite])
+    assert v[0x7F] == 480.0 and v[0xFF] == -480.0 and v[0x80] == 0.0
