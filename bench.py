@@ -73,7 +73,9 @@ MOE_BYTES_PER_ELEM = {
     "grouped_capture": 2.0 + 1 / 8 + 1 / 16,
     "grouped_guided_fwd": 2.0 + 1 / 8 + 1 / 16 + 2.0 + 1 / 8,
     "gather_records": 2 * (1 / 8 + 1 / 16),                        # read + write bits and scale bytes
+    "gather_records_runs": 2 * (1 / 8 + 1 / 16),                   # the same, rows moved in runs
 }
+GATHER_RUN = 256         # rows per run in the run-ordered gather
 CPU_SHARE = 16           # host cores a one-GPU machine grants
 CPU_BUDGET_S = 12.0      # wall-clock budget of the CPU oracle leg
 CHUNK_ROWS = 128
@@ -427,7 +429,9 @@ def workload_rows(tr, workloads, torch, dev, stream, reps=3):
 
 def moe_rows(tr, workloads, torch, dev, stream, layers, reps):
     """Per-expert tensor scales on the packed routed-expert site, and the
-    trainer-side gather of its records into a shuffled row order."""
+    trainer-side gather of its records into a shuffled row order (single
+    rows, and runs of GATHER_RUN consecutive rows), each gather timed after a
+    read-only 1 GiB pass."""
     sigma = 0.02
     d = workloads.cfg1(dev, sigma, sites=["expert_in"])["expert_in"]
     _, experts = workloads.moe_routing(dev)
@@ -436,6 +440,11 @@ def moe_rows(tr, workloads, torch, dev, stream, layers, reps):
     rows, cols = x_roll.shape
     n = rows * cols
     perm = torch.randperm(rows, generator=workloads.generator(dev, "trainer order"), device=dev)
+    # the same rows as shuffled runs of RUN consecutive rows (a trainer that
+    # moves whole token runs rather than single rows)
+    run_order = torch.randperm(rows // GATHER_RUN, generator=workloads.generator(dev, "trainer runs"), device=dev)
+    runs = (run_order[:, None] * GATHER_RUN + torch.arange(GATHER_RUN, device=dev)[None, :]).reshape(-1)
+    flush_ts = torch.empty(1, dtype=torch.float32, device=dev)
     groups = offsets.numel() - 1
     ts = torch.empty(groups, dtype=torch.float32, device=dev)
     ws = torch.empty(max(4, tr.lib.trace_grouped_tensor_scale_workspace_bytes(rows)), dtype=torch.uint8, device=dev)
@@ -455,12 +464,23 @@ def moe_rows(tr, workloads, torch, dev, stream, layers, reps):
         ev["grouped_guided_fwd"][0].record(stream)
         tr.grouped_guided_fakequant_fwd(x_train, offsets, scales, ts, bits, y=y, mask=mask)
         ev["grouped_guided_fwd"][1].record(stream)
-        ev["gather_records"][0].record(stream)
-        tr.gather_records(bits, scales, None, cols, perm)
-        ev["gather_records"][1].record(stream)
         stream.synchronize()
         if it > 0:
-            for k in MOE_BYTES_PER_ELEM:
+            for k in ("grouped_tensor_scale", "grouped_capture", "grouped_guided_fwd"):
+                ms[k] += ev[k][0].elapsed_time(ev[k][1])
+    # the gathers are short (0.375 B per element): each is timed after a
+    # read-only 1 GiB pass, outside the previous kernel's write-back
+    for it in range(reps + 1):
+        ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(2)] for k in ("gather_records",
+                                                                                    "gather_records_runs")}
+        for k, order in (("gather_records", perm), ("gather_records_runs", runs)):
+            tr.tensor_scale(layers[0]["x_roll"], out=flush_ts)
+            ev[k][0].record(stream)
+            tr.gather_records(bits, scales, None, cols, order)
+            ev[k][1].record(stream)
+        stream.synchronize()
+        if it > 0:
+            for k in ev:
                 ms[k] += ev[k][0].elapsed_time(ev[k][1])
     out = {"site": f"routed-expert input {rows}x{cols} bf16, rows grouped by {groups} experts "
                    f"(top-8 of 128 routing of 16384 tokens), Student-t(4)", "kernels": {}}

@@ -561,6 +561,40 @@ __global__ __launch_bounds__(kThreads) void gather_plane_kernel(const V* __restr
   }
 }
 
+// All planes of a record in one launch, when every plane moves in 16-byte
+// words (row widths and base addresses multiples of 16): workgroups
+// [first[k], first[k+1]) gather plane k, one pass over the destination rows
+// each, so the planes' short transfers share one ramp-up and one drain.
+struct GatherPlane {
+  const uint4* src;
+  uint4* dst;
+  uint32_t wpr;    // 16-byte words per row
+  uint32_t rpw;    // rows per workgroup (1 for rows of 256 words or more)
+  uint32_t first;  // first workgroup of this plane
+};
+struct GatherPlanes {
+  GatherPlane p[3];
+  uint32_t count;
+};
+
+__global__ __launch_bounds__(kThreads) void gather_planes_kernel(GatherPlanes P, uint64_t src_rows,
+                                                                 uint64_t dst_rows,
+                                                                 const int64_t* __restrict__ row_index) {
+  const uint32_t k = (P.count > 2 && blockIdx.x >= P.p[2].first) ? 2u
+                     : (P.count > 1 && blockIdx.x >= P.p[1].first) ? 1u : 0u;
+  const GatherPlane g = P.p[k];
+  const uint32_t lr = g.wpr >= kThreads ? 0u : threadIdx.x / g.wpr;
+  if (lr >= g.rpw) return;
+  const uint64_t r = (uint64_t)(blockIdx.x - g.first) * g.rpw + lr;
+  if (r >= dst_rows) return;
+  const uint32_t w0 = threadIdx.x - lr * (g.wpr >= kThreads ? 0u : g.wpr);
+  const uint32_t wstep = g.wpr >= kThreads ? kThreads : g.wpr;
+  const int64_t s = row_index[r];
+  const bool ok = s >= 0 && (uint64_t)s < src_rows;
+  for (uint32_t w = w0; w < g.wpr; w += wstep)
+    g.dst[r * g.wpr + w] = ok ? g.src[(uint64_t)s * g.wpr + w] : zero_word<uint4>();
+}
+
 }  // namespace trace_dev
 
 // ---------------------------------------------------------------------------
@@ -707,9 +741,40 @@ static void launch_gather_plane(const uint8_t* src, uint8_t* dst, uint64_t src_r
     launch_gather_plane_t<uint8_t>(src, dst, src_rows, dst_rows, row_bytes, row_index, stream);
 }
 
+// One launch for every plane when all move in 16-byte words and one pass
+// fits the grid limit; otherwise one launch per plane with its widest word.
+static bool launch_gather_fused(const uint8_t* const (&src)[3], uint8_t* const (&dst)[3], const uint64_t (&row_bytes)[3],
+                                uint32_t nplanes, uint64_t src_rows, uint64_t dst_rows, const int64_t* row_index,
+                                hipStream_t stream) {
+  GatherPlanes P{};
+  uint64_t wg = 0;
+  for (uint32_t k = 0; k < nplanes; ++k) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(src[k]) | reinterpret_cast<uintptr_t>(dst[k]) |
+                        (uintptr_t)row_bytes[k];
+    if ((a & 15) != 0) return false;
+    const uint64_t wpr = row_bytes[k] / 16;
+    const uint64_t rpw = wpr >= kThreads ? 1 : kThreads / wpr;
+    if (wpr > 0xffffffffull) return false;
+    P.p[k] = GatherPlane{reinterpret_cast<const uint4*>(src[k]), reinterpret_cast<uint4*>(dst[k]), (uint32_t)wpr,
+                         (uint32_t)rpw, (uint32_t)wg};
+    wg += (dst_rows + rpw - 1) / rpw;
+    if (wg > kMaxGroups) return false;
+  }
+  P.count = nplanes;
+  hipLaunchKernelGGL(gather_planes_kernel, dim3((unsigned)wg), dim3(kThreads), 0, stream, P, src_rows, dst_rows,
+                     row_index);
+  return true;
+}
+
 hipError_t launch_gather_records(const uint8_t* bits_src, const uint8_t* scales_src, const uint8_t* codes_src,
                                  uint64_t src_rows, uint64_t cols, const int64_t* row_index, uint64_t dst_rows,
                                  uint8_t* bits_dst, uint8_t* scales_dst, uint8_t* codes_dst, hipStream_t stream) {
+  if (dst_rows == 0 || cols == 0) return hipSuccess;  // nothing to move
+  const uint8_t* const src[3] = {bits_src, scales_src, codes_src};
+  uint8_t* const dst[3] = {bits_dst, scales_dst, codes_dst};
+  const uint64_t row_bytes[3] = {cols / 8, cols / 16, cols / 2};
+  if (launch_gather_fused(src, dst, row_bytes, codes_dst ? 3u : 2u, src_rows, dst_rows, row_index, stream))
+    return hipGetLastError();
   launch_gather_plane(bits_src, bits_dst, src_rows, dst_rows, cols / 8, row_index, stream);
   launch_gather_plane(scales_src, scales_dst, src_rows, dst_rows, cols / 16, row_index, stream);
   if (codes_dst) launch_gather_plane(codes_src, codes_dst, src_rows, dst_rows, cols / 2, row_index, stream);
