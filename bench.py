@@ -292,6 +292,13 @@ def main():
         "full_nvfp4_bytes_40_layers": TOTAL_LAYERS * (n // 2 + n // 16),
     }
     cache["ratio"] = round(cache["full_nvfp4_bytes_40_layers"] / cache["compact_bytes_20_layers"], 4)
+    # layer-selection policies (5 / 20 / 40 captured layers) and b cached low
+    # bits: b bit-planes + one scale byte per 16 elements + a 4-byte tensor
+    # scale per captured site, against full NVFP4 codes for all 40 layers
+    full40 = TOTAL_LAYERS * (n // 2 + n // 16 + 4)
+    cache["policies"] = [{"captured_layers": lc, "bits": b, "bytes": lc * (b * n // 8 + n // 16 + 4),
+                          "ratio_vs_full_40": round(full40 / (lc * (b * n // 8 + n // 16 + 4)), 4)}
+                         for lc in (5, 20, 40) for b in (1, 2, 3, 4)]
 
     result = {
         "metric": METRIC,
