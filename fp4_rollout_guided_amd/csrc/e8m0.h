@@ -3,7 +3,8 @@
 // byte b stands for 2^(b - 127), 0xFF is NaN.  A block's shared exponent is
 // floor(log2(amax)) minus the exponent of the element format's largest
 // normal, clamped to E8M0's range.  A lane owns one 16-element half of a
-// 32-element block; lane pairs combine their halves' maxima.
+// 32-element block; lane pairs combine their halves' maxima (pair_swap, in
+// fp4_block.h).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -49,11 +50,6 @@ __device__ __forceinline__ uint32_t half_amax_bits(const uint32_t (&w)[8]) {
   const int lo = best.x, hi = best.y;
   const int m = lo > hi ? lo : hi;
   return m > 0x7f ? (uint32_t)(m - 0x7f) : 0u;
-}
-
-// The partner lane's value (lane ^ 1): a DPP quad permutation [1, 0, 3, 2].
-__device__ __forceinline__ uint32_t pair_swap(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
 }
 
 }  // namespace trace_dev

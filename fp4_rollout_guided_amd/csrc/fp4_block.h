@@ -1,10 +1,12 @@
-// Format-independent block machinery of the libtrace kernels (gfx950):
-// 16-element E2M1 code words held as two dwords of nibbles (even / odd
-// elements), the hardware FP4 conversions, the bit-plane packing, the
-// guided / full-information code selection, the decode to bf16 and the
-// exact per-element fallbacks.  Used by the NVFP4 kernels (kernels.hip) and
-// the MXFP4 kernels (mx_kernels.hip); a 32-element MXFP4 block is two
-// 16-element halves.
+// Format-independent block machinery of the libtrace kernels (gfx950): the
+// hardware FP4 conversions, the bit-plane packing, the guided /
+// full-information / low-bits code selection, the decode to bf16 and the
+// exact per-element fallbacks, for two lane layouts:
+//   - 8-element half blocks, codes as one dword of nibbles in element
+//     order: the NVFP4 kernels (kernels.hip), one 128-bit vector per lane;
+//   - 16 elements, codes as two dwords of nibbles (even / odd elements): the
+//     MXFP4 kernels (mx_kernels.hip, a 32-element block is two 16-element
+//     halves) and the diagnostics kernel (diag_kernels.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -62,6 +64,53 @@ __device__ __forceinline__ uint32_t fp4_rtz_at(uint32_t acc, float a, float b) {
     dst = CVT(dst, (v)[8 + (off)], (v)[10 + (off)], 2);  \
     dst = CVT(dst, (v)[12 + (off)], (v)[14 + (off)], 3); \
   } while (0)
+
+// The partner lane's value (lane ^ 1): a DPP quad permutation [1, 0, 3, 2].
+// Both lanes of the pair must be active.
+__device__ __forceinline__ uint32_t pair_swap(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+}
+
+// ---------------------------------------------------------------------------
+// 8-element half blocks (the NVFP4 kernels: one 128-bit vector of bf16 per
+// lane, codes as one dword of nibbles in element order, nibble j = element j)
+// ---------------------------------------------------------------------------
+
+// Element j (0..7) of a half block held as four packed bf16 pairs.
+__device__ __forceinline__ float half_elem(const uint32_t (&w)[4], int j) {
+  return (j & 1) ? bf16_hi(w[j >> 1]) : bf16_lo(w[j >> 1]);
+}
+
+// Bit j of an 8-bit word to bit 0 of nibble j.
+__device__ __forceinline__ uint32_t spread8(uint32_t x) {
+  x = (x | (x << 12)) & 0x000F000Fu;
+  x = (x | (x << 6)) & 0x03030303u;
+  return (x | (x << 3)) & 0x11111111u;
+}
+
+// Bit 0 of nibble j to bit j (the inverse of spread8).
+__device__ __forceinline__ uint32_t gather8(uint32_t c) {
+  c &= 0x11111111u;
+  c = (c | (c >> 3)) & 0x03030303u;
+  c = (c | (c >> 6)) & 0x000F000Fu;
+  return (c | (c >> 12)) & 0xFFu;
+}
+
+// Largest magnitude's bf16 bits over a half block (NaN and infinity compare
+// above every finite value: 0x7f80 and up).
+__device__ __forceinline__ uint32_t half_max_bits(const uint32_t (&w)[4]) {
+  uint32_t m0 = w[0] & 0x7fff7fffu;
+  u16x2 mx;
+  __builtin_memcpy(&mx, &m0, 4);
+#pragma unroll
+  for (int k = 1; k < 4; ++k) {
+    const uint32_t mk = w[k] & 0x7fff7fffu;
+    u16x2 v;
+    __builtin_memcpy(&v, &mk, 4);
+    mx = __builtin_elementwise_max(mx, v);
+  }
+  return mx.x > mx.y ? mx.x : mx.y;
+}
 
 // Bit 0 of the 16 nibbles of E (elements 0,2,..,14) and O (1,3,..,15),
 // gathered into a 16-bit word in element order.
@@ -272,6 +321,71 @@ __device__ __forceinline__ void decode_block(uint32_t QE, uint32_t QO, float s, 
   decode_scaled_pair<1>(QE, QO, s, out);
   decode_scaled_pair<2>(QE, QO, s, out);
   decode_scaled_pair<3>(QE, QO, s, out);
+}
+
+// Codes of q* for the 8 quotients of a half block, element order (nibble j =
+// element j), and the clip-mask bits (bit j set when |q_j| <= 6).  kMode 0:
+// round to nearest even; 1: guided by the cached bits (bit j = element j);
+// 2: full information (rollout codes, same layout as the result); 3: b
+// cached low bits (residue nibbles, same layout) with rule lb.
+template <int kMode>
+__device__ __forceinline__ uint32_t select_codes8(const float (&q)[8], uint32_t cached, uint32_t roll, uint32_t& Q,
+                                                  const LowBitsRule& lb = LowBitsRule{}) {
+  uint32_t clip = 0;
+#pragma unroll
+  for (int j = 7; j >= 0; --j)
+    clip = __builtin_amdgcn_alignbit(clip, __float_as_uint(6.0f - fabsf(q[j])), 31);
+  float qc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) qc[j] = __builtin_amdgcn_fmed3f(q[j], -6.0f, 6.0f);
+  if (kMode == 0) {
+    Q = 0;
+    Q = FP4_RNE(Q, qc[0], qc[1], 0);
+    Q = FP4_RNE(Q, qc[2], qc[3], 1);
+    Q = FP4_RNE(Q, qc[4], qc[5], 2);
+    Q = FP4_RNE(Q, qc[6], qc[7], 3);
+  } else {
+    // floor codes of q and of its predecessor toward zero: equal exactly when
+    // q lies strictly inside a bracket, so the upper endpoint is floor + 1
+    float pv[8];  // predecessors toward zero (a NaN for +-0, whose floor code differs)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pv[j] = __uint_as_float(__float_as_uint(qc[j]) - 1u);
+    uint32_t F = 0, P = 0;
+    F = FP4_RTZ(F, qc[0], qc[1], 0);
+    F = FP4_RTZ(F, qc[2], qc[3], 1);
+    F = FP4_RTZ(F, qc[4], qc[5], 2);
+    F = FP4_RTZ(F, qc[6], qc[7], 3);
+    P = FP4_RTZ(P, pv[0], pv[1], 0);
+    P = FP4_RTZ(P, pv[2], pv[3], 1);
+    P = FP4_RTZ(P, pv[4], pv[5], 2);
+    P = FP4_RTZ(P, pv[6], pv[7], 3);
+    if (kMode == 1) {
+      uint32_t t = F ^ P;
+      t |= t >> 2;
+      t |= t >> 1;  // bit 0 per nibble: q is a codeword
+      Q = F + (~t & (F ^ spread8(cached)) & 0x11111111u);
+    } else if (kMode == 2) {
+      Q = full_info_select(F, P, roll);
+    } else {
+      Q = lowbits_select(F, P, roll, lb);
+    }
+  }
+  return ~clip & 0xffu;
+}
+
+template <int K>
+__device__ __forceinline__ void decode_pair8(uint32_t Q, float s, uint32_t (&out)[4]) {
+  const f32x2 f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(Q, 1.0f, K);  // elements 2K, 2K + 1
+  const bf16x2 p = __builtin_convertvector((f32x2){s * f.x, s * f.y}, bf16x2);
+  __builtin_memcpy(&out[K], &p, 4);
+}
+
+// y for the 8 codes of a half block: bf16_RNE(fl32(s * q)), 4 packed pairs.
+__device__ __forceinline__ void decode_half(uint32_t Q, float s, uint32_t (&out)[4]) {
+  decode_pair8<0>(Q, s, out);
+  decode_pair8<1>(Q, s, out);
+  decode_pair8<2>(Q, s, out);
+  decode_pair8<3>(Q, s, out);
 }
 
 // ---------------------------------------------------------------------------
