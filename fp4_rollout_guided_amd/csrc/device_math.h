@@ -38,12 +38,12 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
 }
 
 // OCP E4M3FN byte -> value.  Only 0x00..0x7E are scales; 0x7F (NaN) and the
-// negative bytes make the block a zero-scale block, signalled by NaN.
+// negative bytes make the block a zero-scale block, signalled by NaN.  The
+// hardware conversion decodes the byte exactly (subnormals m * 2^-9, normals
+// (1 + m/8) 2^(e-7)); a select replaces the other bytes, without a branch.
 __device__ __forceinline__ float e4m3_decode(uint32_t b) {
-  if (b >= 0x7fu) return __uint_as_float(0x7fc00000u);
-  const uint32_t e = b >> 3, m = b & 7u;
-  if (e == 0) return (float)m * 0x1p-9f;        // subnormals m * 2^-9
-  return __uint_as_float(((e + 120u) << 23) | (m << 20));  // (1 + m/8) 2^(e-7)
+  const float v = __builtin_amdgcn_cvt_f32_fp8((int)b, 0);
+  return b < 0x7fu ? v : __uint_as_float(0x7fc00000u);
 }
 
 // Non-negative fp32 (or NaN) -> E4M3FN byte, round to nearest even,
