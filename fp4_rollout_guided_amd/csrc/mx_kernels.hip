@@ -6,12 +6,14 @@
 // NaN), E2M1 elements.  The block scale is 2^(floor(log2(amax)) - 2) clamped
 // to E8M0's range; elements are rounded as on the NVFP4 path.
 //
-// A lane owns one 16-element half of a block -- the same 32 contiguous bytes
-// of bf16, 16-bit bit-plane words and 8 bytes of codes as on the NVFP4 path
-// -- and lane pairs share a block's scale: the pair exchanges its halves'
-// maxima with one DPP move.  (A lane per 32-element block was measured ~15%
-// slower: its 64-byte stride doubles the cache lines each load instruction
-// touches.)  Dividing by a power of two is a multiplication
+// In the capture a lane owns one 16-element half of a block (32 contiguous
+// bytes of bf16, a 16-bit bit-plane word, 8 bytes of codes) and lane pairs
+// share a block's scale: the pair exchanges its halves' maxima with one DPP
+// move.  (A lane per 32-element block was measured ~15% slower: its 64-byte
+// stride doubles the cache lines each load instruction touches.)  The
+// forwards run one lane per 8-element vector (a quarter block: one 128-bit
+// load, one byte of bits and of mask, one dword of codes), which streams
+// faster still.  Dividing by a power of two is a multiplication
 // by its exact inverse: x * 2^(127 - b) is the correctly rounded x / s, also
 // where it underflows, so there is no division at all.  Blocks holding a NaN
 // or an infinity, or whose quotients overflow, run the exact per-element
@@ -28,7 +30,7 @@ namespace trace_dev {
 
 // ---------------------------------------------------------------------------
 // exact fallbacks (IEEE division, one element at a time) for one lane's
-// 16-element half of a block whose scale byte is already known
+// elements (a capture half, a forward vector) whose scale byte is known
 // ---------------------------------------------------------------------------
 __device__ __noinline__ void mx_capture_half_exact(const uint4* __restrict__ x4, uint64_t h, uint32_t sb,
                                                    uint16_t* __restrict__ bits, uint2* __restrict__ codes) {
@@ -46,28 +48,28 @@ __device__ __noinline__ void mx_capture_half_exact(const uint4* __restrict__ x4,
   if (codes) codes[h] = make_uint2((uint32_t)cw, (uint32_t)(cw >> 32));
 }
 
-__device__ __noinline__ void mx_fakequant_half_exact(int mode, const uint4* __restrict__ x4, uint64_t h,
-                                                     uint32_t sbyte, uint32_t cached, uint2 roll,
-                                                     uint4* __restrict__ y4, uint16_t* __restrict__ mask,
-                                                     uint2* __restrict__ qcodes) {
+// The same for one 8-element vector g (elements 8g..8g+7) of the forward:
+// cached = its 8 bits, roll = its rollout codes (element order).
+__device__ __noinline__ void mx_fakequant_vec_exact(int mode, const uint4* __restrict__ x4, uint64_t g,
+                                                    uint32_t sbyte, uint32_t cached, uint32_t roll,
+                                                    uint4* __restrict__ y4, uint8_t* __restrict__ mask,
+                                                    uint32_t* __restrict__ qcodes) {
   const bool valid = sbyte != 0xffu;
   const float s = valid ? e8m0_value(sbyte) : 1.f;
-  const uint16_t* x = reinterpret_cast<const uint16_t*>(x4) + 16 * h;
-  uint16_t* y = reinterpret_cast<uint16_t*>(y4) + 16 * h;
-  uint32_t maskword = 0;
-  uint64_t cw = 0;
+  const uint16_t* x = reinterpret_cast<const uint16_t*>(x4) + 8 * g;
+  uint16_t* y = reinterpret_cast<uint16_t*>(y4) + 8 * g;
+  uint32_t maskbyte = 0, cw = 0;
 #pragma unroll 1
-  for (int j = 0; j < 16; ++j) {
-    const uint32_t rc = ((j < 8 ? roll.x : roll.y) >> (4 * (j & 7))) & 15u;
+  for (int j = 0; j < 8; ++j) {
     uint32_t code, mk, ybits;
-    exact_forward_element(mode, __uint_as_float((uint32_t)x[j] << 16), s, valid, (cached >> j) & 1u, rc, code, mk,
-                          ybits);
-    maskword |= mk << j;
+    exact_forward_element(mode, __uint_as_float((uint32_t)x[j] << 16), s, valid, (cached >> j) & 1u,
+                          (roll >> (4 * j)) & 15u, code, mk, ybits);
+    maskbyte |= mk << j;
     y[j] = (uint16_t)ybits;
-    cw |= (uint64_t)code << (4 * j);
+    cw |= code << (4 * j);
   }
-  mask[h] = (uint16_t)maskword;
-  if (qcodes) qcodes[h] = make_uint2((uint32_t)cw, (uint32_t)(cw >> 32));
+  mask[g] = (uint8_t)maskbyte;
+  if (qcodes) qcodes[g] = cw;
 }
 
 // ---------------------------------------------------------------------------
@@ -114,48 +116,46 @@ __global__ __launch_bounds__(kThreads) void mx_capture_kernel(const uint4* __res
 
 // ---------------------------------------------------------------------------
 // fake-quant forward; kMode: 0 = RNE, 1 = guided, 2 = full information.  One
-// lane per 16-element half; both lanes of a block read its scale byte.
+// lane per 8-element vector (one 128-bit load; a quarter of a block): a lane
+// with one vector in flight streams faster than one moving 32 bytes.  The
+// four lanes of a block read its scale byte.
 // ---------------------------------------------------------------------------
 template <int kMode>
-__global__ __launch_bounds__(kThreads) void mx_fakequant_kernel(const uint4* __restrict__ x, uint64_t nhalves,
+__global__ __launch_bounds__(kThreads) void mx_fakequant_kernel(const uint4* __restrict__ x, uint64_t nvec,
                                                                 const uint8_t* __restrict__ scales,
-                                                                const uint16_t* __restrict__ bits,
-                                                                const uint2* __restrict__ rcodes,
-                                                                uint4* __restrict__ y, uint16_t* __restrict__ mask,
-                                                                uint2* __restrict__ qcodes) {
+                                                                const uint8_t* __restrict__ bits,
+                                                                const uint32_t* __restrict__ rcodes,
+                                                                uint4* __restrict__ y, uint8_t* __restrict__ mask,
+                                                                uint32_t* __restrict__ qcodes) {
   const uint64_t stride = (uint64_t)gridDim.x * kThreads;
-  for (uint64_t h = (uint64_t)blockIdx.x * kThreads + threadIdx.x; h < nhalves; h += stride) {
-    const uint32_t sbyte = scales[h >> 1];
-    const uint32_t cached = kMode == 1 ? (uint32_t)bits[h] : 0u;
-    const uint2 roll = kMode == 2 ? rcodes[h] : make_uint2(0u, 0u);
-    uint32_t w[8];
-    load_block(x, h, w);
+  for (uint64_t g = (uint64_t)blockIdx.x * kThreads + threadIdx.x; g < nvec; g += stride) {
+    const uint32_t sbyte = scales[g >> 2];
+    const uint32_t cached = kMode == 1 ? (uint32_t)bits[g] : 0u;
+    const uint32_t roll = kMode == 2 ? rcodes[g] : 0u;
+    const uint4 v = x[g];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     // a NaN scale byte makes a zero-scale block: multiplying by 0 maps every
     // finite x to a zero of its own sign, decoded with s = 1
     const bool valid = sbyte != 0xffu;
     const float inv = valid ? e8m0_inverse(sbyte) : 0.f;
     const float s = valid ? e8m0_value(sbyte) : 1.f;
     bool bad = false;
-    float q[16];
+    float q[8];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      q[j] = block_elem(w, j) * inv;
+    for (int j = 0; j < 8; ++j) {
+      q[j] = half_elem(w, j) * inv;
       bad |= __builtin_amdgcn_class(q[j], kBadClass);
     }
-    uint32_t QE, QO;
-    const uint32_t keep = select_codes<kMode>(q, cached, roll, QE, QO);
+    uint32_t Q;
+    const uint32_t keep = select_codes8<kMode>(q, cached, roll, Q);
     if (bad) {
-      mx_fakequant_half_exact(kMode, x, h, sbyte, cached, roll, y, mask, qcodes);
+      mx_fakequant_vec_exact(kMode, x, g, sbyte, cached, roll, y, mask, qcodes);
     } else {
-      uint32_t out[8];
-      decode_block(QE, QO, s, out);
-      store_block(y, h, out);
-      mask[h] = (uint16_t)(valid ? keep : 0u);
-      if (qcodes) {
-        uint32_t c0, c1;
-        interleave_codes(QE, QO, c0, c1);
-        qcodes[h] = make_uint2(c0, c1);
-      }
+      uint32_t out[4];
+      decode_half(Q, s, out);
+      y[g] = make_uint4(out[0], out[1], out[2], out[3]);
+      mask[g] = (uint8_t)(valid ? keep : 0u);
+      if (qcodes) qcodes[g] = Q;
     }
   }
 }
@@ -185,21 +185,20 @@ hipError_t launch_mx_fakequant(int mode, const uint16_t* x, uint64_t nblocks, co
                                const uint8_t* side, uint16_t* y, uint8_t* mask, uint8_t* qcodes,
                                hipStream_t stream) {
   if (nblocks == 0) return hipSuccess;  // an empty grid is not a valid launch
-  const uint64_t nhalves = 2 * nblocks;
+  const uint64_t nvec = 4 * nblocks;
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   uint4* yv = reinterpret_cast<uint4*>(y);
-  uint16_t* mv = reinterpret_cast<uint16_t*>(mask);
-  uint2* qv = reinterpret_cast<uint2*>(qcodes);
-  const dim3 grid(mx_grid(nhalves)), block(kThreads);
+  uint32_t* qv = reinterpret_cast<uint32_t*>(qcodes);
+  const dim3 grid(mx_grid(nvec)), block(kThreads);
   if (mode == 1)
-    hipLaunchKernelGGL(mx_fakequant_kernel<1>, grid, block, 0, stream, xv, nhalves, scales,
-                       reinterpret_cast<const uint16_t*>(side), static_cast<const uint2*>(nullptr), yv, mv, qv);
+    hipLaunchKernelGGL(mx_fakequant_kernel<1>, grid, block, 0, stream, xv, nvec, scales, side,
+                       static_cast<const uint32_t*>(nullptr), yv, mask, qv);
   else if (mode == 2)
-    hipLaunchKernelGGL(mx_fakequant_kernel<2>, grid, block, 0, stream, xv, nhalves, scales,
-                       static_cast<const uint16_t*>(nullptr), reinterpret_cast<const uint2*>(side), yv, mv, qv);
+    hipLaunchKernelGGL(mx_fakequant_kernel<2>, grid, block, 0, stream, xv, nvec, scales,
+                       static_cast<const uint8_t*>(nullptr), reinterpret_cast<const uint32_t*>(side), yv, mask, qv);
   else
-    hipLaunchKernelGGL(mx_fakequant_kernel<0>, grid, block, 0, stream, xv, nhalves, scales,
-                       static_cast<const uint16_t*>(nullptr), static_cast<const uint2*>(nullptr), yv, mv, qv);
+    hipLaunchKernelGGL(mx_fakequant_kernel<0>, grid, block, 0, stream, xv, nvec, scales,
+                       static_cast<const uint8_t*>(nullptr), static_cast<const uint32_t*>(nullptr), yv, mask, qv);
   return hipGetLastError();
 }
 
