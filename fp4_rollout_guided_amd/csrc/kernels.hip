@@ -480,9 +480,11 @@ __device__ __forceinline__ void fakequant_one(const uint4* __restrict__ x, uint6
   }
 }
 
-// kMode: 0 = RNE, 1 = guided by the cached bit, 2 = full information.
-template <int kMode, bool kGrouped>
-__global__ __launch_bounds__(kThreads) void fakequant_kernel(const uint4* __restrict__ x, uint64_t nblocks,
+// The per-expert forwards (one tensor scale per group of rows); kMode: 0 =
+// RNE, 1 = guided by the cached bit, 2 = full information.  One lane per
+// block, so one wave-uniform group search serves 64 blocks.
+template <int kMode>
+__global__ __launch_bounds__(kThreads) void fakequant_grouped_kernel(const uint4* __restrict__ x, uint64_t nblocks,
                                                              const uint8_t* __restrict__ scales,
                                                              const float* __restrict__ ts_ptr, RowGroups groups,
                                                              const uint16_t* __restrict__ bits,
@@ -490,7 +492,6 @@ __global__ __launch_bounds__(kThreads) void fakequant_kernel(const uint4* __rest
                                                              uint4* __restrict__ y,
                                                              uint16_t* __restrict__ mask,
                                                              uint2* __restrict__ qcodes) {
-  const float ts0 = kGrouped ? 0.f : *ts_ptr;
   const uint64_t stride = (uint64_t)gridDim.x * kThreads;
   for (uint64_t b = (uint64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks; b += stride) {
     const uint32_t sbyte = scales[b];
@@ -498,7 +499,7 @@ __global__ __launch_bounds__(kThreads) void fakequant_kernel(const uint4* __rest
     const uint2 roll = kMode == 2 ? rcodes[b] : make_uint2(0u, 0u);
     uint32_t w[8];
     load_block(x, b, w);  // all loads are issued before the group search
-    const float ts = kGrouped ? group_tensor_scale(groups, ts_ptr, b) : ts0;
+    const float ts = group_tensor_scale(groups, ts_ptr, b);
     fakequant_one<kMode>(x, b, w, sbyte, cached, roll, ts, y, mask, qcodes);
   }
 }
@@ -753,19 +754,19 @@ hipError_t launch_lowbits_fakequant(const uint16_t* x, uint64_t nblocks, const u
   return hipGetLastError();
 }
 
-template <bool kGrouped>
-static void launch_fakequant_t(int mode, const uint4* xv, uint64_t nblocks, const uint8_t* scales,
-                               const float* ts, const RowGroups& rg, const uint8_t* side, uint4* yv, uint16_t* mv,
-                               uint2* qv, hipStream_t stream) {
+// Per-expert forwards: one lane per block.
+static void launch_fakequant_grouped(int mode, const uint4* xv, uint64_t nblocks, const uint8_t* scales,
+                                     const float* ts, const RowGroups& rg, const uint8_t* side, uint4* yv,
+                                     uint16_t* mv, uint2* qv, hipStream_t stream) {
   const dim3 grid(grid_for(nblocks)), block(kThreads);
   if (mode == 1)
-    hipLaunchKernelGGL((fakequant_kernel<1, kGrouped>), grid, block, 0, stream, xv, nblocks, scales, ts, rg,
+    hipLaunchKernelGGL(fakequant_grouped_kernel<1>, grid, block, 0, stream, xv, nblocks, scales, ts, rg,
                        reinterpret_cast<const uint16_t*>(side), static_cast<const uint2*>(nullptr), yv, mv, qv);
   else if (mode == 2)
-    hipLaunchKernelGGL((fakequant_kernel<2, kGrouped>), grid, block, 0, stream, xv, nblocks, scales, ts, rg,
+    hipLaunchKernelGGL(fakequant_grouped_kernel<2>, grid, block, 0, stream, xv, nblocks, scales, ts, rg,
                        static_cast<const uint16_t*>(nullptr), reinterpret_cast<const uint2*>(side), yv, mv, qv);
   else
-    hipLaunchKernelGGL((fakequant_kernel<0, kGrouped>), grid, block, 0, stream, xv, nblocks, scales, ts, rg,
+    hipLaunchKernelGGL(fakequant_grouped_kernel<0>, grid, block, 0, stream, xv, nblocks, scales, ts, rg,
                        static_cast<const uint16_t*>(nullptr), static_cast<const uint2*>(nullptr), yv, mv, qv);
 }
 
@@ -793,7 +794,7 @@ hipError_t launch_fakequant(int mode, const uint16_t* x, uint64_t nblocks, const
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   uint4* yv = reinterpret_cast<uint4*>(y);
   if (g)
-    launch_fakequant_t<true>(mode, xv, nblocks, scales, ts, row_groups(*g, nblocks), side, yv,
+    launch_fakequant_grouped(mode, xv, nblocks, scales, ts, row_groups(*g, nblocks), side, yv,
                              reinterpret_cast<uint16_t*>(mask), reinterpret_cast<uint2*>(qcodes), stream);
   else
     launch_fakequant_half(mode, xv, nblocks, scales, ts, side, yv, mask, reinterpret_cast<uint32_t*>(qcodes), stream);

@@ -5,7 +5,8 @@ workload sizes where the oracle runs on sampled rows only:
 
 * y = bf16_RNE(fl32(s * q)) for the codes q each forward reports, with
   s = fl32(E4M3FN(scale byte) * ts) (the decode step; torch's float8 decode,
-  float32 multiply and bfloat16 cast are exact / IEEE round to nearest even);
+  float32 multiply and bfloat16 cast are exact / IEEE round to nearest even),
+  ts being the tensor scale or, with per-expert scales, the row's group's;
 * the clip mask does not depend on the rounding rule (guided, RNE and full
   information report the same mask), and the STE backward passes exactly the
   masked gradient (+0 elsewhere);
@@ -50,18 +51,27 @@ def check_nvfp4_outputs(ctx, x_roll, x_train, grad, ts, out, chunk=1 << 26):
     """``out``: device tensors scales, bits, codes, y_g, mask_g, q_g, y_r,
     mask_r, q_r, y_f, mask_f, q_f, gin (the latter three groups from the
     guided, RNE and full-information forwards; gin = STE backward of the
-    guided mask).  Raises AssertionError naming the first failing property."""
+    guided mask).  ``ts``: the tensor scale (one element), or one per row
+    (per-expert scales: the scale of each row's group).  Raises
+    AssertionError naming the first failing property."""
     n = x_roll.numel()
+    cols = x_roll.shape[-1]
     dev = x_roll.device
+    per_row = ts.numel() > 1
     table = torch.tensor(E2M1, dtype=torch.float32, device=dev)
     xr = x_roll.reshape(-1).view(torch.int16)
     xt = x_train.reshape(-1).view(torch.int16)
     g = grad.reshape(-1).view(torch.int16)
-    ts32 = ts.reshape(1).float()
+    ts32 = ts.reshape(-1).float()
     for lo in range(0, n, chunk):
         hi = min(n, lo + chunk)
         sb = out["scales"][lo // 16: hi // 16]
-        s = sb.view(torch.float8_e4m3fn).float() * ts32                  # fl32(E4M3FN(sb) * ts)
+        if per_row:
+            blk = torch.arange(lo // 16, hi // 16, device=dev)
+            tsb = ts32[(blk * 16) // cols]
+        else:
+            tsb = ts32
+        s = sb.view(torch.float8_e4m3fn).float() * tsb                   # fl32(E4M3FN(sb) * ts)
         valid = (sb < 0x7F) & (s > 0) & torch.isfinite(s)
         s_el = torch.where(valid, s, torch.ones_like(s)).repeat_interleave(16)
         codes = {k: _nibbles(out[f"q_{k}"], lo, hi) for k in ("g", "r", "f")}

@@ -16,6 +16,7 @@ import torch
 import oracle
 import workloads
 from oracle import formats as F
+from tests.full_props import check_nvfp4_outputs
 from tests.gpu_util import from_np_u16, to_np_u8, to_np_u16
 
 pytestmark = pytest.mark.gpu
@@ -175,3 +176,11 @@ def test_moe_expert_site_per_expert_scales(device):
     _compare(sampled, want, "expert site")
     _say(f"  expert site: {idx.size} sampled rows over {int((np.diff(off) > 0).sum())} experts, "
          f"ts range {ts.min():.3e}..{ts.max():.3e}")
+    # every element of every output against the whole-tensor properties, with
+    # each row's own group scale
+    import fp4_rollout_guided_amd as tr
+    grad = workloads.grad_for(x_roll.shape, device, 1, "expert_in")
+    got["gin"] = tr.ste_bwd(grad, got["mask_g"])
+    row_ts = got["ts"].repeat_interleave(torch.from_numpy(np.diff(off)).to(device))
+    torch.cuda.synchronize()
+    check_nvfp4_outputs("expert site", x_roll, x_train, grad, row_ts, got)
