@@ -13,14 +13,24 @@
 //                           against the rollout code, accumulated into a
 //                           histogram of signed grid steps and four counters.
 //
-// One lane owns one 16-element block, as in the forwards.  Counts live in
-// registers per lane (steps 0 and 1, the four counters) and in a
-// workgroup-shared table (steps 2..14, rare); after the grid-stride loop each
-// wave folds its registers with cross-lane adds, one lane per wave adds them
-// to the shared table, and the workgroup adds the table to the 64-bit device
+// One lane owns one 16-element block, as in the forwards.  The four code
+// words of a block (rollout, RNE, guided, full information; even and odd
+// elements in separate dwords, eight nibbles each) are compared with
+// nibble-parallel integer arithmetic: a code's signed grid index is shifted
+// by 7 into a nibble 0..14 (both zeros map to 7), equality and one-step
+// neighbours become per-nibble zero tests, and counts are population counts.
+// That covers every element whose rollout and RNE codes are at most one step
+// apart and whose guided and RNE codes are too; a block with any other
+// element (a two-step mismatch, rare) is counted element by element.  Counts
+// live in registers per lane (steps 0 and 1, the four counters) and in a
+// workgroup-shared table (steps 2..14); after the grid-stride loop each wave
+// folds its registers with cross-lane adds, one lane per wave adds them to
+// the shared table, and the workgroup adds the table to the 64-bit device
 // counters with vector-memory atomics.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <atomic>
 
 #include "device_math.h"
 #include "fp4_block.h"
@@ -30,6 +40,48 @@
 namespace trace_dev {
 
 constexpr int kStatWords = 20;  // see the layout in launch.h
+
+constexpr uint32_t kNib3 = 0x88888888u;  // bit 3 of every nibble
+constexpr uint32_t kOnes = 0x11111111u;
+
+// 7 + signed grid index of every code nibble (sign << 3 | magnitude index).
+__device__ __forceinline__ uint32_t offset_index(uint32_t c) {
+  const uint32_t m = c & 0x77777777u;
+  const uint32_t sb = c & kNib3;
+  const uint32_t neg = sb | (sb - (sb >> 3));  // 0xF in negative nibbles, no borrows
+  // 7 - m and 7 + m stay within their nibble (m <= 7)
+  return (neg & (0x77777777u - m)) | (~neg & (m + 0x77777777u));
+}
+
+// Bit 3 of each nibble set where that nibble of x is zero.
+__device__ __forceinline__ uint32_t zero_nibbles(uint32_t x) {
+  return ~(((x & 0x77777777u) + 0x77777777u) | x) & kNib3;
+}
+
+// Per-nibble flags of one code dword pair; false when some element needs the
+// per-element count.
+struct NibbleStats {
+  uint32_t same, one, straddle, crossed, recovered, violation;
+};
+
+__device__ __forceinline__ bool nibble_stats(uint32_t r, uint32_t n, uint32_t g, uint32_t f, NibbleStats& o) {
+  const uint32_t ur = offset_index(r), un = offset_index(n), ug = offset_index(g), uf = offset_index(f);
+  const uint32_t same = zero_nibbles(ur ^ un);               // rollout == RNE
+  const uint32_t up = zero_nibbles(ur ^ (un + kOnes));       // rollout one step above RNE
+  const uint32_t down = zero_nibbles(un ^ (ur + kOnes));     // rollout one step below RNE
+  const uint32_t g_eq = zero_nibbles(ug ^ un);               // guided == RNE
+  const uint32_t g_up = zero_nibbles(ug ^ (un + kOnes));     // guided one step above RNE
+  const uint32_t g_down = zero_nibbles(un ^ (ug + kOnes));   // guided one step below RNE
+  o.same = same;
+  o.one = up | down;
+  o.straddle = ~same & zero_nibbles(uf ^ ur) & kNib3;
+  o.crossed = o.one & ~o.straddle;
+  o.recovered = ~same & zero_nibbles(ug ^ ur) & kNib3;
+  // guided and RNE adjacent: the guided value is farther from the rollout
+  // codeword exactly when the rollout lies on the RNE side (or on it)
+  o.violation = (g_up & (same | down)) | (g_down & (same | up));
+  return ((same | o.one) & (g_eq | g_up | g_down)) == kNib3;
+}
 
 __device__ __forceinline__ int signed_idx(uint32_t c) {
   const int m = (int)(c & 7u);
@@ -43,14 +95,48 @@ __device__ __forceinline__ int twice_value(uint32_t c) {
   return (c & 8u) ? -m : m;
 }
 
+// Counts of one block by the definitions, one element at a time: steps of 2
+// or more go to the shared table; the rest come back packed five bits each
+// (steps 0, steps 1, straddle, crossed, recovered, violations).
+// Arguments: the code dwords of the even (suffix 0) and odd (suffix 1) elements.
+__device__ __noinline__ uint32_t count_block_slow(uint32_t r0, uint32_t r1, uint32_t n0, uint32_t n1, uint32_t g0,
+                                                  uint32_t g1, uint32_t f0, uint32_t f1, uint32_t* table) {
+  uint32_t packed = 0;
+#pragma unroll 1
+  for (int j = 0; j < 16; ++j) {
+    const bool odd = j >= 8;
+    const int sh = 4 * (j & 7);
+    const uint32_t cr = ((odd ? r1 : r0) >> sh) & 15u, cn = ((odd ? n1 : n0) >> sh) & 15u;
+    const uint32_t cg = ((odd ? g1 : g0) >> sh) & 15u, cf = ((odd ? f1 : f0) >> sh) & 15u;
+    const int sr = signed_idx(cr);
+    const int d = sr - signed_idx(cn);
+    const uint32_t steps = (uint32_t)(d < 0 ? -d : d);
+    if (steps >= 2) atomicAdd(&table[steps], 1u);
+    // the full-information code is the rollout's exactly when the rollout
+    // codeword is an endpoint of the bracket
+    const bool straddle = steps != 0 && signed_idx(cf) == sr;
+    const int vr = twice_value(cr);
+    const int dg = twice_value(cg) - vr, dn = twice_value(cn) - vr;
+    packed += (uint32_t)(steps == 0) + ((uint32_t)(steps == 1) << 5) + ((uint32_t)straddle << 10) +
+              ((uint32_t)(steps == 1 && !straddle) << 15) +
+              ((uint32_t)(steps != 0 && signed_idx(cg) == sr) << 20) +
+              ((uint32_t)((dg < 0 ? -dg : dg) > (dn < 0 ? -dn : dn)) << 25);
+  }
+  return packed;
+}
+
 // RNE, guided and full-information codes of one block (element order, 4
 // bits per element) by the definitions, for the lanes the fast path rejects.
-__device__ __noinline__ void stats_block_exact(const uint4* __restrict__ x4, uint64_t b, uint32_t sbyte, float ts,
-                                               uint32_t cached, uint2 roll, uint64_t (&cw)[3]) {
+struct BlockCodes {
+  uint64_t rne, guided, full;
+};
+
+__device__ __noinline__ BlockCodes stats_block_exact(const uint4* __restrict__ x4, uint64_t b, uint32_t sbyte,
+                                                     float ts, uint32_t cached, uint2 roll) {
   const float s = e4m3_decode(sbyte) * ts;
   const bool valid = s > 0.f && s <= 3.40282347e38f;
   const uint16_t* x = reinterpret_cast<const uint16_t*>(x4) + 16 * b;
-  cw[0] = cw[1] = cw[2] = 0;
+  uint64_t cw[3] = {0, 0, 0};
 #pragma unroll 1
   for (int j = 0; j < 16; ++j) {
     const float xv = __uint_as_float((uint32_t)x[j] << 16);
@@ -59,9 +145,11 @@ __device__ __noinline__ void stats_block_exact(const uint4* __restrict__ x4, uin
     for (int mode = 0; mode < 3; ++mode) {
       uint32_t code, mk, ybits;
       exact_forward_element(mode, xv, s, valid, (cached >> j) & 1u, rc, code, mk, ybits);
-      cw[mode] |= (uint64_t)code << (4 * j);
+      const uint64_t c = (uint64_t)code << (4 * j);
+      if (mode == 0) cw[0] |= c; else if (mode == 1) cw[1] |= c; else cw[2] |= c;
     }
   }
+  return BlockCodes{cw[0], cw[1], cw[2]};
 }
 
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
@@ -93,43 +181,37 @@ __global__ __launch_bounds__(kThreads) void mismatch_stats_kernel(const uint4* _
     float q[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) q[j] = div_fast<true>(block_elem(w, j), e, bad);
-    uint64_t cw[3];
+    // code dwords [even elements, odd elements]: rollout, RNE, guided, full information
+    uint32_t r[2], cn[2], cg[2], cf[2];
+    split_codes(roll.x, roll.y, r[0], r[1]);
     if (bad) {
-      stats_block_exact(x, b, sbyte, ts, cached, roll, cw);
+      const BlockCodes c = stats_block_exact(x, b, sbyte, ts, cached, roll);
+      split_codes((uint32_t)c.rne, (uint32_t)(c.rne >> 32), cn[0], cn[1]);
+      split_codes((uint32_t)c.guided, (uint32_t)(c.guided >> 32), cg[0], cg[1]);
+      split_codes((uint32_t)c.full, (uint32_t)(c.full >> 32), cf[0], cf[1]);
     } else {
-      uint32_t QE, QO, c0, c1;
-      select_codes<0>(q, cached, roll, QE, QO);
-      interleave_codes(QE, QO, c0, c1);
-      cw[0] = ((uint64_t)c1 << 32) | c0;
-      select_codes<1>(q, cached, roll, QE, QO);
-      interleave_codes(QE, QO, c0, c1);
-      cw[1] = ((uint64_t)c1 << 32) | c0;
-      select_codes<2>(q, cached, roll, QE, QO);
-      interleave_codes(QE, QO, c0, c1);
-      cw[2] = ((uint64_t)c1 << 32) | c0;
+      select_codes<0>(q, cached, roll, cn[0], cn[1]);
+      select_codes<1>(q, cached, roll, cg[0], cg[1]);
+      select_codes<2>(q, cached, roll, cf[0], cf[1]);
     }
-    const uint64_t rw = ((uint64_t)roll.y << 32) | roll.x;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint32_t r = (uint32_t)(rw >> (4 * j)) & 15u;
-      const uint32_t cn = (uint32_t)(cw[0] >> (4 * j)) & 15u;
-      const uint32_t cg = (uint32_t)(cw[1] >> (4 * j)) & 15u;
-      const uint32_t cf = (uint32_t)(cw[2] >> (4 * j)) & 15u;
-      const int sr = signed_idx(r);
-      const int d = sr - signed_idx(cn);
-      const uint32_t steps = (uint32_t)(d < 0 ? -d : d);
-      n0 += steps == 0;
-      n1 += steps == 1;
-      if (steps >= 2) atomicAdd(&table[steps], 1u);
-      // the full-information code is the rollout's exactly when the rollout
-      // codeword is an endpoint of the bracket
-      const bool straddle = steps != 0 && signed_idx(cf) == sr;
-      nst += straddle;
-      ncr += steps == 1 && !straddle;
-      nrec += steps != 0 && signed_idx(cg) == sr;
-      const int vr = twice_value(r);
-      const int dg = twice_value(cg) - vr, dn = twice_value(cn) - vr;
-      nvio += (dg < 0 ? -dg : dg) > (dn < 0 ? -dn : dn);
+    NibbleStats s0, s1;
+    const bool ok0 = nibble_stats(r[0], cn[0], cg[0], cf[0], s0);
+    const bool ok1 = nibble_stats(r[1], cn[1], cg[1], cf[1], s1);
+    if (ok0 && ok1) {
+      n0 += __builtin_popcount(s0.same) + __builtin_popcount(s1.same);
+      n1 += __builtin_popcount(s0.one) + __builtin_popcount(s1.one);
+      nst += __builtin_popcount(s0.straddle) + __builtin_popcount(s1.straddle);
+      ncr += __builtin_popcount(s0.crossed) + __builtin_popcount(s1.crossed);
+      nrec += __builtin_popcount(s0.recovered) + __builtin_popcount(s1.recovered);
+      nvio += __builtin_popcount(s0.violation) + __builtin_popcount(s1.violation);
+    } else {
+      const uint32_t p = count_block_slow(r[0], r[1], cn[0], cn[1], cg[0], cg[1], cf[0], cf[1], table);
+      n0 += p & 31u;
+      n1 += (p >> 5) & 31u;
+      nst += (p >> 10) & 31u;
+      ncr += (p >> 15) & 31u;
+      nrec += (p >> 20) & 31u;
+      nvio += (p >> 25) & 31u;
     }
     nel += 16;
   }
@@ -155,11 +237,36 @@ namespace trace_host {
 
 using namespace trace_dev;
 
+// Workgroups of the statistics kernel resident at once on the current device
+// (occupancy x compute units), cached per device.  Every workgroup ends with
+// atomic adds to the same twenty counters, so the grid is held to one
+// resident wave of workgroups that loop over the tensor: one workgroup per
+// 256 blocks would queue ~10^5 atomics per counter at one L2 channel.
+static uint32_t stats_resident_groups() {
+  constexpr uint32_t kDefault = 1024;  // should the queries fail (the launch then reports the error)
+  static std::atomic<uint32_t> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kDefault;
+  uint32_t v = cache[dev].load(std::memory_order_relaxed);
+  if (v) return v;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mismatch_stats_kernel, kThreads, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu <= 0 ||
+      cus <= 0)
+    return kDefault;
+  v = (uint32_t)per_cu * (uint32_t)cus;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
 hipError_t launch_mismatch_stats(const uint16_t* x, uint64_t nblocks, const uint8_t* scales, const float* ts,
                                  const uint8_t* bits, const uint8_t* codes, uint64_t* stats, hipStream_t stream) {
   if (nblocks == 0) return hipSuccess;  // an empty grid is not a valid launch
-  const uint64_t g = (nblocks + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL(mismatch_stats_kernel, dim3((unsigned)(g < kMaxGroups ? g : kMaxGroups)), dim3(kThreads), 0,
+  uint64_t g = (nblocks + kThreads - 1) / kThreads;
+  const uint64_t resident = stats_resident_groups();
+  if (g > resident) g = resident;
+  if (g > kMaxGroups) g = kMaxGroups;
+  hipLaunchKernelGGL(mismatch_stats_kernel, dim3((unsigned)g), dim3(kThreads), 0,
                      stream, reinterpret_cast<const uint4*>(x), nblocks, scales, ts,
                      reinterpret_cast<const uint16_t*>(bits), reinterpret_cast<const uint2*>(codes),
                      reinterpret_cast<unsigned long long*>(stats));

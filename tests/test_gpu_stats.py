@@ -62,6 +62,38 @@ def test_stats_small_shapes(device, shape, consistent):
     assert _gpu(xt, shape, scales, ts, roll, cbits, device) == want
 
 
+def _step_codes(rng, roll, frac):
+    """Move a fraction of the codes one signed grid step up or down (either
+    zero for index 0), so that rollout and training codes sit one step apart."""
+    out = roll.copy()
+    pick = np.flatnonzero(rng.random(roll.size) < frac)
+    m = (roll[pick] & 7).astype(np.int16)
+    si = np.where(roll[pick] & 8, -m, m) + rng.choice(np.array([-1, 1], np.int16), pick.size)
+    si = np.clip(si, -7, 7)
+    zero_sign = rng.integers(0, 2, pick.size).astype(np.uint8) << 3
+    out[pick] = np.where(si < 0, 8 | (-si), np.where(si == 0, zero_sign, si)).astype(np.uint8)
+    return out
+
+
+@pytest.mark.parametrize("consistent", [True, False])
+def test_stats_one_step_neighbours(device, consistent):
+    """Rollout codes one step from the training side's on 5% of the sites (the
+    nibble-parallel path: up, down, through zero), with cached bits from the
+    rollout codes or random (guided moving toward or away from the rollout)."""
+    _say("case stats one-step", consistent)
+    rng = np.random.default_rng(11 + consistent)
+    rows, cols = 96, 2048
+    v = rng.standard_t(4, (rows, cols)) * 0.5
+    xr = F.f32_to_bf16_rne(v.reshape(-1).astype(np.float32))
+    ts = oracle.tensor_scale(xr)
+    cap = oracle.capture(xr, ts, with_codes=True)
+    roll = _step_codes(rng, oracle.unpack_nibbles(cap["codes"], xr.size), 0.05)
+    cbits = (roll & 1) if consistent else rng.integers(0, 2, xr.size)
+    st = oracle.mismatch_stats(xr, cap["scales"], ts, oracle.pack_nibbles(roll), oracle.pack_bits(cbits.astype(np.uint8)))
+    assert st["hist"][1] > 1000 and (consistent or st["violations"] > 1000)
+    assert _gpu(xr, (rows, cols), cap["scales"], ts, roll, cbits, device) == _want(st)
+
+
 def test_stats_specials(device):
     """Crafted blocks (NaN, infinities, zeros, subnormals, huge values) with
     NaN and zero scale bytes and random rollout codes on 30% of the sites."""
