@@ -2,11 +2,13 @@
 // hardware FP4 conversions, the bit-plane packing, the guided /
 // full-information / low-bits code selection, the decode to bf16 and the
 // exact per-element fallbacks, for two lane layouts:
-//   - 8-element half blocks, codes as one dword of nibbles in element
-//     order: the NVFP4 kernels (kernels.hip), one 128-bit vector per lane;
-//   - 16 elements, codes as two dwords of nibbles (even / odd elements): the
-//     MXFP4 kernels (mx_kernels.hip, a 32-element block is two 16-element
-//     halves) and the diagnostics kernel (diag_kernels.hip).
+//   - 8 elements (one 128-bit vector) per lane, codes as one dword of nibbles
+//     in element order: the ungrouped NVFP4 forwards (half blocks,
+//     kernels.hip) and the MXFP4 forwards (quarter blocks, mx_kernels.hip);
+//   - 16 elements (two 128-bit vectors) per lane, codes as two dwords of
+//     nibbles (even / odd elements): the NVFP4 capture, per-expert and
+//     low-bits forwards (kernels.hip), the MXFP4 capture (a 32-element block
+//     is two 16-element halves) and the diagnostics kernel (diag_kernels.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>

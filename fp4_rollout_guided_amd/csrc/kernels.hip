@@ -2,7 +2,10 @@
 // full-information fake-quant forward, STE backward, per-expert (row-group)
 // variants of the tensor scale, capture and forwards, capture to and forward
 // from b cached low bits, and the record gather.  The MXFP4 kernels are in
-// mx_kernels.hip; the block machinery both share is in fp4_block.h.
+// mx_kernels.hip, the MXFP8 ones in mx8_kernels.hip and the agreement
+// statistics in diag_kernels.hip; the block machinery they share is in
+// fp4_block.h and the NVFP4 scale decode and exact division in
+// nvfp4_scale.h.
 //
 // Work decomposition: in the capture, the per-expert forwards and the
 // low-bits forward one lane owns one 16-element NVFP4 block, i.e. 32
@@ -16,7 +19,9 @@
 // forwards (one group lookup per lane) and the low-bits forward (more
 // dependent loads) measured slower that way.  The grid covers the tensor once
 // (one tile per workgroup); the kernels keep a grid-stride loop only for grids
-// larger than the launch limit.
+// larger than the launch limit.  The two amax passes are the exceptions: the
+// tensor amax loops a capped grid (one partial maximum per workgroup) and the
+// per-row amax gives each wave one row.
 //
 // Every kernel has an exact fast path and an exact fallback.  The fast path
 // computes each quotient x / s with a double-word reciprocal and one
@@ -307,8 +312,9 @@ __global__ __launch_bounds__(kThreads) void row_amax_kernel(const uint4* __restr
       uint4 v[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {  // four loads in flight before any is used
+        // past the row's end: its last vector again (a repeat leaves the maximum unchanged)
         const uint64_t c = c0 + 64 * u + lane;
-        v[u] = c < vec_per_row ? x[r * vec_per_row + c] : make_uint4(0u, 0u, 0u, 0u);
+        v[u] = x[r * vec_per_row + (c < vec_per_row ? c : vec_per_row - 1)];
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {

@@ -41,6 +41,8 @@ def _host(v):
         return to_np_u16(v)
     if v.dtype == torch.float32:
         return v.cpu().numpy().view(np.uint32)
+    if v.dtype == torch.int64:
+        return v.cpu().numpy()
     return to_np_u8(v)
 
 
@@ -83,6 +85,7 @@ def _everything(tr, xr, xt, g, offsets, perm):
     lsc, lpl, _ = tr.capture_lowbits(xr, ts, 3)
     y, m, q = tr.lowbits_fakequant_fwd(xt, lsc, ts, 3, lpl, want_codes=True)
     out.update(lsc=lsc, lpl=lpl, y_l=y, m_l=m, q_l=q)
+    out["stats"] = tr.mismatch_stats(xt, sc, ts, bt, cd)
     torch.cuda.synchronize()
     return {k: _host(v) for k, v in out.items()}
 
