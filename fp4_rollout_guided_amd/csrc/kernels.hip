@@ -169,18 +169,6 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v) {
 
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 
-// A 128-bit load with the non-temporal (streaming) hint, for the amax passes,
-// which read each byte once.  Measured in the full step, where the tensor
-// amax follows the STE backward's 1 GiB of stores: with plain loads the pass
-// absorbs most of that kernel's cache write-back and runs at 64% of 8 TB/s,
-// with streaming loads at 79%, the capture after it taking over part of the
-// write-back (the step gains ~1%).
-__device__ __forceinline__ uint4 load_stream(const uint4* p) {
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(t.x, t.y, t.z, t.w);
-}
-
 // The amax and STE kernels have no block structure, so their loads are fully
 // coalesced: a 4096-element tile is 512 128-bit vectors and lane t takes
 // vectors t and t + 256 (every load instruction covers 1 KiB contiguous).
@@ -194,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void amax_partial_kernel(const uint4* __r
     for (int h = 0; h < 2; ++h) {
       const uint64_t i = tile * 512 + 256 * h + threadIdx.x;
       if (i < nvec) {
-        const uint4 v = load_stream(x + i);
+        const uint4 v = x[i];
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -326,7 +314,7 @@ __global__ __launch_bounds__(kThreads) void row_amax_kernel(const uint4* __restr
       for (int u = 0; u < 4; ++u) {  // four loads in flight before any is used
         // past the row's end: its last vector again (a repeat leaves the maximum unchanged)
         const uint64_t c = c0 + 64 * u + lane;
-        v[u] = load_stream(x + r * vec_per_row + (c < vec_per_row ? c : vec_per_row - 1));
+        v[u] = x[r * vec_per_row + (c < vec_per_row ? c : vec_per_row - 1)];
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -454,7 +442,10 @@ __global__ __launch_bounds__(kThreads) void capture_kernel(const uint4* __restri
   const float r6lo = __builtin_fmaf(-6.0f, r6hi, 1.0f) * r6hi;
   const CaptureScale cs0 = kGrouped ? CaptureScale{} : capture_scale(*ts_ptr);
   const uint64_t stride = (uint64_t)gridDim.x * kThreads;
-  for (uint64_t b = (uint64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks; b += stride) {
+  // Tiles are taken from the tensor's end backwards: the tensor amax, which
+  // reads the same tensor just before, leaves its last-read lines in the
+  // 256 MB last-level cache, and the capture reaches them first.
+  for (uint64_t b = (uint64_t)(gridDim.x - 1 - blockIdx.x) * kThreads + threadIdx.x; b < nblocks; b += stride) {
     uint32_t w[8];
     load_block(x, b, w);  // issued before the group search, whose latency it hides
     const CaptureScale cs = kGrouped ? capture_scale(group_tensor_scale(groups, ts_ptr, b)) : cs0;
