@@ -17,7 +17,7 @@
 // words of a block (rollout, RNE, guided, full information; even and odd
 // elements in separate dwords, eight nibbles each) are compared with
 // nibble-parallel integer arithmetic: a code's signed grid index is shifted
-// by 7 into a nibble 0..14 (both zeros map to 7), equality and one-step
+// by 8 into a nibble 1..15 (both zeros map to 8), equality and one-step
 // neighbours become per-nibble zero tests, and counts are population counts.
 // That covers every element whose rollout and RNE codes are at most one step
 // apart and whose guided and RNE codes are too; a block with any other
@@ -44,13 +44,13 @@ constexpr int kStatWords = 20;  // see the layout in launch.h
 constexpr uint32_t kNib3 = 0x88888888u;  // bit 3 of every nibble
 constexpr uint32_t kOnes = 0x11111111u;
 
-// 7 + signed grid index of every code nibble (sign << 3 | magnitude index).
+// 8 + signed grid index of every code nibble (sign << 3 | magnitude index):
+// 1..15, both zeros 8.  Positive codes give c ^ 8 = 8 + m; negative ones
+// (c ^ 15) + 1 = 16 - c = 8 - m, the +1 staying inside the nibble.
 __device__ __forceinline__ uint32_t offset_index(uint32_t c) {
-  const uint32_t m = c & 0x77777777u;
   const uint32_t sb = c & kNib3;
-  const uint32_t neg = sb | (sb - (sb >> 3));  // 0xF in negative nibbles, no borrows
-  // 7 - m and 7 + m stay within their nibble (m <= 7)
-  return (neg & (0x77777777u - m)) | (~neg & (m + 0x77777777u));
+  const uint32_t s1 = sb >> 3;                 // 1 in negative nibbles
+  return (c ^ kNib3 ^ (sb - s1)) + s1;         // sb - s1 = 7 in negative nibbles
 }
 
 // Bit 3 of each nibble set where that nibble of x is zero.
@@ -59,7 +59,8 @@ __device__ __forceinline__ uint32_t zero_nibbles(uint32_t x) {
 }
 
 // Per-nibble flags of one code dword pair; false when some element needs the
-// per-element count.
+// per-element count.  One-step neighbours are tested by subtracting 1 from
+// the larger side (offset indices are >= 1, so no nibble borrows).
 struct NibbleStats {
   uint32_t same, one, straddle, crossed, recovered, violation;
 };
@@ -67,11 +68,11 @@ struct NibbleStats {
 __device__ __forceinline__ bool nibble_stats(uint32_t r, uint32_t n, uint32_t g, uint32_t f, NibbleStats& o) {
   const uint32_t ur = offset_index(r), un = offset_index(n), ug = offset_index(g), uf = offset_index(f);
   const uint32_t same = zero_nibbles(ur ^ un);               // rollout == RNE
-  const uint32_t up = zero_nibbles(ur ^ (un + kOnes));       // rollout one step above RNE
-  const uint32_t down = zero_nibbles(un ^ (ur + kOnes));     // rollout one step below RNE
+  const uint32_t up = zero_nibbles(un ^ (ur - kOnes));       // rollout one step above RNE
+  const uint32_t down = zero_nibbles(ur ^ (un - kOnes));     // rollout one step below RNE
   const uint32_t g_eq = zero_nibbles(ug ^ un);               // guided == RNE
-  const uint32_t g_up = zero_nibbles(ug ^ (un + kOnes));     // guided one step above RNE
-  const uint32_t g_down = zero_nibbles(un ^ (ug + kOnes));   // guided one step below RNE
+  const uint32_t g_up = zero_nibbles(un ^ (ug - kOnes));     // guided one step above RNE
+  const uint32_t g_down = zero_nibbles(ug ^ (un - kOnes));   // guided one step below RNE
   o.same = same;
   o.one = up | down;
   o.straddle = ~same & zero_nibbles(uf ^ ur) & kNib3;
