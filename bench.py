@@ -76,7 +76,7 @@ MOE_BYTES_PER_ELEM = {
     "gather_records_runs": 2 * (1 / 8 + 1 / 16),                   # the same, rows moved in runs
 }
 GATHER_RUN = 256         # rows per run in the run-ordered gather
-CPU_SHARE = 16           # host cores a one-GPU machine grants
+CPU_SHARE = 16           # host cores granted to a process driving one GPU
 CPU_BUDGET_S = 12.0      # wall-clock budget of the CPU oracle leg
 CHUNK_ROWS = 128
 
@@ -140,7 +140,9 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this library's path runs on a single MI355X and has no "
-              "multi-GPU mode (see the sharding paragraph of DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+              "multi-GPU mode (every 16-element block is independent; a sharded tensor would need one "
+              "all-reduce(max) of its tensor amax, which this library does not implement). Run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
     if args.calibrate_copy:

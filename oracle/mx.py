@@ -16,7 +16,7 @@ MXFP4 concrete format and the conversion from a vector of scalars):
 * elements are E2M1 codes of ``x / X`` rounded to nearest (ties to even)
   and clamped to the largest normal 6.
 
-Readings of points the specification leaves open (listed in the design doc):
+Readings of points the specification leaves open:
 
 * amax ignores NaN; an all-zero (or all-NaN) block gets the smallest scale,
   byte 0 (its elements are zeros anyway);

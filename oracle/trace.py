@@ -12,7 +12,7 @@ multiple of 16; a block is 16 consecutive elements.  Record layouts:
 * 4-bit codes: element 2*j in the low nibble of byte j, 2*j+1 in the high
   nibble; a code is sign << 3 | magnitude index.
 
-Readings of points the pages leave open (each also listed in the design doc):
+Readings of points the pages leave open:
 
 * the "one mantissa bit" kept per site is bit 0 of the E2M1 code, which is
   the parity of the codeword's signed grid index: adjacent codewords,
