@@ -201,11 +201,30 @@ __global__ __launch_bounds__(kThreads) void amax_partial_kernel(const uint4* __r
   if (threadIdx.x == 0) partial[blockIdx.x] = r;
 }
 
+// Maximum of words [begin, end) over a workgroup's lanes: every lane issues
+// kFoldLoads loads before it waits for any (a loop of single loads waits one
+// memory round trip per word).  Indices past the end read the last word
+// again, which leaves the maximum unchanged and keeps the loads unconditional.
+constexpr int kFoldLoads = 8;
+
+__device__ __forceinline__ uint32_t fold_max_u32(const uint32_t* __restrict__ v, uint64_t begin, uint64_t end) {
+  uint32_t best = 0;
+  for (uint64_t base = begin; base < end; base += (uint64_t)kFoldLoads * kThreads) {
+    uint32_t w[kFoldLoads];
+#pragma unroll
+    for (int u = 0; u < kFoldLoads; ++u) {
+      const uint64_t i = base + (uint64_t)u * kThreads + threadIdx.x;
+      w[u] = v[i < end ? i : end - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < kFoldLoads; ++u) best = max(best, w[u]);
+  }
+  return block_max_u32(best);
+}
+
 __global__ __launch_bounds__(kThreads) void amax_finalize_kernel(const uint32_t* __restrict__ partial,
                                                                  uint32_t count, float* __restrict__ ts_out) {
-  uint32_t best = 0;
-  for (uint32_t i = threadIdx.x; i < count; i += kThreads) best = max(best, partial[i]);
-  best = block_max_u32(best);
+  const uint32_t best = fold_max_u32(partial, 0, count);
   if (threadIdx.x == 0) *ts_out = __uint_as_float(best << 16) / kTensorDiv;
 }
 
@@ -341,9 +360,7 @@ __global__ __launch_bounds__(kThreads) void group_amax_finalize_kernel(const uin
   const uint32_t g = blockIdx.x;
   const uint64_t r0 = g == 0 ? 0 : group_row(G, g);
   const uint64_t r1 = g + 1 == G.count ? G.rows : group_row(G, g + 1);
-  uint32_t best = 0;
-  for (uint64_t r = r0 + threadIdx.x; r < r1; r += kThreads) best = max(best, row_amax[r]);
-  best = block_max_u32(best);
+  const uint32_t best = fold_max_u32(row_amax, r0, r1);
   if (threadIdx.x == 0) ts_out[g] = __uint_as_float(best << 16) / kTensorDiv;
 }
 
