@@ -113,6 +113,29 @@ def test_grouped_bit_exact(device, name, rows, cols, make):
     _compare(_host(got), _oracle_grouped(xr, xt, rows, cols, off, ts), name)
 
 
+@pytest.mark.parametrize("peak_row", [2048, 4998, 0])
+def test_grouped_tensor_scale_long_groups(device, peak_row):
+    """Groups longer than one pass of the group fold (2048 row maxima per
+    workgroup pass): group 0 holds 4999 rows, with its largest magnitude at
+    the start of the second pass, in the last (partial) pass, or in the
+    first row.  Every group's tensor scale against the oracle, bit for bit."""
+    _say("case grouped long groups, peak row", peak_row)
+    import fp4_rollout_guided_amd as tr
+    rows, cols = 6000, 16
+    off = np.array([0, 4999, 5000, 6000], dtype=np.int64)
+    rng = np.random.default_rng(peak_row + 11)
+    v = rng.standard_normal((rows, cols)).astype(np.float32)
+    v[peak_row, 5] = -700.0     # group 0's maximum
+    v[4999, 3] = 3.0e-3         # group 1: one small row
+    v[5000:] *= 1.0e4           # group 2 orders of magnitude larger
+    xr = F.f32_to_bf16_rne(v.reshape(-1))
+    ts = tr.grouped_tensor_scale(from_np_u16(xr, device, (rows, cols)), torch.from_numpy(off).to(device))
+    torch.cuda.synchronize()
+    want = oracle.grouped_tensor_scale(xr, rows, cols, off)
+    assert np.array_equal(ts.cpu().numpy().view(np.uint32), want.view(np.uint32))
+    assert want[0] == np.float32(700.0) / np.float32(2688.0)
+
+
 def test_single_group_equals_ungrouped(device):
     """With one group the grouped entry points reproduce the ungrouped ones."""
     _say("case grouped single == ungrouped")
