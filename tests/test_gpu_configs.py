@@ -1,8 +1,10 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
-benchmark uses (one call per site tensor), against the oracle on sampled
-rows (the first row, random rows and the last rows, which include the ragged
-tail of the large-hidden workload).  The tensor scale of every site is
-checked over the whole tensor, and every element of every output against
+benchmark uses (one call per site tensor): every element of every output of
+every site against the oracle, bit for bit (``tests/full_compare.py``; of
+the deeper-half sweep, layers 0 and 19), after a quick check on sampled
+rows (the first row, random rows and the last rows, which include the
+ragged tail of the large-hidden workload).  The tensor scale of every site
+is checked over the whole tensor, and every element of every output against
 the whole-tensor properties of ``tests/full_props.py`` (on all 20 layers of
 the deeper-half sweep too).  Where a workload is built around rollout /
 training agreement, the oracle's mismatch statistics on the sample are
@@ -18,6 +20,7 @@ import torch
 
 import oracle
 import workloads
+from tests.full_compare import compare_every_element
 from tests.full_props import check_nvfp4_outputs
 from tests.gpu_util import assert_same, oracle_path, to_np_u16, to_np_u8
 from tests.workload_place import oracle_block_scales, place_kv, place_near_midpoints
@@ -57,13 +60,17 @@ def _gather(t, idx, per_row, u16=False):
 
 def check_site(name, x_roll, x_train, grad, k_rows=128, seed=0):
     rows, cols = x_roll.shape[0], x_roll.numel() // x_roll.shape[0]
-    _say(f"case {name}: {tuple(x_roll.shape)} ({x_roll.numel()} elements), {k_rows} sampled rows")
+    _say(f"case {name}: {tuple(x_roll.shape)} ({x_roll.numel()} elements), {k_rows} sampled rows, then every element")
     got = _gpu_full(x_roll, x_train, grad)
     check_nvfp4_outputs(name, x_roll, x_train, grad, got["ts"], got)
     xr_all = to_np_u16(x_roll)
     ts = oracle.tensor_scale(xr_all)
-    del xr_all
     assert got["ts"].cpu().numpy().view(np.uint32)[0] == np.float32(ts).view(np.uint32), name
+    # every element of every output against the oracle
+    host = {k: (to_np_u16(v) if k in ("y_g", "y_r", "y_f", "gin") else to_np_u8(v))
+            for k, v in got.items() if k != "ts"}
+    compare_every_element(name, xr_all, to_np_u16(x_train), to_np_u16(grad), np.float32(ts), host)
+    del xr_all, host
     idx = _rows(rows, k_rows, seed)
     xr = _gather(x_roll.view(torch.int16), idx, cols, True)
     xt = _gather(x_train.view(torch.int16), idx, cols, True)
@@ -164,6 +171,25 @@ def test_workload3_every_layer_whole_tensor(device):
         got = _gpu_full(d["x_roll"], d["x_train"], d["grad"])
         check_nvfp4_outputs(f"workload 3 layer {layer}", d["x_roll"], d["x_train"], d["grad"], got["ts"], got)
         del d, got
+
+
+@pytest.mark.skipif(os.environ.get("TRACE_FULL_SWEEP") != "1",
+                    reason="every element of all 20 layers takes ~6 minutes; set TRACE_FULL_SWEEP=1 to run it")
+@pytest.mark.parametrize("layer", range(20))
+def test_workload3_layer_every_element(device, layer):
+    """One layer of the deeper-half sweep per case: every element of every
+    output against the oracle (layers 0 and 19 also run by default above)."""
+    d = workloads.cfg3_layer(device, layer)
+    _say(f"case workload 3 layer {layer}: every element")
+    got = _gpu_full(d["x_roll"], d["x_train"], d["grad"])
+    xr_all = to_np_u16(d["x_roll"])
+    ts = oracle.tensor_scale(xr_all)
+    assert got["ts"].cpu().numpy().view(np.uint32)[0] == np.float32(ts).view(np.uint32)
+    host = {k: (to_np_u16(v) if k in ("y_g", "y_r", "y_f", "gin") else to_np_u8(v))
+            for k, v in got.items() if k != "ts"}
+    compare_every_element(f"workload 3 layer {layer}", xr_all, to_np_u16(d["x_train"]), to_np_u16(d["grad"]),
+                          np.float32(ts), host)
+    del d, got, host, xr_all
 
 
 def test_workload4_large_hidden_ragged(device):
