@@ -89,3 +89,67 @@ def compare_every_element(name, xr, xt, g, ts, got):
             _say(f"  {name}: {b} of {n} elements equal to the oracle ({time.perf_counter() - t0:.1f} s, "
                  f"{cores} workers)")
     return n
+
+
+def _oracle_variant_chunk(args):
+    import oracle
+    kind, xr, xt, extra = args
+    if kind in ("mx", "mx8"):
+        cap_f, gd_f, fi_f = ((oracle.mx_capture, oracle.mx_guided_fwd, oracle.mx_full_info_fwd) if kind == "mx" else
+                             (oracle.mx8_capture, oracle.mx8_guided_fwd, oracle.mx8_full_info_fwd))
+        cap = cap_f(xr, with_codes=True)
+        gd = gd_f(xt, cap["scales"], cap["bits"])
+        fi = fi_f(xt, cap["scales"], cap["codes"])
+        return {"scales": cap["scales"], "bits": cap["bits"], "codes": cap["codes"], "y_g": gd["y"],
+                "m_g": gd["mask"], "q_g": gd["codes"], "y_f": fi["y"], "m_f": fi["mask"], "q_f": fi["codes"]}
+    ts, nbits = extra
+    cap = oracle.capture_lowbits(xr, ts, nbits)
+    out = oracle.lowbits_fwd(xt, cap["scales"], ts, cap["planes"], nbits)
+    return {"scales": cap["scales"], "planes": cap["planes"], "y": out["y"], "mask": out["mask"],
+            "codes": out["codes"]}
+
+
+# elements per byte of each variant output; bf16 outputs are one uint16 per element
+_VARIANT_PER = {
+    "mx": {"scales": 32, "bits": 8, "codes": 2, "m_g": 8, "q_g": 2, "m_f": 8, "q_f": 2},
+    "mx8": {"scales": 32, "bits": 8, "codes": 1, "m_g": 8, "q_g": 1, "m_f": 8, "q_f": 1},
+    "lowbits": {"scales": 16, "mask": 8, "codes": 2},
+}
+
+
+def compare_variant_every_element(name, kind, xr, xt, got, extra=None):
+    """The MXFP4 (kind "mx"), MXFP8 ("mx8") or b-low-bits ("lowbits", extra =
+    (the oracle's tensor scale, b)) path on a whole site: got holds the GPU's
+    outputs as host arrays (the low-bits planes as one array of b planes of
+    n / 8 bytes each)."""
+    n = xr.size
+    assert n % 32 == 0
+    p, cores = pool()
+    per = _VARIANT_PER[kind]
+    t0 = time.perf_counter()
+    starts = list(range(0, n, CHUNK_ELEMS))
+    tasks = ((kind, xr[a:a + CHUNK_ELEMS], xt[a:a + CHUNK_ELEMS], extra) for a in starts)
+    step = max(1, len(starts) // 4)
+    for i, want in enumerate(p.imap(_oracle_variant_chunk, tasks, chunksize=1)):
+        a = starts[i]
+        b = min(a + CHUNK_ELEMS, n)
+        for k, w in want.items():
+            if k == "planes":   # b planes: plane j of the chunk sits at j * n / 8 + a / 8 in the whole array
+                nb = extra[1]
+                m = (b - a) // 8
+                pairs = [(got[k][j * (n // 8) + a // 8:j * (n // 8) + b // 8], w[j * m:(j + 1) * m], j * (n // 8) + a // 8)
+                         for j in range(nb)]
+            elif k in per:
+                pairs = [(got[k][a // per[k]:b // per[k]], w, a // per[k])]
+            else:
+                pairs = [(got[k][a:b], w, a)]
+            for have, ww, base in pairs:
+                if not np.array_equal(have, ww):
+                    bad = np.flatnonzero(have != ww)
+                    raise AssertionError(
+                        f"{name} ({kind}): {k} differs from the oracle at {bad.size} positions of chunk [{a}, {b}); "
+                        f"first offsets {(base + bad[:6]).tolist()} got {have[bad[:6]].tolist()} "
+                        f"want {ww[bad[:6]].tolist()}")
+        if (i + 1) % step == 0 or i + 1 == len(starts):
+            _say(f"  {name} ({kind}): {b} of {n} elements equal to the oracle ({time.perf_counter() - t0:.1f} s)")
+    return n

@@ -1,8 +1,8 @@
 """The MXFP4, MXFP8 and b-cached-low-bits variants at full workload sizes: the KV
 cache workload (2 x 131072 x 512) and the ragged large-hidden workload
 (65573 x 7168, half of the training values placed near codeword midpoints),
-every output on sampled rows (first, last, ragged tail, random) against the
-oracle, bit for bit."""
+every element of every output against the oracle, bit for bit
+(``tests/full_compare.py``)."""
 import sys
 
 import numpy as np
@@ -11,6 +11,7 @@ import torch
 
 import oracle
 import workloads
+from tests.full_compare import compare_variant_every_element
 from tests.gpu_util import to_np_u8, to_np_u16
 from tests.workload_place import oracle_block_scales, place_kv, place_near_midpoints
 
@@ -21,89 +22,36 @@ def _say(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def _rows(rows, k, seed):
-    rng = np.random.default_rng(seed)
-    pick = set(rng.choice(rows, size=min(k, rows), replace=False).tolist())
-    pick.update([0, rows - 1, rows - 2])
-    return np.array(sorted(pick))
-
-
-def _take(t, idx, per_row, u16=False):
-    v = (t.view(torch.int16) if u16 else t).reshape(-1, per_row)[torch.from_numpy(idx).to(t.device)]
-    return to_np_u16(v) if u16 else to_np_u8(v)
-
-
-def _check(ctx, got, want):
-    for k, w in want.items():
-        g = got[k]
-        if not np.array_equal(g.reshape(-1), np.asarray(w).reshape(-1)):
-            bad = np.flatnonzero(g.reshape(-1) != np.asarray(w).reshape(-1))
-            raise AssertionError(f"{ctx}: {k} differs at {bad.size} positions, first {bad[:6].tolist()}")
-
-
-def _mx_site(name, x_roll, x_train, k_rows, seed):
+def _mx_site(name, x_roll, x_train, kind):
     import fp4_rollout_guided_amd as tr
     rows, cols = x_roll.shape
-    _say(f"case {name}: MXFP4 {rows}x{cols}")
-    sc, bt, cd = tr.mx_capture(x_roll, want_codes=True)
-    yg, mg, qg = tr.mx_guided_fakequant_fwd(x_train, sc, bt, want_codes=True)
-    yf, mf, qf = tr.mx_full_info_fakequant_fwd(x_train, sc, cd, want_codes=True)
+    _say(f"case {name}: {'MXFP4' if kind == 'mx' else 'MXFP8'} {rows}x{cols}, every element")
+    cap, gfwd, ffwd = ((tr.mx_capture, tr.mx_guided_fakequant_fwd, tr.mx_full_info_fakequant_fwd) if kind == "mx" else
+                       (tr.mx8_capture, tr.mx8_guided_fakequant_fwd, tr.mx8_full_info_fakequant_fwd))
+    sc, bt, cd = cap(x_roll, want_codes=True)
+    yg, mg, qg = gfwd(x_train, sc, bt, want_codes=True)
+    yf, mf, qf = ffwd(x_train, sc, cd, want_codes=True)
     torch.cuda.synchronize()
-    idx = _rows(rows, k_rows, seed)
-    xr, xt = _take(x_roll, idx, cols, True), _take(x_train, idx, cols, True)
-    cap = oracle.mx_capture(xr, with_codes=True)
-    gd = oracle.mx_guided_fwd(xt, cap["scales"], cap["bits"])
-    fi = oracle.mx_full_info_fwd(xt, cap["scales"], cap["codes"])
-    got = {"scales": _take(sc, idx, cols // 32), "bits": _take(bt, idx, cols // 8), "codes": _take(cd, idx, cols // 2),
-           "y_g": _take(yg, idx, cols, True), "m_g": _take(mg, idx, cols // 8), "q_g": _take(qg, idx, cols // 2),
-           "y_f": _take(yf, idx, cols, True), "m_f": _take(mf, idx, cols // 8), "q_f": _take(qf, idx, cols // 2)}
-    want = {"scales": cap["scales"], "bits": cap["bits"], "codes": cap["codes"], "y_g": gd["y"], "m_g": gd["mask"],
-            "q_g": gd["codes"], "y_f": fi["y"], "m_f": fi["mask"], "q_f": fi["codes"]}
-    _check(name, got, want)
+    got = {"scales": to_np_u8(sc), "bits": to_np_u8(bt), "codes": to_np_u8(cd),
+           "y_g": to_np_u16(yg), "m_g": to_np_u8(mg), "q_g": to_np_u8(qg),
+           "y_f": to_np_u16(yf), "m_f": to_np_u8(mf), "q_f": to_np_u8(qf)}
+    compare_variant_every_element(name, kind, to_np_u16(x_roll), to_np_u16(x_train), got)
 
 
-def _mx8_site(name, x_roll, x_train, k_rows, seed):
+def _lowbits_site(name, x_roll, x_train, nbits):
     import fp4_rollout_guided_amd as tr
     rows, cols = x_roll.shape
-    _say(f"case {name}: MXFP8 {rows}x{cols}")
-    sc, bt, cd = tr.mx8_capture(x_roll, want_codes=True)
-    yg, mg, qg = tr.mx8_guided_fakequant_fwd(x_train, sc, bt, want_codes=True)
-    yf, mf, qf = tr.mx8_full_info_fakequant_fwd(x_train, sc, cd, want_codes=True)
-    torch.cuda.synchronize()
-    idx = _rows(rows, k_rows, seed)
-    xr, xt = _take(x_roll, idx, cols, True), _take(x_train, idx, cols, True)
-    cap = oracle.mx8_capture(xr, with_codes=True)
-    gd = oracle.mx8_guided_fwd(xt, cap["scales"], cap["bits"])
-    fi = oracle.mx8_full_info_fwd(xt, cap["scales"], cap["codes"])
-    got = {"scales": _take(sc, idx, cols // 32), "bits": _take(bt, idx, cols // 8), "codes": _take(cd, idx, cols),
-           "y_g": _take(yg, idx, cols, True), "m_g": _take(mg, idx, cols // 8), "q_g": _take(qg, idx, cols),
-           "y_f": _take(yf, idx, cols, True), "m_f": _take(mf, idx, cols // 8), "q_f": _take(qf, idx, cols)}
-    want = {"scales": cap["scales"], "bits": cap["bits"], "codes": cap["codes"], "y_g": gd["y"], "m_g": gd["mask"],
-            "q_g": gd["codes"], "y_f": fi["y"], "m_f": fi["mask"], "q_f": fi["codes"]}
-    _check(name, got, want)
-
-
-def _lowbits_site(name, x_roll, x_train, nbits, k_rows, seed):
-    import fp4_rollout_guided_amd as tr
-    rows, cols = x_roll.shape
-    _say(f"case {name}: b = {nbits} low bits {rows}x{cols}")
+    _say(f"case {name}: b = {nbits} low bits {rows}x{cols}, every element")
     ts = tr.tensor_scale(x_roll)
     sc, pl, _ = tr.capture_lowbits(x_roll, ts, nbits)
     y, m, q = tr.lowbits_fakequant_fwd(x_train, sc, ts, nbits, pl, want_codes=True)
     torch.cuda.synchronize()
-    tsf = np.float32(ts.cpu().numpy()[0])
-    idx = _rows(rows, k_rows, seed)
-    xr, xt = _take(x_roll, idx, cols, True), _take(x_train, idx, cols, True)
-    cap = oracle.capture_lowbits(xr, tsf, nbits)
-    out = oracle.lowbits_fwd(xt, cap["scales"], tsf, cap["planes"], nbits)
-    n = rows * cols
-    planes = pl.reshape(nbits, n // 8)
-    got = {"scales": _take(sc, idx, cols // 16),
-           "planes": np.concatenate([_take(planes[k], idx, cols // 8) for k in range(nbits)]),
-           "y": _take(y, idx, cols, True), "mask": _take(m, idx, cols // 8), "codes": _take(q, idx, cols // 2)}
-    want = {"scales": cap["scales"], "planes": cap["planes"], "y": out["y"], "mask": out["mask"],
-            "codes": out["codes"]}
-    _check(name, got, want)
+    xr = to_np_u16(x_roll)
+    ts_oracle = np.float32(oracle.tensor_scale(xr))   # the oracle's own tensor scale, never the GPU's
+    assert ts.cpu().numpy().view(np.uint32)[0] == ts_oracle.view(np.uint32), name
+    got = {"scales": to_np_u8(sc), "planes": to_np_u8(pl), "y": to_np_u16(y), "mask": to_np_u8(m),
+           "codes": to_np_u8(q)}
+    compare_variant_every_element(name, "lowbits", xr, to_np_u16(x_train), got, extra=(ts_oracle, nbits))
 
 
 @pytest.fixture(scope="module")
@@ -114,16 +62,16 @@ def workload4(device):
 
 
 def test_mx_workload4(device, workload4):
-    _mx_site("workload 4", *workload4, k_rows=96, seed=41)
+    _mx_site("workload 4", *workload4, kind="mx")
 
 
 def test_mx8_workload4(device, workload4):
-    _mx8_site("workload 4", *workload4, k_rows=96, seed=47)
+    _mx_site("workload 4", *workload4, kind="mx8")
 
 
 @pytest.mark.parametrize("nbits", [2, 3])
 def test_lowbits_workload4(device, workload4, nbits):
-    _lowbits_site("workload 4", *workload4, nbits=nbits, k_rows=96, seed=42 + nbits)
+    _lowbits_site("workload 4", *workload4, nbits=nbits)
 
 
 @pytest.mark.parametrize("which", ["k", "v"])
@@ -132,7 +80,6 @@ def test_variants_workload2(device, which):
     _, s_block = oracle_block_scales(x_roll)
     x_train = place_kv(x_roll, which, s_block)
     shape2d = (x_roll.shape[0], x_roll.shape[1] * x_roll.shape[2])
-    _mx_site(f"workload 2 {which}", x_roll.reshape(shape2d), x_train.reshape(shape2d), k_rows=256, seed=21)
-    _mx8_site(f"workload 2 {which}", x_roll.reshape(shape2d), x_train.reshape(shape2d), k_rows=256, seed=23)
-    _lowbits_site(f"workload 2 {which}", x_roll.reshape(shape2d), x_train.reshape(shape2d), nbits=2, k_rows=256,
-                  seed=22)
+    _mx_site(f"workload 2 {which}", x_roll.reshape(shape2d), x_train.reshape(shape2d), kind="mx")
+    _mx_site(f"workload 2 {which}", x_roll.reshape(shape2d), x_train.reshape(shape2d), kind="mx8")
+    _lowbits_site(f"workload 2 {which}", x_roll.reshape(shape2d), x_train.reshape(shape2d), nbits=2)
