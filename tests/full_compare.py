@@ -153,3 +153,49 @@ def compare_variant_every_element(name, kind, xr, xt, got, extra=None):
         if (i + 1) % step == 0 or i + 1 == len(starts):
             _say(f"  {name} ({kind}): {b} of {n} elements equal to the oracle ({time.perf_counter() - t0:.1f} s)")
     return n
+
+
+def _oracle_grouped_chunk(args):
+    import oracle
+    xr, xt, rows, cols, off, ts = args
+    cap = oracle.grouped_capture(xr, rows, cols, off, ts, with_codes=True)
+    gd = oracle.grouped_guided_fwd(xt, rows, cols, off, cap["scales"], ts, cap["bits"])
+    rn = oracle.grouped_rne_fwd(xt, rows, cols, off, cap["scales"], ts)
+    fi = oracle.grouped_full_info_fwd(xt, rows, cols, off, cap["scales"], ts, cap["codes"])
+    return {"scales": cap["scales"], "bits": cap["bits"], "codes": cap["codes"],
+            "y_g": gd["y"], "mask_g": gd["mask"], "q_g": gd["codes"],
+            "y_r": rn["y"], "mask_r": rn["mask"], "q_r": rn["codes"],
+            "y_f": fi["y"], "mask_f": fi["mask"], "q_f": fi["codes"]}
+
+
+def compare_grouped_every_element(name, xr, xt, rows, cols, off, ts, got):
+    """The per-expert path on a whole rows x cols site with row groups off
+    (int64[G + 1]) and the oracle's per-group tensor scales ts: chunks of
+    whole rows, each with the group offsets clipped to its rows, so every row
+    keeps its group's scale."""
+    p, cores = pool()
+    rows_per = max(1, CHUNK_ELEMS // cols)
+    t0 = time.perf_counter()
+    starts = list(range(0, rows, rows_per))
+    off = np.asarray(off, dtype=np.int64)
+
+    def task(r0):
+        r1 = min(r0 + rows_per, rows)
+        sub = np.clip(off - r0, 0, r1 - r0).astype(np.int64)
+        return (xr[r0 * cols:r1 * cols], xt[r0 * cols:r1 * cols], r1 - r0, cols, sub, ts)
+
+    step = max(1, len(starts) // 4)
+    for i, want in enumerate(p.imap(_oracle_grouped_chunk, (task(r) for r in starts), chunksize=1)):
+        a = starts[i] * cols
+        b = min(starts[i] + rows_per, rows) * cols
+        for k, w in want.items():
+            lo, hi = (a, b) if k in _BF16 else (a // _PER[k], b // _PER[k])
+            have = got[k][lo:hi]
+            if not np.array_equal(have, w):
+                bad = np.flatnonzero(have != w)
+                raise AssertionError(
+                    f"{name}: {k} differs from the oracle at {bad.size} positions of elements [{a}, {b}); first "
+                    f"offsets {(lo + bad[:6]).tolist()} got {have[bad[:6]].tolist()} want {w[bad[:6]].tolist()}")
+        if (i + 1) % step == 0 or i + 1 == len(starts):
+            _say(f"  {name}: {b} of {rows * cols} elements equal to the oracle ({time.perf_counter() - t0:.1f} s)")
+    return rows * cols

@@ -16,6 +16,7 @@ import torch
 import oracle
 import workloads
 from oracle import formats as F
+from tests.full_compare import compare_grouped_every_element
 from tests.full_props import check_nvfp4_outputs
 from tests.gpu_util import from_np_u16, to_np_u8, to_np_u16
 
@@ -207,3 +208,8 @@ def test_moe_expert_site_per_expert_scales(device):
     row_ts = got["ts"].repeat_interleave(torch.from_numpy(np.diff(off)).to(device))
     torch.cuda.synchronize()
     check_nvfp4_outputs("expert site", x_roll, x_train, grad, row_ts, got)
+    # every element of every output against the oracle, with the oracle's
+    # per-expert tensor scales
+    host = {k: (to_np_u16(v) if k in ("y_g", "y_r", "y_f") else to_np_u8(v))
+            for k, v in got.items() if k not in ("ts", "gin")}
+    compare_grouped_every_element("expert site", to_np_u16(x_roll), to_np_u16(x_train), rows, cols, off, ts, host)
