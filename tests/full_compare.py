@@ -93,15 +93,22 @@ def compare_every_element(name, xr, xt, g, ts, got):
 
 def _oracle_variant_chunk(args):
     import oracle
-    kind, xr, xt, extra = args
+    kind, xr, xt, extra, g = args
     if kind in ("mx", "mx8"):
-        cap_f, gd_f, fi_f = ((oracle.mx_capture, oracle.mx_guided_fwd, oracle.mx_full_info_fwd) if kind == "mx" else
-                             (oracle.mx8_capture, oracle.mx8_guided_fwd, oracle.mx8_full_info_fwd))
+        cap_f, gd_f, rn_f, fi_f = (
+            (oracle.mx_capture, oracle.mx_guided_fwd, oracle.mx_rne_fwd, oracle.mx_full_info_fwd) if kind == "mx" else
+            (oracle.mx8_capture, oracle.mx8_guided_fwd, oracle.mx8_rne_fwd, oracle.mx8_full_info_fwd))
         cap = cap_f(xr, with_codes=True)
         gd = gd_f(xt, cap["scales"], cap["bits"])
         fi = fi_f(xt, cap["scales"], cap["codes"])
-        return {"scales": cap["scales"], "bits": cap["bits"], "codes": cap["codes"], "y_g": gd["y"],
-                "m_g": gd["mask"], "q_g": gd["codes"], "y_f": fi["y"], "m_f": fi["mask"], "q_f": fi["codes"]}
+        out = {"scales": cap["scales"], "bits": cap["bits"], "codes": cap["codes"], "y_g": gd["y"],
+               "m_g": gd["mask"], "q_g": gd["codes"], "y_f": fi["y"], "m_f": fi["mask"], "q_f": fi["codes"]}
+        if extra == "with_rne":
+            rn = rn_f(xt, cap["scales"])
+            out.update({"y_r": rn["y"], "m_r": rn["mask"], "q_r": rn["codes"]})
+        if g is not None:
+            out["gin"] = oracle.ste_bwd(g, gd["mask"], xt.size)
+        return out
     ts, nbits = extra
     cap = oracle.capture_lowbits(xr, ts, nbits)
     out = oracle.lowbits_fwd(xt, cap["scales"], ts, cap["planes"], nbits)
@@ -111,24 +118,27 @@ def _oracle_variant_chunk(args):
 
 # elements per byte of each variant output; bf16 outputs are one uint16 per element
 _VARIANT_PER = {
-    "mx": {"scales": 32, "bits": 8, "codes": 2, "m_g": 8, "q_g": 2, "m_f": 8, "q_f": 2},
-    "mx8": {"scales": 32, "bits": 8, "codes": 1, "m_g": 8, "q_g": 1, "m_f": 8, "q_f": 1},
+    "mx": {"scales": 32, "bits": 8, "codes": 2, "m_g": 8, "q_g": 2, "m_f": 8, "q_f": 2, "m_r": 8, "q_r": 2},
+    "mx8": {"scales": 32, "bits": 8, "codes": 1, "m_g": 8, "q_g": 1, "m_f": 8, "q_f": 1, "m_r": 8, "q_r": 1},
     "lowbits": {"scales": 16, "mask": 8, "codes": 2},
 }
 
 
-def compare_variant_every_element(name, kind, xr, xt, got, extra=None):
+def compare_variant_every_element(name, kind, xr, xt, got, extra=None, g=None):
     """The MXFP4 (kind "mx"), MXFP8 ("mx8") or b-low-bits ("lowbits", extra =
     (the oracle's tensor scale, b)) path on a whole site: got holds the GPU's
     outputs as host arrays (the low-bits planes as one array of b planes of
-    n / 8 bytes each)."""
+    n / 8 bytes each).  For mx and mx8, extra = "with_rne" also compares the
+    RNE forward (y_r, m_r, q_r), and a gradient g (host uint16) the STE
+    backward on the guided mask (gin)."""
     n = xr.size
     assert n % 32 == 0
     p, cores = pool()
     per = _VARIANT_PER[kind]
     t0 = time.perf_counter()
     starts = list(range(0, n, CHUNK_ELEMS))
-    tasks = ((kind, xr[a:a + CHUNK_ELEMS], xt[a:a + CHUNK_ELEMS], extra) for a in starts)
+    tasks = ((kind, xr[a:a + CHUNK_ELEMS], xt[a:a + CHUNK_ELEMS], extra,
+              None if g is None else g[a:a + CHUNK_ELEMS]) for a in starts)
     step = max(1, len(starts) // 4)
     for i, want in enumerate(p.imap(_oracle_variant_chunk, tasks, chunksize=1)):
         a = starts[i]

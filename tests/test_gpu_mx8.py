@@ -5,7 +5,7 @@ bit.  Covers ragged shapes over several tiles, every bf16 pattern under
 every E8M0 scale byte (random cached bits and rollout bytes, NaN bytes
 included), block maxima over every finite bf16 magnitude, tiny elements
 beside large ones, specials, in-place use, and the deeper-half sweep's layer
-shape on sampled rows."""
+shape, every element."""
 import sys
 
 import numpy as np
@@ -167,21 +167,15 @@ def test_mx8_in_place(device):
     assert np.array_equal(to_np_u16(out), to_np_u16(ref))
 
 
-def test_mx8_deeper_half_layer_sampled_rows(device):
-    """One 262144x2048 layer of the deeper-half sweep on the MXFP8 grid: 160
-    sampled rows (first, last, random) of every output against the oracle."""
-    _say("case mx8 workload 3 layer 0")
+def test_mx8_deeper_half_layer_every_element(device):
+    """One 262144x2048 layer of the deeper-half sweep on MXFP8 scales: every
+    element of the capture, guided, RNE and full-information outputs and of
+    the STE backward on the guided mask against the oracle, bit for bit."""
+    from tests.full_compare import compare_variant_every_element
+    _say("case mx8 workload 3 layer 0, every element")
     d = workloads.cfg3_layer(device, 0)
     got = _gpu_mx8(d["x_roll"], d["x_train"], d["grad"])
-    rows, cols = d["x_roll"].shape
-    rng = np.random.default_rng(12)
-    idx = np.unique(np.r_[0, rows - 1, rng.choice(rows, 158, replace=False)])
-    take = lambda t: to_np_u16(t.view(torch.int16).reshape(rows, cols)[torch.from_numpy(idx).to(device)])
-    xr, xt, g = take(d["x_roll"]), take(d["x_train"]), take(d["grad"])
-    want = _oracle_mx8(xr, xt, g)
-    per = {"scales": cols // 32, "bits": cols // 8, "codes": cols, "mask_g": cols // 8, "q_g": cols,
-           "mask_r": cols // 8, "q_r": cols, "mask_f": cols // 8, "q_f": cols}
-    sampled = {k: got[k].reshape(rows, per[k])[idx].reshape(-1) for k in per}
-    for k in ("y_g", "y_r", "y_f", "gin"):
-        sampled[k] = got[k].reshape(rows, cols)[idx].reshape(-1)
-    _same(sampled, want, "mx8 workload 3 layer 0")
+    ren = {"mask_g": "m_g", "mask_r": "m_r", "mask_f": "m_f"}
+    got = {ren.get(k, k): v for k, v in got.items()}
+    compare_variant_every_element("mx8 workload 3 layer 0", "mx8", to_np_u16(d["x_roll"]),
+                                  to_np_u16(d["x_train"]), got, extra="with_rne", g=to_np_u16(d["grad"]))
