@@ -40,8 +40,10 @@
  *   one site tensor.
  * - Ownership: the caller owns every buffer.  The library allocates nothing,
  *   frees nothing, never synchronizes, and keeps no state between calls
- *   other than a thread-local copy of the last HIP error code.  It is safe to
- *   call from several host threads.
+ *   other than a thread-local copy of the last HIP error code and, per
+ *   device, the resident-workgroup count of the agreement statistics kernel
+ *   (one occupancy query, cached atomically).  It is safe to call from
+ *   several host threads.
  * - Asynchrony: all device work is enqueued on `stream` (a hipStream_t; NULL
  *   is the default stream).  Outputs are valid once that stream reaches the
  *   point of the call.
