@@ -208,15 +208,19 @@ def main():
 
     per_kernel_ms = {k: 0.0 for k in KERNELS}
     nk = len(KERNELS)
-    markers = [torch.cuda.Event(enable_timing=True) for _ in range(nk * L + 1)]   # created once, re-recorded
+    # every step records its own markers, so the steps run back to back with
+    # no host synchronization between them; the markers are read after the
+    # timed region
+    markers = [[torch.cuda.Event(enable_timing=True) for _ in range(nk * L + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        step(markers)
-        stream.synchronize()
-        for i in range(nk * L):
-            per_kernel_ms[KERNELS[i % nk]] += markers[i].elapsed_time(markers[i + 1])
+        step(markers[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    for m in markers:
+        for i in range(nk * L):
+            per_kernel_ms[KERNELS[i % nk]] += m[i].elapsed_time(m[i + 1])
     ms_per_step = 1e3 * wall / args.steps
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step")
 
