@@ -163,7 +163,7 @@ def main():
     log(f"generating {L} layers of {ROWS}x{COLS} bf16 on {torch.cuda.get_device_name(dev)}")
     layers = []
     for l in range(L):
-        d = workloads.cfg3_layer(dev, l)
+        d = workloads.deeper_half_layer(dev, l)
         d["scales"] = torch.empty(n // 16, dtype=torch.uint8, device=dev)
         d["bits"] = torch.empty(n // 8, dtype=torch.uint8, device=dev)
         d["ts"] = torch.empty(1, dtype=torch.float32, device=dev)
@@ -357,7 +357,7 @@ def workload_rows(tr, workloads, torch, dev, stream, reps=3):
     data-dependent path on finite inputs, so where values land does not
     change the time."""
     import json as _json
-    with open(os.path.join(ROOT, "tests", "golden", "cfg1_sigma.json")) as fh:
+    with open(os.path.join(ROOT, "tests", "golden", "moe_layer_sigma.json")) as fh:
         sigma = _json.load(fh)["sigma"]
     flush = torch.zeros(1 << 29, dtype=torch.bfloat16, device=dev)   # 1 GiB
     flush_ts = torch.empty(1, dtype=torch.float32, device=dev)
@@ -365,14 +365,14 @@ def workload_rows(tr, workloads, torch, dev, stream, reps=3):
     def noisy(x, *key):
         return workloads.relative_noise(x, 0.02, workloads.generator(dev, *key))
 
-    sites = {"small 1024x2048": {"x": workloads.cfg0(dev)}}
-    sites["MoE layer"] = workloads.cfg1(dev, sigma)
+    sites = {"small 1024x2048": {"x": workloads.single_site(dev)}}
+    sites["MoE layer"] = workloads.moe_layer(dev, sigma)
     kv = {}
     for which in ("k", "v"):
-        xr = workloads.cfg2_rollout(dev, which)
+        xr = workloads.kv_cache_rollout(dev, which)
         kv[which] = {"x_roll": xr, "x_train": noisy(xr, 2, which, "bench"), "grad": workloads.grad_for(xr.shape, dev, 2, which)}
     sites["KV cache"] = kv
-    xr = workloads.cfg4_rollout(dev)
+    xr = workloads.large_hidden_rollout(dev)
     sites["large hidden 65573x7168"] = {"x": {"x_roll": xr, "x_train": noisy(xr, 4, "bench"),
                                               "grad": workloads.grad_for(xr.shape, dev, 4)}}
     bpe_step = sum(BYTES_PER_ELEM.values())
@@ -446,7 +446,7 @@ def moe_rows(tr, workloads, torch, dev, stream, layers, reps):
     rows, and runs of GATHER_RUN consecutive rows), each gather timed after a
     read-only 1 GiB pass."""
     sigma = 0.02
-    d = workloads.cfg1(dev, sigma, sites=["expert_in"])["expert_in"]
+    d = workloads.moe_layer(dev, sigma, sites=["expert_in"])["expert_in"]
     _, experts = workloads.moe_routing(dev)
     offsets = workloads.moe_expert_offsets(experts)
     x_roll, x_train = d["x_roll"], d["x_train"]
@@ -553,7 +553,7 @@ def read_traffic(kernel):
     """HBM traffic per launch from the committed counter summary, or None
     when there is none for this kernel or the kernel source changed since."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_cfg3.txt")
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_deeper_half.txt")
     if not os.path.exists(path):
         return None
     kv = {}

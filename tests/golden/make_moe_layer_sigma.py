@@ -1,7 +1,7 @@
 """Tune the relative noise of the MoE-layer workload so that ~3% of sites
-straddle an E2M1 midpoint, and store it in cfg1_sigma.json.
+straddle an E2M1 midpoint, and store it in moe_layer_sigma.json.
 
-    python tests/golden/make_cfg1_sigma.py
+    python tests/golden/make_moe_layer_sigma.py
 
 A site straddles when its rollout codeword and the training value's RNE
 codeword differ and the rollout codeword is an endpoint of the training
@@ -57,9 +57,9 @@ def main():
         "straddle_rate_on_tuning_sample": rate,
         "tuning_sample": f"first {ROWS} rows of the attention-input site (Student-t(4), 16384x2048), CPU generator",
         "mismatch_histogram_on_tuning_sample": st["hist"][:5],
-        "written_by": "tests/golden/make_cfg1_sigma.py (oracle + workloads only)",
+        "written_by": "tests/golden/make_moe_layer_sigma.py (oracle + workloads only)",
     }
-    with open(os.path.join(HERE, "cfg1_sigma.json"), "w") as fh:
+    with open(os.path.join(HERE, "moe_layer_sigma.json"), "w") as fh:
         json.dump(out, fh, indent=2)
     print(json.dumps(out, indent=2))
 

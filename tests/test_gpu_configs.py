@@ -110,44 +110,44 @@ def check_site(name, x_roll, x_train, grad, k_rows=128, seed=0):
     return st
 
 
-def test_workload0_full_compare(device):
+def test_single_site_every_element(device):
     """1024 x 2048: every element against the oracle."""
-    d = workloads.cfg0(device)
-    _say("case workload 0 full")
+    d = workloads.single_site(device)
+    _say("case single site, every element")
     from tests.gpu_util import gpu_path
     got = gpu_path(d["x_roll"], d["x_train"], d["grad"])
     want = oracle_path(to_np_u16(d["x_roll"]), to_np_u16(d["x_train"]), to_np_u16(d["grad"]))
-    assert_same(got, want, ctx="workload 0")
+    assert_same(got, want, ctx="single site")
 
 
-def test_workload1_moe_layer(device):
-    with open(os.path.join(HERE, "golden", "cfg1_sigma.json")) as fh:
+def test_moe_layer(device):
+    with open(os.path.join(HERE, "golden", "moe_layer_sigma.json")) as fh:
         sigma = json.load(fh)["sigma"]
-    sites = workloads.cfg1(device, sigma)
+    sites = workloads.moe_layer(device, sigma)
     total = {"n": 0, "straddle": 0, "full_n": 0, "full_straddle": 0}
     for i, (name, d) in enumerate(sites.items()):
-        st = check_site(f"workload 1 {name}", d["x_roll"], d["x_train"], d["grad"], seed=10 + i)
+        st = check_site(f"MoE layer {name}", d["x_roll"], d["x_train"], d["grad"], seed=10 + i)
         total["n"] += st["n"]
         total["straddle"] += st["straddle"]
         total["full_n"] += st["full"][19]
         total["full_straddle"] += st["full"][15]
         assert st["recovered"] >= st["straddle"]
     rate = total["straddle"] / total["n"]
-    _say(f"  workload 1 straddle rate on the samples: {rate:.4f}")
+    _say(f"  MoE layer straddle rate on the samples: {rate:.4f}")
     assert 0.02 < rate < 0.04
     full_rate = total["full_straddle"] / total["full_n"]
-    _say(f"  workload 1 straddle rate over the whole layer: {full_rate:.4f}")
+    _say(f"  MoE layer straddle rate over the whole layer: {full_rate:.4f}")
     assert 0.02 < full_rate < 0.04
 
 
 @pytest.mark.parametrize("which", ["k", "v"])
-def test_workload2_kv_cache(device, which):
-    x_roll = workloads.cfg2_rollout(device, which)
+def test_kv_cache(device, which):
+    x_roll = workloads.kv_cache_rollout(device, which)
     _, s_block = oracle_block_scales(x_roll)
     x_train = place_kv(x_roll, which, s_block)
     grad = workloads.grad_for(x_roll.shape, device, 2, which)
     shape2d = (x_roll.shape[0], x_roll.shape[1] * x_roll.shape[2])
-    st = check_site(f"workload 2 {which}", x_roll.reshape(shape2d), x_train.reshape(shape2d), grad.reshape(shape2d),
+    st = check_site(f"KV cache {which}", x_roll.reshape(shape2d), x_train.reshape(shape2d), grad.reshape(shape2d),
                     k_rows=256, seed=20)
     assert st["recovered"] >= st["straddle"]
     # all mismatches on the sample are the placed one- and two-codeword moves
@@ -155,47 +155,47 @@ def test_workload2_kv_cache(device, which):
 
 
 @pytest.mark.parametrize("layer", [0, 19])
-def test_workload3_deeper_half_layer(device, layer):
-    d = workloads.cfg3_layer(device, layer)
-    st = check_site(f"workload 3 layer {layer}", d["x_roll"], d["x_train"], d["grad"], seed=30 + layer)
+def test_deeper_half_layer(device, layer):
+    d = workloads.deeper_half_layer(device, layer)
+    st = check_site(f"deeper-half layer {layer}", d["x_roll"], d["x_train"], d["grad"], seed=30 + layer)
     assert st["recovered"] >= st["straddle"]
 
 
-def test_workload3_every_layer_whole_tensor(device):
+def test_deeper_half_every_layer_whole_tensor(device):
     """All 20 layers of the deeper-half sweep, every element of every output
     checked against the whole-tensor properties (layers 0 and 19 are also
     compared with the oracle on sampled rows above)."""
     for layer in range(20):
-        d = workloads.cfg3_layer(device, layer)
-        _say(f"case workload 3 layer {layer}: whole-tensor properties")
+        d = workloads.deeper_half_layer(device, layer)
+        _say(f"case deeper-half layer {layer}: whole-tensor properties")
         got = _gpu_full(d["x_roll"], d["x_train"], d["grad"])
-        check_nvfp4_outputs(f"workload 3 layer {layer}", d["x_roll"], d["x_train"], d["grad"], got["ts"], got)
+        check_nvfp4_outputs(f"deeper-half layer {layer}", d["x_roll"], d["x_train"], d["grad"], got["ts"], got)
         del d, got
 
 
 @pytest.mark.skipif(os.environ.get("TRACE_FULL_SWEEP") != "1",
                     reason="every element of all 20 layers takes ~6 minutes; set TRACE_FULL_SWEEP=1 to run it")
 @pytest.mark.parametrize("layer", range(20))
-def test_workload3_layer_every_element(device, layer):
+def test_deeper_half_layer_every_element_sweep(device, layer):
     """One layer of the deeper-half sweep per case: every element of every
     output against the oracle (layers 0 and 19 also run by default above)."""
-    d = workloads.cfg3_layer(device, layer)
-    _say(f"case workload 3 layer {layer}: every element")
+    d = workloads.deeper_half_layer(device, layer)
+    _say(f"case deeper-half layer {layer}: every element")
     got = _gpu_full(d["x_roll"], d["x_train"], d["grad"])
     xr_all = to_np_u16(d["x_roll"])
     ts = oracle.tensor_scale(xr_all)
     assert got["ts"].cpu().numpy().view(np.uint32)[0] == np.float32(ts).view(np.uint32)
     host = {k: (to_np_u16(v) if k in ("y_g", "y_r", "y_f", "gin") else to_np_u8(v))
             for k, v in got.items() if k != "ts"}
-    compare_every_element(f"workload 3 layer {layer}", xr_all, to_np_u16(d["x_train"]), to_np_u16(d["grad"]),
+    compare_every_element(f"deeper-half layer {layer}", xr_all, to_np_u16(d["x_train"]), to_np_u16(d["grad"]),
                           np.float32(ts), host)
     del d, got, host, xr_all
 
 
-def test_workload4_large_hidden_ragged(device):
-    x_roll = workloads.cfg4_rollout(device)
+def test_large_hidden_ragged(device):
+    x_roll = workloads.large_hidden_rollout(device)
     _, s_block = oracle_block_scales(x_roll)
     x_train = place_near_midpoints(x_roll, s_block)
     grad = workloads.grad_for(x_roll.shape, device, 4)
-    st = check_site("workload 4", x_roll, x_train, grad, k_rows=96, seed=40)
+    st = check_site("large hidden", x_roll, x_train, grad, k_rows=96, seed=40)
     assert st["recovered"] >= st["straddle"]

@@ -141,7 +141,7 @@ def test_single_group_equals_ungrouped(device):
     """With one group the grouped entry points reproduce the ungrouped ones."""
     _say("case grouped single == ungrouped")
     import fp4_rollout_guided_amd as tr
-    d = workloads.cfg0(device)
+    d = workloads.single_site(device)
     xr, xt = d["x_roll"], d["x_train"]
     offsets = torch.tensor([0, xr.shape[0]], dtype=torch.int64, device=device)
     got = _host(_gpu_grouped(xr, xt, offsets))
@@ -158,10 +158,10 @@ def test_moe_expert_site_per_expert_scales(device):
     """The packed routed-expert site of the MoE layer workload (131072 x 2048,
     rows grouped by 128 experts) with per-expert tensor scales: every scale
     against the oracle, and sampled rows of every output."""
-    with open(os.path.join(HERE, "golden", "cfg1_sigma.json")) as fh:
+    with open(os.path.join(HERE, "golden", "moe_layer_sigma.json")) as fh:
         sigma = json.load(fh)["sigma"]
-    _say("case workload 1 expert site, per-expert scales")
-    d = workloads.cfg1(device, sigma, sites=["expert_in"])["expert_in"]
+    _say("case MoE layer expert site, per-expert scales")
+    d = workloads.moe_layer(device, sigma, sites=["expert_in"])["expert_in"]
     _, experts = workloads.moe_routing(device)
     offsets = workloads.moe_expert_offsets(experts)
     x_roll, x_train = d["x_roll"], d["x_train"]

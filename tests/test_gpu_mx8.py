@@ -172,10 +172,10 @@ def test_mx8_deeper_half_layer_every_element(device):
     element of the capture, guided, RNE and full-information outputs and of
     the STE backward on the guided mask against the oracle, bit for bit."""
     from tests.full_compare import compare_variant_every_element
-    _say("case mx8 workload 3 layer 0, every element")
-    d = workloads.cfg3_layer(device, 0)
+    _say("case mx8 deeper-half layer 0, every element")
+    d = workloads.deeper_half_layer(device, 0)
     got = _gpu_mx8(d["x_roll"], d["x_train"], d["grad"])
     ren = {"mask_g": "m_g", "mask_r": "m_r", "mask_f": "m_f"}
     got = {ren.get(k, k): v for k, v in got.items()}
-    compare_variant_every_element("mx8 workload 3 layer 0", "mx8", to_np_u16(d["x_roll"]),
+    compare_variant_every_element("mx8 deeper-half layer 0", "mx8", to_np_u16(d["x_roll"]),
                                   to_np_u16(d["x_train"]), got, extra="with_rne", g=to_np_u16(d["grad"]))

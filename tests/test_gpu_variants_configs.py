@@ -55,31 +55,31 @@ def _lowbits_site(name, x_roll, x_train, nbits):
 
 
 @pytest.fixture(scope="module")
-def workload4(device):
-    x_roll = workloads.cfg4_rollout(device)
+def large_hidden(device):
+    x_roll = workloads.large_hidden_rollout(device)
     _, s_block = oracle_block_scales(x_roll)
     return x_roll, place_near_midpoints(x_roll, s_block)
 
 
-def test_mx_workload4(device, workload4):
-    _mx_site("workload 4", *workload4, kind="mx")
+def test_mx_large_hidden(device, large_hidden):
+    _mx_site("large hidden", *large_hidden, kind="mx")
 
 
-def test_mx8_workload4(device, workload4):
-    _mx_site("workload 4", *workload4, kind="mx8")
+def test_mx8_large_hidden(device, large_hidden):
+    _mx_site("large hidden", *large_hidden, kind="mx8")
 
 
 @pytest.mark.parametrize("nbits", [2, 3])
-def test_lowbits_workload4(device, workload4, nbits):
-    _lowbits_site("workload 4", *workload4, nbits=nbits)
+def test_lowbits_large_hidden(device, large_hidden, nbits):
+    _lowbits_site("large hidden", *large_hidden, nbits=nbits)
 
 
 @pytest.mark.parametrize("which", ["k", "v"])
-def test_variants_workload2(device, which):
-    x_roll = workloads.cfg2_rollout(device, which)
+def test_variants_kv_cache(device, which):
+    x_roll = workloads.kv_cache_rollout(device, which)
     _, s_block = oracle_block_scales(x_roll)
     x_train = place_kv(x_roll, which, s_block)
     shape2d = (x_roll.shape[0], x_roll.shape[1] * x_roll.shape[2])
-    _mx_site(f"workload 2 {which}", x_roll.reshape(shape2d), x_train.reshape(shape2d), kind="mx")
-    _mx_site(f"workload 2 {which}", x_roll.reshape(shape2d), x_train.reshape(shape2d), kind="mx8")
-    _lowbits_site(f"workload 2 {which}", x_roll.reshape(shape2d), x_train.reshape(shape2d), nbits=2)
+    _mx_site(f"KV cache {which}", x_roll.reshape(shape2d), x_train.reshape(shape2d), kind="mx")
+    _mx_site(f"KV cache {which}", x_roll.reshape(shape2d), x_train.reshape(shape2d), kind="mx8")
+    _lowbits_site(f"KV cache {which}", x_roll.reshape(shape2d), x_train.reshape(shape2d), nbits=2)

@@ -41,7 +41,7 @@ def place_kv(x_roll, which, s_block):
     dev = x_roll.device
     x = x_roll.float().reshape(-1)
     n = x.numel()
-    d = workloads.cfg2_perturbation_draws(dev, which, n)
+    d = workloads.kv_cache_perturbation_draws(dev, which, n)
     s = torch.from_numpy(s_block).to(dev).repeat_interleave(16)
     ok = torch.isfinite(s)
     z = torch.where(ok, x / torch.where(ok, s, torch.ones_like(s)), torch.zeros_like(x))
@@ -72,7 +72,7 @@ def place_near_midpoints(x_roll, s_block):
     dev = x_roll.device
     x = x_roll.float().reshape(-1)
     n = x.numel()
-    d = workloads.cfg4_draws(dev, n)
+    d = workloads.large_hidden_draws(dev, n)
     s = torch.from_numpy(s_block).to(dev).repeat_interleave(16)
     ok = torch.isfinite(s)
     z = torch.where(ok, x / torch.where(ok, s, torch.ones_like(s)), torch.zeros_like(x))

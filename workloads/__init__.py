@@ -100,10 +100,10 @@ def relative_noise(x_bf16, sigma, g):
 
 
 # ----------------------------------------------------------------------------
-# workload 0
+# single site (1024 x 2048)
 # ----------------------------------------------------------------------------
 
-def cfg0(device):
+def single_site(device):
     rows, cols = SHAPES[0]["x"]
     g = generator(device, 0, "x")
     x = normal((rows, cols), g, device)
@@ -115,7 +115,7 @@ def cfg0(device):
 
 
 # ----------------------------------------------------------------------------
-# workload 1 (MoE layer); x_train is relative noise whose sigma the caller
+# MoE layer; x_train is relative noise whose sigma the caller
 # chooses (tuned so that ~3% of sites straddle an E2M1 midpoint)
 # ----------------------------------------------------------------------------
 
@@ -140,7 +140,7 @@ def moe_expert_offsets(expert_of_row):
     return torch.cat([torch.zeros(1, dtype=torch.int64, device=counts.device), torch.cumsum(counts, 0)])
 
 
-def cfg1(device, sigma, sites=None):
+def moe_layer(device, sigma, sites=None):
     """Dict site -> {x_roll, x_train, grad} for the MoE layer sites."""
     sites = sites or list(SHAPES[1])
     out = {}
@@ -162,10 +162,10 @@ def cfg1(device, sigma, sites=None):
 
 
 # ----------------------------------------------------------------------------
-# workload 2 (KV cache)
+# KV cache
 # ----------------------------------------------------------------------------
 
-def cfg2_rollout(device, which):
+def kv_cache_rollout(device, which):
     """K or V rollout tensor [131072, 4, 128]: N(0,1), per head 2 of 128
     dims scaled x20 (separate draws for K and V and for every head)."""
     tokens, heads, hd = SHAPES[2][which]
@@ -176,7 +176,7 @@ def cfg2_rollout(device, which):
     return bf16(x)
 
 
-def cfg2_perturbation_draws(device, which, n):
+def kv_cache_perturbation_draws(device, which, n):
     """Raw draws for placing training values near the rollout grid:
     ``one`` / ``two`` = disjoint site masks of ~1% and ~0.01%, ``up`` = the
     direction (+1 / -1) of the neighbour to move toward, ``u`` in [0, 1) =
@@ -192,10 +192,10 @@ def cfg2_perturbation_draws(device, which, n):
 
 
 # ----------------------------------------------------------------------------
-# workload 3 (deeper-half sweep, one layer per call)
+# deeper-half sweep, one layer per call
 # ----------------------------------------------------------------------------
 
-def cfg3_layer(device, layer, with_grad=True):
+def deeper_half_layer(device, layer, with_grad=True):
     rows, cols = SHAPES[3]["x"]
     g = generator(device, 3, layer, "x")
     x = normal((rows, cols), g, device)
@@ -211,10 +211,10 @@ def cfg3_layer(device, layer, with_grad=True):
 
 
 # ----------------------------------------------------------------------------
-# workload 4 (large hidden, ragged rows)
+# large hidden, ragged rows
 # ----------------------------------------------------------------------------
 
-def cfg4_rollout(device):
+def large_hidden_rollout(device):
     rows, cols = SHAPES[4]["x"]
     g = generator(device, 4, "x")
     x = laplace((rows, cols), g, device)
@@ -222,7 +222,7 @@ def cfg4_rollout(device):
     return bf16(x)
 
 
-def cfg4_draws(device, n):
+def large_hidden_draws(device, n):
     """``near`` = the ~50% of elements placed near a codeword midpoint,
     ``off`` in [-1e-3, 1e-3) = their offset from it."""
     g = generator(device, 4, "place")
