@@ -23,6 +23,8 @@ Functions mirror the C ABI in ``include/trace.h``:
     mx8_capture / mx8_guided_fakequant_fwd / mx8_rne_fakequant_fwd /
     mx8_full_info_fakequant_fwd: the MXFP8 (E4M3) activation grid of the W4A8
     setting (32-element blocks, E8M0 scales, one code byte per element)
+    tensor_scale_batch(xs)                           -> [ts, ...] (up to 8 sites, one pass)
+    capture_batch(xs, tss, want_codes=False)         -> [(scales, bits, codes), ...] (one launch)
     capture_lowbits(x_roll, ts, nbits)               -> (scales, planes, codes)
     lowbits_fakequant_fwd(x_train, scales, ts, nbits, planes) -> (y, mask, qcodes)
     ste_bwd(grad_out, mask)                          -> grad_in
@@ -43,7 +45,7 @@ __all__ = [
     "grouped_full_info_fakequant_fwd", "mx_capture", "mx_guided_fakequant_fwd", "mx_rne_fakequant_fwd",
     "mx_full_info_fakequant_fwd", "mx8_capture", "mx8_guided_fakequant_fwd", "mx8_rne_fakequant_fwd",
     "mx8_full_info_fakequant_fwd", "capture_lowbits", "lowbits_fakequant_fwd", "mismatch_stats", "STAT_FIELDS",
-    "GuidedFakeQuant",
+    "GuidedFakeQuant", "tensor_scale_batch", "capture_batch", "MAX_BATCH_SITES",
     "STATUS",
 ]
 
@@ -101,6 +103,9 @@ def load_library(path):
         "trace_mx8_guided_fakequant_fwd": ([p, i64, i64, p, p, p, p, p, p], st),
         "trace_mx8_rne_fakequant_fwd": ([p, i64, i64, p, p, p, p, p], st),
         "trace_mx8_full_info_fakequant_fwd": ([p, i64, i64, p, p, p, p, p, p], st),
+        "trace_tensor_scale_batch_workspace_bytes": ([p, ctypes.c_int32], sz),
+        "trace_tensor_scale_batch": ([p, ctypes.c_int32, p, sz, p], st),
+        "trace_capture_batch": ([p, ctypes.c_int32, p], st),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -188,6 +193,62 @@ def capture(x_roll, ts, want_codes=False, scales=None, bits=None, codes=None):
     _check(lib.trace_capture(_ptr(x_roll), rows, cols, _ptr(ts), _ptr(scales), _ptr(bits), _ptr(codes),
                              _stream(x_roll)), "trace_capture")
     return scales, bits, codes
+
+
+class _Site(ctypes.Structure):
+    """trace_site of include/trace.h."""
+    _fields_ = [("x", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("ts", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("bits", ctypes.c_void_p),
+                ("codes", ctypes.c_void_p)]
+
+
+MAX_BATCH_SITES = 8
+
+
+def _sites(xs, tss, records=None):
+    if len(xs) > MAX_BATCH_SITES:
+        raise ValueError(f"at most {MAX_BATCH_SITES} sites per batch, got {len(xs)}")
+    arr = (_Site * max(1, len(xs)))()
+    for i, x in enumerate(xs):
+        _bf16(x, f"xs[{i}]")
+        rows, cols = _rows_cols(x)
+        sc, bt, cd = records[i] if records is not None else (None, None, None)
+        arr[i] = _Site(x.data_ptr() if x.numel() else None, rows, cols, tss[i].data_ptr(),
+                       None if sc is None else sc.data_ptr(), None if bt is None else bt.data_ptr(),
+                       None if cd is None else cd.data_ptr())
+    return arr
+
+
+def tensor_scale_batch(xs, outs=None, workspace=None):
+    """Tensor scales of up to 8 site tensors in one pass: a list of
+    float32[1] device tensors, each equal to tensor_scale(x)."""
+    if not xs:
+        return []
+    dev = xs[0].device
+    outs = outs if outs is not None else [torch.empty(1, dtype=torch.float32, device=dev) for _ in xs]
+    arr = _sites(xs, outs)
+    need = lib.trace_tensor_scale_batch_workspace_bytes(arr, len(xs))
+    if workspace is None:
+        workspace = torch.empty(max(4, need), dtype=torch.uint8, device=dev)
+    _check(lib.trace_tensor_scale_batch(arr, len(xs), _ptr(workspace), workspace.numel(), _stream(xs[0])),
+           "trace_tensor_scale_batch")
+    return outs
+
+
+def capture_batch(xs, tss, want_codes=False, records=None):
+    """Compact records of up to 8 site tensors in one launch: a list of
+    (scales, bits, codes or None), each equal to capture(x, ts)."""
+    if not xs:
+        return []
+    if records is None:
+        records = []
+        for x in xs:
+            n = x.numel()
+            records.append((_u8(n // 16, x, None, "scales"), _u8(n // 8, x, None, "bits"),
+                            _u8(n // 2, x, None, "codes") if want_codes else None))
+    arr = _sites(xs, tss, records)
+    _check(lib.trace_capture_batch(arr, len(xs), _stream(xs[0])), "trace_capture_batch")
+    return records
 
 
 def _fwd(mode, x, scales, ts, side, y, mask, want_codes, qcodes):

@@ -97,6 +97,42 @@ trace_status trace_tensor_scale(const uint16_t* x, int64_t n, void* workspace, s
                                                     static_cast<hipStream_t>(stream)));
 }
 
+static_assert(TRACE_MAX_BATCH_SITES == trace_host::kMaxBatchSites, "batch size limits differ");
+
+// Validates a batch and fills one launcher spec per site.  with_record: the
+// capture batch (scales and bits required, codes optional) rather than the
+// tensor scale pass (ts written).  extra: the workspace range of the tensor
+// scale pass (an output), or an empty range.
+static trace_status batch_specs(const trace_site* sites, int32_t count, bool with_record, Range extra,
+                                trace_host::BatchSiteSpec* spec) {
+  if (count < 0 || count > TRACE_MAX_BATCH_SITES) return TRACE_E_SHAPE;
+  if (count > 0 && !sites) return TRACE_E_NULL;
+  Range outs[3 * TRACE_MAX_BATCH_SITES + 1], ins[2 * TRACE_MAX_BATCH_SITES];
+  int nout = 0, nin = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const trace_site& t = sites[i];
+    uint64_t n = 0;
+    if (trace_status st = site_size(t.rows, t.cols, &n)) return st;
+    if ((n > 0 && !t.x) || (!t.ts && (n > 0 || !with_record))) return TRACE_E_NULL;
+    if (with_record && n > 0 && (!t.scales || !t.bits)) return TRACE_E_NULL;
+    if (!aligned(t.x, 16) || !aligned(t.ts, 4)) return TRACE_E_ALIGN;
+    if (with_record && (!aligned(t.bits, 2) || (t.codes && !aligned(t.codes, 8)))) return TRACE_E_ALIGN;
+    ins[nin++] = rng(t.x, 2 * n);
+    if (with_record) {
+      ins[nin++] = rng(t.ts, n > 0 ? 4 : 0);
+      outs[nout++] = rng(t.scales, n / 16);
+      outs[nout++] = rng(t.bits, n / 8);
+      outs[nout++] = rng(t.codes, t.codes ? n / 2 : 0);
+    } else {
+      outs[nout++] = rng(t.ts, 4);
+    }
+    spec[i] = trace_host::BatchSiteSpec{t.x, n / 16, t.ts, with_record ? t.scales : nullptr,
+                                        with_record ? t.bits : nullptr, with_record ? t.codes : nullptr};
+  }
+  outs[nout++] = extra;
+  return check_alias(outs, nout, ins, nin);
+}
+
 // Row groups of a grouped call: 1 <= groups <= kMaxRowGroups and an
 // 8-byte-aligned offsets array of groups + 1 entries.  Fills *spec.
 static trace_status group_spec(const int64_t* offsets, int64_t groups, int64_t rows, int64_t cols,
@@ -126,6 +162,33 @@ static trace_status capture(const uint16_t* x_roll, int64_t rows, int64_t cols, 
   if (trace_status st = check_alias(outs, 3, ins, 3)) return st;
   return hip_status(trace_host::launch_capture(x_roll, n / 16, ts, grouped ? &spec : nullptr, scales, bits, codes,
                                                static_cast<hipStream_t>(stream)));
+}
+
+size_t trace_tensor_scale_batch_workspace_bytes(const trace_site* sites, int32_t count) {
+  trace_host::BatchSiteSpec spec[TRACE_MAX_BATCH_SITES];
+  if (batch_specs(sites, count, false, Range{0, 0}, spec) != TRACE_OK) return 0;
+  return (size_t)trace_host::batch_amax_partial_count(spec, (uint32_t)count) * sizeof(uint32_t);
+}
+
+trace_status trace_tensor_scale_batch(const trace_site* sites, int32_t count, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  trace_host::BatchSiteSpec spec[TRACE_MAX_BATCH_SITES];
+  if (trace_status st = batch_specs(sites, count, false, Range{0, 0}, spec)) return st;
+  if (count == 0) return TRACE_OK;
+  const size_t need = (size_t)trace_host::batch_amax_partial_count(spec, (uint32_t)count) * sizeof(uint32_t);
+  if (need > 0 && !workspace) return TRACE_E_NULL;
+  if (workspace_bytes < need) return TRACE_E_SHAPE;
+  if (!aligned(workspace, 4)) return TRACE_E_ALIGN;
+  if (trace_status st = batch_specs(sites, count, false, rng(workspace, need), spec)) return st;
+  return hip_status(trace_host::launch_tensor_scale_batch(spec, (uint32_t)count, static_cast<uint32_t*>(workspace),
+                                                          static_cast<hipStream_t>(stream)));
+}
+
+trace_status trace_capture_batch(const trace_site* sites, int32_t count, void* stream) {
+  trace_host::BatchSiteSpec spec[TRACE_MAX_BATCH_SITES];
+  if (trace_status st = batch_specs(sites, count, true, Range{0, 0}, spec)) return st;
+  if (count == 0) return TRACE_OK;
+  return hip_status(trace_host::launch_capture_batch(spec, (uint32_t)count, static_cast<hipStream_t>(stream)));
 }
 
 trace_status trace_capture(const uint16_t* x_roll, int64_t rows, int64_t cols, const float* ts,

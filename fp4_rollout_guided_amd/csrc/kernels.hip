@@ -172,12 +172,13 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 // The amax and STE kernels have no block structure, so their loads are fully
 // coalesced: a 4096-element tile is 512 128-bit vectors and lane t takes
 // vectors t and t + 256 (every load instruction covers 1 KiB contiguous).
-__global__ __launch_bounds__(kThreads) void amax_partial_kernel(const uint4* __restrict__ x,
-                                                                uint64_t nblocks,
-                                                                uint32_t* __restrict__ partial) {
+// The workgroup's partial maximum (bf16 magnitude bits) over tiles g, g + G,
+// g + 2G, ... of the tensor.
+__device__ __forceinline__ uint32_t amax_partial_body(const uint4* __restrict__ x, uint64_t nblocks, uint64_t g,
+                                                      uint64_t G) {
   s16x2 best = {0, 0};  // holds max(m + 0x7f) over non-NaN halves, >= 0x7f once any was seen
   const uint64_t nvec = 2 * nblocks;
-  for (uint64_t tile = blockIdx.x; tile * 512 < nvec; tile += gridDim.x) {
+  for (uint64_t tile = g; tile * 512 < nvec; tile += G) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint64_t i = tile * 512 + 256 * h + threadIdx.x;
@@ -196,8 +197,14 @@ __global__ __launch_bounds__(kThreads) void amax_partial_kernel(const uint4* __r
   }
   const int lo = best.x, hi = best.y;
   const int m = lo > hi ? lo : hi;
-  uint32_t r = m > 0x7f ? (uint32_t)(m - 0x7f) : 0u;
-  r = block_max_u32(r);
+  const uint32_t r = m > 0x7f ? (uint32_t)(m - 0x7f) : 0u;
+  return block_max_u32(r);
+}
+
+__global__ __launch_bounds__(kThreads) void amax_partial_kernel(const uint4* __restrict__ x,
+                                                                uint64_t nblocks,
+                                                                uint32_t* __restrict__ partial) {
+  const uint32_t r = amax_partial_body(x, nblocks, blockIdx.x, gridDim.x);
   if (threadIdx.x == 0) partial[blockIdx.x] = r;
 }
 
@@ -471,6 +478,70 @@ __global__ __launch_bounds__(kThreads) void capture_kernel(const uint4* __restri
 }
 
 // ---------------------------------------------------------------------------
+// batches of site tensors (the rollout side of one layer: its activation and
+// KV sites in one tensor-scale pass and one capture launch).  Site k owns
+// workgroups [wg_begin, wg_begin + wg_count) of the batch grid; a workgroup
+// finds its site wave-uniformly from the kernel arguments.  Every site keeps
+// its own tensor scale and record, so the results equal per-site calls.
+// ---------------------------------------------------------------------------
+struct BatchSite {
+  const uint4* x;
+  uint64_t nblocks;
+  float* ts;          // the tensor scale pass writes it; the capture reads it
+  uint8_t* scales;
+  uint16_t* bits;
+  uint2* codes;       // nullable
+  uint32_t wg_begin;
+  uint32_t wg_count;
+};
+
+struct BatchSites {
+  BatchSite site[trace_host::kMaxBatchSites];
+  uint32_t count;
+};
+
+// The site whose workgroup range holds workgroup wg: the last site starting
+// at or before it (sites without workgroups share their successor's start
+// and are passed over).
+__device__ __forceinline__ uint32_t batch_site_of(const BatchSites& B, uint32_t wg) {
+  uint32_t k = 0;
+#pragma unroll
+  for (uint32_t i = 1; i < trace_host::kMaxBatchSites; ++i) k = (i < B.count && B.site[i].wg_begin <= wg) ? i : k;
+  return k;
+}
+
+__global__ __launch_bounds__(kThreads) void amax_partial_batch_kernel(BatchSites B, uint32_t* __restrict__ partial) {
+  const BatchSite& S = B.site[batch_site_of(B, blockIdx.x)];
+  const uint32_t r = amax_partial_body(S.x, S.nblocks, blockIdx.x - S.wg_begin, S.wg_count);
+  if (threadIdx.x == 0) partial[blockIdx.x] = r;
+}
+
+// One workgroup per site: the site's tensor scale from its partial maxima (a
+// site without workgroups, an empty tensor, gets 0).
+__global__ __launch_bounds__(kThreads) void amax_finalize_batch_kernel(BatchSites B,
+                                                                       const uint32_t* __restrict__ partial) {
+  const BatchSite& S = B.site[blockIdx.x];
+  const uint32_t best = fold_max_u32(partial, S.wg_begin, (uint64_t)S.wg_begin + S.wg_count);
+  if (threadIdx.x == 0) *S.ts = __uint_as_float(best << 16) / kTensorDiv;
+}
+
+// One 256-block tile per workgroup.  The grid is walked from its end, across
+// sites and within each site, so the capture first meets the lines the tensor
+// scale pass read last.
+__global__ __launch_bounds__(kThreads) void capture_batch_kernel(BatchSites B) {
+  const uint32_t gw = gridDim.x - 1 - blockIdx.x;
+  const BatchSite& S = B.site[batch_site_of(B, gw)];
+  const uint64_t b = (uint64_t)(S.wg_count - 1 - (gw - S.wg_begin)) * kThreads + threadIdx.x;
+  if (b >= S.nblocks) return;
+  uint32_t w[8];
+  load_block(S.x, b, w);
+  const float r6hi = 1.0f / 6.0f;
+  const float r6lo = __builtin_fmaf(-6.0f, r6hi, 1.0f) * r6hi;
+  const CaptureScale cs = capture_scale(*S.ts);
+  capture_one<false>(S.x, b, w, cs, r6hi, r6lo, S.scales, S.bits, S.codes, Planes{1, 0});
+}
+
+// ---------------------------------------------------------------------------
 // fake-quant forward (guided or plain RNE)
 // ---------------------------------------------------------------------------
 // One block of a fake-quant forward.
@@ -728,6 +799,80 @@ hipError_t launch_tensor_scale(const uint16_t* x, uint64_t nblocks, uint32_t* pa
                        reinterpret_cast<const uint4*>(x), nblocks, partial);
   hipLaunchKernelGGL(amax_finalize_kernel, dim3(1), dim3(kThreads), 0, stream, partial,
                      nblocks > 0 ? groups : 0u, ts_out);
+  return hipGetLastError();
+}
+
+// Workgroups of each site in the batch tensor-scale pass: one per tile when
+// all tiles fit in kAmaxMaxGroups, otherwise that budget shared in
+// proportion to the sites' tiles (at least one workgroup per non-empty site).
+static void batch_amax_split(const BatchSiteSpec* sites, uint32_t count, uint32_t* wg) {
+  uint64_t total = 0;
+  for (uint32_t i = 0; i < count; ++i) total += (sites[i].nblocks + kThreads - 1) / kThreads;
+  for (uint32_t i = 0; i < count; ++i) {
+    const uint64_t t = (sites[i].nblocks + kThreads - 1) / kThreads;
+    uint64_t g = t;
+    if (total > kAmaxMaxGroups && t > 0) {
+      g = (uint64_t)kAmaxMaxGroups * t / total;
+      g = g < 1 ? 1 : (g > t ? t : g);
+    }
+    wg[i] = (uint32_t)g;
+  }
+}
+
+uint32_t batch_amax_partial_count(const BatchSiteSpec* sites, uint32_t count) {
+  uint32_t wg[kMaxBatchSites];
+  batch_amax_split(sites, count, wg);
+  uint32_t total = 0;
+  for (uint32_t i = 0; i < count; ++i) total += wg[i];
+  return total;
+}
+
+static BatchSites batch_sites(const BatchSiteSpec* sites, uint32_t count, const uint32_t* wg) {
+  BatchSites B{};
+  B.count = count;
+  uint32_t begin = 0;
+  for (uint32_t i = 0; i < count; ++i) {
+    B.site[i] = BatchSite{reinterpret_cast<const uint4*>(sites[i].x), sites[i].nblocks, sites[i].ts,
+                          sites[i].scales, reinterpret_cast<uint16_t*>(sites[i].bits),
+                          reinterpret_cast<uint2*>(sites[i].codes), begin, wg[i]};
+    begin += wg[i];
+  }
+  return B;
+}
+
+hipError_t launch_tensor_scale_batch(const BatchSiteSpec* sites, uint32_t count, uint32_t* partial,
+                                     hipStream_t stream) {
+  if (count == 0) return hipSuccess;
+  uint32_t wg[kMaxBatchSites];
+  batch_amax_split(sites, count, wg);
+  const BatchSites B = batch_sites(sites, count, wg);
+  const uint32_t total = batch_amax_partial_count(sites, count);
+  if (total > 0)
+    hipLaunchKernelGGL(amax_partial_batch_kernel, dim3(total), dim3(kThreads), 0, stream, B, partial);
+  hipLaunchKernelGGL(amax_finalize_batch_kernel, dim3(count), dim3(kThreads), 0, stream, B,
+                     static_cast<const uint32_t*>(partial));
+  return hipGetLastError();
+}
+
+hipError_t launch_capture_batch(const BatchSiteSpec* sites, uint32_t count, hipStream_t stream) {
+  uint32_t wg[kMaxBatchSites];
+  uint64_t total = 0;
+  for (uint32_t i = 0; i < count; ++i) {
+    const uint64_t t = (sites[i].nblocks + kThreads - 1) / kThreads;
+    wg[i] = (uint32_t)(t < kMaxGroups ? t : kMaxGroups);
+    total += t;
+  }
+  if (total == 0) return hipSuccess;  // an empty grid is not a valid launch
+  if (total > kMaxGroups) {           // too many tiles for one grid: one launch per site
+    for (uint32_t i = 0; i < count; ++i) {
+      const hipError_t e = launch_capture(sites[i].x, sites[i].nblocks, sites[i].ts, nullptr, sites[i].scales,
+                                          sites[i].bits, sites[i].codes, stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  const BatchSites B = batch_sites(sites, count, wg);
+  hipLaunchKernelGGL(capture_batch_kernel, dim3((unsigned)total), dim3(kThreads), 0, stream, B);
   return hipGetLastError();
 }
 

@@ -40,6 +40,23 @@ struct GroupSpec {
 
 uint32_t amax_partial_count(uint64_t nblocks);
 
+// Batches of site tensors (tensor scale pass and capture over up to
+// kMaxBatchSites sites in one launch each).
+constexpr uint32_t kMaxBatchSites = 8;
+struct BatchSiteSpec {
+  const uint16_t* x;
+  uint64_t nblocks;
+  float* ts;
+  uint8_t* scales;
+  uint8_t* bits;
+  uint8_t* codes;  // nullable
+};
+// Partial-maximum words the batch tensor scale pass needs (its workspace).
+uint32_t batch_amax_partial_count(const BatchSiteSpec* sites, uint32_t count);
+hipError_t launch_tensor_scale_batch(const BatchSiteSpec* sites, uint32_t count, uint32_t* partial,
+                                     hipStream_t stream);
+hipError_t launch_capture_batch(const BatchSiteSpec* sites, uint32_t count, hipStream_t stream);
+
 hipError_t launch_tensor_scale(const uint16_t* x, uint64_t nblocks, uint32_t* partial, float* ts_out,
                                hipStream_t stream);
 // row_amax: u32[rows] workspace; ts_out: fp32[count]

@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define TRACE_ABI_VERSION 6
+#define TRACE_ABI_VERSION 7
 
 #if defined(__GNUC__)
 #define TRACE_API __attribute__((visibility("default")))
@@ -135,6 +135,45 @@ TRACE_API trace_status trace_tensor_scale(const uint16_t* x, int64_t n, void* wo
 TRACE_API trace_status trace_capture(const uint16_t* x_roll, int64_t rows, int64_t cols,
                            const float* ts, uint8_t* scales, uint8_t* bits,
                            uint8_t* codes, void* stream);
+
+/*
+ * The rollout side of several site tensors at once (a layer's activation and
+ * KV sites: the listing captures every site, the bandwidth paragraph logs
+ * every activation and KV entry).  Each site keeps its own tensor scale and
+ * record; the results equal trace_tensor_scale and trace_capture called per
+ * site, bit for bit.  The batch runs as one tensor-scale pass (two kernel
+ * launches) and one capture launch instead of three launches per site,
+ * which saves the fixed cost of filling and draining the GPU per launch on
+ * small and medium sites.
+ *   sites : host array of count descriptors, 0 <= count <= TRACE_MAX_BATCH_SITES
+ *           (count == 0 is a successful no-op); per site:
+ *     x, rows, cols : the site tensor as in trace_capture (bf16[rows*cols],
+ *                     cols % 16 == 0, 16-byte aligned; NULL when empty);
+ *     ts            : one fp32 (device): written by trace_tensor_scale_batch
+ *                     (0 for an empty site), read by trace_capture_batch;
+ *     scales, bits, codes : the record, as in trace_capture (codes may be
+ *                     NULL); unused by trace_tensor_scale_batch.
+ *   workspace : device scratch of at least
+ *               trace_tensor_scale_batch_workspace_bytes(sites, count) bytes,
+ *               4-byte aligned, caller-owned; its contents are not preserved.
+ * No output may overlap any site's input or another output (sites may share
+ * inputs, and trace_capture_batch's ts are inputs).  Errors as for the
+ * per-site calls; nothing is enqueued unless every site is valid.
+ */
+#define TRACE_MAX_BATCH_SITES 8
+typedef struct trace_site {
+  const uint16_t* x;
+  int64_t rows;
+  int64_t cols;
+  float* ts;
+  uint8_t* scales;
+  uint8_t* bits;
+  uint8_t* codes;
+} trace_site;
+TRACE_API size_t trace_tensor_scale_batch_workspace_bytes(const trace_site* sites, int32_t count);
+TRACE_API trace_status trace_tensor_scale_batch(const trace_site* sites, int32_t count, void* workspace,
+                                                size_t workspace_bytes, void* stream);
+TRACE_API trace_status trace_capture_batch(const trace_site* sites, int32_t count, void* stream);
 
 /*
  * Training-side rollout-guided fake-quant forward (the QAT half of the

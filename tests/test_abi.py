@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert tr.abi_version() == 6
+    assert tr.abi_version() == 7
     for code in range(6):
         assert L.trace_status_string(code).decode().startswith("TRACE")
     assert b"unknown" in L.trace_status_string(99)
@@ -308,3 +308,60 @@ def test_header_is_c99_and_links(tmp_path):
     subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
                     str(src), "-L", libdir, "-l:libtrace.so", f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True)
     assert subprocess.run([str(exe)]).returncode == 0
+
+
+def _batch(*sites):
+    arr = (tr._Site * max(1, len(sites)))()
+    for i, s in enumerate(sites):
+        arr[i] = tr._Site(*s)
+    return arr
+
+
+def test_batch_validation():
+    """trace_tensor_scale_batch / trace_capture_batch: every per-site rule,
+    the batch size limit and aliasing across sites, all before any HIP call."""
+    ts_b, cap_b, ws_b = L.trace_tensor_scale_batch, L.trace_capture_batch, L.trace_tensor_scale_batch_workspace_bytes
+    # site = (x, rows, cols, ts, scales, bits, codes); 4 x 4096 elements each
+    good = [(A + k * 0x1000000, 4, 4096, A + 0x8000000 + 16 * k, A + 0x9000000 + k * 0x100000,
+             A + 0xA000000 + k * 0x100000, None) for k in range(3)]
+    ws = A + 0xB000000
+    need = ws_b(_batch(*good), 3)
+    assert need == 4 * 3 * 4  # one workgroup per 4096-element tile, 4 tiles per site
+    assert ws_b(_batch(*good), 9) == 0  # an invalid batch needs no workspace
+    assert ts_b(_batch(), 0, None, 0, None) == OK and cap_b(_batch(), 0, None) == OK
+    assert ts_b(None, 2, P(ws), need, None) == E_NULL
+    assert cap_b(None, 1, None) == E_NULL
+    assert ts_b(_batch(*good), 9, P(ws), need, None) == E_SHAPE
+    assert ts_b(_batch(*good), -1, P(ws), need, None) == E_SHAPE
+    assert cap_b(_batch(*good), 9, None) == E_SHAPE
+    assert ts_b(_batch(*good), 3, P(ws), need - 4, None) == E_SHAPE
+    assert ts_b(_batch(*good), 3, None, need, None) == E_NULL
+    assert ts_b(_batch(*good), 3, P(ws + 2), need, None) == E_ALIGN
+    bad = list(good)
+    bad[1] = (good[1][0], 4, 4095) + good[1][3:]
+    assert ts_b(_batch(*bad), 3, P(ws), need, None) == E_SHAPE
+    bad[1] = (None,) + good[1][1:]
+    assert ts_b(_batch(*bad), 3, P(ws), need, None) == E_NULL
+    bad[1] = (good[1][0] + 8,) + good[1][1:]
+    assert cap_b(_batch(*bad), 3, None) == E_ALIGN
+    bad[1] = good[1][:5] + (good[1][5] + 1, None)
+    assert cap_b(_batch(*bad), 3, None) == E_ALIGN
+    bad[1] = good[1][:4] + (None,) + good[1][5:]
+    assert cap_b(_batch(*bad), 3, None) == E_NULL
+    # empty sites: NULL data is fine; the tensor scale pass still writes ts
+    empty = (None, 0, 4096, A + 0x8000100, None, None, None)
+    assert cap_b(_batch(empty, (None, 0, 16, None, None, None, None)), 2, None) == OK
+    assert ws_b(_batch(empty), 1) == 0
+    assert ts_b(_batch((None, 0, 16, None, None, None, None)), 1, P(ws), 4, None) == E_NULL
+    # aliasing across sites: site 2's ts inside site 0's tensor; site 1's bits
+    # overlapping site 0's scales; the workspace over a ts; two ts the same
+    bad = list(good)
+    bad[2] = good[2][:3] + (good[0][0] + 64,) + good[2][4:]
+    assert ts_b(_batch(*bad), 3, P(ws), need, None) == E_ALIAS
+    bad = list(good)
+    bad[1] = good[1][:5] + (good[0][4],) + good[1][6:]
+    assert cap_b(_batch(*bad), 3, None) == E_ALIAS
+    assert ts_b(_batch(*good), 3, P(good[1][3]), need, None) == E_ALIAS
+    bad = list(good)
+    bad[1] = good[1][:3] + (good[0][3],) + good[1][4:]
+    assert ts_b(_batch(*bad), 3, P(ws), need, None) == E_ALIAS

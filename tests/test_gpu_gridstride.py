@@ -1,4 +1,5 @@
-"""The grid-stride paths of every kernel.  Production grids cover a tensor
+"""The grid-stride paths of every kernel (and the batch entry points'
+small-grid splits).  Production grids cover a tensor
 in one pass up to 2^34 elements, so these loops only run for larger
 tensors; the small-grid build of the same sources (grids capped at 3
 workgroups) runs them for several iterations on test-sized tensors.  Every
@@ -86,6 +87,14 @@ def _everything(tr, xr, xt, g, offsets, perm):
     y, m, q = tr.lowbits_fakequant_fwd(xt, lsc, ts, 3, lpl, want_codes=True)
     out.update(lsc=lsc, lpl=lpl, y_l=y, m_l=m, q_l=q)
     out["stats"] = tr.mismatch_stats(xt, sc, ts, bt, cd)
+    # a batch of three sites (rows of the same tensor): in the small-grid build
+    # the tensor scale pass splits three workgroups among them and the capture
+    # falls back to one grid-stride launch per site
+    sites = [xr[0:100], xr[100:], xr[5:6]]
+    for i, (t, (bsc, bbt, bcd)) in enumerate(zip(tr.tensor_scale_batch(sites),
+                                                 tr.capture_batch(sites, tr.tensor_scale_batch(sites),
+                                                                  want_codes=True))):
+        out.update({f"batch_ts{i}": t, f"batch_sc{i}": bsc, f"batch_bt{i}": bbt, f"batch_cd{i}": bcd})
     torch.cuda.synchronize()
     return {k: _host(v) for k, v in out.items()}
 
