@@ -345,6 +345,46 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def rollout_side_rows(tr, torch, dev, stream, sites, flush, flush_ts, reps):
+    """The rollout side of a multi-site workload (tensor scale and capture of
+    every site): per-site calls against the batch entry points, each timed
+    between two HIP events after a read-only 1 GiB pass."""
+    xs = [d["x_roll"].reshape(d["x_roll"].shape[0], -1) for d in sites.values()]
+    tss = [torch.empty(1, dtype=torch.float32, device=dev) for _ in xs]
+    recs = [(torch.empty(x.numel() // 16, dtype=torch.uint8, device=dev),
+             torch.empty(x.numel() // 8, dtype=torch.uint8, device=dev), None) for x in xs]
+    ws1 = [torch.empty(tr.lib.trace_tensor_scale_workspace_bytes(x.numel()), dtype=torch.uint8, device=dev) for x in xs]
+    wsb = torch.empty(max(4, tr.lib.trace_tensor_scale_batch_workspace_bytes(tr._sites(xs, tss), len(xs))),
+                      dtype=torch.uint8, device=dev)
+
+    def per_site():
+        for x, t, w, (sc, bt, _) in zip(xs, tss, ws1, recs):
+            tr.tensor_scale(x, out=t, workspace=w)
+            tr.capture(x, t, scales=sc, bits=bt)
+
+    def batched():
+        tr.tensor_scale_batch(xs, outs=tss, workspace=wsb)
+        tr.capture_batch(xs, tss, records=recs)
+
+    per_site()
+    batched()
+    t = {"per_site": 0.0, "batched": 0.0}
+    for _ in range(reps):
+        for name, fn in (("per_site", per_site), ("batched", batched)):
+            tr.tensor_scale(flush, out=flush_ts)        # read-only 1 GiB pass
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            stream.synchronize()
+            t[name] += e0.elapsed_time(e1) / reps
+    nbytes = sum((BYTES_PER_ELEM["tensor_scale"] + BYTES_PER_ELEM["capture"]) * x.numel() for x in xs)
+    return {"sites": len(xs), "algorithmic_bytes": int(nbytes),
+            "per_site_us": round(t["per_site"] * 1e3, 1), "batched_us": round(t["batched"] * 1e3, 1),
+            "per_site_GB_s": round(nbytes / (t["per_site"] * 1e-3) / 1e9, 1),
+            "batched_GB_s": round(nbytes / (t["batched"] * 1e-3) / 1e9, 1)}
+
+
 def workload_rows(tr, workloads, torch, dev, stream, reps=3):
     """The step's five kernels on each site of the other workloads (the MoE
     layer's four sites, K and V of the KV cache, the ragged large-hidden
@@ -436,6 +476,9 @@ def workload_rows(tr, workloads, torch, dev, stream, reps=3):
         out[wname] = {"sites": res, "cold_GB_s": round(tot["bytes"] / tot["cold_s"] / 1e9, 1),
                       "warm_GB_s": round(tot["bytes"] / tot["warm_s"] / 1e9, 1)}
         log(f"workload {wname}: cold {out[wname]['cold_GB_s']} GB/s, warm {out[wname]['warm_GB_s']} GB/s")
+        if len(ws_) > 1:
+            out[wname]["rollout_side"] = rollout_side_rows(tr, torch, dev, stream, ws_, flush, flush_ts, reps)
+            log(f"  rollout side of {wname}: {out[wname]['rollout_side']}")
     del sites, flush
     return out
 
