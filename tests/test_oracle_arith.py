@@ -56,3 +56,28 @@ def test_float32_multiplication_is_correctly_rounded():
         assert float(pi) == round_f32(Fraction(float(si)) * Fraction(float(gi)))
         want = round_f32(Fraction(float(xi)) * Fraction(float(si)))
         assert float(ti) == want or (np.isinf(want) and np.isinf(ti))
+
+
+def test_sharded_tensor_scale_is_the_max_of_local_scales():
+    """Division by 2688 rounds monotonically, so max_i fl32(amax_i / 2688) =
+    fl32(max_i amax_i / 2688): an all-reduce(max) of per-shard tensor scales
+    gives the whole tensor's scale exactly (NaN, infinity and all-zero shards
+    included)."""
+    import oracle
+    rng = np.random.default_rng(2688)
+    for trial in range(200):
+        n = 16 * int(rng.integers(1, 400))
+        v = rng.standard_t(3, n) * 10.0 ** rng.uniform(-40, 38)
+        if trial % 7 == 0:
+            v[rng.integers(0, n)] = np.nan
+        if trial % 11 == 0:
+            v[rng.integers(0, n)] = np.inf
+        if trial % 13 == 0:
+            v[: n // 2] = 0.0
+        with np.errstate(over="ignore"):  # values past the fp32 range become infinities, which the rule covers
+            x = F.f32_to_bf16_rne(v.astype(np.float32))
+        cuts = np.sort(rng.choice(np.arange(0, n + 1, 16), size=int(rng.integers(1, 6)), replace=True))
+        shards = np.split(x, cuts)
+        local = [np.float32(oracle.tensor_scale(s)) for s in shards]
+        whole = np.float32(oracle.tensor_scale(x))
+        assert np.float32(max(local)).view(np.uint32) == whole.view(np.uint32), trial
