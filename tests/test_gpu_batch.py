@@ -69,7 +69,8 @@ def test_batch_mixed_sites_against_the_oracle(device, count):
 
 
 def test_batch_capture_with_a_shared_tensor_scale(device):
-    """Two sites captured with one tensor scale (an input shared by both)."""
+    """Two sites captured with one tensor scale (an input shared by both),
+    and one tensor given as two sites."""
     import fp4_rollout_guided_amd as tr
     _say("case batch capture, shared ts")
     rng = np.random.default_rng(7)
@@ -81,6 +82,13 @@ def test_batch_capture_with_a_shared_tensor_scale(device):
         cap = oracle.capture(x, np.float32(oracle.tensor_scale(host[0])), with_codes=True)
         for k, got in zip(("scales", "bits", "codes"), rec[i]):
             assert np.array_equal(to_np_u8(got), cap[k]), (i, k)
+    # one input tensor in two sites of a batch (inputs may be shared)
+    ts2 = tr.tensor_scale_batch([dev[1], dev[1]])
+    rec2 = tr.capture_batch([dev[1], dev[1]], ts2, want_codes=True)
+    torch.cuda.synchronize()
+    assert _ts_bits(ts2[0]) == _ts_bits(ts2[1]) == np.float32(oracle.tensor_scale(host[1])).view(np.uint32)
+    for a, b in zip(rec2[0], rec2[1]):
+        assert torch.equal(a, b)
 
 
 def _against_per_site(name, xs):
