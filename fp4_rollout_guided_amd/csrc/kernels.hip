@@ -246,7 +246,8 @@ struct RowGroups {
   uint32_t count;
   uint64_t rows;
   uint64_t bpr;        // 16-element blocks per row
-  float per_block;     // count / blocks: the group a block would fall in if all groups were equal
+  uint64_t per_block;  // count / blocks in 32.32 fixed point, below 2^32: the group a block
+                       // would fall in if all groups were equal
 };
 
 __device__ __forceinline__ uint64_t group_row(const RowGroups& G, uint32_t g) {
@@ -262,19 +263,20 @@ __device__ __forceinline__ uint64_t group_start(const RowGroups& G, uint32_t g) 
   return group_row(G, g) * G.bpr;
 }
 
-// Tensor scale of block b's group.  The group of the wave's first active
-// block is found wave-uniformly with scalar loads: first from a guess that
-// assumes equal groups, checked against a window of three groups whose
-// starts and scales are fetched in one round of independent loads (enough
-// for balanced expert loads); otherwise by binary search.  Lanes past the
-// next group start (a group boundary inside the wave's span, rare) walk on
-// with per-lane loads.
-__device__ __forceinline__ float group_tensor_scale(const RowGroups& G, const float* __restrict__ ts, uint64_t b) {
-  const uint32_t b0lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
-  const uint32_t b0hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
-  const uint64_t b0 = ((uint64_t)b0hi << 32) | b0lo;
-  const float gf = __builtin_fminf((float)b0 * G.per_block, (float)(G.count - 1));
-  const uint32_t guess = __builtin_amdgcn_readfirstlane((uint32_t)gf);
+// Tensor scale of block b's group; b0 is the first block of the workgroup's
+// tile (workgroup-uniform, b0 <= b).  The group of b0 is found with scalar
+// work only: a guess that assumes equal groups (an integer multiply by the
+// fixed-point count / blocks, no vector-to-scalar moves), checked against a
+// window of three groups whose starts and scales come in one round of
+// independent scalar loads (enough for balanced expert loads); otherwise by
+// binary search.  Lanes past the next group start (a group boundary inside
+// the tile, rare) walk on with per-lane loads.  Computing the guess from a
+// lane's block instead (a readfirstlane and float arithmetic before the
+// loads) made the per-expert capture 12% slower.
+__device__ __forceinline__ float group_tensor_scale(const RowGroups& G, const float* __restrict__ ts, uint64_t b0,
+                                                   uint64_t b) {
+  const uint32_t g0 = (uint32_t)__umul64hi(b0, G.per_block << 32);  // floor(b0 * count / blocks), within 2
+  const uint32_t guess = g0 < G.count - 1 ? g0 : G.count - 1;
   uint32_t lo = G.count;  // not found yet
   float t = 0.f;
   uint64_t next = 0;
@@ -469,10 +471,11 @@ __global__ __launch_bounds__(kThreads) void capture_kernel(const uint4* __restri
   // Tiles are taken from the tensor's end backwards: the tensor amax, which
   // reads the same tensor just before, leaves its last-read lines in the
   // 256 MB last-level cache, and the capture reaches them first.
-  for (uint64_t b = (uint64_t)(gridDim.x - 1 - blockIdx.x) * kThreads + threadIdx.x; b < nblocks; b += stride) {
+  uint64_t b0 = (uint64_t)(gridDim.x - 1 - blockIdx.x) * kThreads;  // the tile's first block (uniform)
+  for (uint64_t b = b0 + threadIdx.x; b < nblocks; b += stride, b0 += stride) {
     uint32_t w[8];
     load_block(x, b, w);  // issued before the group search, whose latency it hides
-    const CaptureScale cs = kGrouped ? capture_scale(group_tensor_scale(groups, ts_ptr, b)) : cs0;
+    const CaptureScale cs = kGrouped ? capture_scale(group_tensor_scale(groups, ts_ptr, b0, b)) : cs0;
     capture_one<kPlanes>(x, b, w, cs, r6hi, r6lo, scales, bits, codes, planes);
   }
 }
@@ -590,13 +593,14 @@ __global__ __launch_bounds__(kThreads) void fakequant_grouped_kernel(const uint4
                                                              uint16_t* __restrict__ mask,
                                                              uint2* __restrict__ qcodes) {
   const uint64_t stride = (uint64_t)gridDim.x * kThreads;
-  for (uint64_t b = (uint64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks; b += stride) {
+  uint64_t b0 = (uint64_t)blockIdx.x * kThreads;  // the tile's first block (uniform)
+  for (uint64_t b = b0 + threadIdx.x; b < nblocks; b += stride, b0 += stride) {
     const uint32_t sbyte = scales[b];
     const uint32_t cached = kMode == 1 ? (uint32_t)bits[b] : 0u;
     const uint2 roll = kMode == 2 ? rcodes[b] : make_uint2(0u, 0u);
     uint32_t w[8];
     load_block(x, b, w);  // all loads are issued before the group search
-    const float ts = group_tensor_scale(groups, ts_ptr, b);
+    const float ts = group_tensor_scale(groups, ts_ptr, b0, b);
     fakequant_one<kMode>(x, b, w, sbyte, cached, roll, ts, y, mask, qcodes);
   }
 }
@@ -877,8 +881,14 @@ hipError_t launch_capture_batch(const BatchSiteSpec* sites, uint32_t count, hipS
 }
 
 static RowGroups row_groups(const GroupSpec& g, uint64_t nblocks = 0) {
-  return RowGroups{g.offsets, (uint32_t)g.count, g.rows, g.cols / 16,
-                   nblocks ? (float)((double)g.count / (double)nblocks) : 0.f};
+  // count / blocks in 32.32 fixed point, kept below 2^32 (more groups than
+  // blocks: the guess is then off and the binary search finds the group)
+  uint64_t fx = 0;
+  if (nblocks) {
+    const unsigned __int128 q = ((unsigned __int128)g.count << 32) / nblocks;
+    fx = q < 0xffffffffull ? (uint64_t)q : 0xffffffffull;
+  }
+  return RowGroups{g.offsets, (uint32_t)g.count, g.rows, g.cols / 16, fx};
 }
 
 hipError_t launch_grouped_tensor_scale(const uint16_t* x, const GroupSpec& g, uint32_t* row_amax, float* ts_out,
