@@ -50,6 +50,8 @@ CASES = [
     ("balanced-16", 1024, 64, lambda rng: np.arange(0, 1025, 64)),
     ("near-balanced", 4096, 32, lambda rng: np.r_[0, np.arange(1, 64) * 64 + rng.integers(-25, 25, 63), 4096]),
     ("balanced-empties", 960, 48, lambda rng: np.array([0, 0, 240, 240, 480, 720, 720, 960, 960])),
+    # more groups than blocks: the fixed-point ratio clamps, the binary search finds the group
+    ("more-groups-than-blocks", 3, 16, lambda rng: np.array([0, 0, 0, 1, 1, 1, 2, 2, 3, 3, 3])),
 ]
 
 
