@@ -102,33 +102,30 @@ def e4m3fn_encode_rne_sat(values) -> np.ndarray:
     return np.where(take_hi, hi, lo).astype(np.uint8)
 
 
-def e2m1_rne_index(a, chunk: int = 1 << 20) -> np.ndarray:
+def e2m1_rne_index(a) -> np.ndarray:
     """Magnitude index (0..7) of the E2M1 value nearest to ``a`` (a float32
     array with values in [0, 6]); ties go to the even index, i.e. to the
-    codeword whose mantissa bit is 0."""
-    a = np.asarray(a, dtype=np.float32).reshape(-1)
-    out = np.empty(a.shape, dtype=np.uint8)
-    for start in range(0, a.size, chunk):
-        seg = a[start:start + chunk].astype(np.float64)
-        d = np.abs(seg[:, None] - E2M1_MAGNITUDES[None, :])
-        dmin = d.min(axis=1)
-        at_min = d == dmin[:, None]
-        first = np.argmax(at_min, axis=1)
-        nxt = np.minimum(first + 1, 7)
-        second = at_min[np.arange(seg.size), nxt] & (nxt != first)
-        out[start:start + chunk] = np.where(second & (first % 2 == 1), nxt, first)
-    return out
+    codeword whose mantissa bit is 0.
+
+    The two candidates are the smallest grid value >= a and the one below
+    it (the grid is sorted); their distances to a are exact in float64, so
+    the nearer one wins and an exact tie goes to the even index."""
+    v = np.asarray(a, dtype=np.float32).reshape(-1).astype(np.float64)
+    hi = np.minimum(np.searchsorted(E2M1_MAGNITUDES, v, side="left"), 7)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = np.abs(v - E2M1_MAGNITUDES[lo])
+    d_hi = np.abs(E2M1_MAGNITUDES[hi] - v)
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    return np.where(take_hi, hi, lo).astype(np.uint8)
 
 
-def e2m1_bracket(a, chunk: int = 1 << 20):
+def e2m1_bracket(a):
     """Indices (lo, hi) of the two E2M1 magnitudes enclosing ``a`` in [0, 6]:
     lo = largest grid value <= a, hi = smallest grid value >= a.  They are
-    equal exactly when ``a`` is itself a grid value."""
-    a = np.asarray(a, dtype=np.float32).reshape(-1)
-    lo = np.empty(a.shape, dtype=np.uint8)
-    hi = np.empty(a.shape, dtype=np.uint8)
-    for start in range(0, a.size, chunk):
-        seg = a[start:start + chunk].astype(np.float64)[:, None]
-        lo[start:start + chunk] = (seg >= E2M1_MAGNITUDES[None, :]).sum(axis=1) - 1
-        hi[start:start + chunk] = (seg > E2M1_MAGNITUDES[None, :]).sum(axis=1)
-    return lo, hi
+    equal exactly when ``a`` is itself a grid value.  On the sorted grid, the
+    number of grid values <= a, minus one, is lo, and the number of grid
+    values < a is hi."""
+    v = np.asarray(a, dtype=np.float32).reshape(-1).astype(np.float64)
+    lo = np.searchsorted(E2M1_MAGNITUDES, v, side="right") - 1
+    hi = np.searchsorted(E2M1_MAGNITUDES, v, side="left")
+    return lo.astype(np.uint8), hi.astype(np.uint8)

@@ -14,7 +14,7 @@ import time
 import numpy as np
 
 CPU_SHARE = 16          # host cores granted to a process driving one GPU
-CHUNK_ELEMS = 1 << 20   # elements per worker task (a multiple of 16)
+CHUNK_ELEMS = 1 << 17   # elements per worker task (a multiple of 16; small chunks keep the oracle's temporaries in cache)
 
 _POOL = None
 
