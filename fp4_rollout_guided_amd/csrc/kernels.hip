@@ -427,7 +427,14 @@ __device__ __forceinline__ void capture_one(const uint4* __restrict__ x, uint64_
   sb = cs.valid ? sb : 0u;
 
   const ScaleEntry e = make_scale_entry(sb, ts);
-  bad |= !(e.dhi == e.dhi);  // scale outside the fast range
+  // The first approximation q1 = fma(x, dhi, x*dlo) is monotone in |x|
+  // (dhi, dlo >= 0), so the block maximum's bounds every element's.  Below
+  // 2^127 every quotient of the block is finite and Markstein's correction
+  // applies; at or above it (a saturated scale byte under a small tensor
+  // scale with a huge element: |x| / (448 ts) near binary32 overflow), and
+  // for a scale outside the fast range (dhi NaN), the block takes the exact
+  // path.  No per-element flag is needed.
+  bad |= !(__builtin_fmaf(amax, e.dhi, amax * e.dlo) < 0x1p127f);
 
   float q[16];
 #pragma unroll

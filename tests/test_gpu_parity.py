@@ -93,6 +93,13 @@ def test_special_values_bit_exact(device):
     for ts in (0.5, 1.0, 2.0 ** -20, np.inf, 0.0, -1.0, np.nan):
         got, want = _run_both(xr, xt, g, shape, device, ts=np.float32(ts))
         assert_same(got, want, ctx=f"special ts={ts}")
+    # a +-2^117 block under ts = 2^-20: scale byte 0x7E, |x| / s past the largest float
+    big = _bf16_np([2.0 ** 117, -2.0 ** 117, 2.0 ** 117, -1.0] + [-2.0 ** 117] * 4 + [3.0, -0.0] + [2.0 ** 116] * 6)
+    xr2, xt2, g2 = np.concatenate([xr, big]), np.concatenate([xt, big]), np.concatenate([g, g[:16]])
+    got, want = _run_both(xr2, xt2, g2, (xr2.size // 16, 16), device, ts=np.float32(2.0 ** -20))
+    # s = 448 * 2^-20: every quotient clips to +-6 (code 7 with the sign), -0 stays -0 (0x8)
+    assert want["codes"][-8:].tolist() == [0xF7, 0xF7, 0xFF, 0xFF, 0x87, 0x77, 0x77, 0x77]
+    assert_same(got, want, ctx="special +-2^117 block, ts=2^-20")
 
 
 def test_tensor_scale_cases(device):
@@ -150,11 +157,13 @@ def test_fwd_exhaustive_bf16_by_scale_byte(device, ts):
     assert_same({"y": to_np_u16(yf), "mask": to_np_u8(mf), "codes": to_np_u8(qf)}, wf, ctx=f"full ts={ts}")
 
 
-@pytest.mark.parametrize("ts", [1.0, 0.0123456, 7.5e-37, 1.0e30])
+@pytest.mark.parametrize("ts", [1.0, 0.0123456, 7.5e-37, 1.0e30, 2.0 ** -20, 2.0 ** -60])
 def test_capture_exhaustive_block_amax(device, ts):
     """Block maxima over every finite positive bf16 magnitude (plus Inf and
     NaN blocks), the other 15 elements random fractions of the maximum,
-    under an explicit tensor scale: exercises every scale-byte path."""
+    under an explicit tensor scale: exercises every scale-byte path.  Under
+    2^-20 and 2^-60 the largest maxima saturate the scale byte and their
+    quotients pass the largest float (codes +-7)."""
     import fp4_rollout_guided_amd as tr
     _say("case capture amax sweep ts", ts)
     rng = np.random.default_rng(42)
