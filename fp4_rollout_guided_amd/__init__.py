@@ -143,6 +143,31 @@ def _bf16(t, name):
     return t
 
 
+_U8 = (torch.uint8,)
+_F32 = (torch.float32,)
+_I64 = (torch.int64,)
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _arg(t, name, like, dtypes, numel):
+    """Check a tensor argument before its pointer reaches the C ABI (which
+    sees no sizes or devices): on ``like``'s device, contiguous, of one of
+    ``dtypes``, and holding at least ``numel`` elements.  A host tensor
+    beside device data, or a short buffer, would otherwise be read or
+    written out of bounds by a kernel."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor, got {type(t).__name__}")
+    if t.device != like.device:
+        raise ValueError(f"{name} must be on {like.device} (the data's device), got {t.device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must be {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} needs at least {numel} elements, got {t.numel()}")
+    return t
+
+
 def _rows_cols(t):
     cols = t.shape[-1] if t.dim() > 0 else 1
     rows = t.numel() // cols if cols else 0
@@ -152,9 +177,13 @@ def _rows_cols(t):
 def _u8(n, like, out, name):
     if out is None:
         return torch.empty(n, dtype=torch.uint8, device=like.device)
-    if out.dtype != torch.uint8 or out.numel() < n or not out.is_contiguous() or out.device != like.device:
-        raise ValueError(f"{name} must be a contiguous uint8 device tensor of at least {n} bytes")
-    return out
+    return _arg(out, name, like, _U8, n)
+
+
+def _bf16_out(out, like, n, name):
+    if out is None:
+        return torch.empty_like(like)
+    return _arg(out, name, like, _BF16, n)
 
 
 def _check(status, what):
@@ -173,8 +202,10 @@ def tensor_scale(x, out=None, workspace=None):
     need = lib.trace_tensor_scale_workspace_bytes(n)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _arg(workspace, "workspace", x, _U8, need)
     if out is None:
         out = torch.empty(1, dtype=torch.float32, device=x.device)
+    _arg(out, "out", x, _F32, 1)
     _check(lib.trace_tensor_scale(_ptr(x), n, _ptr(workspace), workspace.numel(), _ptr(out), _stream(x)),
            "trace_tensor_scale")
     return out
@@ -186,6 +217,7 @@ def capture(x_roll, ts, want_codes=False, scales=None, bits=None, codes=None):
     _bf16(x_roll, "x_roll")
     rows, cols = _rows_cols(x_roll)
     n = rows * cols
+    _arg(ts, "ts", x_roll, _F32, 1)
     scales = _u8(n // 16, x_roll, scales, "scales")
     bits = _u8(n // 8, x_roll, bits, "bits")
     if want_codes or codes is not None:
@@ -209,10 +241,19 @@ def _sites(xs, tss, records=None):
     if len(xs) > MAX_BATCH_SITES:
         raise ValueError(f"at most {MAX_BATCH_SITES} sites per batch, got {len(xs)}")
     arr = (_Site * max(1, len(xs)))()
+    if len(tss) != len(xs) or (records is not None and len(records) != len(xs)):
+        raise ValueError("one tensor scale (and record) per site is required")
     for i, x in enumerate(xs):
         _bf16(x, f"xs[{i}]")
         rows, cols = _rows_cols(x)
+        n = rows * cols
+        _arg(tss[i], f"ts[{i}]", x, _F32, 1)
         sc, bt, cd = records[i] if records is not None else (None, None, None)
+        if records is not None:
+            _arg(sc, f"scales[{i}]", x, _U8, n // 16)
+            _arg(bt, f"bits[{i}]", x, _U8, n // 8)
+            if cd is not None:
+                _arg(cd, f"codes[{i}]", x, _U8, n // 2)
         arr[i] = _Site(x.data_ptr() if x.numel() else None, rows, cols, tss[i].data_ptr(),
                        None if sc is None else sc.data_ptr(), None if bt is None else bt.data_ptr(),
                        None if cd is None else cd.data_ptr())
@@ -230,6 +271,7 @@ def tensor_scale_batch(xs, outs=None, workspace=None):
     need = lib.trace_tensor_scale_batch_workspace_bytes(arr, len(xs))
     if workspace is None:
         workspace = torch.empty(max(4, need), dtype=torch.uint8, device=dev)
+    _arg(workspace, "workspace", xs[0], _U8, need)
     _check(lib.trace_tensor_scale_batch(arr, len(xs), _ptr(workspace), workspace.numel(), _stream(xs[0])),
            "trace_tensor_scale_batch")
     return outs
@@ -255,10 +297,11 @@ def _fwd(mode, x, scales, ts, side, y, mask, want_codes, qcodes):
     _bf16(x, "x_train")
     rows, cols = _rows_cols(x)
     n = rows * cols
-    if y is None:
-        y = torch.empty_like(x)
-    else:
-        _bf16(y, "y")
+    _arg(scales, "scales", x, _U8, n // 16)
+    _arg(ts, "ts", x, _F32, 1)
+    if mode != "rne":
+        _arg(side, "bits" if mode == "guided" else "codes", x, _U8, n // 8 if mode == "guided" else n // 2)
+    y = _bf16_out(y, x, n, "y")
     mask = _u8(n // 8, x, mask, "mask")
     if want_codes or qcodes is not None:
         qcodes = _u8(n // 2, x, qcodes, "qcodes")
@@ -294,10 +337,9 @@ def full_info_fakequant_fwd(x_train, scales, ts, codes, y=None, mask=None, want_
 def ste_bwd(grad_out, mask, grad_in=None):
     """Straight-through estimator backward: grad_out where mask is set."""
     _bf16(grad_out, "grad_out")
-    if grad_in is None:
-        grad_in = torch.empty_like(grad_out)
-    else:
-        _bf16(grad_in, "grad_in")
+    n = grad_out.numel()
+    _arg(mask, "mask", grad_out, _U8, n // 8)
+    grad_in = _bf16_out(grad_in, grad_out, n, "grad_in")
     _check(lib.trace_ste_bwd(_ptr(grad_out), _ptr(mask), grad_out.numel(), _ptr(grad_in), _stream(grad_out)),
            "trace_ste_bwd")
     return grad_in
@@ -311,6 +353,11 @@ def gather_records(bits, scales, codes, cols, row_index):
     src_rows = scales.numel() * 16 // cols if cols else 0
     dst_rows = row_index.numel()
     n = dst_rows * cols
+    n_src = src_rows * cols
+    _arg(scales, "scales", row_index, _U8, n_src // 16)
+    _arg(bits, "bits", row_index, _U8, n_src // 8)
+    if codes is not None:
+        _arg(codes, "codes", row_index, _U8, n_src // 2)
     bits_d = torch.empty(n // 8, dtype=torch.uint8, device=bits.device)
     scales_d = torch.empty(n // 16, dtype=torch.uint8, device=bits.device)
     codes_d = torch.empty(n // 2, dtype=torch.uint8, device=bits.device) if codes is not None else None
@@ -320,9 +367,10 @@ def gather_records(bits, scales, codes, cols, row_index):
     return bits_d, scales_d, codes_d
 
 
-def _offsets(offsets, rows):
-    if not offsets.is_cuda or offsets.dtype != torch.int64 or not offsets.is_contiguous() or offsets.dim() != 1:
-        raise ValueError("offsets must be a contiguous 1-D int64 device tensor of groups + 1 entries")
+def _offsets(offsets, x):
+    _arg(offsets, "offsets", x, _I64, 2)
+    if offsets.dim() != 1:
+        raise ValueError("offsets must be a 1-D int64 device tensor of groups + 1 entries")
     groups = offsets.numel() - 1
     if groups < 1:
         raise ValueError("at least one group is required")
@@ -334,12 +382,14 @@ def grouped_tensor_scale(x, offsets, out=None, workspace=None):
     [offsets[g], offsets[g+1]) / 2688), as a float32[groups] device tensor."""
     _bf16(x, "x")
     rows, cols = _rows_cols(x)
-    groups = _offsets(offsets, rows)
+    groups = _offsets(offsets, x)
     need = lib.trace_grouped_tensor_scale_workspace_bytes(rows)
     if workspace is None:
         workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=x.device)
+    _arg(workspace, "workspace", x, _U8, need)
     if out is None:
         out = torch.empty(groups, dtype=torch.float32, device=x.device)
+    _arg(out, "out", x, _F32, groups)
     _check(lib.trace_grouped_tensor_scale(_ptr(x), rows, cols, _ptr(offsets), groups, _ptr(workspace),
                                           workspace.numel(), _ptr(out), _stream(x)), "trace_grouped_tensor_scale")
     return out
@@ -349,8 +399,9 @@ def grouped_capture(x_roll, offsets, ts, want_codes=False, scales=None, bits=Non
     """``capture`` with ts[group of the row] as each row's tensor scale."""
     _bf16(x_roll, "x_roll")
     rows, cols = _rows_cols(x_roll)
-    groups = _offsets(offsets, rows)
+    groups = _offsets(offsets, x_roll)
     n = rows * cols
+    _arg(ts, "ts", x_roll, _F32, groups)
     scales = _u8(n // 16, x_roll, scales, "scales")
     bits = _u8(n // 8, x_roll, bits, "bits")
     if want_codes or codes is not None:
@@ -363,12 +414,13 @@ def grouped_capture(x_roll, offsets, ts, want_codes=False, scales=None, bits=Non
 def _grouped_fwd(mode, x, offsets, scales, ts, side, y, mask, want_codes, qcodes):
     _bf16(x, "x_train")
     rows, cols = _rows_cols(x)
-    groups = _offsets(offsets, rows)
+    groups = _offsets(offsets, x)
     n = rows * cols
-    if y is None:
-        y = torch.empty_like(x)
-    else:
-        _bf16(y, "y")
+    _arg(scales, "scales", x, _U8, n // 16)
+    _arg(ts, "ts", x, _F32, groups)
+    if mode != "rne":
+        _arg(side, "bits" if mode == "guided" else "codes", x, _U8, n // 8 if mode == "guided" else n // 2)
+    y = _bf16_out(y, x, n, "y")
     mask = _u8(n // 8, x, mask, "mask")
     if want_codes or qcodes is not None:
         qcodes = _u8(n // 2, x, qcodes, "qcodes")
@@ -408,8 +460,9 @@ def capture_lowbits(x_roll, ts, nbits, want_codes=False, scales=None, planes=Non
     _bf16(x_roll, "x_roll")
     rows, cols = _rows_cols(x_roll)
     n = rows * cols
+    _arg(ts, "ts", x_roll, _F32, 1)
     scales = _u8(n // 16, x_roll, scales, "scales")
-    planes = _u8(nbits * (n // 8), x_roll, planes, "planes")
+    planes = _u8(max(0, nbits) * (n // 8), x_roll, planes, "planes")
     if want_codes or codes is not None:
         codes = _u8(n // 2, x_roll, codes, "codes")
     _check(lib.trace_capture_lowbits(_ptr(x_roll), rows, cols, _ptr(ts), nbits, _ptr(scales), _ptr(planes),
@@ -422,10 +475,10 @@ def lowbits_fakequant_fwd(x_train, scales, ts, nbits, planes, y=None, mask=None,
     _bf16(x_train, "x_train")
     rows, cols = _rows_cols(x_train)
     n = rows * cols
-    if y is None:
-        y = torch.empty_like(x_train)
-    else:
-        _bf16(y, "y")
+    _arg(scales, "scales", x_train, _U8, n // 16)
+    _arg(ts, "ts", x_train, _F32, 1)
+    _arg(planes, "planes", x_train, _U8, max(0, nbits) * (n // 8))
+    y = _bf16_out(y, x_train, n, "y")
     mask = _u8(n // 8, x_train, mask, "mask")
     if want_codes or qcodes is not None:
         qcodes = _u8(n // 2, x_train, qcodes, "qcodes")
@@ -453,10 +506,10 @@ def _mx_fwd(mode, x, scales, side, y, mask, want_codes, qcodes):
     _bf16(x, "x_train")
     rows, cols = _rows_cols(x)
     n = rows * cols
-    if y is None:
-        y = torch.empty_like(x)
-    else:
-        _bf16(y, "y")
+    _arg(scales, "scales", x, _U8, n // 32)
+    if mode != "rne":
+        _arg(side, "bits" if mode == "guided" else "codes", x, _U8, n // 8 if mode == "guided" else n // 2)
+    y = _bf16_out(y, x, n, "y")
     mask = _u8(n // 8, x, mask, "mask")
     if want_codes or qcodes is not None:
         qcodes = _u8(n // 2, x, qcodes, "qcodes")
@@ -507,10 +560,10 @@ def _mx8_fwd(mode, x, scales, side, y, mask, want_codes, qcodes):
     _bf16(x, "x_train")
     rows, cols = _rows_cols(x)
     n = rows * cols
-    if y is None:
-        y = torch.empty_like(x)
-    else:
-        _bf16(y, "y")
+    _arg(scales, "scales", x, _U8, n // 32)
+    if mode != "rne":
+        _arg(side, "bits" if mode == "guided" else "codes", x, _U8, n // 8 if mode == "guided" else n)
+    y = _bf16_out(y, x, n, "y")
     mask = _u8(n // 8, x, mask, "mask")
     if want_codes or qcodes is not None:
         qcodes = _u8(n, x, qcodes, "qcodes")
@@ -556,10 +609,14 @@ def mismatch_stats(x_train, scales, ts, bits, codes, stats=None):
     violations, elements (the counts are below 2^63)."""
     _bf16(x_train, "x_train")
     rows, cols = _rows_cols(x_train)
+    n = rows * cols
+    _arg(scales, "scales", x_train, _U8, n // 16)
+    _arg(ts, "ts", x_train, _F32, 1)
+    _arg(bits, "bits", x_train, _U8, n // 8)
+    _arg(codes, "codes", x_train, _U8, n // 2)
     if stats is None:
         stats = torch.zeros(20, dtype=torch.int64, device=x_train.device)
-    elif stats.dtype != torch.int64 or stats.numel() != 20 or not stats.is_contiguous():
-        raise ValueError("stats must be a contiguous int64 tensor of 20 elements")
+    _arg(stats, "stats", x_train, _I64, 20)
     _check(lib.trace_mismatch_stats(_ptr(x_train), rows, cols, _ptr(scales), _ptr(ts), _ptr(bits), _ptr(codes),
                                     _ptr(stats), _stream(x_train)), "trace_mismatch_stats")
     return stats

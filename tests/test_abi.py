@@ -365,3 +365,25 @@ def test_batch_validation():
     bad = list(good)
     bad[1] = good[1][:3] + (good[0][3],) + good[1][4:]
     assert ts_b(_batch(*bad), 3, P(ws), need, None) == E_ALIAS
+
+
+def test_binding_argument_checks():
+    """The binding's check of every tensor argument (the C ABI sees neither
+    sizes nor devices): another device than the data's, wrong dtype,
+    non-contiguous and short buffers are refused with an exception."""
+    import torch
+    x = torch.zeros(4, 32, dtype=torch.bfloat16)
+    ok = torch.zeros(16, dtype=torch.uint8)
+    assert tr._arg(ok, "bits", x, tr._U8, 16) is ok
+    with pytest.raises(ValueError, match="must be on"):
+        tr._arg(torch.zeros(16, dtype=torch.uint8, device="meta"), "bits", x, tr._U8, 16)
+    with pytest.raises(TypeError, match="must be"):
+        tr._arg(torch.zeros(16, dtype=torch.int8), "bits", x, tr._U8, 16)
+    with pytest.raises(ValueError, match="at least 16"):
+        tr._arg(torch.zeros(15, dtype=torch.uint8), "bits", x, tr._U8, 16)
+    with pytest.raises(ValueError, match="contiguous"):
+        tr._arg(torch.zeros(32, dtype=torch.uint8)[::2], "bits", x, tr._U8, 16)
+    with pytest.raises(TypeError, match="tensor"):
+        tr._arg(None, "ts", x, tr._F32, 1)
+    with pytest.raises(TypeError):
+        tr._arg(torch.zeros(1, dtype=torch.float64), "ts", x, tr._F32, 1)

@@ -1,12 +1,12 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
 benchmark uses (one call per site tensor): every element of every output of
-every site against the oracle, bit for bit (``tests/full_compare.py``; of
-the deeper-half sweep, layers 0 and 19), after a quick check on sampled
-rows (the first row, random rows and the last rows, which include the
-ragged tail of the large-hidden workload).  The tensor scale of every site
-is checked over the whole tensor, and every element of every output against
-the whole-tensor properties of ``tests/full_props.py`` (on all 20 layers of
-the deeper-half sweep too).  Where a workload is built around rollout /
+every site against the oracle, bit for bit (``tests/full_compare.py``), on
+every workload including all 20 layers of the deeper-half sweep (one case
+per layer), and on sampled rows (the first row, random rows and the last
+rows, which include the ragged tail of the large-hidden workload).  The
+tensor scale of every site is checked over the whole tensor, and every
+element of every output against the whole-tensor properties of
+``tests/full_props.py``.  Where a workload is built around rollout /
 training agreement, the oracle's mismatch statistics on the sample are
 checked against what the rule guarantees (straddle sites are recovered,
 two-codeword mismatches fall back to RNE) and printed."""
@@ -20,14 +20,13 @@ import torch
 
 import oracle
 import workloads
-from tests.full_compare import compare_every_element
+from tests.full_compare import Shared, compare_every_element, tensor_scale_of
 from tests.full_props import check_nvfp4_outputs
 from tests.gpu_util import assert_same, oracle_path, to_np_u16, to_np_u8
 from tests.workload_place import oracle_block_scales, place_kv, place_near_midpoints
 
 pytestmark = pytest.mark.gpu
 HERE = os.path.dirname(os.path.abspath(__file__))
-FULL_SWEEP = os.environ.get("TRACE_FULL_SWEEP") == "1"
 
 
 def _say(*a):
@@ -59,21 +58,16 @@ def _gather(t, idx, per_row, u16=False):
     return to_np_u16(v) if u16 else to_np_u8(v)
 
 
-def check_site(name, x_roll, x_train, grad, k_rows=128, seed=0, every_element=True):
+def check_site(name, x_roll, x_train, grad, k_rows=128, seed=0):
     rows, cols = x_roll.shape[0], x_roll.numel() // x_roll.shape[0]
-    _say(f"case {name}: {tuple(x_roll.shape)} ({x_roll.numel()} elements), {k_rows} sampled rows, then every element")
-    got = _gpu_full(x_roll, x_train, grad)
-    check_nvfp4_outputs(name, x_roll, x_train, grad, got["ts"], got)
-    xr_all = to_np_u16(x_roll)
-    ts = oracle.tensor_scale(xr_all)
-    assert got["ts"].cpu().numpy().view(np.uint32)[0] == np.float32(ts).view(np.uint32), name
-    # every element of every output against the oracle
-    if every_element:
-        host = {k: (to_np_u16(v) if k in ("y_g", "y_r", "y_f", "gin") else to_np_u8(v))
-                for k, v in got.items() if k != "ts"}
-        compare_every_element(name, xr_all, to_np_u16(x_train), to_np_u16(grad), np.float32(ts), host)
-        del host
-    del xr_all
+    _say(f"case {name}: {tuple(x_roll.shape)} ({x_roll.numel()} elements), every element, then {k_rows} sampled rows")
+    with Shared({"xr": x_roll, "xt": x_train, "g": grad}) as sh:
+        ts = tensor_scale_of(sh)          # the oracle's, over the whole tensor
+        got = _gpu_full(x_roll, x_train, grad)
+        check_nvfp4_outputs(name, x_roll, x_train, grad, got["ts"], got)
+        assert got["ts"].cpu().numpy().view(np.uint32)[0] == np.float32(ts).view(np.uint32), name
+        # every element of every output against the oracle
+        compare_every_element(name, sh, {k: v for k, v in got.items() if k != "ts"}, ts)
     idx = _rows(rows, k_rows, seed)
     xr = _gather(x_roll.view(torch.int16), idx, cols, True)
     xt = _gather(x_train.view(torch.int16), idx, cols, True)
@@ -157,44 +151,16 @@ def test_kv_cache(device, which):
     assert st["hist"][1] > 0 and sum(st["hist"][4:]) == 0
 
 
-@pytest.mark.parametrize("layer", [0, 19])
-def test_deeper_half_layer(device, layer):
-    d = workloads.deeper_half_layer(device, layer)
-    # layer 0 in full by default; every layer in full under TRACE_FULL_SWEEP=1
-    st = check_site(f"deeper-half layer {layer}", d["x_roll"], d["x_train"], d["grad"], seed=30 + layer,
-                    every_element=layer == 0 or FULL_SWEEP)
-    assert st["recovered"] >= st["straddle"]
-
-
-def test_deeper_half_every_layer_whole_tensor(device):
-    """All 20 layers of the deeper-half sweep, every element of every output
-    checked against the whole-tensor properties (layers 0 and 19 are also
-    compared with the oracle on sampled rows above)."""
-    for layer in range(20):
-        d = workloads.deeper_half_layer(device, layer)
-        _say(f"case deeper-half layer {layer}: whole-tensor properties")
-        got = _gpu_full(d["x_roll"], d["x_train"], d["grad"])
-        check_nvfp4_outputs(f"deeper-half layer {layer}", d["x_roll"], d["x_train"], d["grad"], got["ts"], got)
-        del d, got
-
-
-@pytest.mark.skipif(not FULL_SWEEP,
-                    reason="every element of all 20 layers takes ~6 minutes; set TRACE_FULL_SWEEP=1 to run it")
 @pytest.mark.parametrize("layer", range(20))
-def test_deeper_half_layer_every_element_sweep(device, layer):
-    """One layer of the deeper-half sweep per case: every element of every
-    output against the oracle (layers 0 and 19 also run by default above)."""
+def test_deeper_half_layer(device, layer):
+    """One layer of the deeper-half sweep per case (the latter 20 of 40
+    layers): every element of every output against the oracle and against
+    the whole-tensor properties, the oracle's agreement statistics on
+    sampled rows and the GPU's over the whole layer."""
     d = workloads.deeper_half_layer(device, layer)
-    _say(f"case deeper-half layer {layer}: every element")
-    got = _gpu_full(d["x_roll"], d["x_train"], d["grad"])
-    xr_all = to_np_u16(d["x_roll"])
-    ts = oracle.tensor_scale(xr_all)
-    assert got["ts"].cpu().numpy().view(np.uint32)[0] == np.float32(ts).view(np.uint32)
-    host = {k: (to_np_u16(v) if k in ("y_g", "y_r", "y_f", "gin") else to_np_u8(v))
-            for k, v in got.items() if k != "ts"}
-    compare_every_element(f"deeper-half layer {layer}", xr_all, to_np_u16(d["x_train"]), to_np_u16(d["grad"]),
-                          np.float32(ts), host)
-    del d, got, host, xr_all
+    st = check_site(f"deeper-half layer {layer}", d["x_roll"], d["x_train"], d["grad"], seed=30 + layer)
+    assert st["recovered"] >= st["straddle"]
+    del d
 
 
 def test_large_hidden_ragged(device):

@@ -4,8 +4,8 @@ backward on their mask) through the C ABI against ``oracle.mx8``, bit for
 bit.  Covers ragged shapes over several tiles, every bf16 pattern under
 every E8M0 scale byte (random cached bits and rollout bytes, NaN bytes
 included), block maxima over every finite bf16 magnitude, tiny elements
-beside large ones, specials, in-place use, and the deeper-half sweep's layer
-shape (first and last rows; every element under TRACE_FULL_SWEEP=1)."""
+beside large ones, specials, in-place use, and every element of a layer of the
+deeper-half sweep."""
 import sys
 
 import numpy as np
@@ -170,22 +170,13 @@ def test_mx8_in_place(device):
 def test_mx8_deeper_half_layer(device):
     """One 262144x2048 layer of the deeper-half sweep on MXFP8 scales: the
     capture, guided, RNE and full-information outputs and the STE backward
-    on the guided mask against the oracle, bit for bit, on the first and
-    last 4096 rows (every element under TRACE_FULL_SWEEP=1; the large-hidden
-    and KV sites are compared in full by default)."""
-    import os
-    from tests.full_compare import _VARIANT_PER, compare_variant_every_element
-    full = os.environ.get("TRACE_FULL_SWEEP") == "1"
-    _say(f"case mx8 deeper-half layer 0, {'every element' if full else 'first and last 4096 rows'}")
+    on the guided mask against the oracle, bit for bit, every element."""
+    from tests.full_compare import compare_variant_every_element
+    _say("case mx8 deeper-half layer 0, every element")
     d = workloads.deeper_half_layer(device, 0)
     got = _gpu_mx8(d["x_roll"], d["x_train"], d["grad"])
     ren = {"mask_g": "m_g", "mask_r": "m_r", "mask_f": "m_f"}
     got = {ren.get(k, k): v for k, v in got.items()}
     rows, cols = d["x_roll"].shape
     xr, xt, g = (to_np_u16(d[k]) for k in ("x_roll", "x_train", "grad"))
-    per = _VARIANT_PER["mx8"]
-    for r0, r1 in ([(0, rows)] if full else [(0, 4096), (rows - 4096, rows)]):
-        a, b = r0 * cols, r1 * cols
-        part = {k: v[a // per.get(k, 1):b // per.get(k, 1)] for k, v in got.items()}
-        compare_variant_every_element(f"mx8 deeper-half layer 0 rows {r0}..{r1}", "mx8", xr[a:b], xt[a:b], part,
-                                      extra="with_rne", g=g[a:b])
+    compare_variant_every_element("mx8 deeper-half layer 0", "mx8", xr, xt, got, extra="with_rne", g=g)
