@@ -8,6 +8,7 @@ importing this package fails if the library has not been built.
 Functions mirror the C ABI in ``include/trace.h``:
 
     tensor_scale(x)                                  -> ts (fp32[1])
+    tensor_scale_noalloc(x)                          -> ts, without a workspace
     capture(x_roll, ts, want_codes=False)            -> (scales, bits, codes)
     guided_fakequant_fwd(x_train, scales, ts, bits)  -> (y, mask, qcodes)
     rne_fakequant_fwd(x_train, scales, ts)           -> (y, mask, qcodes)
@@ -39,7 +40,8 @@ import os
 import torch
 
 __all__ = [
-    "TraceError", "LIB_PATH", "SMALLGRID_LIB_PATH", "lib", "load_library", "abi_version", "tensor_scale", "capture",
+    "TraceError", "LIB_PATH", "SMALLGRID_LIB_PATH", "lib", "load_library", "abi_version", "tensor_scale",
+    "tensor_scale_noalloc", "capture",
     "guided_fakequant_fwd", "rne_fakequant_fwd", "full_info_fakequant_fwd", "ste_bwd", "gather_records",
     "grouped_tensor_scale", "grouped_capture", "grouped_guided_fakequant_fwd", "grouped_rne_fakequant_fwd",
     "grouped_full_info_fakequant_fwd", "mx_capture", "mx_guided_fakequant_fwd", "mx_rne_fakequant_fwd",
@@ -80,6 +82,7 @@ def load_library(path):
         "trace_last_hip_error": ([], ctypes.c_int),
         "trace_tensor_scale_workspace_bytes": ([i64], sz),
         "trace_tensor_scale": ([p, i64, p, sz, p, p], st),
+        "trace_tensor_scale_noalloc": ([p, i64, p, p], st),
         "trace_capture": ([p, i64, i64, p, p, p, p, p], st),
         "trace_guided_fakequant_fwd": ([p, i64, i64, p, p, p, p, p, p, p], st),
         "trace_rne_fakequant_fwd": ([p, i64, i64, p, p, p, p, p, p], st),
@@ -208,6 +211,18 @@ def tensor_scale(x, out=None, workspace=None):
     _arg(out, "out", x, _F32, 1)
     _check(lib.trace_tensor_scale(_ptr(x), n, _ptr(workspace), workspace.numel(), _ptr(out), _stream(x)),
            "trace_tensor_scale")
+    return out
+
+
+def tensor_scale_noalloc(x, out=None):
+    """``tensor_scale`` without a workspace: the library's per-GPU scratch
+    array holds the partial maxima (for callers that cannot allocate; calls
+    that overlap on one GPU race)."""
+    _bf16(x, "x")
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=x.device)
+    _arg(out, "out", x, _F32, 1)
+    _check(lib.trace_tensor_scale_noalloc(_ptr(x), x.numel(), _ptr(out), _stream(x)), "trace_tensor_scale_noalloc")
     return out
 
 

@@ -97,6 +97,22 @@ trace_status trace_tensor_scale(const uint16_t* x, int64_t n, void* workspace, s
                                                     static_cast<hipStream_t>(stream)));
 }
 
+static_assert(TRACE_NOALLOC_SCRATCH_BYTES == sizeof(uint32_t) * trace_host::kAmaxMaxGroups ||
+                  trace_host::kAmaxMaxGroups < 1536u,
+              "the allocation-free scratch size differs from the header");
+
+trace_status trace_tensor_scale_noalloc(const uint16_t* x, int64_t n, float* ts_out, void* stream) {
+  if (!ts_out || (n > 0 && !x)) return TRACE_E_NULL;
+  if (n < 0 || (n % 16) != 0 || n > (INT64_MAX / 4)) return TRACE_E_SHAPE;
+  if (trace_tensor_scale_workspace_bytes(n) > trace_host::noalloc_scratch_bytes()) return TRACE_E_SHAPE;
+  if (!aligned(x, 16) || !aligned(ts_out, 4)) return TRACE_E_ALIGN;
+  const Range outs[1] = {rng(ts_out, 4)};
+  const Range ins[1] = {rng(x, 2 * (uint64_t)n)};
+  if (trace_status st = check_alias(outs, 1, ins, 1)) return st;
+  return hip_status(trace_host::launch_tensor_scale_noalloc(x, (uint64_t)n / 16, ts_out,
+                                                            static_cast<hipStream_t>(stream)));
+}
+
 static_assert(TRACE_MAX_BATCH_SITES == trace_host::kMaxBatchSites, "batch size limits differ");
 
 // Validates a batch and fills one launcher spec per site.  with_record: the

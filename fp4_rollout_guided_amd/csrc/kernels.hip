@@ -34,6 +34,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "device_math.h"
 #include "fp4_block.h"
 #include "launch.h"
@@ -1073,6 +1075,60 @@ hipError_t launch_gather_records(const uint8_t* bits_src, const uint8_t* scales_
   launch_gather_plane(scales_src, scales_dst, src_rows, dst_rows, cols / 16, row_index, stream);
   if (codes_dst) launch_gather_plane(codes_src, codes_dst, src_rows, dst_rows, cols / 2, row_index, stream);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// allocation-free tensor scale: the partial maxima live in the library's own
+// device array instead of a caller's workspace
+// ---------------------------------------------------------------------------
+}  // namespace trace_host
+
+// One partial maximum per workgroup of the capped tensor-scale grid.  Every
+// GPU the library runs on holds its own copy until the process ends.  In
+// host code this name is a host-side stand-in, never a device address: host
+// code uses only the address hipGetSymbolAddress returns for the device.
+static __device__ __align__(256) uint32_t scratch[trace_host::kAmaxMaxGroups];
+
+namespace trace_host {
+
+constexpr int kMaxDevices = 64;
+static std::atomic<uint32_t*> g_scratch[kMaxDevices];
+
+size_t noalloc_scratch_bytes() { return sizeof(uint32_t) * kAmaxMaxGroups; }
+
+// The device address of `scratch` on the current device, looked up on the
+// first call per device (with that device current) and kept.
+static hipError_t scratch_on_current_device(uint32_t** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  uint32_t* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!a) return hipErrorInvalidSymbol;
+    p = static_cast<uint32_t*>(a);
+    g_scratch[dev].store(p, std::memory_order_release);  // a racing first call stores the same address
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+hipError_t launch_tensor_scale_noalloc(const uint16_t* x, uint64_t nblocks, float* ts_out, hipStream_t stream) {
+  if (amax_partial_count(nblocks) > kAmaxMaxGroups) return hipErrorInvalidValue;  // cannot happen: the grid is capped
+  if (stream) {  // the stream must run on the current device, whose copy of the array is used
+    int cur = -1, sdev = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess) e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return e;
+    if (sdev != cur) return hipErrorInvalidDevice;
+  }
+  uint32_t* partial = nullptr;
+  const hipError_t e = scratch_on_current_device(&partial);
+  if (e != hipSuccess) return e;
+  return launch_tensor_scale(x, nblocks, partial, ts_out, stream);
 }
 
 }  // namespace trace_host

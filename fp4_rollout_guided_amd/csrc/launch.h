@@ -59,6 +59,10 @@ hipError_t launch_capture_batch(const BatchSiteSpec* sites, uint32_t count, hipS
 
 hipError_t launch_tensor_scale(const uint16_t* x, uint64_t nblocks, uint32_t* partial, float* ts_out,
                                hipStream_t stream);
+// The same with the library's per-device scratch array (noalloc_scratch_bytes()
+// bytes) in place of a workspace; the stream must belong to the current device.
+size_t noalloc_scratch_bytes();
+hipError_t launch_tensor_scale_noalloc(const uint16_t* x, uint64_t nblocks, float* ts_out, hipStream_t stream);
 // row_amax: u32[rows] workspace; ts_out: fp32[count]
 hipError_t launch_grouped_tensor_scale(const uint16_t* x, const GroupSpec& g, uint32_t* row_amax, float* ts_out,
                                        hipStream_t stream);

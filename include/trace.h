@@ -42,8 +42,10 @@
  *   frees nothing, never synchronizes, and keeps no state between calls
  *   other than a thread-local copy of the last HIP error code and, per
  *   device, the resident-workgroup count of the agreement statistics kernel
- *   (one occupancy query, cached atomically).  It is safe to call from
- *   several host threads.
+ *   (one occupancy query, cached atomically) and the address of the 6 KiB
+ *   device array of trace_tensor_scale_noalloc (below), whose contents are
+ *   shared by that entry point's calls on the device.  It is safe to call
+ *   from several host threads.
  * - Asynchrony: all device work is enqueued on `stream` (a hipStream_t; NULL
  *   is the default stream).  Outputs are valid once that stream reaches the
  *   point of the call.
@@ -66,7 +68,7 @@
 extern "C" {
 #endif
 
-#define TRACE_ABI_VERSION 7
+#define TRACE_ABI_VERSION 8
 
 #if defined(__GNUC__)
 #define TRACE_API __attribute__((visibility("default")))
@@ -115,6 +117,27 @@ TRACE_API size_t trace_tensor_scale_workspace_bytes(int64_t n);
 TRACE_API trace_status trace_tensor_scale(const uint16_t* x, int64_t n, void* workspace,
                                 size_t workspace_bytes, float* ts_out,
                                 void* stream);
+
+/*
+ * trace_tensor_scale without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc.  Same result, arguments and errors as
+ * trace_tensor_scale minus the workspace.  The partial maxima go to a device
+ * array inside the library of TRACE_NOALLOC_SCRATCH_BYTES (6 KiB), one copy
+ * per GPU, held until the process ends; the call itself allocates nothing.
+ * Its address is looked up on the first call on each device (that device
+ * current).  Every tensor size is accepted (the partial-maximum grid is
+ * capped at the array's 1536 words; a size needing more would be
+ * TRACE_E_SHAPE).  `stream` must belong to the current device (else
+ * TRACE_E_HIP with hipErrorInvalidDevice).  Each call writes every word it
+ * reads, so nothing needs clearing between calls; but every call on one GPU
+ * shares that GPU's array, so calls that overlap in time on one GPU (on
+ * different streams, or from several host threads) race and may return a
+ * wrong scale: order them on one stream.
+ */
+#define TRACE_NOALLOC_SCRATCH_BYTES 6144
+TRACE_API trace_status trace_tensor_scale_noalloc(const uint16_t* x, int64_t n, float* ts_out,
+                                                  void* stream);
 
 /*
  * Rollout-side capture (fp4_quantize and low_bits(q_roll, b=1) in the

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert tr.abi_version() == 7
+    assert tr.abi_version() == 8
     for code in range(6):
         assert L.trace_status_string(code).decode().startswith("TRACE")
     assert b"unknown" in L.trace_status_string(99)
@@ -47,6 +47,18 @@ def test_workspace_size():
     assert L.trace_tensor_scale_workspace_bytes(4096 * 2) == 8
     big = L.trace_tensor_scale_workspace_bytes(1 << 34)
     assert 4 <= big <= 4 * 4096
+
+
+def test_tensor_scale_noalloc_validation():
+    f = L.trace_tensor_scale_noalloc
+    assert f(None, 4096, P(A + 0x200000), None) == E_NULL
+    assert f(P(A), 4096, None, None) == E_NULL
+    assert f(P(A), -16, P(A + 0x200000), None) == E_SHAPE
+    assert f(P(A), 4095, P(A + 0x200000), None) == E_SHAPE
+    assert f(P(A + 8), 4096, P(A + 0x200000), None) == E_ALIGN
+    assert f(P(A), 4096, P(A + 0x200002), None) == E_ALIGN
+    assert f(P(A), 4096, P(A + 0x100), None) == E_ALIAS      # ts_out inside x
+    assert L.trace_tensor_scale_workspace_bytes(1 << 40) <= 6144  # every size fits the 6 KiB scratch
 
 
 def test_tensor_scale_validation():
