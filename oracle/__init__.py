@@ -75,6 +75,7 @@ from .trace import (
     decode_scales,
     full_info_fwd,
     gather_records,
+    gathered_fwd,
     grouped_capture,
     grouped_full_info_fwd,
     grouped_guided_fwd,
@@ -98,7 +99,7 @@ __all__ = [
     "E2M1_MAGNITUDES", "E4M3FN_MAX", "bf16_to_f32", "e2m1_bracket",
     "e2m1_rne_index", "e4m3fn_decode", "e4m3fn_encode_rne_sat",
     "f32_to_bf16_rne", "BLOCK", "TENSOR_SCALE_DIVISOR", "block_scales",
-    "capture", "compact_cache_bytes", "decode_scales", "full_info_fwd", "gather_records",
+    "capture", "compact_cache_bytes", "decode_scales", "full_info_fwd", "gather_records", "gathered_fwd",
     "grouped_capture", "grouped_full_info_fwd", "grouped_guided_fwd", "grouped_rne_fwd",
     "grouped_tensor_scale", "MX_BLOCK", "e8m0_decode", "floor_log2", "mx_block_scales", "mx_capture",
     "mx_full_info_fwd", "mx_guided_fwd", "mx_rne_fwd", "capture_lowbits", "lowbits_fwd", "lowbits_reconstruct",

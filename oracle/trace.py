@@ -122,7 +122,7 @@ def block_scales(x_bits, ts) -> np.ndarray:
 def decode_scales(scale_bytes, ts):
     """Decoded block scales ``s = fl32(dec(byte) * ts)`` and the mask of
     blocks whose s is a positive finite number (all others are zero-scale
-    blocks)."""
+    blocks).  ts is one tensor scale, or one per block."""
     dec = e4m3fn_decode(scale_bytes).astype(np.float32)
     with np.errstate(over="ignore", invalid="ignore", under="ignore"):
         s = dec * _F32(ts)
@@ -381,6 +381,30 @@ def gather_records(record, row_index, src_rows: int, cols: int) -> dict:
         dst[ok] = src[idx[ok]]
         out[name] = dst.reshape(-1)
     return out
+
+
+def gathered_fwd(mode, x_bits, cols: int, record, src_rows: int, row_index, ts, offsets=None) -> dict:
+    """The training side's forward on records read back in its own row order
+    (the trainer reads the rollout's records back): destination row r takes
+    its record from source row ``row_index[r]`` (``gather_records``: an index
+    outside [0, src_rows) gives an all-zero row, i.e. zero-scale blocks) and
+    the tensor scale of that source row -- ``ts[0]`` for one tensor scale, or,
+    with ``offsets`` describing groups of source rows (per-expert scales),
+    ``ts[g]`` of the group holding it.  mode "guided" reads the record's
+    bits, "full" its codes.  Outputs as ``guided_fwd``."""
+    rec = gather_records(record, row_index, src_rows, cols)
+    idx = np.asarray(row_index, dtype=np.int64).reshape(-1)
+    tsv = np.asarray(ts, dtype=np.float32).reshape(-1)
+    row_ts = np.full(idx.size, tsv[0], dtype=np.float32)   # rows outside every group keep ts[0]: zero-scale anyway
+    if offsets is not None:
+        for g, (a, b) in enumerate(_group_slices(offsets, src_rows)):
+            row_ts[(idx >= a) & (idx < b)] = tsv[g]
+    block_ts = np.repeat(row_ts, cols // BLOCK)             # one tensor scale per block of the destination
+    if mode == "guided":
+        return guided_fwd(x_bits, rec["scales"], block_ts, rec["bits"])
+    if mode == "full":
+        return full_info_fwd(x_bits, rec["scales"], block_ts, rec["codes"])
+    raise ValueError("mode must be 'guided' or 'full'")
 
 
 # --------------------------------------------------------------------------
