@@ -75,6 +75,15 @@ MOE_BYTES_PER_ELEM = {
     "gather_records": 2 * (1 / 8 + 1 / 16),                        # read + write bits and scale bytes
     "gather_records_runs": 2 * (1 / 8 + 1 / 16),                   # the same, rows moved in runs
 }
+# records read back in the trainer's (shuffled) row order, then the guided
+# forward: the gather and the forward as two launches, against one fused
+# launch that reads the record rows in place (one tensor scale, and
+# per-expert scales, which only the fused call can apply in that order)
+READBACK_BYTES_PER_ELEM = {
+    "gather_then_guided_fwd": 2 * (1 / 8 + 1 / 16) + 2.0 + 1 / 8 + 1 / 16 + 2.0 + 1 / 8,
+    "fused_guided_fwd": 2.0 + 1 / 8 + 1 / 16 + 2.0 + 1 / 8,
+    "fused_guided_fwd_per_expert": 2.0 + 1 / 8 + 1 / 16 + 2.0 + 1 / 8,
+}
 GATHER_RUN = 256         # rows per run in the run-ordered gather
 CPU_SHARE = 16           # host cores granted to a process driving one GPU
 CPU_BUDGET_S = 12.0      # wall-clock budget of the CPU oracle leg
@@ -290,6 +299,7 @@ def main():
                         "Gelem_s": round(n / (avg_ms * 1e-3) / 1e9, 2), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                         "bytes_per_launch": int(bpe * n)}
 
+    cold = cold_rows(tr, torch, dev, stream, layers, next_steps)
     moe = moe_rows(tr, workloads, torch, dev, stream, layers, next_steps)
     other = workload_rows(tr, workloads, torch, dev, stream)
 
@@ -327,6 +337,7 @@ def main():
         "gelem_per_s": round(L * n / (ms_per_step * 1e-3) / 1e9, 3),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "kernels": kernels,
+        "kernels_cold": cold,
         "next_rows": next_rows,
         "moe_expert_site": moe,
         "other_workloads": other,
@@ -343,6 +354,53 @@ def main():
         pool.close()
         pool.join()
     print(json.dumps(result), flush=True)
+
+
+def cold_rows(tr, torch, dev, stream, layers, reps):
+    """The tensor scale and the capture of one deeper-half layer without the
+    step's neighbours: each after a read-only 1 GiB pass over another
+    layer's tensor (which evicts the 256 MB last-level cache and leaves no
+    dirty lines), and the capture right after the tensor scale of the same
+    tensor (as a rollout runs them).  In the step, the capture follows the
+    tensor scale and reads first the lines that pass read last, so part of
+    its input comes from the last-level cache; these rows give its figure
+    from HBM alone."""
+    d = layers[0]
+    flush = layers[-1]["x_roll"] if len(layers) > 1 else torch.zeros(1 << 29, dtype=torch.bfloat16, device=dev)
+    flush_ts = torch.empty(1, dtype=torch.float32, device=dev)
+    n = d["x_roll"].numel()
+    ws = torch.empty(tr.lib.trace_tensor_scale_workspace_bytes(n), dtype=torch.uint8, device=dev)
+    names = ("tensor_scale_after_read", "capture_after_read", "capture_after_tensor_scale")
+    t = {k: 0.0 for k in names}
+    for it in range(reps + 1):
+        ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(2)] for k in names}
+        tr.tensor_scale(flush, out=flush_ts)
+        ev["tensor_scale_after_read"][0].record(stream)
+        tr.tensor_scale(d["x_roll"], out=d["ts"], workspace=ws)
+        ev["tensor_scale_after_read"][1].record(stream)
+        tr.tensor_scale(flush, out=flush_ts)
+        ev["capture_after_read"][0].record(stream)
+        tr.capture(d["x_roll"], d["ts"], scales=d["scales"], bits=d["bits"])
+        ev["capture_after_read"][1].record(stream)
+        tr.tensor_scale(flush, out=flush_ts)
+        tr.tensor_scale(d["x_roll"], out=d["ts"], workspace=ws)
+        ev["capture_after_tensor_scale"][0].record(stream)
+        tr.capture(d["x_roll"], d["ts"], scales=d["scales"], bits=d["bits"])
+        ev["capture_after_tensor_scale"][1].record(stream)
+        stream.synchronize()
+        if it > 0:
+            for k in names:
+                t[k] += ev[k][0].elapsed_time(ev[k][1])
+    out = {"protocol": "layer 0 of the sweep; 'after_read': after a read-only 1 GiB pass over another layer "
+                       "(no last-level-cache reuse, no dirty lines); 'capture_after_tensor_scale': right after the "
+                       "tensor scale of the same tensor, itself after such a pass (the capture then reads part of "
+                       "its input from the 256 MB last-level cache, as in the step)"}
+    for k in names:
+        bpe = BYTES_PER_ELEM["tensor_scale" if k.startswith("tensor") else "capture"]
+        avg = t[k] / reps
+        gbs = bpe * n / (avg * 1e-3) / 1e9
+        out[k] = {"avg_us": round(avg * 1e3, 2), "GB_s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    return out
 
 
 def rollout_side_rows(tr, torch, dev, stream, sites, flush, flush_ts, reps):
@@ -495,7 +553,7 @@ def moe_rows(tr, workloads, torch, dev, stream, layers, reps):
     x_roll, x_train = d["x_roll"], d["x_train"]
     rows, cols = x_roll.shape
     n = rows * cols
-    perm = torch.randperm(rows, generator=workloads.generator(dev, "trainer order"), device=dev)
+    perm = workloads.trainer_order(rows, dev)
     # the same rows as shuffled runs of RUN consecutive rows (a trainer that
     # moves whole token runs rather than single rows)
     run_order = torch.randperm(rows // GATHER_RUN, generator=workloads.generator(dev, "trainer runs"), device=dev)
@@ -538,6 +596,31 @@ def moe_rows(tr, workloads, torch, dev, stream, layers, reps):
         if it > 0:
             for k in ev:
                 ms[k] += ev[k][0].elapsed_time(ev[k][1])
+    # the trainer's forward on its rows in its own order, each variant after
+    # a read-only 1 GiB pass
+    xt_perm = x_train[perm]
+    ts1 = tr.tensor_scale(x_roll)
+    sc1, bt1, _ = tr.capture(x_roll, ts1)
+    rb = {k: 0.0 for k in READBACK_BYTES_PER_ELEM}
+    for it in range(reps + 1):
+        ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(2)] for k in READBACK_BYTES_PER_ELEM}
+        tr.tensor_scale(layers[0]["x_roll"], out=flush_ts)
+        ev["gather_then_guided_fwd"][0].record(stream)
+        g_bits, g_scales, _ = tr.gather_records(bt1, sc1, None, cols, perm)
+        tr.guided_fakequant_fwd(xt_perm, g_scales, ts1, g_bits, y=y, mask=mask)
+        ev["gather_then_guided_fwd"][1].record(stream)
+        tr.tensor_scale(layers[0]["x_roll"], out=flush_ts)
+        ev["fused_guided_fwd"][0].record(stream)
+        tr.gathered_guided_fakequant_fwd(xt_perm, perm, sc1, ts1, bt1, y=y, mask=mask)
+        ev["fused_guided_fwd"][1].record(stream)
+        tr.tensor_scale(layers[0]["x_roll"], out=flush_ts)
+        ev["fused_guided_fwd_per_expert"][0].record(stream)
+        tr.gathered_guided_fakequant_fwd(xt_perm, perm, scales, ts, bits, offsets=offsets, y=y, mask=mask)
+        ev["fused_guided_fwd_per_expert"][1].record(stream)
+        stream.synchronize()
+        if it > 0:
+            for k in ev:
+                rb[k] += ev[k][0].elapsed_time(ev[k][1])
     out = {"site": f"routed-expert input {rows}x{cols} bf16, rows grouped by {groups} experts "
                    f"(top-8 of 128 routing of 16384 tokens), Student-t(4)", "kernels": {}}
     for k, bpe in MOE_BYTES_PER_ELEM.items():
@@ -546,7 +629,15 @@ def moe_rows(tr, workloads, torch, dev, stream, layers, reps):
         out["kernels"][k] = {"avg_us": round(avg * 1e3, 2), "GB_s": round(gbs, 1),
                              "Gelem_s": round(n / (avg * 1e-3) / 1e9, 2), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                              "bytes_per_launch": int(bpe * n)}
-    del d, x_roll, x_train, y
+    out["readback_trainer_order"] = {}
+    for k, bpe in READBACK_BYTES_PER_ELEM.items():
+        avg = rb[k] / reps
+        gbs = bpe * n / (avg * 1e-3) / 1e9
+        out["readback_trainer_order"][k] = {"avg_us": round(avg * 1e3, 2), "GB_s": round(gbs, 1),
+                                            "Gelem_s": round(n / (avg * 1e-3) / 1e9, 2),
+                                            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                                            "bytes_per_launch": int(bpe * n)}
+    del d, x_roll, x_train, y, xt_perm
     return out
 
 

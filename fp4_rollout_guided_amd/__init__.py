@@ -89,6 +89,8 @@ def load_library(path):
         "trace_full_info_fakequant_fwd": ([p, i64, i64, p, p, p, p, p, p, p], st),
         "trace_ste_bwd": ([p, p, i64, p, p], st),
         "trace_gather_records": ([p, p, p, i64, i64, p, i64, p, p, p, p], st),
+        "trace_gathered_guided_fakequant_fwd": ([p, i64, i64, p, i64, p, i64, p, p, p, p, p, p, p], st),
+        "trace_gathered_full_info_fakequant_fwd": ([p, i64, i64, p, i64, p, i64, p, p, p, p, p, p, p], st),
         "trace_grouped_tensor_scale_workspace_bytes": ([i64], sz),
         "trace_grouped_tensor_scale": ([p, i64, i64, p, i64, p, sz, p, p], st),
         "trace_grouped_capture": ([p, i64, i64, p, i64, p, p, p, p, p], st),
@@ -380,6 +382,48 @@ def gather_records(bits, scales, codes, cols, row_index):
                                     dst_rows, _ptr(bits_d), _ptr(scales_d), _ptr(codes_d), _stream(bits)),
            "trace_gather_records")
     return bits_d, scales_d, codes_d
+
+
+def _gathered_fwd(mode, x, row_index, scales, ts, side, offsets, y, mask, want_codes, qcodes):
+    _bf16(x, "x_train")
+    rows, cols = _rows_cols(x)
+    _arg(row_index, "row_index", x, _I64, rows)
+    if row_index.numel() != rows:
+        raise ValueError(f"row_index needs one entry per row of x_train ({rows}), got {row_index.numel()}")
+    _arg(scales, "scales", x, _U8, 0)
+    src_rows = scales.numel() * 16 // cols if cols else 0
+    n, n_src = rows * cols, src_rows * cols
+    groups = 0
+    if offsets is not None:
+        groups = _offsets(offsets, x)
+    _arg(ts, "ts", x, _F32, max(groups, 1))
+    _arg(side, "bits" if mode == "guided" else "codes", x, _U8, n_src // 8 if mode == "guided" else n_src // 2)
+    y = _bf16_out(y, x, n, "y")
+    mask = _u8(n // 8, x, mask, "mask")
+    if want_codes or qcodes is not None:
+        qcodes = _u8(n // 2, x, qcodes, "qcodes")
+    fn = lib.trace_gathered_guided_fakequant_fwd if mode == "guided" else lib.trace_gathered_full_info_fakequant_fwd
+    _check(fn(_ptr(x), rows, cols, _ptr(row_index), src_rows, _ptr(offsets), groups, _ptr(scales), _ptr(ts),
+              _ptr(side), _ptr(y), _ptr(mask), _ptr(qcodes), _stream(x)),
+           "trace_gathered_guided_fakequant_fwd" if mode == "guided" else "trace_gathered_full_info_fakequant_fwd")
+    return y, mask, qcodes
+
+
+def gathered_guided_fakequant_fwd(x_train, row_index, scales, ts, bits, offsets=None, y=None, mask=None,
+                                  want_codes=False, qcodes=None):
+    """``guided_fakequant_fwd`` of x_train row r on source row row_index[r]
+    of the record (scales, bits; the source's row count is
+    scales.numel() * 16 / cols) without a gathered copy; ts is one tensor
+    scale, or one per group of source rows when ``offsets`` is given.
+    Out-of-range indices give zero-scale blocks."""
+    return _gathered_fwd("guided", x_train, row_index, scales, ts, bits, offsets, y, mask, want_codes, qcodes)
+
+
+def gathered_full_info_fakequant_fwd(x_train, row_index, scales, ts, codes, offsets=None, y=None, mask=None,
+                                     want_codes=False, qcodes=None):
+    """``full_info_fakequant_fwd`` on source rows row_index[r] of the record
+    (scales, codes), as ``gathered_guided_fakequant_fwd``."""
+    return _gathered_fwd("full", x_train, row_index, scales, ts, codes, offsets, y, mask, want_codes, qcodes)
 
 
 def _offsets(offsets, x):

@@ -283,6 +283,58 @@ trace_status trace_grouped_full_info_fakequant_fwd(const uint16_t* x_train, int6
   return fakequant(2, x_train, rows, cols, offsets, groups, true, scales, ts, codes, y, mask, qcodes, stream);
 }
 
+// mode 1: guided (side = bit-plane of the source, src_n/8 bytes); 2: full
+// information (side = codes of the source, src_n/2 bytes, 8-byte aligned).
+static trace_status gathered_fakequant(int mode, const uint16_t* x, int64_t rows, int64_t cols,
+                                       const int64_t* row_index, int64_t src_rows, const int64_t* offsets,
+                                       int64_t groups, const uint8_t* scales_src, const float* ts,
+                                       const uint8_t* side_src, uint16_t* y, uint8_t* mask, uint8_t* qcodes,
+                                       void* stream) {
+  uint64_t n = 0, n_src = 0;
+  if (trace_status st = site_size(rows, cols, &n)) return st;
+  if (trace_status st = site_size(src_rows, cols, &n_src)) return st;
+  const bool grouped = offsets != nullptr;
+  if (!grouped && groups != 0) return TRACE_E_NULL;
+  trace_host::GroupSpec spec{};
+  if (grouped)
+    if (trace_status st = group_spec(offsets, groups, src_rows, cols, &spec)) return st;
+  if (n == 0) return TRACE_OK;
+  uint64_t bound = 0;  // the kernel finds a half block's row with one multiply-high
+  if (__builtin_mul_overflow(n / 8, (uint64_t)cols / 8, &bound)) return TRACE_E_SHAPE;
+  if (!x || !row_index || !ts || !y || !mask || (n_src > 0 && (!scales_src || !side_src))) return TRACE_E_NULL;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ts, 4) || !aligned(mask, 2) || !aligned(row_index, 8) ||
+      (mode == 2 && !aligned(side_src, 8)) || (qcodes && !aligned(qcodes, 8)))
+    return TRACE_E_ALIGN;
+  const uint64_t ts_len = 4 * (grouped ? spec.count : 1);
+  const uint64_t side_len = mode == 1 ? n_src / 8 : n_src / 2;
+  const Range outs[3] = {rng(y, 2 * n), rng(mask, n / 8), rng(qcodes, qcodes ? n / 2 : 0)};
+  const Range ins[6] = {rng(x, 2 * n),           rng(scales_src, n_src / 16),
+                        rng(ts, ts_len),         rng(side_src, side_len),
+                        rng(row_index, 8 * (uint64_t)rows), rng(offsets, grouped ? 8 * (spec.count + 1) : 0)};
+  if (trace_status st = check_alias(outs, 3, ins, 6, /*inplace_out=*/0, /*inplace_in=*/0)) return st;
+  return hip_status(trace_host::launch_gathered_fakequant(mode, x, (uint64_t)rows, (uint64_t)cols, row_index,
+                                                          (uint64_t)src_rows, grouped ? &spec : nullptr, scales_src, ts,
+                                                          side_src, y, mask, qcodes, static_cast<hipStream_t>(stream)));
+}
+
+trace_status trace_gathered_guided_fakequant_fwd(const uint16_t* x_train, int64_t rows, int64_t cols,
+                                                 const int64_t* row_index, int64_t src_rows, const int64_t* offsets,
+                                                 int64_t groups, const uint8_t* scales_src, const float* ts,
+                                                 const uint8_t* bits_src, uint16_t* y, uint8_t* mask, uint8_t* qcodes,
+                                                 void* stream) {
+  return gathered_fakequant(1, x_train, rows, cols, row_index, src_rows, offsets, groups, scales_src, ts, bits_src, y,
+                            mask, qcodes, stream);
+}
+
+trace_status trace_gathered_full_info_fakequant_fwd(const uint16_t* x_train, int64_t rows, int64_t cols,
+                                                    const int64_t* row_index, int64_t src_rows,
+                                                    const int64_t* offsets, int64_t groups, const uint8_t* scales_src,
+                                                    const float* ts, const uint8_t* codes_src, uint16_t* y,
+                                                    uint8_t* mask, uint8_t* qcodes, void* stream) {
+  return gathered_fakequant(2, x_train, rows, cols, row_index, src_rows, offsets, groups, scales_src, ts, codes_src, y,
+                            mask, qcodes, stream);
+}
+
 size_t trace_grouped_tensor_scale_workspace_bytes(int64_t rows) {
   if (rows < 0) return 0;
   return (size_t)rows * sizeof(uint32_t);

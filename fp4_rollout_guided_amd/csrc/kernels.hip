@@ -690,6 +690,178 @@ __global__ __launch_bounds__(kThreads) void fakequant_half_kernel(const uint4* _
   }
 }
 
+// ---------------------------------------------------------------------------
+// trainer-side forward on records read back in the trainer's row order:
+// destination row r of x_train takes the record of source row row_index[r]
+// (its scale bytes and cached bits or codes, and the tensor scale of its
+// group), read in place; no gathered copy of the record is written first.
+// An index outside [0, src_rows) gives zero-scale blocks.
+// ---------------------------------------------------------------------------
+struct GatherMap {
+  const int64_t* row_index;  // int64[destination rows]
+  uint64_t src_rows;
+  uint64_t hpr;              // half blocks (8 elements) per row
+  uint64_t inv;              // ceil(2^64 / hpr): h / hpr = mulhi(h, inv) for h * hpr < 2^64
+};
+
+// Tensor scale of the group holding source row s, in two steps so that a
+// wave can issue the loads for several rows before it waits on any: the
+// window (group_window_load) is three groups around a guess that assumes
+// equal groups (the fixed-point count / blocks, as in group_tensor_scale),
+// whose four starts and three scales are loaded together, in bounds for any
+// s; group_window_pick takes the group holding s from it, or, when s lies
+// outside the window (unbalanced groups, or fewer than three), binary
+// searches for the last group starting at or before s.  With a
+// wave-uniform s the compiler issues scalar loads.
+struct GroupWindow {
+  uint32_t i;  // first group of the window
+  int64_t ov[4];
+  float tw[3];
+};
+
+__device__ __forceinline__ GroupWindow group_window_load(const RowGroups& G, const float* __restrict__ ts, uint64_t s) {
+  GroupWindow w{};
+  if (G.count >= 3) {
+    const uint32_t g0 = (uint32_t)__umul64hi(s * G.bpr, G.per_block << 32);
+    const uint32_t guess = g0 < G.count - 1 ? g0 : G.count - 1;
+    w.i = guess == 0 ? 0 : (guess - 1 > G.count - 3 ? G.count - 3 : guess - 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w.ov[j] = G.off[w.i + j];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) w.tw[j] = ts[w.i + j];
+  }
+  return w;
+}
+
+// For a row s in [0, rows), comparing s with a clamped offset equals
+// comparing it with the raw offset as a signed number, so no clamping is
+// needed here; group 0 starts at 0 and the last group has no end.
+__device__ __forceinline__ float group_window_pick(const RowGroups& G, const float* __restrict__ ts,
+                                                   const GroupWindow& w, uint64_t s) {
+  const int64_t si = (int64_t)s;
+  if (G.count >= 3) {
+    float t = 0.f;
+    bool found = false;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const bool in = (w.i + j == 0 || w.ov[j] <= si) && (w.i + j + 1 >= G.count || si < w.ov[j + 1]);
+      t = in ? w.tw[j] : t;
+      found |= in;
+    }
+    if (found) return t;
+  }
+  uint32_t l = 0, h = G.count;  // the last group starting at or before s
+  while (h - l > 1) {
+    const uint32_t mid = (l + h) >> 1;
+    if (G.off[mid] <= si) l = mid; else h = mid;
+  }
+  return ts[l];
+}
+
+__device__ __forceinline__ uint64_t readfirstlane_u64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Each wave takes kGatherSegs segments of 64 consecutive half blocks of the
+// destination (lane t: half t of every segment).  A half block's record
+// bytes sit behind two dependent loads (its row's index, then the source
+// row's bytes), so a wave issues all its x loads and row-index loads first,
+// then all record loads (and group windows), before it computes.  On the
+// 131072x2048 routed-expert site in a shuffled row order, after a read-only
+// pass: one segment per wave 198-203 us, two 189-194, four 190-199, eight
+// 210 (registers); the gather and then the forward take 204-222 us.
+// kWaveRow: every segment lies inside one destination row (half blocks per
+// row a multiple of 64, so rows start at segment boundaries); the row index,
+// its source row and the group lookup are then scalar work per segment, and
+// a segment in the same row as the previous one reuses its lookups
+// (per-expert scales: 215-240 -> 194-203 us).  Otherwise each lane finds its
+// own row.
+#ifndef TRACE_GATHER_SEGS
+#define TRACE_GATHER_SEGS 2
+#endif
+constexpr int kGatherSegs = TRACE_GATHER_SEGS;
+
+template <int kMode, bool kGrouped, bool kWaveRow>
+__global__ __launch_bounds__(kThreads) void fakequant_gathered_kernel(const uint4* __restrict__ x, uint64_t nhalves,
+                                                                      GatherMap gm,
+                                                                      const uint8_t* __restrict__ scales_src,
+                                                                      const float* __restrict__ ts_ptr,
+                                                                      RowGroups groups,
+                                                                      const uint8_t* __restrict__ bits_src,
+                                                                      const uint32_t* __restrict__ codes_src,
+                                                                      uint4* __restrict__ y,
+                                                                      uint8_t* __restrict__ mask,
+                                                                      uint32_t* __restrict__ qcodes) {
+  constexpr int K = kGatherSegs;
+  const float ts0 = kGrouped ? 0.f : *ts_ptr;
+  const uint32_t lane = threadIdx.x & 63;
+  const uint64_t per_wg = (uint64_t)kThreads * K;
+  const uint64_t stride = (uint64_t)gridDim.x * per_wg;
+  // the wave's first half block (wave-uniform)
+  uint64_t base = readfirstlane_u64((uint64_t)blockIdx.x * per_wg + (uint64_t)(threadIdx.x >> 6) * 64 * K);
+  for (; base < nhalves; base += stride) {
+    uint4 v[K];
+    int64_t s[K];
+    uint64_t c[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const uint64_t h = base + 64 * k + lane;
+      v[k] = h < nhalves ? x[h] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    bool dup[K];  // kWaveRow: segment k lies in the same row as segment k - 1
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const uint64_t h0 = base + 64 * k;  // the segment's first half block (wave-uniform)
+      const uint64_t h = h0 + lane;
+      const bool live = kWaveRow ? h0 < nhalves : h < nhalves;
+      const uint64_t r = __umul64hi(kWaveRow ? h0 : h, gm.inv);  // destination row
+      c[k] = h - r * gm.hpr;                                     // half block within the row
+      dup[k] = kWaveRow && k > 0 && live && h0 - r * gm.hpr >= 64;
+      s[k] = dup[k] ? s[k > 0 ? k - 1 : 0] : (live ? gm.row_index[r] : -1);
+    }
+    uint32_t sbyte[K], side[K];
+    float ts[K];
+    bool ok[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      ok[k] = s[k] >= 0 && (uint64_t)s[k] < gm.src_rows;
+      sbyte[k] = 0;  // a row the rollout never produced: zero-scale blocks
+      side[k] = 0;
+      ts[k] = ts0;
+      if (ok[k]) {
+        const uint64_t sh = (uint64_t)s[k] * gm.hpr + c[k];  // the same half block of the source row
+        sbyte[k] = scales_src[sh >> 1];
+        if (kMode == 1) side[k] = bits_src[sh];
+        if (kMode == 2) side[k] = codes_src[sh];
+      }
+    }
+    if (kGrouped) {
+      GroupWindow gw[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k)
+        if (!dup[k]) gw[k] = group_window_load(groups, ts_ptr, ok[k] ? (uint64_t)s[k] : 0);
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        if (dup[k])
+          ts[k] = ts[k > 0 ? k - 1 : 0];
+        else if (ok[k])
+          ts[k] = group_window_pick(groups, ts_ptr, gw[k], (uint64_t)s[k]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const uint64_t h = base + 64 * k + lane;
+      if (h < nhalves) {
+        const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+        fakequant_half<kMode>(x, h, w, sbyte[k], kMode == 1 ? side[k] : 0u, kMode == 2 ? side[k] : 0u, ts[k], y,
+                              mask, qcodes);
+      }
+    }
+  }
+}
+
 // b cached low bits (kMode 3): the residues come from b bit-planes.
 __global__ __launch_bounds__(kThreads) void lowbits_fakequant_kernel(const uint4* __restrict__ x, uint64_t nblocks,
                                                                      const uint8_t* __restrict__ scales,
@@ -1022,6 +1194,46 @@ hipError_t launch_fakequant(int mode, const uint16_t* x, uint64_t nblocks, const
                              reinterpret_cast<uint16_t*>(mask), reinterpret_cast<uint2*>(qcodes), stream);
   else
     launch_fakequant_half(mode, xv, nblocks, scales, ts, side, yv, mask, reinterpret_cast<uint32_t*>(qcodes), stream);
+  return hipGetLastError();
+}
+
+template <int kMode, bool kGrouped>
+static void launch_gathered_mode(dim3 grid, bool wave_row, const uint4* x, uint64_t nhalves, const GatherMap& gm,
+                                 const uint8_t* scales_src, const float* ts, const RowGroups& rg,
+                                 const uint8_t* side_src, uint4* y, uint8_t* mask, uint32_t* qcodes,
+                                 hipStream_t stream) {
+  const uint8_t* bits = kMode == 1 ? side_src : nullptr;
+  const uint32_t* codes = kMode == 2 ? reinterpret_cast<const uint32_t*>(side_src) : nullptr;
+  if (wave_row)
+    hipLaunchKernelGGL((fakequant_gathered_kernel<kMode, kGrouped, true>), grid, dim3(kThreads), 0, stream, x,
+                       nhalves, gm, scales_src, ts, rg, bits, codes, y, mask, qcodes);
+  else
+    hipLaunchKernelGGL((fakequant_gathered_kernel<kMode, kGrouped, false>), grid, dim3(kThreads), 0, stream, x,
+                       nhalves, gm, scales_src, ts, rg, bits, codes, y, mask, qcodes);
+}
+
+hipError_t launch_gathered_fakequant(int mode, const uint16_t* x, uint64_t rows, uint64_t cols,
+                                     const int64_t* row_index, uint64_t src_rows, const GroupSpec* g,
+                                     const uint8_t* scales_src, const float* ts, const uint8_t* side_src, uint16_t* y,
+                                     uint8_t* mask, uint8_t* qcodes, hipStream_t stream) {
+  const uint64_t hpr = cols / 8, nhalves = rows * hpr;
+  if (nhalves == 0) return hipSuccess;  // an empty grid is not a valid launch
+  const unsigned __int128 two64 = (unsigned __int128)1 << 64;
+  const GatherMap gm{row_index, src_rows, hpr, (uint64_t)((two64 + hpr - 1) / hpr)};
+  const RowGroups rg = g ? row_groups(*g, g->rows * (g->cols / 16)) : RowGroups{};
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  uint4* yv = reinterpret_cast<uint4*>(y);
+  uint32_t* qv = reinterpret_cast<uint32_t*>(qcodes);
+  const dim3 grid(grid_for((nhalves + kGatherSegs - 1) / kGatherSegs));
+  const bool wave_row = hpr % 64 == 0;
+  if (mode == 1 && g)
+    launch_gathered_mode<1, true>(grid, wave_row, xv, nhalves, gm, scales_src, ts, rg, side_src, yv, mask, qv, stream);
+  else if (mode == 1)
+    launch_gathered_mode<1, false>(grid, wave_row, xv, nhalves, gm, scales_src, ts, rg, side_src, yv, mask, qv, stream);
+  else if (g)
+    launch_gathered_mode<2, true>(grid, wave_row, xv, nhalves, gm, scales_src, ts, rg, side_src, yv, mask, qv, stream);
+  else
+    launch_gathered_mode<2, false>(grid, wave_row, xv, nhalves, gm, scales_src, ts, rg, side_src, yv, mask, qv, stream);
   return hipGetLastError();
 }
 

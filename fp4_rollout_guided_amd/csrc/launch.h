@@ -81,6 +81,17 @@ hipError_t launch_lowbits_fakequant(const uint16_t* x, uint64_t nblocks, const u
 hipError_t launch_fakequant(int mode, const uint16_t* x, uint64_t nblocks, const uint8_t* scales,
                             const float* ts, const GroupSpec* g, const uint8_t* side, uint16_t* y, uint8_t* mask,
                             uint8_t* qcodes, hipStream_t stream);
+// Forward on records read back in the trainer's row order: destination row r
+// of the rows x cols x_train reads source row row_index[r] of the record
+// (scales_src, and side_src = bits for mode 1 or codes for mode 2) of a
+// src_rows x cols site; g == nullptr: one tensor scale ts[0], else g
+// describes groups of the source rows (ts[group of the source row]).
+// Requires rows * (cols / 8) * (cols / 8) < 2^64 (checked by the caller): the
+// row of a half block is then one 64-bit multiply-high by ceil(2^64 / (cols / 8)).
+hipError_t launch_gathered_fakequant(int mode, const uint16_t* x, uint64_t rows, uint64_t cols,
+                                     const int64_t* row_index, uint64_t src_rows, const GroupSpec* g,
+                                     const uint8_t* scales_src, const float* ts, const uint8_t* side_src, uint16_t* y,
+                                     uint8_t* mask, uint8_t* qcodes, hipStream_t stream);
 // MXFP4 (32-element blocks, E8M0 scales); sizes in 32-element blocks.
 hipError_t launch_mx_capture(const uint16_t* x, uint64_t nblocks, uint8_t* scales, uint8_t* bits, uint8_t* codes,
                              hipStream_t stream);

@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define TRACE_ABI_VERSION 8
+#define TRACE_ABI_VERSION 9
 
 #if defined(__GNUC__)
 #define TRACE_API __attribute__((visibility("default")))
@@ -283,6 +283,44 @@ TRACE_API trace_status trace_gather_records(const uint8_t* bits_src, const uint8
                                             const int64_t* row_index, int64_t dst_rows,
                                             uint8_t* bits_dst, uint8_t* scales_dst,
                                             uint8_t* codes_dst, void* stream);
+
+/*
+ * Training-side forwards on records read back in the trainer's row order,
+ * without a gathered copy of the record (rcap.io post, limitations list: a
+ * cache tier holds the rollout's records and the training engine reads them
+ * back).  The result equals trace_gather_records into the trainer's order
+ * followed by the guided (or full-information) forward, with each
+ * destination row's tensor scale taken from its source row:
+ *   destination row r of x_train (rows x cols) uses source row
+ *   s = row_index[r] of the record (scales_src, bits_src or codes_src) of a
+ *   src_rows x cols site, and tensor scale ts[0], or, with offsets, ts[g]
+ *   for the group g of source rows [offsets[g], offsets[g+1]) holding s;
+ *   an index outside [0, src_rows) gives zero-scale blocks (y = +-0 with
+ *   the input's sign, mask 0), as a gathered all-zero record row would.
+ *   row_index : int64[rows] in device memory, 8-byte aligned;
+ *   offsets, groups : NULL and 0 for one tensor scale; otherwise the
+ *               per-expert groups of the source rows, with the rules of the
+ *               grouped entry points below (offsets[groups] = src_rows);
+ *   scales_src u8[src_rows*cols/16]; bits_src u8[src_rows*cols/8];
+ *   codes_src u8[src_rows*cols/2], 8-byte aligned; ts fp32[1 or groups];
+ *   the record pointers may be NULL when src_rows == 0;
+ *   y, mask, qcodes : as trace_guided_fakequant_fwd, in destination order;
+ *   y may be exactly x_train.
+ * Also TRACE_E_SHAPE when rows * (cols/8)^2 reaches 2^64.  rows == 0 is a
+ * no-op.  Other errors as trace_guided_fakequant_fwd.
+ */
+TRACE_API trace_status trace_gathered_guided_fakequant_fwd(const uint16_t* x_train, int64_t rows, int64_t cols,
+                                                           const int64_t* row_index, int64_t src_rows,
+                                                           const int64_t* offsets, int64_t groups,
+                                                           const uint8_t* scales_src, const float* ts,
+                                                           const uint8_t* bits_src, uint16_t* y, uint8_t* mask,
+                                                           uint8_t* qcodes, void* stream);
+TRACE_API trace_status trace_gathered_full_info_fakequant_fwd(const uint16_t* x_train, int64_t rows, int64_t cols,
+                                                              const int64_t* row_index, int64_t src_rows,
+                                                              const int64_t* offsets, int64_t groups,
+                                                              const uint8_t* scales_src, const float* ts,
+                                                              const uint8_t* codes_src, uint16_t* y, uint8_t* mask,
+                                                              uint8_t* qcodes, void* stream);
 
 /*
  * Per-expert tensor scales for packed MoE rows.  Only the routed experts (and

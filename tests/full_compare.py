@@ -135,6 +135,7 @@ _PER = {
     "lowbits": {"scales": 16, "mask": 8, "codes": 2},
 }
 _PER["grouped"] = _PER["nvfp4"]
+_PER["gathered"] = _PER["nvfp4"]
 
 
 def _oracle_nvfp4(xr, xt, g, ts):
@@ -186,6 +187,31 @@ def _oracle_grouped(xr, xt, rows, cols, off, ts):
             "y_f": fi["y"], "mask_f": fi["mask"], "q_f": fi["codes"]}
 
 
+def _oracle_gathered(xt, idx, xr_rows_of, cols, src_rows, off, ts):
+    """Guided and full-information forwards of destination rows xt (their
+    source rows idx) on records read back in place, all from the oracle: the
+    record of the distinct source rows the chunk refers to (in ascending
+    order, so every group's rows stay together) is the oracle's capture of
+    those rows with their groups' scales; the indices are mapped into it."""
+    import oracle
+    valid = (idx >= 0) & (idx < src_rows)
+    u = np.unique(idx[valid])
+    xr = xr_rows_of(u)
+    if off is None:
+        cap = oracle.capture(xr, ts, with_codes=True)
+        sub = None
+    else:
+        group = np.searchsorted(off, u, side="right") - 1
+        sub = np.r_[0, np.cumsum(np.bincount(group, minlength=len(off) - 1))].astype(np.int64)
+        cap = oracle.grouped_capture(xr, u.size, cols, sub, ts, with_codes=True)
+    local = np.full(idx.size, -1, dtype=np.int64)
+    local[valid] = np.searchsorted(u, idx[valid])
+    gd = oracle.gathered_fwd("guided", xt, cols, cap, u.size, local, ts, sub)
+    fi = oracle.gathered_fwd("full", xt, cols, cap, u.size, local, ts, sub)
+    return {"y_g": gd["y"], "mask_g": gd["mask"], "q_g": gd["codes"],
+            "y_f": fi["y"], "mask_f": fi["mask"], "q_f": fi["codes"]}
+
+
 # --------------------------------------------------------------------------
 # worker tasks
 # --------------------------------------------------------------------------
@@ -201,7 +227,20 @@ def _check_task(args):
     with the GPU's outputs in the shared files.  Returns None when every
     byte is equal, else a description of the first differences."""
     kind, specs, a, b, extra = args
-    if kind == "grouped":
+    if kind == "gathered":
+        cols, src_rows, off, ts = extra
+        r0, r1 = a // cols, b // cols
+        idx = _read(specs["idx"], r0, r1)
+        path, dt, nx = specs["xr"]
+
+        def rows_of(u):
+            mm = np.memmap(path, dtype=np.dtype(dt), mode="r", shape=(max(1, nx),))
+            out = np.array(mm[: src_rows * cols].reshape(src_rows, cols)[u]).reshape(-1)
+            del mm
+            return out
+
+        want = _oracle_gathered(_read(specs["xt"], a, b), idx, rows_of, cols, src_rows, off, ts)
+    elif kind == "grouped":
         cols, off, ts = extra
         r0, r1 = a // cols, b // cols
         sub = np.clip(np.asarray(off, dtype=np.int64) - r0, 0, r1 - r0).astype(np.int64)
@@ -287,6 +326,22 @@ def compare_variant_every_element(name, kind, xr, xt, got, extra=None, g=None):
         for k, v in got.items():
             sh.put(k, v)
         return _run_checks(name, kind, sh, n, extra, CHUNK_ELEMS, progress=4)
+
+
+def compare_gathered_every_element(name, xr, src_rows, xt, idx, cols, off, ts, got):
+    """The forwards on records read back in place: xr the source site
+    (src_rows x cols), xt the destination rows, idx their source rows
+    (int64, out-of-range allowed), off the source's row groups (None: one
+    tensor scale ts) and the oracle's tensor scale(s) ts; got the GPU's
+    y_g, mask_g, q_g, y_f, mask_f, q_f.  Chunks of whole destination rows."""
+    with Shared({"xr": xr, "xt": xt, "idx": np.asarray(idx, dtype=np.int64)}) as sh:
+        for k, v in got.items():
+            sh.put(k, v)
+        n = sh.specs["xt"][2]
+        chunk = max(1, CHUNK_ELEMS // cols) * cols
+        extra = (cols, src_rows, None if off is None else np.asarray(off, dtype=np.int64),
+                 np.float32(ts) if off is None else np.asarray(ts, dtype=np.float32))
+        return _run_checks(name, "gathered", sh, n, extra, chunk, progress=4)
 
 
 def compare_grouped_every_element(name, xr, xt, rows, cols, off, ts, got):

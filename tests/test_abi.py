@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert tr.abi_version() == 8
+    assert tr.abi_version() == 9
     for code in range(6):
         assert L.trace_status_string(code).decode().startswith("TRACE")
     assert b"unknown" in L.trace_status_string(99)
@@ -191,6 +191,36 @@ def test_gather_records_validation():
     assert call(bd=bs + 8) == E_ALIAS     # destination over source plane
     assert call(sd=idx + 8) == E_ALIAS    # destination over the index array
     assert call(dst_rows=0) == OK
+
+
+def test_gathered_fwd_validation():
+    """Every call below is rejected before any HIP call, or is a no-op."""
+    x, idx, off, sc, ts, sd, y, mk, qc = (A + k * 0x1000000 for k in range(9))
+
+    def call(f=L.trace_gathered_guided_fakequant_fwd, x=x, rows=8, cols=64, idx=idx, src_rows=6, off=None, groups=0,
+             sc=sc, ts=ts, sd=sd, y=y, mk=mk, qc=None):
+        q = lambda v: P(v) if v is not None else None
+        return f(q(x), rows, cols, q(idx), src_rows, q(off), groups, q(sc), q(ts), q(sd), q(y), q(mk), q(qc), None)
+
+    full = L.trace_gathered_full_info_fakequant_fwd
+    assert call(idx=None) == E_NULL
+    assert call(ts=None) == E_NULL
+    assert call(sd=None) == E_NULL
+    assert call(groups=3) == E_NULL                    # groups without offsets
+    assert call(off=off, groups=0) == E_SHAPE
+    assert call(cols=40) == E_SHAPE
+    assert call(rows=-1) == E_SHAPE
+    assert call(src_rows=-1) == E_SHAPE
+    assert call(rows=1 << 40, cols=1 << 16) == E_SHAPE  # rows * (cols/8)^2 reaches 2^64
+    assert call(idx=idx + 4) == E_ALIGN
+    assert call(x=x + 8) == E_ALIGN
+    assert call(mk=mk + 1) == E_ALIGN
+    assert call(off=off + 4, groups=2) == E_ALIGN
+    assert call(f=full, sd=sd + 4) == E_ALIGN          # codes 8-byte aligned
+    assert call(y=idx + 16) == E_ALIAS                 # output over the index array
+    assert call(mk=sc) == E_ALIAS                      # mask over the source scale bytes
+    assert call(qc=off, off=off, groups=2) == E_ALIAS  # qcodes over the offsets
+    assert call(rows=0) == OK
 
 
 def test_build_script_loads_without_the_library():

@@ -89,3 +89,32 @@ def test_shared_files_hold_tensor_bytes():
         assert np.array_equal(fc._read(sh.specs["x"], 0, x.numel()), x.view(torch.int16).numpy().view(np.uint16).reshape(-1))
         assert np.array_equal(fc._read(sh.specs["b"], 0, 777), b.numpy())
         assert fc._read(sh.specs["h"], 1, 4).tolist() == [1, 2, 3]
+
+
+@pytest.mark.parametrize("grouped", [False, True])
+def test_gathered_harness_rebuilds_each_chunks_records(grouped):
+    """The per-chunk record of the referenced source rows (and the index
+    remapping into it) reproduces the whole-site oracle: gathered_fwd on the
+    full source record."""
+    src_rows, cols = 80, 512
+    xr, _, _ = _site(src_rows, cols, seed=7)
+    rng = np.random.default_rng(8)
+    idx = np.r_[rng.permutation(src_rows), rng.integers(0, src_rows, 30), [-1, src_rows, 5]].astype(np.int64)
+    xt = F.f32_to_bf16_rne(rng.standard_normal(idx.size * cols).astype(np.float32))
+    off = np.array([0, 0, 17, 17, 60, 80], dtype=np.int64) if grouped else None
+    if grouped:
+        ts = oracle.grouped_tensor_scale(xr, src_rows, cols, off)
+        rec = oracle.grouped_capture(xr, src_rows, cols, off, ts, with_codes=True)
+    else:
+        ts = np.float32(oracle.tensor_scale(xr))
+        rec = oracle.capture(xr, ts, with_codes=True)
+    want = {}
+    for mode, tag in (("guided", "g"), ("full", "f")):
+        r = oracle.gathered_fwd(mode, xt, cols, rec, src_rows, idx, ts, off)
+        want.update({f"y_{tag}": r["y"], f"mask_{tag}": r["mask"], f"q_{tag}": r["codes"]})
+    assert fc.compare_gathered_every_element("ok", xr, src_rows, xt, idx, cols, off, ts, want) == idx.size * cols
+    bad = dict(want)
+    bad["q_f"] = want["q_f"].copy()
+    bad["q_f"][(idx.size - 2) * cols // 2] ^= 0x10     # the row whose index is out of range
+    with pytest.raises(AssertionError, match="q_f"):
+        fc.compare_gathered_every_element("planted", xr, src_rows, xt, idx, cols, off, ts, bad)

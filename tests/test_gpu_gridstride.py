@@ -69,6 +69,24 @@ def _everything(tr, xr, xt, g, offsets, perm):
                      ("gf", lambda: tr.grouped_full_info_fakequant_fwd(xt, offsets, gsc, gts, gcd, want_codes=True))):
         y, m, q = fn()
         out.update({f"y_{name}": y, f"m_{name}": m, f"q_{name}": q})
+    # forwards on records read back in place: x_train gets one row per entry
+    # of perm (a waves-inside-rows width), and the same record read as rows
+    # of 64 elements (waves spanning rows; the record is in flat order)
+    rows, cols = xr.shape
+    xg = torch.cat([xt, xt[:perm.numel() - rows]])
+    n64 = xr.numel() // 64
+    perm64 = torch.cat([torch.randperm(n64, generator=torch.Generator(device=xr.device).manual_seed(5),
+                                       device=xr.device),
+                        torch.tensor([-1, n64], dtype=torch.int64, device=xr.device)])
+    x64 = torch.cat([xt.reshape(n64, 64), xt.reshape(n64, 64)[:2]])
+    for name, fn in (("xg", lambda: tr.gathered_guided_fakequant_fwd(xg, perm, sc, ts, bt, want_codes=True)),
+                     ("xf", lambda: tr.gathered_full_info_fakequant_fwd(xg, perm, sc, ts, cd, want_codes=True)),
+                     ("xgg", lambda: tr.gathered_guided_fakequant_fwd(xg, perm, gsc, gts, gbt, offsets=offsets,
+                                                                      want_codes=True)),
+                     ("x64", lambda: tr.gathered_guided_fakequant_fwd(x64, perm64, sc, ts, bt, want_codes=True)),
+                     ("x64f", lambda: tr.gathered_full_info_fakequant_fwd(x64, perm64, sc, ts, cd, want_codes=True))):
+        y, m, q = fn()
+        out.update({f"y_{name}": y, f"m_{name}": m, f"q_{name}": q})
     msc, mbt, mcd = tr.mx_capture(xr, want_codes=True)
     out.update(msc=msc, mbt=mbt, mcd=mcd)
     for name, fn in (("mg", lambda: tr.mx_guided_fakequant_fwd(xt, msc, mbt, want_codes=True)),

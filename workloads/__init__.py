@@ -140,6 +140,12 @@ def moe_expert_offsets(expert_of_row):
     return torch.cat([torch.zeros(1, dtype=torch.int64, device=counts.device), torch.cumsum(counts, 0)])
 
 
+def trainer_order(rows, device):
+    """The training side's row order for records read back from the
+    rollout: a seeded random permutation of the rows (int64 on device)."""
+    return torch.randperm(rows, generator=generator(device, "trainer order"), device=_dev(device))
+
+
 def moe_layer(device, sigma, sites=None):
     """Dict site -> {x_roll, x_train, grad} for the MoE layer sites."""
     sites = sites or list(SHAPES[1])
