@@ -21,7 +21,8 @@
 // (one tile per workgroup); the kernels keep a grid-stride loop only for grids
 // larger than the launch limit.  The two amax passes are the exceptions: the
 // tensor amax loops a capped grid (one partial maximum per workgroup) and the
-// per-row amax gives each wave one row.
+// per-row amax gives each row a workgroup (rows of 2048 elements or more) or
+// a wave (narrower rows).
 //
 // Every kernel has an exact fast path and an exact fallback.  The fast path
 // computes each quotient x / s with a double-word reciprocal and one
@@ -340,8 +341,42 @@ __device__ __forceinline__ float group_tensor_scale(const RowGroups& G, const fl
 }
 
 
+// Maximum over a wave of non-negative values by DPP (row shifts within each
+// 16-lane row, then the row broadcasts of lanes 15 and 31); the result is
+// valid in lane 63.  Lanes a shift reaches from outside their row read 0,
+// which leaves a maximum of non-negative values unchanged.
+__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true));   // row_shr:1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true));   // row_shr:2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true));   // row_shr:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true));   // row_shr:8
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return v;
+}
+
+// Magnitude-bit maximum of a 128-bit vector's halves folded into best (NaN
+// halves map below every other value, as in amax_partial_body).
+__device__ __forceinline__ void fold_vec_max(const uint4 v, s16x2& best) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t m = (w[k] & 0x7fff7fffu) + 0x007f007fu;
+    s16x2 vv;
+    __builtin_memcpy(&vv, &m, 4);
+    best = __builtin_elementwise_max(best, vv);
+  }
+}
+
+__device__ __forceinline__ uint32_t best_to_bits(s16x2 best) {
+  const int lo = best.x, hi = best.y;
+  const int m = lo > hi ? lo : hi;
+  return m > 0x7f ? (uint32_t)(m - 0x7f) : 0u;
+}
+
 // Grouped tensor scale, pass 1: the magnitude-bit maximum of every row (NaN
-// excluded as in amax_partial_kernel); one wave per row.
+// excluded as in amax_partial_kernel).  Rows of fewer than 256 vectors (2048
+// elements): one wave per row, four loads in flight per lane.
 __global__ __launch_bounds__(kThreads) void row_amax_kernel(const uint4* __restrict__ x, uint64_t rows,
                                                             uint64_t vec_per_row,
                                                             uint32_t* __restrict__ row_amax) {
@@ -358,21 +393,31 @@ __global__ __launch_bounds__(kThreads) void row_amax_kernel(const uint4* __restr
         v[u] = x[r * vec_per_row + (c < vec_per_row ? c : vec_per_row - 1)];
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t m = (w[k] & 0x7fff7fffu) + 0x007f007fu;
-          s16x2 vv;
-          __builtin_memcpy(&vv, &m, 4);
-          best = __builtin_elementwise_max(best, vv);
-        }
-      }
+      for (int u = 0; u < 4; ++u) fold_vec_max(v[u], best);
     }
-    const int lo = best.x, hi = best.y;
-    const int m = lo > hi ? lo : hi;
-    const uint32_t rmax = wave_max_u32(m > 0x7f ? (uint32_t)(m - 0x7f) : 0u);
-    if (lane == 0) row_amax[r] = rmax;
+    const uint32_t rmax = wave_max_dpp(best_to_bits(best));
+    if (lane == 63) row_amax[r] = rmax;
+  }
+}
+
+// Rows of 256 vectors or more: one workgroup per row, lane t loading vectors
+// t, t + 256, ... of it.  On the 131072x2048 routed-expert site this streams
+// 4-8% faster than a wave per row (one vector per lane in flight, the
+// layout the streaming kernels favour): 88 against 91-93 us after a
+// read-only pass, 114 against 122-126 us right after a 512 MB writer.
+__global__ __launch_bounds__(kThreads) void row_amax_wg_kernel(const uint4* __restrict__ x, uint64_t rows,
+                                                               uint64_t vec_per_row,
+                                                               uint32_t* __restrict__ row_amax) {
+  __shared__ uint32_t red[kThreads / 64];
+  for (uint64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    s16x2 best = {0, 0};
+    const uint4* row = x + r * vec_per_row;
+    for (uint64_t c = threadIdx.x; c < vec_per_row; c += kThreads) fold_vec_max(row[c], best);
+    const uint32_t wm = wave_max_dpp(best_to_bits(best));
+    if ((threadIdx.x & 63) == 63) red[threadIdx.x >> 6] = wm;
+    __syncthreads();
+    if (threadIdx.x == 0) row_amax[r] = max(max(red[0], red[1]), max(red[2], red[3]));
+    __syncthreads();  // red is rewritten for the next row
   }
 }
 
@@ -1110,9 +1155,13 @@ hipError_t launch_grouped_tensor_scale(const uint16_t* x, const GroupSpec& g, ui
                                        hipStream_t stream) {
   const uint64_t rows_per_group = kThreads / 64;
   const uint64_t wg = (g.rows + rows_per_group - 1) / rows_per_group;
-  if (g.rows > 0)  // every row gets its word, also rows of zero width
+  const uint64_t vpr = g.cols / 8;
+  if (g.rows > 0 && vpr >= kThreads)
+    hipLaunchKernelGGL(row_amax_wg_kernel, dim3((unsigned)(g.rows < kMaxGroups ? g.rows : kMaxGroups)),
+                       dim3(kThreads), 0, stream, reinterpret_cast<const uint4*>(x), g.rows, vpr, row_amax);
+  else if (g.rows > 0)  // every row gets its word, also rows of zero width
     hipLaunchKernelGGL(row_amax_kernel, dim3((unsigned)(wg < kMaxGroups ? wg : kMaxGroups)), dim3(kThreads), 0,
-                       stream, reinterpret_cast<const uint4*>(x), g.rows, g.cols / 8, row_amax);
+                       stream, reinterpret_cast<const uint4*>(x), g.rows, vpr, row_amax);
   hipLaunchKernelGGL(group_amax_finalize_kernel, dim3((unsigned)g.count), dim3(kThreads), 0, stream, row_amax,
                      row_groups(g), ts_out);
   return hipGetLastError();
