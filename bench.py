@@ -8,9 +8,11 @@ grad ~ N(0, 1).  All 20 layers' inputs are generated on the GPU and resident
 in HBM (distinct 1 GiB buffers, far larger than the 256 MB last-level cache)
 before timing starts.
 
-One step = for every layer, in order: tensor scale (amax pass), capture
-(scale bytes + parity bit-plane), guided fake-quant forward (y + clip mask),
-plain RNE fake-quant forward (y + clip mask), STE backward.  A HIP event
+One step = the rollout side over every layer (tensor scale, i.e. the amax
+pass, then capture: scale bytes + parity bit-plane), then the training side
+over every layer (guided fake-quant forward: y + clip mask, plain RNE
+fake-quant forward: y + clip mask, STE backward), the order of an RL step's
+rollout and training phases.  A HIP event
 marker on the kernels' stream sits before the first kernel and after every
 kernel, so each kernel is timed between the markers around it; the step's
 wall time is taken between device synchronizations.  After the timed steps, a separate
@@ -19,8 +21,10 @@ full-information forward, MXFP4 capture and guided forward, and capture to
 and forward from b = 3 cached low bits, on the same layers) and reports them
 under ``next_rows``; another
 times the per-expert (grouped) tensor scale, capture and guided forward and
-the record gather on the packed routed-expert site of the MoE layer workload
-(``moe_expert_site``); a last one runs the step's kernels on the sites of
+the record gather, and the forwards on records read back in a shuffled row
+order, on the packed routed-expert site of the MoE layer workload
+(``moe_expert_site``); ``kernels_cold`` times one layer's tensor scale and
+capture after a read-only pass; a last one runs the step's kernels on the sites of
 the other workloads, cold and repeated (``other_workloads``).
 
 Prints one JSON line (last line of stdout).  ``value`` is the algorithmic
@@ -187,8 +191,14 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
 
+    # An RL step runs the rollout (which captures every layer's site) and then
+    # the training pass (which reads every layer's record back), so a step
+    # here is the rollout side over all layers, then the training side over
+    # all layers.  STEP_ORDER names the kernel of each launch in that order.
+    STEP_ORDER = ["tensor_scale", "capture"] * L + ["guided_fwd", "rne_fwd", "ste_bwd"] * L
+
     def step(markers=None):
-        """One pass over all layers.  markers: None, or len(KERNELS) * L + 1
+        """One pass over all layers.  markers: None, or len(STEP_ORDER) + 1
         timing events, recorded before the first kernel and after every
         kernel (one shared marker between consecutive kernels: a kernel's
         duration is the time between the markers around it; two markers per
@@ -199,11 +209,12 @@ def main():
             if it is not None:
                 next(it).record(stream)
         mark()
-        for d in layers:
+        for d in layers:  # rollout side
             tr.tensor_scale(d["x_roll"], out=d["ts"], workspace=ws)
             mark()
             tr.capture(d["x_roll"], d["ts"], scales=d["scales"], bits=d["bits"])
             mark()
+        for d in layers:  # training side
             tr.guided_fakequant_fwd(d["x_train"], d["scales"], d["ts"], d["bits"], y=y_g, mask=mask_g)
             mark()
             tr.rne_fakequant_fwd(d["x_train"], d["scales"], d["ts"], y=y_r, mask=mask_r)
@@ -216,11 +227,10 @@ def main():
     torch.cuda.synchronize()
 
     per_kernel_ms = {k: 0.0 for k in KERNELS}
-    nk = len(KERNELS)
     # every step records its own markers, so the steps run back to back with
     # no host synchronization between them; the markers are read after the
     # timed region
-    markers = [[torch.cuda.Event(enable_timing=True) for _ in range(nk * L + 1)] for _ in range(args.steps)]
+    markers = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STEP_ORDER) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -228,8 +238,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     for m in markers:
-        for i in range(nk * L):
-            per_kernel_ms[KERNELS[i % nk]] += m[i].elapsed_time(m[i + 1])
+        for i, k in enumerate(STEP_ORDER):
+            per_kernel_ms[k] += m[i].elapsed_time(m[i + 1])
     ms_per_step = 1e3 * wall / args.steps
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step")
 
@@ -333,7 +343,8 @@ def main():
                                f"bf16 site per layer (64 trajectories x 4096 tokens), Gaussian with 0.1% outlier "
                                f"channels x100",
                    "layers": L, "rows": ROWS, "cols": COLS, "elements_per_step": L * n,
-                   "step": "tensor_scale + capture + guided_fwd + rne_fwd + ste_bwd per layer"},
+                   "step": "rollout side (tensor_scale + capture) over all layers, then training side "
+                           "(guided_fwd + rne_fwd + ste_bwd) over all layers"},
         "gelem_per_s": round(L * n / (ms_per_step * 1e-3) / 1e9, 3),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "kernels": kernels,
