@@ -39,6 +39,7 @@ write-only stream on the same GPU (``bench_ceiling.hip``).
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -89,6 +90,7 @@ READBACK_BYTES_PER_ELEM = {
     "fused_guided_fwd_per_expert": 2.0 + 1 / 8 + 1 / 16 + 2.0 + 1 / 8,
 }
 GATHER_RUN = 256         # rows per run in the run-ordered gather
+MOE_REPS, MOE_WARM_S = 8, 0.1  # timed reps of the routed-expert site rows, after this long of untimed ones
 CPU_SHARE = 16           # host cores granted to a process driving one GPU
 CPU_BUDGET_S = 12.0      # wall-clock budget of the CPU oracle leg
 CHUNK_ROWS = 128
@@ -553,10 +555,14 @@ def workload_rows(tr, workloads, torch, dev, stream, reps=3):
 
 
 def moe_rows(tr, workloads, torch, dev, stream, layers, reps):
-    """Per-expert tensor scales on the packed routed-expert site, and the
-    trainer-side gather of its records into a shuffled row order (single
-    rows, and runs of GATHER_RUN consecutive rows), each gather timed after a
-    read-only 1 GiB pass."""
+    """Per-expert tensor scales on the packed routed-expert site (the
+    sequence tensor scale, capture, guided forward: in sequence, and each rep
+    after a read-only 1 GiB pass), the trainer-side gather of its records
+    into a shuffled row order (single rows, and runs of GATHER_RUN
+    consecutive rows), and the trainer's forward on its rows in that order
+    (gather then forward, against the fused read-back forwards); every
+    gather and read-back variant after a read-only 1 GiB pass.  Medians of
+    MOE_REPS reps."""
     sigma = 0.02
     d = workloads.moe_layer(dev, sigma, sites=["expert_in"])["expert_in"]
     _, experts = workloads.moe_routing(dev)
@@ -577,89 +583,91 @@ def moe_rows(tr, workloads, torch, dev, stream, layers, reps):
     bits = torch.empty(n // 8, dtype=torch.uint8, device=dev)
     y = torch.empty_like(x_train)
     mask = torch.empty(n // 8, dtype=torch.uint8, device=dev)
-    ms = {k: 0.0 for k in MOE_BYTES_PER_ELEM}
-    ms_cold = {k: 0.0 for k in ("grouped_tensor_scale", "grouped_capture", "grouped_guided_fwd")}
-    for it in range(2 * (reps + 1)):
-        cold = it > reps  # the second half: every sequence after a read-only 1 GiB pass
+    flush = layers[0]["x_roll"]
+
+    def medians(run, names):
+        """run(ev) enqueues one rep, recording ev[name] = (start, end) events;
+        returns the median microseconds of each name over MOE_REPS reps.
+        Untimed reps run first for MOE_WARM_S seconds: after the data
+        generation the GPU's clocks settle over ~20-40 ms of sustained work,
+        during which the capture and the forward measured up to 40% and 15%
+        slower."""
+        t = {k: [] for k in names}
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < MOE_WARM_S:
+            run({k: (torch.cuda.Event(), torch.cuda.Event()) for k in names})
+            stream.synchronize()
+        for _ in range(MOE_REPS):
+            ev = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for k in names}
+            run(ev)
+            stream.synchronize()
+            for k in names:
+                t[k].append(ev[k][0].elapsed_time(ev[k][1]) * 1e3)
+        return {k: statistics.median(v) for k, v in t.items()}
+
+    def timed(ev, k, fn):
+        ev[k][0].record(stream)
+        fn()
+        ev[k][1].record(stream)
+
+    seq_names = ("grouped_tensor_scale", "grouped_capture", "grouped_guided_fwd")
+
+    def sequence(ev, cold):
         if cold:
-            tr.tensor_scale(layers[0]["x_roll"], out=flush_ts)
-        ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(2)] for k in MOE_BYTES_PER_ELEM}
-        ev["grouped_tensor_scale"][0].record(stream)
-        tr.grouped_tensor_scale(x_roll, offsets, out=ts, workspace=ws)
-        ev["grouped_tensor_scale"][1].record(stream)
-        ev["grouped_capture"][0].record(stream)
-        tr.grouped_capture(x_roll, offsets, ts, scales=scales, bits=bits)
-        ev["grouped_capture"][1].record(stream)
-        ev["grouped_guided_fwd"][0].record(stream)
-        tr.grouped_guided_fakequant_fwd(x_train, offsets, scales, ts, bits, y=y, mask=mask)
-        ev["grouped_guided_fwd"][1].record(stream)
-        stream.synchronize()
-        if it > 0 and it != reps + 1:
-            for k in ("grouped_tensor_scale", "grouped_capture", "grouped_guided_fwd"):
-                (ms_cold if cold else ms)[k] += ev[k][0].elapsed_time(ev[k][1])
+            tr.tensor_scale(flush, out=flush_ts)  # read-only 1 GiB pass
+        timed(ev, "grouped_tensor_scale", lambda: tr.grouped_tensor_scale(x_roll, offsets, out=ts, workspace=ws))
+        timed(ev, "grouped_capture", lambda: tr.grouped_capture(x_roll, offsets, ts, scales=scales, bits=bits))
+        timed(ev, "grouped_guided_fwd",
+              lambda: tr.grouped_guided_fakequant_fwd(x_train, offsets, scales, ts, bits, y=y, mask=mask))
+
+    us = medians(lambda ev: sequence(ev, False), seq_names)
+    us_cold = medians(lambda ev: sequence(ev, True), seq_names)
+
     # the gathers are short (0.375 B per element): each is timed after a
     # read-only 1 GiB pass, outside the previous kernel's write-back
-    for it in range(reps + 1):
-        ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(2)] for k in ("gather_records",
-                                                                                    "gather_records_runs")}
+    def gathers(ev):
         for k, order in (("gather_records", perm), ("gather_records_runs", runs)):
-            tr.tensor_scale(layers[0]["x_roll"], out=flush_ts)
-            ev[k][0].record(stream)
-            tr.gather_records(bits, scales, None, cols, order)
-            ev[k][1].record(stream)
-        stream.synchronize()
-        if it > 0:
-            for k in ev:
-                ms[k] += ev[k][0].elapsed_time(ev[k][1])
+            tr.tensor_scale(flush, out=flush_ts)
+            timed(ev, k, lambda: tr.gather_records(bits, scales, None, cols, order))
+
+    us.update(medians(gathers, ("gather_records", "gather_records_runs")))
+
     # the trainer's forward on its rows in its own order, each variant after
     # a read-only 1 GiB pass
     xt_perm = x_train[perm]
     ts1 = tr.tensor_scale(x_roll)
     sc1, bt1, _ = tr.capture(x_roll, ts1)
-    rb = {k: 0.0 for k in READBACK_BYTES_PER_ELEM}
-    for it in range(reps + 1):
-        ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(2)] for k in READBACK_BYTES_PER_ELEM}
-        tr.tensor_scale(layers[0]["x_roll"], out=flush_ts)
-        ev["gather_then_guided_fwd"][0].record(stream)
+
+    def two_step():
         g_bits, g_scales, _ = tr.gather_records(bt1, sc1, None, cols, perm)
         tr.guided_fakequant_fwd(xt_perm, g_scales, ts1, g_bits, y=y, mask=mask)
-        ev["gather_then_guided_fwd"][1].record(stream)
-        tr.tensor_scale(layers[0]["x_roll"], out=flush_ts)
-        ev["fused_guided_fwd"][0].record(stream)
-        tr.gathered_guided_fakequant_fwd(xt_perm, perm, sc1, ts1, bt1, y=y, mask=mask)
-        ev["fused_guided_fwd"][1].record(stream)
-        tr.tensor_scale(layers[0]["x_roll"], out=flush_ts)
-        ev["fused_guided_fwd_per_expert"][0].record(stream)
-        tr.gathered_guided_fakequant_fwd(xt_perm, perm, scales, ts, bits, offsets=offsets, y=y, mask=mask)
-        ev["fused_guided_fwd_per_expert"][1].record(stream)
-        stream.synchronize()
-        if it > 0:
-            for k in ev:
-                rb[k] += ev[k][0].elapsed_time(ev[k][1])
+
+    def readback(ev):
+        for k, fn in (("gather_then_guided_fwd", two_step),
+                      ("fused_guided_fwd",
+                       lambda: tr.gathered_guided_fakequant_fwd(xt_perm, perm, sc1, ts1, bt1, y=y, mask=mask)),
+                      ("fused_guided_fwd_per_expert",
+                       lambda: tr.gathered_guided_fakequant_fwd(xt_perm, perm, scales, ts, bits, offsets=offsets,
+                                                                y=y, mask=mask))):
+            tr.tensor_scale(flush, out=flush_ts)
+            timed(ev, k, fn)
+
+    us_rb = medians(readback, tuple(READBACK_BYTES_PER_ELEM))
+
+    def row(k_us, bpe):
+        gbs = bpe * n / (k_us * 1e-6) / 1e9
+        return {"median_us": round(k_us, 2), "GB_s": round(gbs, 1), "Gelem_s": round(n / (k_us * 1e-6) / 1e9, 2),
+                "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": int(bpe * n)}
+
     out = {"site": f"routed-expert input {rows}x{cols} bf16, rows grouped by {groups} experts "
-                   f"(top-8 of 128 routing of 16384 tokens), Student-t(4)", "kernels": {}}
-    for k, bpe in MOE_BYTES_PER_ELEM.items():
-        avg = ms[k] / reps
-        gbs = bpe * n / (avg * 1e-3) / 1e9
-        out["kernels"][k] = {"avg_us": round(avg * 1e3, 2), "GB_s": round(gbs, 1),
-                             "Gelem_s": round(n / (avg * 1e-3) / 1e9, 2), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-                             "bytes_per_launch": int(bpe * n)}
+                   f"(top-8 of 128 routing of 16384 tokens), Student-t(4)",
+           "timing": f"median of {MOE_REPS} reps after {MOE_WARM_S} s of untimed ones, HIP events",
+           "kernels": {k: row(us[k], bpe) for k, bpe in MOE_BYTES_PER_ELEM.items()}}
     out["kernels_cold"] = {"protocol": "the same sequence (grouped tensor scale, capture, guided forward), each "
                                        "rep after a read-only 1 GiB pass instead of right after the previous "
                                        "rep's forward (whose output lines are then still being written back)"}
-    for k, tot in ms_cold.items():
-        avg = tot / reps
-        gbs = MOE_BYTES_PER_ELEM[k] * n / (avg * 1e-3) / 1e9
-        out["kernels_cold"][k] = {"avg_us": round(avg * 1e3, 2), "GB_s": round(gbs, 1),
-                                  "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
-    out["readback_trainer_order"] = {}
-    for k, bpe in READBACK_BYTES_PER_ELEM.items():
-        avg = rb[k] / reps
-        gbs = bpe * n / (avg * 1e-3) / 1e9
-        out["readback_trainer_order"][k] = {"avg_us": round(avg * 1e3, 2), "GB_s": round(gbs, 1),
-                                            "Gelem_s": round(n / (avg * 1e-3) / 1e9, 2),
-                                            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-                                            "bytes_per_launch": int(bpe * n)}
+    out["kernels_cold"].update({k: row(us_cold[k], MOE_BYTES_PER_ELEM[k]) for k in seq_names})
+    out["readback_trainer_order"] = {k: row(us_rb[k], bpe) for k, bpe in READBACK_BYTES_PER_ELEM.items()}
     del d, x_roll, x_train, y, xt_perm
     return out
 
