@@ -57,4 +57,26 @@ def test_entry_points_refuse_host_and_short_tensors(device):
         tr.capture_batch([x], [host_ts])
     with pytest.raises(ValueError, match="at least"):
         tr.mismatch_stats(x, sc, ts, bt, short(cd))
+    # forwards on records read back in place: the source's row count comes
+    # from the scale bytes, and every other record plane must cover it
+    idx = torch.arange(rows, dtype=torch.int64, device=device)
+    with pytest.raises(ValueError, match="at least"):
+        tr.gathered_guided_fakequant_fwd(x, idx, sc, ts, short(bt))
+    with pytest.raises(ValueError, match="at least"):
+        tr.gathered_full_info_fakequant_fwd(x, idx, sc, ts, short(cd))
+    with pytest.raises(ValueError, match="one entry per row"):
+        tr.gathered_guided_fakequant_fwd(x, torch.cat([idx, idx[:1]]), sc, ts, bt)
+    with pytest.raises(ValueError, match="at least"):
+        tr.gathered_guided_fakequant_fwd(x, idx[:-1], sc, ts, bt)
+    with pytest.raises(ValueError, match="must be on"):
+        tr.gathered_guided_fakequant_fwd(x, idx.cpu(), sc, ts, bt)
+    with pytest.raises(ValueError, match="must be on"):
+        tr.gathered_guided_fakequant_fwd(x, idx, sc, host_ts, bt)
+    with pytest.raises(ValueError, match="at least"):
+        tr.gathered_guided_fakequant_fwd(x, idx, sc, short(gts), bt, offsets=offsets)
+    with pytest.raises(ValueError, match="must be on"):
+        tr.gathered_guided_fakequant_fwd(x, idx, sc, gts, bt, offsets=offsets.cpu())
+    with pytest.raises(ValueError, match="at least"):
+        tr.gathered_guided_fakequant_fwd(x, idx, sc, ts, bt, mask=torch.empty(n // 8 - 1, dtype=torch.uint8,
+                                                                              device=device))
     torch.cuda.synchronize()
