@@ -64,6 +64,19 @@ def _command(out, defines=()):
 CEILING_SRC = os.path.join(ROOT, "bench_ceiling.hip")
 CEILING_BIN = os.path.join(ROOT, "_build", "bench_ceiling")
 
+# A plain C caller of the library (tests/c/trace_c_smoke.c), built with the
+# host C compiler against include/trace.h and libtrace.so; run by a GPU test.
+C_SMOKE_SRC = os.path.join(ROOT, "tests", "c", "trace_c_smoke.c")
+C_SMOKE_BIN = os.path.join(ROOT, "_build", "trace_c_smoke")
+
+
+def _c_smoke_command(out):
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    return [os.environ.get("CC", "gcc"), "-std=c99", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(rocm, "include"), C_SMOKE_SRC,
+            "-L", PKG, "-l:libtrace.so", "-Wl,-rpath,$ORIGIN/../fp4_rollout_guided_amd",
+            "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-Wl,-rpath," + os.path.join(rocm, "lib"), "-o", out]
+
 
 def build(verbose: bool = False) -> str:
     """Compile every source into fp4_rollout_guided_amd/libtrace.so (and the
@@ -91,6 +104,15 @@ def build(verbose: bool = False) -> str:
             if lines:
                 print("\n".join(lines))
         os.replace(out + ".tmp", out)
+    if os.path.exists(C_SMOKE_SRC):  # links against the library just built
+        cmd = _c_smoke_command(C_SMOKE_BIN + ".tmp")
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+        if p.returncode != 0:
+            sys.stderr.write(p.stdout + p.stderr)
+            raise RuntimeError(f"the C caller failed to build (exit code {p.returncode})")
+        os.replace(C_SMOKE_BIN + ".tmp", C_SMOKE_BIN)
     return LIB
 
 
