@@ -817,18 +817,19 @@ __device__ __forceinline__ uint64_t readfirstlane_u64(uint64_t v) {
 // 131072x2048 routed-expert site in a shuffled row order, after a read-only
 // pass: one segment per wave 198-203 us, two 189-194, four 190-199, eight
 // 210 (registers); the gather and then the forward take 204-222 us.
-// kWaveRow: every segment lies inside one destination row (half blocks per
-// row a multiple of 64, so rows start at segment boundaries); the row index,
-// its source row and the group lookup are then scalar work per segment, and
-// a segment in the same row as the previous one reuses its lookups
-// (per-expert scales: 215-240 -> 194-203 us).  Otherwise each lane finds its
-// own row.
+// kRowScalar (rows of 64 half blocks or more): a segment spans at most two
+// rows, so its row indices, source rows and group lookups are scalar work
+// (two at most per segment) and each lane picks the one of its row; a
+// segment that starts in the row the previous one looked up reuses that
+// lookup (per-expert scales on the 2048-wide site: 215-240 -> 194-203 us;
+// on the 131072x768 site without groups 89 -> 80 us, where the gather and
+// then the forward take 84 us).  Otherwise each lane finds its own row.
 #ifndef TRACE_GATHER_SEGS
 #define TRACE_GATHER_SEGS 2
 #endif
 constexpr int kGatherSegs = TRACE_GATHER_SEGS;
 
-template <int kMode, bool kGrouped, bool kWaveRow>
+template <int kMode, bool kGrouped, bool kRowScalar>
 __global__ __launch_bounds__(kThreads) void fakequant_gathered_kernel(const uint4* __restrict__ x, uint64_t nhalves,
                                                                       GatherMap gm,
                                                                       const uint8_t* __restrict__ scales_src,
@@ -848,23 +849,45 @@ __global__ __launch_bounds__(kThreads) void fakequant_gathered_kernel(const uint
   uint64_t base = readfirstlane_u64((uint64_t)blockIdx.x * per_wg + (uint64_t)(threadIdx.x >> 6) * 64 * K);
   for (; base < nhalves; base += stride) {
     uint4 v[K];
-    int64_t s[K];
-    uint64_t c[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const uint64_t h = base + 64 * k + lane;
       v[k] = h < nhalves ? x[h] : make_uint4(0u, 0u, 0u, 0u);
     }
-    bool dup[K];  // kWaveRow: segment k lies in the same row as segment k - 1
+    int64_t s[K];     // each lane's source row (-1: none)
+    uint64_t c[K];    // each lane's half block within its row
+    bool second[K];   // kRowScalar: the lane lies in the segment's second row
+    int64_t sa[K], sb[K];  // kRowScalar: source rows of the segment's first and second row
+    uint64_t ra[K];        // kRowScalar: the segment's first row
+    bool two[K];           // kRowScalar: the segment reaches into row ra + 1
+    bool fresh_a[K], fresh_b[K];  // kRowScalar: that lookup is not a copy of an earlier one
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const uint64_t h0 = base + 64 * k;  // the segment's first half block (wave-uniform)
       const uint64_t h = h0 + lane;
-      const bool live = kWaveRow ? h0 < nhalves : h < nhalves;
-      const uint64_t r = __umul64hi(kWaveRow ? h0 : h, gm.inv);  // destination row
-      c[k] = h - r * gm.hpr;                                     // half block within the row
-      dup[k] = kWaveRow && k > 0 && live && h0 - r * gm.hpr >= 64;
-      s[k] = dup[k] ? s[k > 0 ? k - 1 : 0] : (live ? gm.row_index[r] : -1);
+      if (kRowScalar) {
+        const bool live = h0 < nhalves;
+        ra[k] = __umul64hi(h0, gm.inv);
+        const uint64_t next = (ra[k] + 1) * gm.hpr;  // where the following row starts
+        two[k] = live && next < h0 + 64 && next < nhalves;
+        // reuse: the previous segment looked up this segment's first row as
+        // its own first row, or as its second row
+        const int p = k > 0 ? k - 1 : 0;
+        const bool same_a = k > 0 && live && ra[p] == ra[k];
+        const bool prev_b = k > 0 && live && two[p] && ra[p] + 1 == ra[k];
+        sa[k] = !live ? -1 : (same_a ? sa[p] : (prev_b ? sb[p] : gm.row_index[ra[k]]));
+        fresh_a[k] = live && !same_a && !prev_b;
+        sb[k] = two[k] ? gm.row_index[ra[k] + 1] : sa[k];
+        fresh_b[k] = two[k];
+        second[k] = h >= next;
+        s[k] = h >= nhalves ? -1 : (second[k] ? sb[k] : sa[k]);
+        c[k] = h - (second[k] ? next : ra[k] * gm.hpr);
+      } else {
+        const uint64_t r = __umul64hi(h, gm.inv);  // destination row
+        c[k] = h - r * gm.hpr;
+        s[k] = h < nhalves ? gm.row_index[r] : -1;
+        second[k] = false;
+      }
     }
     uint32_t sbyte[K], side[K];
     float ts[K];
@@ -883,16 +906,34 @@ __global__ __launch_bounds__(kThreads) void fakequant_gathered_kernel(const uint
       }
     }
     if (kGrouped) {
-      GroupWindow gw[K];
+      auto valid = [&](int64_t r) { return r >= 0 && (uint64_t)r < gm.src_rows; };
+      if (kRowScalar) {
+        // scalar lookups for the segments' first and second rows, windows
+        // loaded for all of them before any is compared
+        GroupWindow wa[K], wb[K];
+        float ta[K], tb[K];
 #pragma unroll
-      for (int k = 0; k < K; ++k)
-        if (!dup[k]) gw[k] = group_window_load(groups, ts_ptr, ok[k] ? (uint64_t)s[k] : 0);
+        for (int k = 0; k < K; ++k) {
+          if (fresh_a[k]) wa[k] = group_window_load(groups, ts_ptr, valid(sa[k]) ? (uint64_t)sa[k] : 0);
+          if (fresh_b[k]) wb[k] = group_window_load(groups, ts_ptr, valid(sb[k]) ? (uint64_t)sb[k] : 0);
+        }
 #pragma unroll
-      for (int k = 0; k < K; ++k) {
-        if (dup[k])
-          ts[k] = ts[k > 0 ? k - 1 : 0];
-        else if (ok[k])
-          ts[k] = group_window_pick(groups, ts_ptr, gw[k], (uint64_t)s[k]);
+        for (int k = 0; k < K; ++k) {
+          // a reused lookup copies the scale of the same source row
+          const int p = k > 0 ? k - 1 : 0;
+          ta[k] = fresh_a[k] ? (valid(sa[k]) ? group_window_pick(groups, ts_ptr, wa[k], (uint64_t)sa[k]) : 0.f)
+                             : (sa[k] == sa[p] ? ta[p] : tb[p]);
+          tb[k] = fresh_b[k] ? (valid(sb[k]) ? group_window_pick(groups, ts_ptr, wb[k], (uint64_t)sb[k]) : 0.f)
+                             : ta[k];
+          if (ok[k]) ts[k] = second[k] ? tb[k] : ta[k];
+        }
+      } else {
+        GroupWindow gw[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) gw[k] = group_window_load(groups, ts_ptr, ok[k] ? (uint64_t)s[k] : 0);
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+          if (ok[k]) ts[k] = group_window_pick(groups, ts_ptr, gw[k], (uint64_t)s[k]);
       }
     }
 #pragma unroll
@@ -1274,7 +1315,12 @@ hipError_t launch_gathered_fakequant(int mode, const uint16_t* x, uint64_t rows,
   uint4* yv = reinterpret_cast<uint4*>(y);
   uint32_t* qv = reinterpret_cast<uint32_t*>(qcodes);
   const dim3 grid(grid_for((nhalves + kGatherSegs - 1) / kGatherSegs));
-  const bool wave_row = hpr % 64 == 0;
+  // scalar row lookups when a 64-half segment spans at most two rows; with
+  // per-expert scales only when it spans one (hpr % 64 == 0): each scalar
+  // group lookup is ~40 scalar instructions, and one scalar unit serves a
+  // compute unit's waves, so two rows per segment made the 131072x768
+  // per-expert forward slower (87 -> 95 us) than per-lane lookups
+  const bool wave_row = g ? hpr % 64 == 0 : hpr >= 64;
   if (mode == 1 && g)
     launch_gathered_mode<1, true>(grid, wave_row, xv, nhalves, gm, scales_src, ts, rg, side_src, yv, mask, qv, stream);
   else if (mode == 1)
