@@ -817,19 +817,24 @@ __device__ __forceinline__ uint64_t readfirstlane_u64(uint64_t v) {
 // 131072x2048 routed-expert site in a shuffled row order, after a read-only
 // pass: one segment per wave 198-203 us, two 189-194, four 190-199, eight
 // 210 (registers); the gather and then the forward take 204-222 us.
-// kRowScalar (rows of 64 half blocks or more): a segment spans at most two
-// rows, so its row indices, source rows and group lookups are scalar work
-// (two at most per segment) and each lane picks the one of its row; a
-// segment that starts in the row the previous one looked up reuses that
-// lookup (per-expert scales on the 2048-wide site: 215-240 -> 194-203 us;
-// on the 131072x768 site without groups 89 -> 80 us, where the gather and
-// then the forward take 84 us).  Otherwise each lane finds its own row.
+// kRows = 1 (half blocks per row a multiple of 64): every segment lies
+// inside one row, so its row index, source row and group lookup are scalar
+// work, and a segment in the same row as the previous one reuses them
+// (per-expert scales on the 2048-wide site: 215-240 -> 194-203 us).
+// kRows = 2 (rows of 64 half blocks or more, one tensor scale): a segment
+// spans at most two rows; both are looked up as scalar work and each lane
+// picks its own (131072x768 site: 89 -> 80 us, where the gather and then
+// the forward take 84 us).  Per-expert scales stay per lane there: two
+// scalar group windows per segment overflow the scalar registers (49-64
+// spilled), and each scalar lookup is ~40 scalar instructions on a unit
+// that serves all of a compute unit's waves (87 -> 95 us).  kRows = 0:
+// each lane finds its own row.
 #ifndef TRACE_GATHER_SEGS
 #define TRACE_GATHER_SEGS 2
 #endif
 constexpr int kGatherSegs = TRACE_GATHER_SEGS;
 
-template <int kMode, bool kGrouped, bool kRowScalar>
+template <int kMode, bool kGrouped, int kRows>
 __global__ __launch_bounds__(kThreads) void fakequant_gathered_kernel(const uint4* __restrict__ x, uint64_t nhalves,
                                                                       GatherMap gm,
                                                                       const uint8_t* __restrict__ scales_src,
@@ -840,6 +845,7 @@ __global__ __launch_bounds__(kThreads) void fakequant_gathered_kernel(const uint
                                                                       uint4* __restrict__ y,
                                                                       uint8_t* __restrict__ mask,
                                                                       uint32_t* __restrict__ qcodes) {
+  static_assert(!(kGrouped && kRows == 2), "per-expert scales take scalar lookups only for one row per segment");
   constexpr int K = kGatherSegs;
   const float ts0 = kGrouped ? 0.f : *ts_ptr;
   const uint32_t lane = threadIdx.x & 63;
@@ -854,39 +860,46 @@ __global__ __launch_bounds__(kThreads) void fakequant_gathered_kernel(const uint
       const uint64_t h = base + 64 * k + lane;
       v[k] = h < nhalves ? x[h] : make_uint4(0u, 0u, 0u, 0u);
     }
-    int64_t s[K];     // each lane's source row (-1: none)
-    uint64_t c[K];    // each lane's half block within its row
-    bool second[K];   // kRowScalar: the lane lies in the segment's second row
-    int64_t sa[K], sb[K];  // kRowScalar: source rows of the segment's first and second row
-    uint64_t ra[K];        // kRowScalar: the segment's first row
-    bool two[K];           // kRowScalar: the segment reaches into row ra + 1
-    bool fresh_a[K], fresh_b[K];  // kRowScalar: that lookup is not a copy of an earlier one
+    int64_t s[K];  // each lane's source row (-1: none)
+    uint64_t c[K];  // each lane's half block within its row
+    bool dup[K];    // kRows 1: the segment lies in the same row as the previous one
+    // kRows 2: the segment's rows ra and ra + 1 (two: it reaches into the
+    // second) and their source rows
+    uint64_t ra[K];
+    bool two[K];
+    int64_t sa[K], sb[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       const uint64_t h0 = base + 64 * k;  // the segment's first half block (wave-uniform)
       const uint64_t h = h0 + lane;
-      if (kRowScalar) {
+      const int p = k > 0 ? k - 1 : 0;
+      dup[k] = false;
+      if (kRows == 0) {
+        const uint64_t r = __umul64hi(h, gm.inv);  // destination row
+        c[k] = h - r * gm.hpr;
+        s[k] = h < nhalves ? gm.row_index[r] : -1;
+      } else if (kRows == 1) {
+        // rows start at segment boundaries and nhalves is a multiple of 64:
+        // a live segment has every lane live
+        const bool live = h0 < nhalves;
+        const uint64_t r = __umul64hi(h0, gm.inv);
+        c[k] = h - r * gm.hpr;
+        dup[k] = k > 0 && live && h0 - r * gm.hpr >= 64;
+        s[k] = dup[k] ? s[p] : (live ? gm.row_index[r] : -1);
+      } else {
         const bool live = h0 < nhalves;
         ra[k] = __umul64hi(h0, gm.inv);
         const uint64_t next = (ra[k] + 1) * gm.hpr;  // where the following row starts
         two[k] = live && next < h0 + 64 && next < nhalves;
         // reuse: the previous segment looked up this segment's first row as
         // its own first row, or as its second row
-        const int p = k > 0 ? k - 1 : 0;
         const bool same_a = k > 0 && live && ra[p] == ra[k];
         const bool prev_b = k > 0 && live && two[p] && ra[p] + 1 == ra[k];
         sa[k] = !live ? -1 : (same_a ? sa[p] : (prev_b ? sb[p] : gm.row_index[ra[k]]));
-        fresh_a[k] = live && !same_a && !prev_b;
         sb[k] = two[k] ? gm.row_index[ra[k] + 1] : sa[k];
-        fresh_b[k] = two[k];
-        second[k] = h >= next;
-        s[k] = h >= nhalves ? -1 : (second[k] ? sb[k] : sa[k]);
-        c[k] = h - (second[k] ? next : ra[k] * gm.hpr);
-      } else {
-        const uint64_t r = __umul64hi(h, gm.inv);  // destination row
-        c[k] = h - r * gm.hpr;
-        s[k] = h < nhalves ? gm.row_index[r] : -1;
-        second[k] = false;
+        const bool second = h >= next;
+        s[k] = h >= nhalves ? -1 : (second ? sb[k] : sa[k]);
+        c[k] = h - (second ? next : ra[k] * gm.hpr);
       }
     }
     uint32_t sbyte[K], side[K];
@@ -905,36 +918,27 @@ __global__ __launch_bounds__(kThreads) void fakequant_gathered_kernel(const uint
         if (kMode == 2) side[k] = codes_src[sh];
       }
     }
-    if (kGrouped) {
-      auto valid = [&](int64_t r) { return r >= 0 && (uint64_t)r < gm.src_rows; };
-      if (kRowScalar) {
-        // scalar lookups for the segments' first and second rows, windows
-        // loaded for all of them before any is compared
-        GroupWindow wa[K], wb[K];
-        float ta[K], tb[K];
+    if (kGrouped && kRows == 1) {
+      // one scalar window at a time (two live at once spilled scalar
+      // registers); where rows are 128 half blocks or longer the second
+      // segment of a wave always reuses the first one's lookup
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-          if (fresh_a[k]) wa[k] = group_window_load(groups, ts_ptr, valid(sa[k]) ? (uint64_t)sa[k] : 0);
-          if (fresh_b[k]) wb[k] = group_window_load(groups, ts_ptr, valid(sb[k]) ? (uint64_t)sb[k] : 0);
+      for (int k = 0; k < K; ++k) {
+        if (dup[k]) {
+          ts[k] = ts[k > 0 ? k - 1 : 0];
+        } else if (ok[k]) {
+          const GroupWindow gw = group_window_load(groups, ts_ptr, (uint64_t)s[k]);
+          ts[k] = group_window_pick(groups, ts_ptr, gw, (uint64_t)s[k]);
         }
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-          // a reused lookup copies the scale of the same source row
-          const int p = k > 0 ? k - 1 : 0;
-          ta[k] = fresh_a[k] ? (valid(sa[k]) ? group_window_pick(groups, ts_ptr, wa[k], (uint64_t)sa[k]) : 0.f)
-                             : (sa[k] == sa[p] ? ta[p] : tb[p]);
-          tb[k] = fresh_b[k] ? (valid(sb[k]) ? group_window_pick(groups, ts_ptr, wb[k], (uint64_t)sb[k]) : 0.f)
-                             : ta[k];
-          if (ok[k]) ts[k] = second[k] ? tb[k] : ta[k];
-        }
-      } else {
-        GroupWindow gw[K];
-#pragma unroll
-        for (int k = 0; k < K; ++k) gw[k] = group_window_load(groups, ts_ptr, ok[k] ? (uint64_t)s[k] : 0);
-#pragma unroll
-        for (int k = 0; k < K; ++k)
-          if (ok[k]) ts[k] = group_window_pick(groups, ts_ptr, gw[k], (uint64_t)s[k]);
       }
+    } else if (kGrouped) {
+      // per lane: every window is loaded before any is compared
+      GroupWindow gw[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) gw[k] = group_window_load(groups, ts_ptr, ok[k] ? (uint64_t)s[k] : 0);
+#pragma unroll
+      for (int k = 0; k < K; ++k)
+        if (ok[k]) ts[k] = group_window_pick(groups, ts_ptr, gw[k], (uint64_t)s[k]);
     }
 #pragma unroll
     for (int k = 0; k < K; ++k) {
@@ -1287,19 +1291,33 @@ hipError_t launch_fakequant(int mode, const uint16_t* x, uint64_t nblocks, const
   return hipGetLastError();
 }
 
-template <int kMode, bool kGrouped>
-static void launch_gathered_mode(dim3 grid, bool wave_row, const uint4* x, uint64_t nhalves, const GatherMap& gm,
+template <int kMode, bool kGrouped, int kRows>
+static void launch_gathered_rows(dim3 grid, const uint4* x, uint64_t nhalves, const GatherMap& gm,
                                  const uint8_t* scales_src, const float* ts, const RowGroups& rg,
                                  const uint8_t* side_src, uint4* y, uint8_t* mask, uint32_t* qcodes,
                                  hipStream_t stream) {
   const uint8_t* bits = kMode == 1 ? side_src : nullptr;
   const uint32_t* codes = kMode == 2 ? reinterpret_cast<const uint32_t*>(side_src) : nullptr;
-  if (wave_row)
-    hipLaunchKernelGGL((fakequant_gathered_kernel<kMode, kGrouped, true>), grid, dim3(kThreads), 0, stream, x,
-                       nhalves, gm, scales_src, ts, rg, bits, codes, y, mask, qcodes);
+  hipLaunchKernelGGL((fakequant_gathered_kernel<kMode, kGrouped, kRows>), grid, dim3(kThreads), 0, stream, x,
+                     nhalves, gm, scales_src, ts, rg, bits, codes, y, mask, qcodes);
+}
+
+// The row mode: 1 when every 64-half segment lies inside one row, 2 when it
+// spans at most two (one tensor scale only), else 0 (per lane).
+template <int kMode, bool kGrouped>
+static void launch_gathered_mode(dim3 grid, uint64_t hpr, const uint4* x, uint64_t nhalves, const GatherMap& gm,
+                                 const uint8_t* scales_src, const float* ts, const RowGroups& rg,
+                                 const uint8_t* side_src, uint4* y, uint8_t* mask, uint32_t* qcodes,
+                                 hipStream_t stream) {
+  if (hpr % 64 == 0)
+    launch_gathered_rows<kMode, kGrouped, 1>(grid, x, nhalves, gm, scales_src, ts, rg, side_src, y, mask, qcodes,
+                                             stream);
+  else if (!kGrouped && hpr >= 64)
+    launch_gathered_rows<kMode, false, 2>(grid, x, nhalves, gm, scales_src, ts, rg, side_src, y, mask, qcodes,
+                                          stream);
   else
-    hipLaunchKernelGGL((fakequant_gathered_kernel<kMode, kGrouped, false>), grid, dim3(kThreads), 0, stream, x,
-                       nhalves, gm, scales_src, ts, rg, bits, codes, y, mask, qcodes);
+    launch_gathered_rows<kMode, kGrouped, 0>(grid, x, nhalves, gm, scales_src, ts, rg, side_src, y, mask, qcodes,
+                                             stream);
 }
 
 hipError_t launch_gathered_fakequant(int mode, const uint16_t* x, uint64_t rows, uint64_t cols,
@@ -1315,20 +1333,14 @@ hipError_t launch_gathered_fakequant(int mode, const uint16_t* x, uint64_t rows,
   uint4* yv = reinterpret_cast<uint4*>(y);
   uint32_t* qv = reinterpret_cast<uint32_t*>(qcodes);
   const dim3 grid(grid_for((nhalves + kGatherSegs - 1) / kGatherSegs));
-  // scalar row lookups when a 64-half segment spans at most two rows; with
-  // per-expert scales only when it spans one (hpr % 64 == 0): each scalar
-  // group lookup is ~40 scalar instructions, and one scalar unit serves a
-  // compute unit's waves, so two rows per segment made the 131072x768
-  // per-expert forward slower (87 -> 95 us) than per-lane lookups
-  const bool wave_row = g ? hpr % 64 == 0 : hpr >= 64;
   if (mode == 1 && g)
-    launch_gathered_mode<1, true>(grid, wave_row, xv, nhalves, gm, scales_src, ts, rg, side_src, yv, mask, qv, stream);
+    launch_gathered_mode<1, true>(grid, hpr, xv, nhalves, gm, scales_src, ts, rg, side_src, yv, mask, qv, stream);
   else if (mode == 1)
-    launch_gathered_mode<1, false>(grid, wave_row, xv, nhalves, gm, scales_src, ts, rg, side_src, yv, mask, qv, stream);
+    launch_gathered_mode<1, false>(grid, hpr, xv, nhalves, gm, scales_src, ts, rg, side_src, yv, mask, qv, stream);
   else if (g)
-    launch_gathered_mode<2, true>(grid, wave_row, xv, nhalves, gm, scales_src, ts, rg, side_src, yv, mask, qv, stream);
+    launch_gathered_mode<2, true>(grid, hpr, xv, nhalves, gm, scales_src, ts, rg, side_src, yv, mask, qv, stream);
   else
-    launch_gathered_mode<2, false>(grid, wave_row, xv, nhalves, gm, scales_src, ts, rg, side_src, yv, mask, qv, stream);
+    launch_gathered_mode<2, false>(grid, hpr, xv, nhalves, gm, scales_src, ts, rg, side_src, yv, mask, qv, stream);
   return hipGetLastError();
 }
 
