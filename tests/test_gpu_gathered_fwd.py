@@ -194,3 +194,37 @@ def test_moe_expert_site_read_back_in_trainer_order(device):
     n = compare_gathered_every_element("expert site, trainer order", xr_h, rows, to_np_u16(x_train),
                                        perm.cpu().numpy(), cols, off, ts, host)
     _say(f"  expert site read back: {n} elements of both forwards equal to the oracle")
+
+
+# Row widths around the kernel's row modes (half blocks per row = cols / 8):
+# 512 (64, one row per segment, every segment a new row), 528 (66: segments
+# span two rows), 768 (96), 1008 (126), 1024 (128), 1536 (192), 2560 (320),
+# 496 (62: per lane), with row counts that leave a partial last segment.
+@pytest.mark.parametrize("cols", [496, 512, 528, 768, 1008, 1024, 1536, 2560])
+@pytest.mark.parametrize("grouped", [False, True])
+def test_gathered_fwd_row_mode_edges(device, cols, grouped):
+    _say("case gathered fwd row-mode edges", cols, grouped)
+    import fp4_rollout_guided_amd as tr
+    rng = np.random.default_rng(cols * 2 + grouped)
+    for src_rows, dst_rows in ((37, 53), (130, 7), (3, 129)):
+        idx = _index(rng, src_rows, dst_rows)
+        xr, xt = _inputs(rng, src_rows, dst_rows, cols, idx)
+        off = np.r_[0, np.sort(rng.integers(0, src_rows + 1, 5)), src_rows].astype(np.int64) if grouped else None
+        if off is None:
+            ts = np.float32(oracle.tensor_scale(xr))
+            rec = oracle.capture(xr, ts, with_codes=True)
+        else:
+            ts = oracle.grouped_tensor_scale(xr, src_rows, cols, off)
+            rec = oracle.grouped_capture(xr, src_rows, cols, off, ts, with_codes=True)
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
+        x_train = from_np_u16(xt, device, (dst_rows, cols))
+        args = (dev(idx), dev(rec["scales"]), dev(np.atleast_1d(np.asarray(ts, dtype=np.float32))))
+        kw = {"offsets": dev(off)} if grouped else {}
+        y, m, q = tr.gathered_guided_fakequant_fwd(x_train, *args, dev(rec["bits"]), want_codes=True, **kw)
+        yf, mf, qf = tr.gathered_full_info_fakequant_fwd(x_train, *args, dev(rec["codes"]), want_codes=True, **kw)
+        torch.cuda.synchronize()
+        g = oracle.gathered_fwd("guided", xt, cols, rec, src_rows, idx, ts, off)
+        f = oracle.gathered_fwd("full", xt, cols, rec, src_rows, idx, ts, off)
+        ctx = f"cols {cols} grouped {grouped} {src_rows}->{dst_rows}"
+        assert_same({"y": to_np_u16(y), "mask": to_np_u8(m), "codes": to_np_u8(q)}, g, ctx=ctx + " guided")
+        assert_same({"y": to_np_u16(yf), "mask": to_np_u8(mf), "codes": to_np_u8(qf)}, f, ctx=ctx + " full")
