@@ -820,7 +820,8 @@ __device__ __forceinline__ uint64_t readfirstlane_u64(uint64_t v) {
 // kRows = 1 (half blocks per row a multiple of 64): every segment lies
 // inside one row, so its row index, source row and group lookup are scalar
 // work, and a segment in the same row as the previous one reuses them
-// (per-expert scales on the 2048-wide site: 215-240 -> 194-203 us).
+// (per-expert scales on the 2048-wide site: 215-240 -> 187-188 us, with one
+// scalar group window live at a time; two live at once spilled registers).
 // kRows = 2 (rows of 64 half blocks or more, one tensor scale): a segment
 // spans at most two rows; both are looked up as scalar work and each lane
 // picks its own (131072x768 site: 89 -> 80 us, where the gather and then
