@@ -391,7 +391,8 @@ def gathered_fwd(mode, x_bits, cols: int, record, src_rows: int, row_index, ts, 
     the tensor scale of that source row -- ``ts[0]`` for one tensor scale, or,
     with ``offsets`` describing groups of source rows (per-expert scales),
     ``ts[g]`` of the group holding it.  mode "guided" reads the record's
-    bits, "full" its codes.  Outputs as ``guided_fwd``."""
+    bits, "full" its codes, "rne" only its scale bytes (the vanilla-QAT
+    baseline on the same records).  Outputs as ``guided_fwd``."""
     rec = gather_records(record, row_index, src_rows, cols)
     idx = np.asarray(row_index, dtype=np.int64).reshape(-1)
     tsv = np.asarray(ts, dtype=np.float32).reshape(-1)
@@ -404,7 +405,9 @@ def gathered_fwd(mode, x_bits, cols: int, record, src_rows: int, row_index, ts, 
         return guided_fwd(x_bits, rec["scales"], block_ts, rec["bits"])
     if mode == "full":
         return full_info_fwd(x_bits, rec["scales"], block_ts, rec["codes"])
-    raise ValueError("mode must be 'guided' or 'full'")
+    if mode == "rne":
+        return rne_fwd(x_bits, rec["scales"], block_ts)
+    raise ValueError("mode must be 'guided', 'full' or 'rne'")
 
 
 # --------------------------------------------------------------------------

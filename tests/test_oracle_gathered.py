@@ -3,7 +3,7 @@ read back in its own row order (the trainer reads the rollout's records
 back), against independent paths through already pinned functions:
 
 * a per-row loop: each destination row through ``guided_fwd`` /
-  ``full_info_fwd`` with that row's record bytes taken by hand from the
+  ``full_info_fwd`` / ``rne_fwd`` with that row's record bytes taken by hand from the
   source row and its group's scalar tensor scale;
 * the identity order: equal to the ungrouped and per-expert forwards;
 * rows whose index is out of range: the zero-scale rule written out
@@ -39,9 +39,9 @@ def _record(xr, rows, cols, off):
 
 
 @pytest.mark.parametrize("grouped", [False, True])
-@pytest.mark.parametrize("mode", ["guided", "full"])
+@pytest.mark.parametrize("mode", ["guided", "full", "rne"])
 def test_gathered_against_a_per_row_loop(grouped, mode):
-    rng = np.random.default_rng(11 + grouped + 2 * (mode == "full"))
+    rng = np.random.default_rng(11 + grouped + 2 * ["guided", "full", "rne"].index(mode))
     src_rows, cols, dst_rows = 40, 96, 57
     off = np.array([0, 7, 7, 20, 33, 40], dtype=np.int64) if grouped else None
     xr = _rollout(rng, src_rows, cols, off)
@@ -63,7 +63,8 @@ def test_gathered_against_a_per_row_loop(grouped, mode):
         else:
             t = ts[0]
             scales, bits, codes = (np.zeros(k, np.uint8) for k in (sb, bb, cb))
-        want = oracle.guided_fwd(x, scales, t, bits) if mode == "guided" else oracle.full_info_fwd(x, scales, t, codes)
+        want = (oracle.guided_fwd(x, scales, t, bits) if mode == "guided" else
+                oracle.full_info_fwd(x, scales, t, codes) if mode == "full" else oracle.rne_fwd(x, scales, t))
         assert np.array_equal(got["y"][r * cols:(r + 1) * cols], want["y"]), r
         assert np.array_equal(got["mask"][r * bb:(r + 1) * bb], want["mask"]), r
         assert np.array_equal(got["codes"][r * cb:(r + 1) * cb], want["codes"]), r
@@ -82,12 +83,16 @@ def test_gathered_identity_order_equals_the_forwards():
                               oracle.guided_fwd(xt, cap["scales"], ts[0], cap["bits"])[k])
         assert np.array_equal(oracle.gathered_fwd("full", xt, cols, cap, rows, idx, ts)[k],
                               oracle.full_info_fwd(xt, cap["scales"], ts[0], cap["codes"])[k])
+        assert np.array_equal(oracle.gathered_fwd("rne", xt, cols, cap, rows, idx, ts)[k],
+                              oracle.rne_fwd(xt, cap["scales"], ts[0])[k])
     capg, tsg = _record(xr, rows, cols, off)
     for k in ("y", "mask", "codes"):
         assert np.array_equal(oracle.gathered_fwd("guided", xt, cols, capg, rows, idx, tsg, off)[k],
                               oracle.grouped_guided_fwd(xt, rows, cols, off, capg["scales"], tsg, capg["bits"])[k])
         assert np.array_equal(oracle.gathered_fwd("full", xt, cols, capg, rows, idx, tsg, off)[k],
                               oracle.grouped_full_info_fwd(xt, rows, cols, off, capg["scales"], tsg, capg["codes"])[k])
+        assert np.array_equal(oracle.gathered_fwd("rne", xt, cols, capg, rows, idx, tsg, off)[k],
+                              oracle.grouped_rne_fwd(xt, rows, cols, off, capg["scales"], tsg)[k])
 
 
 def test_gathered_out_of_range_rows_are_zero_scale():
@@ -111,6 +116,6 @@ def test_gathered_rejects_a_bad_mode_and_bad_offsets():
     xr = _rollout(rng, 4, 16)
     cap, ts = _record(xr, 4, 16, None)
     with pytest.raises(ValueError):
-        oracle.gathered_fwd("rne", xr, 16, cap, 4, np.arange(4), ts)
+        oracle.gathered_fwd("nearest", xr, 16, cap, 4, np.arange(4), ts)
     with pytest.raises(ValueError):
         oracle.gathered_fwd("guided", xr, 16, cap, 4, np.arange(4), ts, np.array([0, 3, 2, 4]))
