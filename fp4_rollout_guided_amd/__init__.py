@@ -43,6 +43,7 @@ __all__ = [
     "TraceError", "LIB_PATH", "SMALLGRID_LIB_PATH", "lib", "load_library", "abi_version", "tensor_scale",
     "tensor_scale_noalloc", "capture",
     "guided_fakequant_fwd", "rne_fakequant_fwd", "full_info_fakequant_fwd", "ste_bwd", "gather_records",
+    "gathered_guided_fakequant_fwd", "gathered_rne_fakequant_fwd", "gathered_full_info_fakequant_fwd",
     "grouped_tensor_scale", "grouped_capture", "grouped_guided_fakequant_fwd", "grouped_rne_fakequant_fwd",
     "grouped_full_info_fakequant_fwd", "mx_capture", "mx_guided_fakequant_fwd", "mx_rne_fakequant_fwd",
     "mx_full_info_fakequant_fwd", "mx8_capture", "mx8_guided_fakequant_fwd", "mx8_rne_fakequant_fwd",
@@ -91,6 +92,7 @@ def load_library(path):
         "trace_gather_records": ([p, p, p, i64, i64, p, i64, p, p, p, p], st),
         "trace_gathered_guided_fakequant_fwd": ([p, i64, i64, p, i64, p, i64, p, p, p, p, p, p, p], st),
         "trace_gathered_full_info_fakequant_fwd": ([p, i64, i64, p, i64, p, i64, p, p, p, p, p, p, p], st),
+        "trace_gathered_rne_fakequant_fwd": ([p, i64, i64, p, i64, p, i64, p, p, p, p, p, p], st),
         "trace_grouped_tensor_scale_workspace_bytes": ([i64], sz),
         "trace_grouped_tensor_scale": ([p, i64, i64, p, i64, p, sz, p, p], st),
         "trace_grouped_capture": ([p, i64, i64, p, i64, p, p, p, p, p], st),
@@ -397,15 +399,18 @@ def _gathered_fwd(mode, x, row_index, scales, ts, side, offsets, y, mask, want_c
     if offsets is not None:
         groups = _offsets(offsets, x)
     _arg(ts, "ts", x, _F32, max(groups, 1))
-    _arg(side, "bits" if mode == "guided" else "codes", x, _U8, n_src // 8 if mode == "guided" else n_src // 2)
+    if mode != "rne":
+        _arg(side, "bits" if mode == "guided" else "codes", x, _U8, n_src // 8 if mode == "guided" else n_src // 2)
     y = _bf16_out(y, x, n, "y")
     mask = _u8(n // 8, x, mask, "mask")
     if want_codes or qcodes is not None:
         qcodes = _u8(n // 2, x, qcodes, "qcodes")
-    fn = lib.trace_gathered_guided_fakequant_fwd if mode == "guided" else lib.trace_gathered_full_info_fakequant_fwd
-    _check(fn(_ptr(x), rows, cols, _ptr(row_index), src_rows, _ptr(offsets), groups, _ptr(scales), _ptr(ts),
-              _ptr(side), _ptr(y), _ptr(mask), _ptr(qcodes), _stream(x)),
-           "trace_gathered_guided_fakequant_fwd" if mode == "guided" else "trace_gathered_full_info_fakequant_fwd")
+    head = (_ptr(x), rows, cols, _ptr(row_index), src_rows, _ptr(offsets), groups, _ptr(scales), _ptr(ts))
+    tail = (_ptr(y), _ptr(mask), _ptr(qcodes), _stream(x))
+    name = {"guided": "trace_gathered_guided_fakequant_fwd", "full": "trace_gathered_full_info_fakequant_fwd",
+            "rne": "trace_gathered_rne_fakequant_fwd"}[mode]
+    fn = getattr(lib, name)
+    _check(fn(*head, *tail) if mode == "rne" else fn(*head, _ptr(side), *tail), name)
     return y, mask, qcodes
 
 
@@ -417,6 +422,13 @@ def gathered_guided_fakequant_fwd(x_train, row_index, scales, ts, bits, offsets=
     scale, or one per group of source rows when ``offsets`` is given.
     Out-of-range indices give zero-scale blocks."""
     return _gathered_fwd("guided", x_train, row_index, scales, ts, bits, offsets, y, mask, want_codes, qcodes)
+
+
+def gathered_rne_fakequant_fwd(x_train, row_index, scales, ts, offsets=None, y=None, mask=None, want_codes=False,
+                               qcodes=None):
+    """``rne_fakequant_fwd`` on source rows row_index[r] of the record's
+    scale bytes, as ``gathered_guided_fakequant_fwd``."""
+    return _gathered_fwd("rne", x_train, row_index, scales, ts, None, offsets, y, mask, want_codes, qcodes)
 
 
 def gathered_full_info_fakequant_fwd(x_train, row_index, scales, ts, codes, offsets=None, y=None, mask=None,

@@ -283,8 +283,9 @@ trace_status trace_grouped_full_info_fakequant_fwd(const uint16_t* x_train, int6
   return fakequant(2, x_train, rows, cols, offsets, groups, true, scales, ts, codes, y, mask, qcodes, stream);
 }
 
-// mode 1: guided (side = bit-plane of the source, src_n/8 bytes); 2: full
-// information (side = codes of the source, src_n/2 bytes, 8-byte aligned).
+// mode 0: RNE (no side plane); 1: guided (side = bit-plane of the source,
+// src_n/8 bytes); 2: full information (side = codes of the source, src_n/2
+// bytes, 8-byte aligned).
 static trace_status gathered_fakequant(int mode, const uint16_t* x, int64_t rows, int64_t cols,
                                        const int64_t* row_index, int64_t src_rows, const int64_t* offsets,
                                        int64_t groups, const uint8_t* scales_src, const float* ts,
@@ -301,12 +302,13 @@ static trace_status gathered_fakequant(int mode, const uint16_t* x, int64_t rows
   if (n == 0) return TRACE_OK;
   uint64_t bound = 0;  // the kernel finds a half block's row with one multiply-high
   if (__builtin_mul_overflow(n / 8, (uint64_t)cols / 8, &bound)) return TRACE_E_SHAPE;
-  if (!x || !row_index || !ts || !y || !mask || (n_src > 0 && (!scales_src || !side_src))) return TRACE_E_NULL;
+  if (!x || !row_index || !ts || !y || !mask || (n_src > 0 && (!scales_src || (mode != 0 && !side_src))))
+    return TRACE_E_NULL;
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ts, 4) || !aligned(mask, 2) || !aligned(row_index, 8) ||
       (mode == 2 && !aligned(side_src, 8)) || (qcodes && !aligned(qcodes, 8)))
     return TRACE_E_ALIGN;
   const uint64_t ts_len = 4 * (grouped ? spec.count : 1);
-  const uint64_t side_len = mode == 1 ? n_src / 8 : n_src / 2;
+  const uint64_t side_len = mode == 1 ? n_src / 8 : (mode == 2 ? n_src / 2 : 0);
   const Range outs[3] = {rng(y, 2 * n), rng(mask, n / 8), rng(qcodes, qcodes ? n / 2 : 0)};
   const Range ins[6] = {rng(x, 2 * n),           rng(scales_src, n_src / 16),
                         rng(ts, ts_len),         rng(side_src, side_len),
@@ -323,6 +325,14 @@ trace_status trace_gathered_guided_fakequant_fwd(const uint16_t* x_train, int64_
                                                  const uint8_t* bits_src, uint16_t* y, uint8_t* mask, uint8_t* qcodes,
                                                  void* stream) {
   return gathered_fakequant(1, x_train, rows, cols, row_index, src_rows, offsets, groups, scales_src, ts, bits_src, y,
+                            mask, qcodes, stream);
+}
+
+trace_status trace_gathered_rne_fakequant_fwd(const uint16_t* x_train, int64_t rows, int64_t cols,
+                                              const int64_t* row_index, int64_t src_rows, const int64_t* offsets,
+                                              int64_t groups, const uint8_t* scales_src, const float* ts, uint16_t* y,
+                                              uint8_t* mask, uint8_t* qcodes, void* stream) {
+  return gathered_fakequant(0, x_train, rows, cols, row_index, src_rows, offsets, groups, scales_src, ts, nullptr, y,
                             mask, qcodes, stream);
 }
 

@@ -1334,7 +1334,11 @@ hipError_t launch_gathered_fakequant(int mode, const uint16_t* x, uint64_t rows,
   uint4* yv = reinterpret_cast<uint4*>(y);
   uint32_t* qv = reinterpret_cast<uint32_t*>(qcodes);
   const dim3 grid(grid_for((nhalves + kGatherSegs - 1) / kGatherSegs));
-  if (mode == 1 && g)
+  if (mode == 0 && g)
+    launch_gathered_mode<0, true>(grid, hpr, xv, nhalves, gm, scales_src, ts, rg, side_src, yv, mask, qv, stream);
+  else if (mode == 0)
+    launch_gathered_mode<0, false>(grid, hpr, xv, nhalves, gm, scales_src, ts, rg, side_src, yv, mask, qv, stream);
+  else if (mode == 1 && g)
     launch_gathered_mode<1, true>(grid, hpr, xv, nhalves, gm, scales_src, ts, rg, side_src, yv, mask, qv, stream);
   else if (mode == 1)
     launch_gathered_mode<1, false>(grid, hpr, xv, nhalves, gm, scales_src, ts, rg, side_src, yv, mask, qv, stream);

@@ -83,7 +83,8 @@ hipError_t launch_fakequant(int mode, const uint16_t* x, uint64_t nblocks, const
                             uint8_t* qcodes, hipStream_t stream);
 // Forward on records read back in the trainer's row order: destination row r
 // of the rows x cols x_train reads source row row_index[r] of the record
-// (scales_src, and side_src = bits for mode 1 or codes for mode 2) of a
+// (scales_src, and side_src = bits for mode 1 or codes for mode 2; mode 0,
+// RNE, reads no side plane) of a
 // src_rows x cols site; g == nullptr: one tensor scale ts[0], else g
 // describes groups of the source rows (ts[group of the source row]).
 // Requires rows * (cols / 8) * (cols / 8) < 2^64 (checked by the caller): the

@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define TRACE_ABI_VERSION 9
+#define TRACE_ABI_VERSION 10
 
 #if defined(__GNUC__)
 #define TRACE_API __attribute__((visibility("default")))
@@ -289,7 +289,7 @@ TRACE_API trace_status trace_gather_records(const uint8_t* bits_src, const uint8
  * without a gathered copy of the record (rcap.io post, limitations list: a
  * cache tier holds the rollout's records and the training engine reads them
  * back).  The result equals trace_gather_records into the trainer's order
- * followed by the guided (or full-information) forward, with each
+ * followed by the guided (full-information, RNE) forward, with each
  * destination row's tensor scale taken from its source row:
  *   destination row r of x_train (rows x cols) uses source row
  *   s = row_index[r] of the record (scales_src, bits_src or codes_src) of a
@@ -302,7 +302,8 @@ TRACE_API trace_status trace_gather_records(const uint8_t* bits_src, const uint8
  *               per-expert groups of the source rows, with the rules of the
  *               grouped entry points below (offsets[groups] = src_rows);
  *   scales_src u8[src_rows*cols/16]; bits_src u8[src_rows*cols/8];
- *   codes_src u8[src_rows*cols/2], 8-byte aligned; ts fp32[1 or groups];
+ *   codes_src u8[src_rows*cols/2], 8-byte aligned (the RNE forward reads
+ *   neither: the vanilla-QAT baseline on the same records); ts fp32[1 or groups];
  *   the record pointers may be NULL when src_rows == 0;
  *   y, mask, qcodes : as trace_guided_fakequant_fwd, in destination order;
  *   y may be exactly x_train.
@@ -315,6 +316,11 @@ TRACE_API trace_status trace_gathered_guided_fakequant_fwd(const uint16_t* x_tra
                                                            const uint8_t* scales_src, const float* ts,
                                                            const uint8_t* bits_src, uint16_t* y, uint8_t* mask,
                                                            uint8_t* qcodes, void* stream);
+TRACE_API trace_status trace_gathered_rne_fakequant_fwd(const uint16_t* x_train, int64_t rows, int64_t cols,
+                                                        const int64_t* row_index, int64_t src_rows,
+                                                        const int64_t* offsets, int64_t groups,
+                                                        const uint8_t* scales_src, const float* ts, uint16_t* y,
+                                                        uint8_t* mask, uint8_t* qcodes, void* stream);
 TRACE_API trace_status trace_gathered_full_info_fakequant_fwd(const uint16_t* x_train, int64_t rows, int64_t cols,
                                                               const int64_t* row_index, int64_t src_rows,
                                                               const int64_t* offsets, int64_t groups,

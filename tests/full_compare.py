@@ -208,8 +208,10 @@ def _oracle_gathered(xt, idx, xr_rows_of, cols, src_rows, off, ts):
     local[valid] = np.searchsorted(u, idx[valid])
     gd = oracle.gathered_fwd("guided", xt, cols, cap, u.size, local, ts, sub)
     fi = oracle.gathered_fwd("full", xt, cols, cap, u.size, local, ts, sub)
+    rn = oracle.gathered_fwd("rne", xt, cols, cap, u.size, local, ts, sub)
     return {"y_g": gd["y"], "mask_g": gd["mask"], "q_g": gd["codes"],
-            "y_f": fi["y"], "mask_f": fi["mask"], "q_f": fi["codes"]}
+            "y_f": fi["y"], "mask_f": fi["mask"], "q_f": fi["codes"],
+            "y_r": rn["y"], "mask_r": rn["mask"], "q_r": rn["codes"]}
 
 
 # --------------------------------------------------------------------------
@@ -333,7 +335,8 @@ def compare_gathered_every_element(name, xr, src_rows, xt, idx, cols, off, ts, g
     (src_rows x cols), xt the destination rows, idx their source rows
     (int64, out-of-range allowed), off the source's row groups (None: one
     tensor scale ts) and the oracle's tensor scale(s) ts; got the GPU's
-    y_g, mask_g, q_g, y_f, mask_f, q_f.  Chunks of whole destination rows."""
+    y_g, mask_g, q_g, y_f, mask_f, q_f (and y_r, mask_r, q_r of the RNE
+    forward).  Chunks of whole destination rows."""
     with Shared({"xr": xr, "xt": xt, "idx": np.asarray(idx, dtype=np.int64)}) as sh:
         for k, v in got.items():
             sh.put(k, v)

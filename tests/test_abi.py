@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert tr.abi_version() == 9
+    assert tr.abi_version() == 10
     for code in range(6):
         assert L.trace_status_string(code).decode().startswith("TRACE")
     assert b"unknown" in L.trace_status_string(99)
@@ -221,6 +221,20 @@ def test_gathered_fwd_validation():
     assert call(mk=sc) == E_ALIAS                      # mask over the source scale bytes
     assert call(qc=off, off=off, groups=2) == E_ALIAS  # qcodes over the offsets
     assert call(rows=0) == OK
+    # the RNE forward reads no side plane (its signature has none)
+    rne = L.trace_gathered_rne_fakequant_fwd
+    q = lambda v: P(v) if v is not None else None
+
+    def call_rne(x=x, rows=8, cols=64, idx=idx, src_rows=6, off=None, groups=0, sc=sc, ts=ts, y=y, mk=mk):
+        return rne(q(x), rows, cols, q(idx), src_rows, q(off), groups, q(sc), q(ts), q(y), q(mk), None, None)
+
+    assert call_rne(sc=None) == E_NULL
+    assert call_rne(idx=None) == E_NULL
+    assert call_rne(groups=2) == E_NULL
+    assert call_rne(cols=24) == E_SHAPE
+    assert call_rne(idx=idx + 2) == E_ALIGN
+    assert call_rne(mk=sc) == E_ALIAS
+    assert call_rne(rows=0) == OK
 
 
 def test_build_script_loads_without_the_library():

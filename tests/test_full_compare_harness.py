@@ -109,7 +109,7 @@ def test_gathered_harness_rebuilds_each_chunks_records(grouped):
         ts = np.float32(oracle.tensor_scale(xr))
         rec = oracle.capture(xr, ts, with_codes=True)
     want = {}
-    for mode, tag in (("guided", "g"), ("full", "f")):
+    for mode, tag in (("guided", "g"), ("full", "f"), ("rne", "r")):
         r = oracle.gathered_fwd(mode, xt, cols, rec, src_rows, idx, ts, off)
         want.update({f"y_{tag}": r["y"], f"mask_{tag}": r["mask"], f"q_{tag}": r["codes"]})
     assert fc.compare_gathered_every_element("ok", xr, src_rows, xt, idx, cols, off, ts, want) == idx.size * cols

@@ -1,5 +1,5 @@
 """GPU parity of the training-side forwards on records read back in place
-(trace_gathered_guided_fakequant_fwd / trace_gathered_full_info_fakequant_fwd)
+(trace_gathered_{guided,full_info,rne}_fakequant_fwd)
 against ``oracle.gathered_fwd``: permuted, repeated and out-of-range row
 indices, one tensor scale or per-expert groups of source rows (balanced,
 unbalanced, empty, fewer than three), row widths whose waves each lie inside
@@ -110,13 +110,15 @@ def test_gathered_fwd_bit_exact(device, src_rows, dst_rows, cols, groups):
     got.update(y_g=y, mask_g=m, q_g=q)
     y, m, q = tr.gathered_full_info_fakequant_fwd(x_train, row_index, sc, ts_d, cd, offsets=off_d, want_codes=True)
     got.update(y_f=y, mask_f=m, q_f=q)
+    y, m, q = tr.gathered_rne_fakequant_fwd(x_train, row_index, sc, ts_d, offsets=off_d, want_codes=True)
+    got.update(y_r=y, mask_r=m, q_r=q)
     # without codes, and in place (y is x_train)
     y_nc, m_nc, _ = tr.gathered_guided_fakequant_fwd(x_train, row_index, sc, ts_d, bt, offsets=off_d)
     inplace = x_train.clone()
     y_ip, m_ip, _ = tr.gathered_full_info_fakequant_fwd(inplace, row_index, sc, ts_d, cd, offsets=off_d, y=inplace)
     torch.cuda.synchronize()
     want = {}
-    for mode, tag in (("guided", "g"), ("full", "f")):
+    for mode, tag in (("guided", "g"), ("full", "f"), ("rne", "r")):
         r = oracle.gathered_fwd(mode, xt, cols, rec, src_rows, idx, ts, off)
         want.update({f"y_{tag}": r["y"], f"mask_{tag}": r["mask"], f"q_{tag}": r["codes"]})
     host = {k: (to_np_u16(v) if k.startswith("y") else to_np_u8(v)) for k, v in got.items()}
@@ -173,6 +175,8 @@ def test_moe_expert_site_read_back_in_trainer_order(device):
     got.update(y_g=y, mask_g=m, q_g=q)
     y, m, q = tr.gathered_full_info_fakequant_fwd(x_train, perm, sc, gts, cd, offsets=offsets, want_codes=True)
     got.update(y_f=y, mask_f=m, q_f=q)
+    y, m, q = tr.gathered_rne_fakequant_fwd(x_train, perm, sc, gts, offsets=offsets, want_codes=True)
+    got.update(y_r=y, mask_r=m, q_r=q)
     # one tensor scale: fused == gather + forward (both paths on the GPU)
     ts1 = tr.tensor_scale(x_roll)
     sc1, bt1, cd1 = tr.capture(x_roll, ts1, want_codes=True)
@@ -193,7 +197,7 @@ def test_moe_expert_site_read_back_in_trainer_order(device):
     host = {k: (to_np_u16(v) if k.startswith("y") else to_np_u8(v)) for k, v in got.items()}
     n = compare_gathered_every_element("expert site, trainer order", xr_h, rows, to_np_u16(x_train),
                                        perm.cpu().numpy(), cols, off, ts, host)
-    _say(f"  expert site read back: {n} elements of both forwards equal to the oracle")
+    _say(f"  expert site read back: {n} elements of the three forwards equal to the oracle")
 
 
 # Row widths around the kernel's row modes (half blocks per row = cols / 8):
@@ -222,9 +226,12 @@ def test_gathered_fwd_row_mode_edges(device, cols, grouped):
         kw = {"offsets": dev(off)} if grouped else {}
         y, m, q = tr.gathered_guided_fakequant_fwd(x_train, *args, dev(rec["bits"]), want_codes=True, **kw)
         yf, mf, qf = tr.gathered_full_info_fakequant_fwd(x_train, *args, dev(rec["codes"]), want_codes=True, **kw)
+        yr, mr, qr = tr.gathered_rne_fakequant_fwd(x_train, *args, want_codes=True, **kw)
         torch.cuda.synchronize()
         g = oracle.gathered_fwd("guided", xt, cols, rec, src_rows, idx, ts, off)
         f = oracle.gathered_fwd("full", xt, cols, rec, src_rows, idx, ts, off)
+        r = oracle.gathered_fwd("rne", xt, cols, rec, src_rows, idx, ts, off)
         ctx = f"cols {cols} grouped {grouped} {src_rows}->{dst_rows}"
         assert_same({"y": to_np_u16(y), "mask": to_np_u8(m), "codes": to_np_u8(q)}, g, ctx=ctx + " guided")
         assert_same({"y": to_np_u16(yf), "mask": to_np_u8(mf), "codes": to_np_u8(qf)}, f, ctx=ctx + " full")
+        assert_same({"y": to_np_u16(yr), "mask": to_np_u8(mr), "codes": to_np_u8(qr)}, r, ctx=ctx + " rne")

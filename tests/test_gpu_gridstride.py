@@ -84,7 +84,9 @@ def _everything(tr, xr, xt, g, offsets, perm):
                      ("xgg", lambda: tr.gathered_guided_fakequant_fwd(xg, perm, gsc, gts, gbt, offsets=offsets,
                                                                       want_codes=True)),
                      ("x64", lambda: tr.gathered_guided_fakequant_fwd(x64, perm64, sc, ts, bt, want_codes=True)),
-                     ("x64f", lambda: tr.gathered_full_info_fakequant_fwd(x64, perm64, sc, ts, cd, want_codes=True))):
+                     ("x64f", lambda: tr.gathered_full_info_fakequant_fwd(x64, perm64, sc, ts, cd, want_codes=True)),
+                     ("xr", lambda: tr.gathered_rne_fakequant_fwd(xg, perm, gsc, gts, offsets=offsets, want_codes=True)),
+                     ("x64r", lambda: tr.gathered_rne_fakequant_fwd(x64, perm64, sc, ts, want_codes=True))):
         y, m, q = fn()
         out.update({f"y_{name}": y, f"m_{name}": m, f"q_{name}": q})
     msc, mbt, mcd = tr.mx_capture(xr, want_codes=True)
