@@ -79,4 +79,8 @@ def test_entry_points_refuse_host_and_short_tensors(device):
     with pytest.raises(ValueError, match="at least"):
         tr.gathered_guided_fakequant_fwd(x, idx, sc, ts, bt, mask=torch.empty(n // 8 - 1, dtype=torch.uint8,
                                                                               device=device))
+    with pytest.raises(ValueError, match="must be on"):
+        tr.gathered_rne_fakequant_fwd(x, idx, sc, host_ts)
+    with pytest.raises(ValueError, match="at least"):
+        tr.gathered_rne_fakequant_fwd(x, idx, sc, short(gts), offsets=offsets)
     torch.cuda.synchronize()
