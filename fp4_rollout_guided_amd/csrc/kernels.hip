@@ -1039,11 +1039,19 @@ __global__ __launch_bounds__(kThreads) void gather_plane_kernel(const V* __restr
 // words (row widths and base addresses multiples of 16): workgroups
 // [first[k], first[k+1]) gather plane k, one pass over the destination rows
 // each, so the planes' short transfers share one ramp-up and one drain.
+// A lane moves the same word of kGatherRows rows, rpw rows apart: it issues
+// their row-index loads, then their source loads, before it stores, so the
+// two dependent loads per word overlap across the rows.
+#ifndef TRACE_GATHER_ROWS
+#define TRACE_GATHER_ROWS 4
+#endif
+constexpr int kGatherRows = TRACE_GATHER_ROWS;
+
 struct GatherPlane {
   const uint4* src;
   uint4* dst;
   uint32_t wpr;    // 16-byte words per row
-  uint32_t rpw;    // rows per workgroup (1 for rows of 256 words or more)
+  uint32_t rpw;    // rows per workgroup and repetition (1 for rows of 256 words or more)
   uint32_t first;  // first workgroup of this plane
 };
 struct GatherPlanes {
@@ -1054,19 +1062,32 @@ struct GatherPlanes {
 __global__ __launch_bounds__(kThreads) void gather_planes_kernel(GatherPlanes P, uint64_t src_rows,
                                                                  uint64_t dst_rows,
                                                                  const int64_t* __restrict__ row_index) {
+  constexpr int J = kGatherRows;
   const uint32_t k = (P.count > 2 && blockIdx.x >= P.p[2].first) ? 2u
                      : (P.count > 1 && blockIdx.x >= P.p[1].first) ? 1u : 0u;
   const GatherPlane g = P.p[k];
   const uint32_t lr = g.wpr >= kThreads ? 0u : threadIdx.x / g.wpr;
   if (lr >= g.rpw) return;
-  const uint64_t r = (uint64_t)(blockIdx.x - g.first) * g.rpw + lr;
-  if (r >= dst_rows) return;
+  const uint64_t base = (uint64_t)(blockIdx.x - g.first) * g.rpw * J + lr;  // row of repetition 0
   const uint32_t w0 = threadIdx.x - lr * (g.wpr >= kThreads ? 0u : g.wpr);
   const uint32_t wstep = g.wpr >= kThreads ? kThreads : g.wpr;
-  const int64_t s = row_index[r];
-  const bool ok = s >= 0 && (uint64_t)s < src_rows;
-  for (uint32_t w = w0; w < g.wpr; w += wstep)
-    g.dst[r * g.wpr + w] = ok ? g.src[(uint64_t)s * g.wpr + w] : zero_word<uint4>();
+  int64_t s[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const uint64_t r = base + (uint64_t)j * g.rpw;
+    s[j] = r < dst_rows ? row_index[r] : -1;
+  }
+  for (uint32_t w = w0; w < g.wpr; w += wstep) {
+    uint4 v[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+      v[j] = (s[j] >= 0 && (uint64_t)s[j] < src_rows) ? g.src[(uint64_t)s[j] * g.wpr + w] : zero_word<uint4>();
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const uint64_t r = base + (uint64_t)j * g.rpw;
+      if (r < dst_rows) g.dst[r * g.wpr + w] = v[j];
+    }
+  }
 }
 
 }  // namespace trace_dev
@@ -1401,7 +1422,7 @@ static bool launch_gather_fused(const uint8_t* const (&src)[3], uint8_t* const (
     if (wpr > 0xffffffffull) return false;
     P.p[k] = GatherPlane{reinterpret_cast<const uint4*>(src[k]), reinterpret_cast<uint4*>(dst[k]), (uint32_t)wpr,
                          (uint32_t)rpw, (uint32_t)wg};
-    wg += (dst_rows + rpw - 1) / rpw;
+    wg += (dst_rows + rpw * kGatherRows - 1) / (rpw * kGatherRows);
     if (wg > kMaxGroups) return false;
   }
   P.count = nplanes;
