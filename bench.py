@@ -575,8 +575,8 @@ def moe_rows(tr, workloads, torch, dev, stream, layers, reps):
     into a shuffled row order (single rows, and runs of GATHER_RUN
     consecutive rows), and the trainer's forward on its rows in that order
     (gather then forward, against the fused read-back forwards); every
-    gather and read-back variant after a read-only 1 GiB pass.  Medians of
-    MOE_REPS reps."""
+    gather and read-back variant after a read-only 1 GiB pass, and the
+    read-back variants also rep after rep.  Medians of MOE_REPS reps."""
     sigma = 0.02
     d = workloads.moe_layer(dev, sigma, sites=["expert_in"])["expert_in"]
     _, experts = workloads.moe_routing(dev)
@@ -605,16 +605,22 @@ def moe_rows(tr, workloads, torch, dev, stream, layers, reps):
         Untimed reps run first for MOE_WARM_S seconds: after the data
         generation the GPU's clocks settle over ~20-40 ms of sustained work,
         during which the capture and the forward measured up to 40% and 15%
-        slower."""
+        slower.  The timed reps are all enqueued before the host waits, so
+        the GPU runs them back to back: with a wait after each rep, a start
+        event fires on an idle GPU while the host is still issuing the
+        launch, and that gap (up to ~16 us here) lands inside the interval."""
         t = {k: [] for k in names}
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < MOE_WARM_S:
             run({k: (torch.cuda.Event(), torch.cuda.Event()) for k in names})
             stream.synchronize()
+        evs = []
         for _ in range(MOE_REPS):
-            ev = {k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for k in names}
-            run(ev)
-            stream.synchronize()
+            evs.append({k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                        for k in names})
+            run(evs[-1])
+        stream.synchronize()
+        for ev in evs:
             for k in names:
                 t[k].append(ev[k][0].elapsed_time(ev[k][1]) * 1e3)
         return {k: statistics.median(v) for k, v in t.items()}
@@ -664,17 +670,25 @@ def moe_rows(tr, workloads, torch, dev, stream, layers, reps):
         g_bits, g_scales, _ = tr.gather_records(bt1, sc1, None, cols, perm)
         tr.guided_fakequant_fwd(xt_perm, g_scales, ts1, g_bits, y=y, mask=mask)
 
+    rb_calls = (("gather_then_guided_fwd", two_step),
+                ("fused_guided_fwd",
+                 lambda: tr.gathered_guided_fakequant_fwd(xt_perm, perm, sc1, ts1, bt1, y=y, mask=mask)),
+                ("fused_guided_fwd_per_expert",
+                 lambda: tr.gathered_guided_fakequant_fwd(xt_perm, perm, scales, ts, bits, offsets=offsets,
+                                                          y=y, mask=mask)))
+
     def readback(ev):
-        for k, fn in (("gather_then_guided_fwd", two_step),
-                      ("fused_guided_fwd",
-                       lambda: tr.gathered_guided_fakequant_fwd(xt_perm, perm, sc1, ts1, bt1, y=y, mask=mask)),
-                      ("fused_guided_fwd_per_expert",
-                       lambda: tr.gathered_guided_fakequant_fwd(xt_perm, perm, scales, ts, bits, offsets=offsets,
-                                                                y=y, mask=mask))):
+        for k, fn in rb_calls:
             tr.tensor_scale(flush, out=flush_ts)
             timed(ev, k, fn)
 
     us_rb = medians(readback, tuple(READBACK_BYTES_PER_ELEM))
+    # and each variant rep after rep, as a training step streams its
+    # forwards: each rep then also pays the write-back the previous one left
+    # in the last-level cache, which the read-only pass above takes off
+    us_rb_seq = {}
+    for k, fn in rb_calls:
+        us_rb_seq.update(medians(lambda ev, k=k, fn=fn: timed(ev, k, fn), (k,)))
 
     def row(k_us, bpe):
         gbs = bpe * n / (k_us * 1e-6) / 1e9
@@ -691,6 +705,10 @@ def moe_rows(tr, workloads, torch, dev, stream, layers, reps):
                                        "reuse, no dirty lines)"}
     out["kernels_cold"].update({k: row(us_cold[k], MOE_BYTES_PER_ELEM[k]) for k in seq_names})
     out["readback_trainer_order"] = {k: row(us_rb[k], bpe) for k, bpe in READBACK_BYTES_PER_ELEM.items()}
+    out["readback_trainer_order"]["protocol"] = "each rep after a read-only 1 GiB pass"
+    out["readback_trainer_order_in_sequence"] = {k: row(us_rb_seq[k], bpe)
+                                                 for k, bpe in READBACK_BYTES_PER_ELEM.items()}
+    out["readback_trainer_order_in_sequence"]["protocol"] = "each variant rep after rep"
     del d, x_roll, x_train, y, xt_perm
     return out
 

@@ -49,10 +49,12 @@ def hipcc() -> str:
 
 # The same sources with grids capped at 3 workgroups, so that every kernel's
 # grid-stride loop runs several iterations on test-sized tensors (the
-# production caps are reached only beyond 2^34 elements).  Loaded by the GPU
-# tests only.
+# production caps are reached only beyond 2^34 elements), and with the
+# non-temporal stream threshold at 0 bytes, so that test-sized tensors run
+# the instantiations that production uses for tensors past 256 MiB.  Loaded
+# by the GPU tests only.
 SMALLGRID_LIB = os.path.join(PKG, "libtrace_smallgrid.so")
-SMALLGRID_DEFINES = ["-DTRACE_MAX_GROUPS=3u", "-DTRACE_AMAX_MAX_GROUPS=3u"]
+SMALLGRID_DEFINES = ["-DTRACE_MAX_GROUPS=3u", "-DTRACE_AMAX_MAX_GROUPS=3u", "-DTRACE_NT_STREAM_BYTES=0ull"]
 
 
 def _command(out, defines=()):

@@ -27,16 +27,62 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 // v_cmp_class mask: signalling/quiet NaN and +-infinity.
 constexpr int kBadClass = 0x001 | 0x002 | 0x004 | 0x200;
 
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Loads and stores with an optional non-temporal hint (kNT).  A kernel whose
+// input is larger than the 256 MB memory-side last-level cache cannot leave
+// lines there for a consumer (the cache keeps only the stream's last
+// quarter-gigabyte, which a consumer reading from the start has evicted
+// again before it gets there), so such streams bypass it: the forwards and
+// the STE backward read x and write their outputs with the hint, the capture
+// writes its record with it.  The hint changes where lines are allocated,
+// never the values.
+template <bool kNT>
+__device__ __forceinline__ uint4 load_vec(const uint4* __restrict__ p) {
+  const u32x4* q = reinterpret_cast<const u32x4*>(p);
+  const u32x4 v = kNT ? __builtin_nontemporal_load(q) : *q;
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+template <bool kNT>
+__device__ __forceinline__ void store_vec(uint4* __restrict__ p, uint4 v) {
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  if (kNT)
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+  else
+    *reinterpret_cast<u32x4*>(p) = w;
+}
+
+template <bool kNT>
+__device__ __forceinline__ void store_pair(uint2* __restrict__ p, uint2 v) {
+  const u32x2 w = {v.x, v.y};
+  if (kNT)
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(p));
+  else
+    *reinterpret_cast<u32x2*>(p) = w;
+}
+
+template <bool kNT, typename T>
+__device__ __forceinline__ void store_word(T* __restrict__ p, T v) {
+  if (kNT)
+    __builtin_nontemporal_store(v, p);
+  else
+    *p = v;
+}
+
+template <bool kNT = false>
 __device__ __forceinline__ void load_block(const uint4* __restrict__ x, uint64_t b, uint32_t (&w)[8]) {
-  const uint4 v0 = x[2 * b];
-  const uint4 v1 = x[2 * b + 1];
+  const uint4 v0 = load_vec<kNT>(x + 2 * b);
+  const uint4 v1 = load_vec<kNT>(x + 2 * b + 1);
   w[0] = v0.x; w[1] = v0.y; w[2] = v0.z; w[3] = v0.w;
   w[4] = v1.x; w[5] = v1.y; w[6] = v1.z; w[7] = v1.w;
 }
 
+template <bool kNT = false>
 __device__ __forceinline__ void store_block(uint4* __restrict__ y, uint64_t b, const uint32_t (&w)[8]) {
-  y[2 * b] = make_uint4(w[0], w[1], w[2], w[3]);
-  y[2 * b + 1] = make_uint4(w[4], w[5], w[6], w[7]);
+  store_vec<kNT>(y + 2 * b, make_uint4(w[0], w[1], w[2], w[3]));
+  store_vec<kNT>(y + 2 * b + 1, make_uint4(w[4], w[5], w[6], w[7]));
 }
 
 // Toward-zero E2M1 codes of two values into byte SEL of acc: the stochastic-

@@ -1,11 +1,14 @@
 """The grid-stride paths of every kernel (and the batch entry points'
-small-grid splits).  Production grids cover a tensor
-in one pass up to 2^34 elements, so these loops only run for larger
-tensors; the small-grid build of the same sources (grids capped at 3
-workgroups) runs them for several iterations on test-sized tensors.  Every
-entry point's outputs must equal the production build's bit for bit (which
-the other GPU tests tie to the oracle); capture is also checked against the
-oracle directly."""
+small-grid splits), and the non-temporal instantiations.  Production grids
+cover a tensor in one pass up to 2^34 elements, so these loops only run for
+larger tensors; the small-grid build of the same sources (grids capped at 3
+workgroups) runs them for several iterations on test-sized tensors.  That
+build also streams every tensor with the non-temporal hint, which
+production applies past 256 MiB only, so the comparison pins those
+instantiations on a ragged tensor with NaN and infinite blocks as well.
+Every entry point's outputs must equal the production build's bit for bit
+(which the other GPU tests tie to the oracle); capture is also checked
+against the oracle directly."""
 import contextlib
 import sys
 
