@@ -589,6 +589,8 @@ struct BatchSite {
   uint2* codes;       // nullable
   uint32_t wg_begin;
   uint32_t wg_count;
+  uint64_t nt_tiles;  // tensor scale pass: tiles below it are loaded with the non-temporal hint
+  uint32_t nt;        // capture: the record is stored with the non-temporal hint
 };
 
 struct BatchSites {
@@ -608,7 +610,7 @@ __device__ __forceinline__ uint32_t batch_site_of(const BatchSites& B, uint32_t 
 
 __global__ __launch_bounds__(kThreads) void amax_partial_batch_kernel(BatchSites B, uint32_t* __restrict__ partial) {
   const BatchSite& S = B.site[batch_site_of(B, blockIdx.x)];
-  const uint32_t r = amax_partial_body(S.x, S.nblocks, blockIdx.x - S.wg_begin, S.wg_count);
+  const uint32_t r = amax_partial_body(S.x, S.nblocks, blockIdx.x - S.wg_begin, S.wg_count, S.nt_tiles);
   if (threadIdx.x == 0) partial[blockIdx.x] = r;
 }
 
@@ -623,7 +625,8 @@ __global__ __launch_bounds__(kThreads) void amax_finalize_batch_kernel(BatchSite
 
 // One 256-block tile per workgroup.  The grid is walked from its end, across
 // sites and within each site, so the capture first meets the lines the tensor
-// scale pass read last.
+// scale pass read last.  Each site takes the record stores a capture of it
+// alone would (non-temporal past the last-level cache's size).
 __global__ __launch_bounds__(kThreads) void capture_batch_kernel(BatchSites B) {
   const uint32_t gw = gridDim.x - 1 - blockIdx.x;
   const BatchSite& S = B.site[batch_site_of(B, gw)];
@@ -634,7 +637,10 @@ __global__ __launch_bounds__(kThreads) void capture_batch_kernel(BatchSites B) {
   const float r6hi = 1.0f / 6.0f;
   const float r6lo = __builtin_fmaf(-6.0f, r6hi, 1.0f) * r6hi;
   const CaptureScale cs = capture_scale(*S.ts);
-  capture_one<false, false>(S.x, b, w, cs, r6hi, r6lo, S.scales, S.bits, S.codes, Planes{1, 0});
+  if (S.nt)
+    capture_one<false, true>(S.x, b, w, cs, r6hi, r6lo, S.scales, S.bits, S.codes, Planes{1, 0});
+  else
+    capture_one<false, false>(S.x, b, w, cs, r6hi, r6lo, S.scales, S.bits, S.codes, Planes{1, 0});
 }
 
 // ---------------------------------------------------------------------------
@@ -1196,14 +1202,20 @@ uint32_t amax_partial_count(uint64_t nblocks) {
 // (0 bytes: 158.7 / 222.5 us), and tensors of up to 256 MiB are unchanged.
 constexpr uint64_t kAmaxKeepBytes = kLastLevelCacheBytes;
 
+// Tiles (8 KiB) of an nblocks tensor that the tensor amax loads with the
+// non-temporal hint: all but the kept tail, never the last (partial) tile.
+static uint64_t amax_nt_tiles(uint64_t nblocks) {
+  const uint64_t tiles = (nblocks + kThreads - 1) / kThreads;
+  const uint64_t keep = kAmaxKeepBytes / (2 * 16 * kThreads);
+  return tiles > keep ? tiles - keep : 0ull;
+}
+
 hipError_t launch_tensor_scale(const uint16_t* x, uint64_t nblocks, uint32_t* partial, float* ts_out,
                                hipStream_t stream) {
   const uint32_t groups = amax_partial_count(nblocks);
-  const uint64_t tiles = (nblocks + kThreads - 1) / kThreads;
-  const uint64_t keep = kAmaxKeepBytes / (2 * 16 * kThreads);  // tiles of 8 KiB
   if (nblocks > 0)
     hipLaunchKernelGGL(amax_partial_kernel, dim3(groups), dim3(kThreads), 0, stream,
-                       reinterpret_cast<const uint4*>(x), nblocks, tiles > keep ? tiles - keep : 0ull, partial);
+                       reinterpret_cast<const uint4*>(x), nblocks, amax_nt_tiles(nblocks), partial);
   hipLaunchKernelGGL(amax_finalize_kernel, dim3(1), dim3(kThreads), 0, stream, partial,
                      nblocks > 0 ? groups : 0u, ts_out);
   return hipGetLastError();
@@ -1241,7 +1253,8 @@ static BatchSites batch_sites(const BatchSiteSpec* sites, uint32_t count, const 
   for (uint32_t i = 0; i < count; ++i) {
     B.site[i] = BatchSite{reinterpret_cast<const uint4*>(sites[i].x), sites[i].nblocks, sites[i].ts,
                           sites[i].scales, reinterpret_cast<uint16_t*>(sites[i].bits),
-                          reinterpret_cast<uint2*>(sites[i].codes), begin, wg[i]};
+                          reinterpret_cast<uint2*>(sites[i].codes), begin, wg[i],
+                          amax_nt_tiles(sites[i].nblocks), past_cache(sites[i].nblocks * 32) ? 1u : 0u};
     begin += wg[i];
   }
   return B;
