@@ -1,8 +1,10 @@
 // Practical HBM ceilings of this GPU for the access mixes of the libtrace
 // kernels: a plain 128-bit copy (read + write, the layout of the STE
-// backward: one vector per lane), a read-only stream and a write-only fill,
-// each over 1 GiB buffers with one-shot grids, plus the runtime's
-// device-to-device copy.
+// backward: one vector per lane), the same copy with the non-temporal hint on
+// its loads and stores (as the kernels stream tensors larger than the 256 MB
+// last-level cache), a read-only stream and a write-only fill, each over
+// 1 GiB buffers with one-shot grids, plus the runtime's device-to-device
+// copy.
 // Each is timed (median of 15 HIP-event-timed launches) in three settings:
 // back to back, after a read-only pass over another 1 GiB buffer, and after
 // a 1 GiB write to another buffer (whose dirty lines are then written back
@@ -34,6 +36,14 @@ __global__ __launch_bounds__(256) void copy_kernel(const uint4* __restrict__ s, 
   if (i < n) d[i] = s[i];
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void copy_nt_kernel(const u32x4* __restrict__ s, u32x4* __restrict__ d,
+                                                      uint64_t n) {
+  const uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) __builtin_nontemporal_store(__builtin_nontemporal_load(s + i), d + i);
+}
+
 __global__ __launch_bounds__(256) void read_kernel(const uint4* __restrict__ s, uint32_t* __restrict__ out,
                                                    uint64_t n) {
   const uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x;
@@ -56,12 +66,16 @@ struct Buffers {
   uint64_t n;  // uint4 per buffer
 };
 
-enum Kind { kCopy, kRead, kFill, kMemcpy };
+enum Kind { kCopy, kCopyNT, kRead, kFill, kMemcpy };
 
 static void launch(Kind k, const Buffers& b) {
   const dim3 blk(256);
   switch (k) {
     case kCopy: hipLaunchKernelGGL(copy_kernel, dim3((unsigned)((b.n + 255) / 256)), blk, 0, 0, b.src, b.dst, b.n); break;
+    case kCopyNT:
+      hipLaunchKernelGGL(copy_nt_kernel, dim3((unsigned)((b.n + 255) / 256)), blk, 0, 0,
+                         reinterpret_cast<const u32x4*>(b.src), reinterpret_cast<u32x4*>(b.dst), b.n);
+      break;
     case kRead: hipLaunchKernelGGL(read_kernel, dim3((unsigned)((b.n + 255) / 256)), blk, 0, 0, b.src, b.sink, b.n); break;
     case kFill: hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((b.n + 255) / 256)), blk, 0, 0, b.dst, b.n); break;
     case kMemcpy: CHECK(hipMemcpyAsync(b.dst, b.src, b.n * 16, hipMemcpyDeviceToDevice, 0)); break;
@@ -108,7 +122,8 @@ int main() {
   CHECK(hipMemset(b.other, 3, bytes));
   CHECK(hipDeviceSynchronize());
   const struct { const char* name; Kind k; double traffic; } tests[] = {
-      {"copy", kCopy, 2.0 * bytes}, {"read", kRead, 1.0 * bytes}, {"fill", kFill, 1.0 * bytes},
+      {"copy", kCopy, 2.0 * bytes}, {"copy_nontemporal", kCopyNT, 2.0 * bytes}, {"read", kRead, 1.0 * bytes},
+      {"fill", kFill, 1.0 * bytes},
       {"runtime_d2d_copy", kMemcpy, 2.0 * bytes}};
   const char* modes[] = {"back_to_back", "after_read_pass", "after_write_pass"};
   printf("{\"buffer_bytes\": %llu, \"peak_GB_s\": 8000", (unsigned long long)bytes);
