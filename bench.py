@@ -609,7 +609,8 @@ def moe_rows(tr, workloads, torch, dev, stream, layers, reps):
         slower.  The timed reps are all enqueued before the host waits, so
         the GPU runs them back to back: with a wait after each rep, a start
         event fires on an idle GPU while the host is still issuing the
-        launch, and that gap (up to ~16 us here) lands inside the interval."""
+        launch, and that gap (~4 us on the per-expert forward) lands inside
+        the interval."""
         t = {k: [] for k in names}
         t0 = time.perf_counter()
         while time.perf_counter() - t0 < MOE_WARM_S:
@@ -631,26 +632,52 @@ def moe_rows(tr, workloads, torch, dev, stream, layers, reps):
         fn()
         ev[k][1].record(stream)
 
+    def seq_medians(calls):
+        """calls: (name, fn) pairs run in order, rep after rep, with one
+        marker event after each call (as the step times its kernels, rather
+        than a start and an end event around each): the median microseconds
+        of each name over MOE_REPS reps, after MOE_WARM_S seconds of untimed
+        reps."""
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < MOE_WARM_S:
+            for _, fn in calls:
+                fn()
+            stream.synchronize()
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(MOE_REPS * len(calls) + 1)]
+        marks[0].record(stream)
+        i = 0
+        for _ in range(MOE_REPS):
+            for _, fn in calls:
+                fn()
+                i += 1
+                marks[i].record(stream)
+        stream.synchronize()
+        t = {k: [] for k, _ in calls}
+        for j in range(MOE_REPS * len(calls)):
+            t[calls[j % len(calls)][0]].append(marks[j].elapsed_time(marks[j + 1]) * 1e3)
+        return {k: statistics.median(v) for k, v in t.items()}
+
     seq_names = ("grouped_tensor_scale", "grouped_capture", "grouped_guided_fwd")
 
-    def rollout_side(ev, cold):
-        if cold:
-            tr.tensor_scale(flush, out=flush_ts)  # read-only 1 GiB pass
+    def rollout_side(ev):
+        tr.tensor_scale(flush, out=flush_ts)  # read-only 1 GiB pass
         timed(ev, "grouped_tensor_scale", lambda: tr.grouped_tensor_scale(x_roll, offsets, out=ts, workspace=ws))
         timed(ev, "grouped_capture", lambda: tr.grouped_capture(x_roll, offsets, ts, scales=scales, bits=bits))
 
-    def training_side(ev, cold):
-        if cold:
-            tr.tensor_scale(flush, out=flush_ts)
+    def training_side(ev):
+        tr.tensor_scale(flush, out=flush_ts)
         timed(ev, "grouped_guided_fwd",
               lambda: tr.grouped_guided_fakequant_fwd(x_train, offsets, scales, ts, bits, y=y, mask=mask))
 
     # in the step's phase order: the rollout side rep after rep, then the
     # training side rep after rep; and each rep after a read-only pass
-    us = medians(lambda ev: rollout_side(ev, False), seq_names[:2])
-    us.update(medians(lambda ev: training_side(ev, False), seq_names[2:]))
-    us_cold = medians(lambda ev: rollout_side(ev, True), seq_names[:2])
-    us_cold.update(medians(lambda ev: training_side(ev, True), seq_names[2:]))
+    us = seq_medians((("grouped_tensor_scale", lambda: tr.grouped_tensor_scale(x_roll, offsets, out=ts, workspace=ws)),
+                      ("grouped_capture", lambda: tr.grouped_capture(x_roll, offsets, ts, scales=scales, bits=bits))))
+    us.update(seq_medians((("grouped_guided_fwd",
+                            lambda: tr.grouped_guided_fakequant_fwd(x_train, offsets, scales, ts, bits, y=y,
+                                                                    mask=mask)),)))
+    us_cold = medians(rollout_side, seq_names[:2])
+    us_cold.update(medians(training_side, seq_names[2:]))
 
     # the gathers are short (0.375 B per element): each is timed after a
     # read-only 1 GiB pass, outside the previous kernel's write-back
@@ -689,7 +716,7 @@ def moe_rows(tr, workloads, torch, dev, stream, layers, reps):
     # in the last-level cache, which the read-only pass above takes off
     us_rb_seq = {}
     for k, fn in rb_calls:
-        us_rb_seq.update(medians(lambda ev, k=k, fn=fn: timed(ev, k, fn), (k,)))
+        us_rb_seq.update(seq_medians(((k, fn),)))
 
     def row(k_us, bpe):
         gbs = bpe * n / (k_us * 1e-6) / 1e9
