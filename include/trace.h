@@ -32,7 +32,7 @@
  *     scales : uint8_t[n/16], one E4M3FN byte per block, in block order;
  *     bits   : uint8_t[n/8], bit k of byte j is the parity bit of element
  *              8*j + k (bit 0 of its E2M1 code = parity of its signed grid
- *              index, the "one mantissa bit");
+ *              index: the single low bit the post keeps per element);
  *     codes  : uint8_t[n/2], optional full 4-bit codes (sign << 3 | index),
  *              element 2*j in the low nibble of byte j;
  *     ts     : one IEEE fp32 tensor scale, in device memory.
@@ -223,8 +223,8 @@ TRACE_API trace_status trace_guided_fakequant_fwd(const uint16_t* x_train, int64
 
 /*
  * Plain round-to-nearest-even fake-quant forward on the same scales, the
- * vanilla-QAT baseline the post compares against ("instead of standard
- * round-to-nearest"): as trace_guided_fakequant_fwd with m = the E2M1
+ * vanilla-QAT baseline the post compares against (the rounding that the
+ * guided rule replaces): as trace_guided_fakequant_fwd with m = the E2M1
  * magnitude nearest to |z|, ties to the even index.  Same arguments minus
  * `bits`; y may be exactly x_train.
  */
@@ -384,7 +384,7 @@ TRACE_API trace_status trace_grouped_full_info_fakequant_fwd(const uint16_t* x_t
 
 /*
  * b cached low bits, b = 1..4 (low_bits(q_roll, b) in the listing, which the
- * post runs with b = 1; the bandwidth paragraph's "one mantissa bit").
+ * post runs with b = 1: the single bit of the bandwidth paragraph).
  * Reading for b > 1: the b low bits of each codeword's signed grid index
  * (-7..7) in two's complement; for b = 1 this is the parity bit above.  The
  * record keeps them as b bit-planes of n/8 bytes each, back to back: plane k

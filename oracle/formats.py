@@ -12,8 +12,8 @@ those distances are exact and the tie test is exact.
 import numpy as np
 
 # E2M1 (FP4) magnitudes indexed by the code's three low bits (exponent,
-# mantissa).  Bit 3 of a code is the sign.  The rcap.io TRACE post calls this
-# the "coarse E2M1 grid"; its listing clips to [-6, 6], the grid's end points.
+# mantissa).  Bit 3 of a code is the sign.  The rcap.io TRACE post rounds
+# onto this grid; its listing clips to [-6, 6], the grid's end points.
 E2M1_MAGNITUDES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
 
 E4M3FN_MAX = 448.0

@@ -14,7 +14,7 @@ multiple of 16; a block is 16 consecutive elements.  Record layouts:
 
 Readings of points the pages leave open:
 
-* the "one mantissa bit" kept per site is bit 0 of the E2M1 code, which is
+* the single low bit kept per site is bit 0 of the E2M1 code, which is
   the parity of the codeword's signed grid index: adjacent codewords,
   including the pair around zero, always differ in it;
 * ``reconstruct_from_mantissa(c, z)`` is the endpoint of z's bracket whose
