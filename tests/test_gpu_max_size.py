@@ -5,7 +5,9 @@ checked against the whole-tensor properties of ``tests/full_props.py``; the
 tensor scale against torch's amax of the whole tensor; sampled rows --
 around the 2^31-byte and 2^32-element boundaries, the ragged end and random
 rows -- against the oracle, for the NVFP4 path, per-expert scales (64 row
-groups) and the MXFP4 and MXFP8 variants.  Inputs are generated on the
+groups), the forward on records read back in a shuffled row order (source
+rows around the same boundaries, and out of range) and the MXFP4 and MXFP8
+variants.  Inputs are generated on the
 device: N(0, 1) with 2 outlier channels x100 and x_train = x_roll plus 2%
 relative noise, as in the deeper-half sweep."""
 import sys
@@ -119,6 +121,33 @@ def test_max_size_grouped(device, big):
                "codes": _rows_of(q, idx[j:j + 1], COLS // 2)}
         assert_same(got, {"scales": cap["scales"], "bits": cap["bits"], "y": gd["y"], "mask": gd["mask"],
                           "codes": gd["codes"]}, ctx=f"max size grouped row {r}")
+
+
+def test_max_size_gathered(device, big):
+    """The guided forward on records read back in place: destination row r
+    reads source row perm[r] (a seeded permutation), with the sampled
+    destination rows pointed at source rows around the 2^31-byte and
+    2^32-element boundaries, the ragged end and two out-of-range indices."""
+    import fp4_rollout_guided_amd as tr
+    x_roll, x_train, idx = big["x_roll"], big["x_train"], big["idx"]
+    _say("case max size: forward on records read back in a shuffled row order")
+    ts = tr.tensor_scale(x_roll)
+    scales, bits, _ = tr.capture(x_roll, ts)
+    b31, b32 = (1 << 31) // (2 * COLS), (1 << 32) // COLS
+    perm = workloads.trainer_order(ROWS, device).clone()
+    for r, src in zip(idx[::2], (b31 - 1, b31, b32 - 1, b32, b32 + 1, ROWS - 1, -1, ROWS)):
+        perm[int(r)] = src
+    y, mask, q = tr.gathered_guided_fakequant_fwd(x_train, perm, scales, ts, bits, want_codes=True)
+    torch.cuda.synchronize()
+    src = perm.cpu().numpy()[idx]
+    live = sorted({int(v) for v in src if 0 <= v < ROWS})
+    pos = {v: i for i, v in enumerate(live)}
+    ts_v = np.float32(ts.item())
+    rec = oracle.capture(_rows_of(x_roll, np.array(live), COLS, True), ts_v)   # the record of the rows read
+    row_index = np.array([pos.get(int(v), -1) for v in src], dtype=np.int64)
+    want = oracle.gathered_fwd("guided", _rows_of(x_train, idx, COLS, True), COLS, rec, len(live), row_index, ts_v)
+    got = {"y": _rows_of(y, idx, COLS, True), "mask": _rows_of(mask, idx, COLS // 8), "codes": _rows_of(q, idx, COLS // 2)}
+    assert_same(got, {"y": want["y"], "mask": want["mask"], "codes": want["codes"]}, ctx="max size read back")
 
 
 def test_max_size_mx_variants(device, big):
