@@ -277,8 +277,8 @@ __device__ __forceinline__ uint64_t group_start(const RowGroups& G, uint32_t g) 
   return group_row(G, g) * G.bpr;
 }
 
-// Tensor scale of block b's group; b0 is the first block of the workgroup's
-// tile (workgroup-uniform, b0 <= b).  The group of b0 is found with scalar
+// Tensor scale of block b's group; b0 is the first block of the tile or
+// segment (wave-uniform, b0 <= b).  The group of b0 is found with scalar
 // work only: a guess that assumes equal groups (an integer multiply by the
 // fixed-point count / blocks, no vector-to-scalar moves), checked against a
 // window of three groups whose starts and scales come in one round of
@@ -751,7 +751,7 @@ struct GatherMap {
 // Tensor scale of the group holding source row s, in two steps so that a
 // wave can issue the loads for several rows before it waits on any: the
 // window (group_window_load) is three groups around a guess that assumes
-// equal groups (the fixed-point count / blocks, as in group_tensor_scale),
+// equal groups (the fixed-point count / blocks, as in group_at),
 // whose four starts and three scales are loaded together, in bounds for any
 // s; group_window_pick takes the group holding s from it, or, when s lies
 // outside the window (unbalanced groups, or fewer than three), binary
@@ -1196,10 +1196,13 @@ uint32_t amax_partial_count(uint64_t nblocks) {
 // last-level cache for the capture (which walks the same tensor from its
 // end).  After a large writer, the cache's dirty lines are written back
 // while the next kernel streams; non-temporal loads leave them to the
-// capture.  Measured on 262144x2048 layers in the step order: the amax
-// 201.6 -> 189.0 us, the capture 194.8 -> 195.5 us, the step -0.7%; a
-// smaller kept tail speeds the amax further but slows the capture by more
-// (0 bytes: 158.7 / 222.5 us), and tensors of up to 256 MiB are unchanged.
+// capture.  Measured on 262144x2048 layers with each layer's kernels in
+// turn, right after a 1 GiB plain writer: the amax 201.6 -> 189.0 us, the
+// capture 194.8 -> 195.5 us, the step -0.7%; a smaller kept tail speeds the
+// amax further but slows the capture by more (0 bytes: 158.7 / 222.5 us),
+// and tensors of up to 256 MiB are unchanged.  In the phase-ordered step
+// the amax follows the previous layer's capture, whose non-temporal record
+// leaves no dirty lines, and runs at the read ceiling (~162 us).
 constexpr uint64_t kAmaxKeepBytes = kLastLevelCacheBytes;
 
 // Tiles (8 KiB) of an nblocks tensor that the tensor amax loads with the
