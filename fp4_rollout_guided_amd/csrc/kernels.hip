@@ -1175,16 +1175,8 @@ static unsigned grid_for(uint64_t nblocks) {
 // side), with identical outputs: guided forward 376 -> 366 us, RNE 361 ->
 // 341 us, STE backward 364 -> 345 us, and the tensor amax after a capture
 // with a non-temporal record 172 -> 161 us; the step 29.3 -> 28.1 ms.
-// Smaller tensors keep plain accesses, so a consumer can still find their
-// lines in the cache.  (The test build that caps grids also sets the
-// threshold to 0, so that its tensors run the non-temporal instantiations.)
+// Smaller tensors keep plain accesses (past_cache, launch.h).
 constexpr uint64_t kLastLevelCacheBytes = 256ull << 20;
-#ifndef TRACE_NT_STREAM_BYTES
-#define TRACE_NT_STREAM_BYTES (256ull << 20)
-#endif
-constexpr uint64_t kNTStreamBytes = TRACE_NT_STREAM_BYTES;
-
-static bool past_cache(uint64_t bytes) { return bytes > kNTStreamBytes; }
 
 uint32_t amax_partial_count(uint64_t nblocks) {
   const uint64_t g = (nblocks + kThreads - 1) / kThreads;

@@ -28,6 +28,18 @@ constexpr uint32_t kAmaxMaxGroups = TRACE_AMAX_MAX_GROUPS;
 constexpr uint32_t kMaxGroups = TRACE_MAX_GROUPS;
 static_assert((uint64_t)TRACE_MAX_GROUPS * 256 <= 0xffffffffull, "grid exceeds 2^32 - 1 work-items");
 
+// Tensors larger than MI355X's 256 MB memory-side last-level cache are
+// streamed with the non-temporal hint: the kernels' instantiations with kNT
+// set load x and store their outputs (the captures: their records) that
+// way; smaller tensors keep plain accesses, so a consumer can still find
+// their lines in the cache.  The test build that caps grids sets the
+// threshold to 0, so that its tensors run the hinted instantiations.
+#ifndef TRACE_NT_STREAM_BYTES
+#define TRACE_NT_STREAM_BYTES (256ull << 20)
+#endif
+constexpr uint64_t kNTStreamBytes = TRACE_NT_STREAM_BYTES;
+inline bool past_cache(uint64_t bytes) { return bytes > kNTStreamBytes; }
+
 // Row groups with one tensor scale each: group g holds rows
 // [offsets[g], offsets[g+1]) of a rows x cols site tensor (device int64[count + 1]).
 constexpr uint32_t kMaxRowGroups = 1u << 20;

@@ -178,6 +178,9 @@ __device__ __forceinline__ void fp8_decode_scaled(const uint32_t (&Q)[N / 4], fl
 // lane writes the scale byte.  The half count is even, so both lanes of a
 // pair are always active together.
 // ---------------------------------------------------------------------------
+// kNT: the record is stored with the non-temporal hint (tensors past the
+// last-level cache; the loads stay plain, as in the NVFP4 capture).
+template <bool kNT>
 __global__ __launch_bounds__(kThreads) void mx8_capture_kernel(const uint4* __restrict__ x, uint64_t nhalves,
                                                                uint8_t* __restrict__ scales,
                                                                uint16_t* __restrict__ bits,
@@ -196,9 +199,9 @@ __global__ __launch_bounds__(kThreads) void mx8_capture_kernel(const uint4* __re
     for (int j = 0; j < 16; ++j) q[j] = __builtin_amdgcn_fmed3f(q[j], -448.f, 448.f);
     uint32_t C[4];
     fp8_rne_codes<16>(q, C);
-    if ((h & 1) == 0) scales[h >> 1] = (uint8_t)sb;
-    bits[h] = (uint16_t)fp8_parity_word<16>(C);
-    if (codes) codes[h] = make_uint4(C[0], C[1], C[2], C[3]);
+    if ((h & 1) == 0) store_word<kNT>(&scales[h >> 1], (uint8_t)sb);
+    store_word<kNT>(&bits[h], (uint16_t)fp8_parity_word<16>(C));
+    if (codes) store_vec<kNT>(&codes[h], make_uint4(C[0], C[1], C[2], C[3]));
   }
 }
 
@@ -206,9 +209,11 @@ __global__ __launch_bounds__(kThreads) void mx8_capture_kernel(const uint4* __re
 // fake-quant forward; kMode: 0 = RNE, 1 = guided, 2 = full information.  One
 // lane per 8-element vector (a quarter block: one 128-bit load of x, one
 // byte of bits and of mask, 8 code bytes), which streams faster than a lane
-// per 16-element half; the four lanes of a block read its scale byte.
+// per 16-element half; the four lanes of a block read its scale byte.  kNT:
+// x is loaded and every output stored with the non-temporal hint (tensors
+// past the last-level cache).
 // ---------------------------------------------------------------------------
-template <int kMode>
+template <int kMode, bool kNT>
 __global__ __launch_bounds__(kThreads) void mx8_fakequant_kernel(const uint4* __restrict__ x, uint64_t nvec,
                                                                  const uint8_t* __restrict__ scales,
                                                                  const uint8_t* __restrict__ bits,
@@ -220,7 +225,7 @@ __global__ __launch_bounds__(kThreads) void mx8_fakequant_kernel(const uint4* __
     const uint32_t sbyte = scales[g >> 2];
     const uint32_t cached = kMode == 1 ? (uint32_t)bits[g] : 0u;
     const uint2 rv = kMode == 2 ? rcodes[g] : make_uint2(0u, 0u);
-    const uint4 v = x[g];
+    const uint4 v = load_vec<kNT>(&x[g]);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     // a NaN scale byte makes a zero-scale block: multiplying by 0 maps every
     // finite x to a zero of its own sign, decoded with s = 1
@@ -238,9 +243,9 @@ __global__ __launch_bounds__(kThreads) void mx8_fakequant_kernel(const uint4* __
     mx8_select_codes<kMode, 8>(q, cached, R, Q);
     uint32_t out[4];
     fp8_decode_scaled<8>(Q, s, out);
-    y[g] = make_uint4(out[0], out[1], out[2], out[3]);
-    mask[g] = (uint8_t)(valid ? keep : 0u);
-    if (qcodes) qcodes[g] = make_uint2(Q[0], Q[1]);
+    store_vec<kNT>(&y[g], make_uint4(out[0], out[1], out[2], out[3]));
+    store_word<kNT>(&mask[g], (uint8_t)(valid ? keep : 0u));
+    if (qcodes) store_pair<kNT>(&qcodes[g], make_uint2(Q[0], Q[1]));
   }
 }
 
@@ -259,10 +264,31 @@ hipError_t launch_mx8_capture(const uint16_t* x, uint64_t nblocks, uint8_t* scal
                               hipStream_t stream) {
   if (nblocks == 0) return hipSuccess;  // an empty grid is not a valid launch
   const uint64_t nhalves = 2 * nblocks;
-  hipLaunchKernelGGL(mx8_capture_kernel, dim3(mx8_grid(nhalves)), dim3(kThreads), 0, stream,
-                     reinterpret_cast<const uint4*>(x), nhalves, scales, reinterpret_cast<uint16_t*>(bits),
-                     reinterpret_cast<uint4*>(codes));
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  uint16_t* bv = reinterpret_cast<uint16_t*>(bits);
+  uint4* cv = reinterpret_cast<uint4*>(codes);
+  if (past_cache(nblocks * 64))
+    hipLaunchKernelGGL(mx8_capture_kernel<true>, dim3(mx8_grid(nhalves)), dim3(kThreads), 0, stream, xv, nhalves,
+                       scales, bv, cv);
+  else
+    hipLaunchKernelGGL(mx8_capture_kernel<false>, dim3(mx8_grid(nhalves)), dim3(kThreads), 0, stream, xv, nhalves,
+                       scales, bv, cv);
   return hipGetLastError();
+}
+
+template <bool kNT>
+static void launch_mx8_fakequant_t(int mode, const uint4* xv, uint64_t nvec, const uint8_t* scales,
+                                   const uint8_t* side, uint4* yv, uint8_t* mask, uint2* qv, hipStream_t stream) {
+  const dim3 grid(mx8_grid(nvec)), block(kThreads);
+  if (mode == 1)
+    hipLaunchKernelGGL((mx8_fakequant_kernel<1, kNT>), grid, block, 0, stream, xv, nvec, scales, side,
+                       static_cast<const uint2*>(nullptr), yv, mask, qv);
+  else if (mode == 2)
+    hipLaunchKernelGGL((mx8_fakequant_kernel<2, kNT>), grid, block, 0, stream, xv, nvec, scales,
+                       static_cast<const uint8_t*>(nullptr), reinterpret_cast<const uint2*>(side), yv, mask, qv);
+  else
+    hipLaunchKernelGGL((mx8_fakequant_kernel<0, kNT>), grid, block, 0, stream, xv, nvec, scales,
+                       static_cast<const uint8_t*>(nullptr), static_cast<const uint2*>(nullptr), yv, mask, qv);
 }
 
 hipError_t launch_mx8_fakequant(int mode, const uint16_t* x, uint64_t nblocks, const uint8_t* scales,
@@ -273,16 +299,10 @@ hipError_t launch_mx8_fakequant(int mode, const uint16_t* x, uint64_t nblocks, c
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   uint4* yv = reinterpret_cast<uint4*>(y);
   uint2* qv = reinterpret_cast<uint2*>(qcodes);
-  const dim3 grid(mx8_grid(nvec)), block(kThreads);
-  if (mode == 1)
-    hipLaunchKernelGGL(mx8_fakequant_kernel<1>, grid, block, 0, stream, xv, nvec, scales, side,
-                       static_cast<const uint2*>(nullptr), yv, mask, qv);
-  else if (mode == 2)
-    hipLaunchKernelGGL(mx8_fakequant_kernel<2>, grid, block, 0, stream, xv, nvec, scales,
-                       static_cast<const uint8_t*>(nullptr), reinterpret_cast<const uint2*>(side), yv, mask, qv);
+  if (past_cache(nblocks * 64))
+    launch_mx8_fakequant_t<true>(mode, xv, nvec, scales, side, yv, mask, qv, stream);
   else
-    hipLaunchKernelGGL(mx8_fakequant_kernel<0>, grid, block, 0, stream, xv, nvec, scales,
-                       static_cast<const uint8_t*>(nullptr), static_cast<const uint2*>(nullptr), yv, mask, qv);
+    launch_mx8_fakequant_t<false>(mode, xv, nvec, scales, side, yv, mask, qv, stream);
   return hipGetLastError();
 }
 

@@ -78,6 +78,9 @@ __device__ __noinline__ void mx_fakequant_vec_exact(int mode, const uint4* __res
 // halves' maxima, and the even lane writes the scale byte.  The half count
 // n/16 is even, so both lanes of a pair are always active together.
 // ---------------------------------------------------------------------------
+// kNT: the record is stored with the non-temporal hint (tensors past the
+// last-level cache; the loads stay plain, as in the NVFP4 capture).
+template <bool kNT>
 __global__ __launch_bounds__(kThreads) void mx_capture_kernel(const uint4* __restrict__ x, uint64_t nhalves,
                                                               uint8_t* __restrict__ scales,
                                                               uint16_t* __restrict__ bits,
@@ -100,15 +103,15 @@ __global__ __launch_bounds__(kThreads) void mx_capture_kernel(const uint4* __res
     uint32_t E = 0, O = 0;
     FP4_PACK8(FP4_RNE, E, q, 0);
     FP4_PACK8(FP4_RNE, O, q, 1);
-    if ((h & 1) == 0) scales[h >> 1] = (uint8_t)sb;
+    if ((h & 1) == 0) store_word<kNT>(&scales[h >> 1], (uint8_t)sb);
     if (bad) {
       mx_capture_half_exact(x, h, sb, bits, codes);
     } else {
-      bits[h] = (uint16_t)gather_parity(E, O);
+      store_word<kNT>(&bits[h], (uint16_t)gather_parity(E, O));
       if (codes) {
         uint32_t c0, c1;
         interleave_codes(E, O, c0, c1);
-        codes[h] = make_uint2(c0, c1);
+        store_pair<kNT>(&codes[h], make_uint2(c0, c1));
       }
     }
   }
@@ -118,9 +121,11 @@ __global__ __launch_bounds__(kThreads) void mx_capture_kernel(const uint4* __res
 // fake-quant forward; kMode: 0 = RNE, 1 = guided, 2 = full information.  One
 // lane per 8-element vector (one 128-bit load; a quarter of a block): a lane
 // with one vector in flight streams faster than one moving 32 bytes.  The
-// four lanes of a block read its scale byte.
+// four lanes of a block read its scale byte.  kNT: x is loaded and every
+// output stored with the non-temporal hint (tensors past the last-level
+// cache).
 // ---------------------------------------------------------------------------
-template <int kMode>
+template <int kMode, bool kNT>
 __global__ __launch_bounds__(kThreads) void mx_fakequant_kernel(const uint4* __restrict__ x, uint64_t nvec,
                                                                 const uint8_t* __restrict__ scales,
                                                                 const uint8_t* __restrict__ bits,
@@ -132,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void mx_fakequant_kernel(const uint4* __r
     const uint32_t sbyte = scales[g >> 2];
     const uint32_t cached = kMode == 1 ? (uint32_t)bits[g] : 0u;
     const uint32_t roll = kMode == 2 ? rcodes[g] : 0u;
-    const uint4 v = x[g];
+    const uint4 v = load_vec<kNT>(&x[g]);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     // a NaN scale byte makes a zero-scale block: multiplying by 0 maps every
     // finite x to a zero of its own sign, decoded with s = 1
@@ -153,9 +158,9 @@ __global__ __launch_bounds__(kThreads) void mx_fakequant_kernel(const uint4* __r
     } else {
       uint32_t out[4];
       decode_half(Q, s, out);
-      y[g] = make_uint4(out[0], out[1], out[2], out[3]);
-      mask[g] = (uint8_t)(valid ? keep : 0u);
-      if (qcodes) qcodes[g] = Q;
+      store_vec<kNT>(&y[g], make_uint4(out[0], out[1], out[2], out[3]));
+      store_word<kNT>(&mask[g], (uint8_t)(valid ? keep : 0u));
+      if (qcodes) store_word<kNT>(&qcodes[g], Q);
     }
   }
 }
@@ -175,10 +180,31 @@ hipError_t launch_mx_capture(const uint16_t* x, uint64_t nblocks, uint8_t* scale
                              hipStream_t stream) {
   if (nblocks == 0) return hipSuccess;  // an empty grid is not a valid launch
   const uint64_t nhalves = 2 * nblocks;
-  hipLaunchKernelGGL(mx_capture_kernel, dim3(mx_grid(nhalves)), dim3(kThreads), 0, stream,
-                     reinterpret_cast<const uint4*>(x), nhalves, scales, reinterpret_cast<uint16_t*>(bits),
-                     reinterpret_cast<uint2*>(codes));
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  uint16_t* bv = reinterpret_cast<uint16_t*>(bits);
+  uint2* cv = reinterpret_cast<uint2*>(codes);
+  if (past_cache(nblocks * 64))
+    hipLaunchKernelGGL(mx_capture_kernel<true>, dim3(mx_grid(nhalves)), dim3(kThreads), 0, stream, xv, nhalves,
+                       scales, bv, cv);
+  else
+    hipLaunchKernelGGL(mx_capture_kernel<false>, dim3(mx_grid(nhalves)), dim3(kThreads), 0, stream, xv, nhalves,
+                       scales, bv, cv);
   return hipGetLastError();
+}
+
+template <bool kNT>
+static void launch_mx_fakequant_t(int mode, const uint4* xv, uint64_t nvec, const uint8_t* scales,
+                                  const uint8_t* side, uint4* yv, uint8_t* mask, uint32_t* qv, hipStream_t stream) {
+  const dim3 grid(mx_grid(nvec)), block(kThreads);
+  if (mode == 1)
+    hipLaunchKernelGGL((mx_fakequant_kernel<1, kNT>), grid, block, 0, stream, xv, nvec, scales, side,
+                       static_cast<const uint32_t*>(nullptr), yv, mask, qv);
+  else if (mode == 2)
+    hipLaunchKernelGGL((mx_fakequant_kernel<2, kNT>), grid, block, 0, stream, xv, nvec, scales,
+                       static_cast<const uint8_t*>(nullptr), reinterpret_cast<const uint32_t*>(side), yv, mask, qv);
+  else
+    hipLaunchKernelGGL((mx_fakequant_kernel<0, kNT>), grid, block, 0, stream, xv, nvec, scales,
+                       static_cast<const uint8_t*>(nullptr), static_cast<const uint32_t*>(nullptr), yv, mask, qv);
 }
 
 hipError_t launch_mx_fakequant(int mode, const uint16_t* x, uint64_t nblocks, const uint8_t* scales,
@@ -189,16 +215,10 @@ hipError_t launch_mx_fakequant(int mode, const uint16_t* x, uint64_t nblocks, co
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   uint4* yv = reinterpret_cast<uint4*>(y);
   uint32_t* qv = reinterpret_cast<uint32_t*>(qcodes);
-  const dim3 grid(mx_grid(nvec)), block(kThreads);
-  if (mode == 1)
-    hipLaunchKernelGGL(mx_fakequant_kernel<1>, grid, block, 0, stream, xv, nvec, scales, side,
-                       static_cast<const uint32_t*>(nullptr), yv, mask, qv);
-  else if (mode == 2)
-    hipLaunchKernelGGL(mx_fakequant_kernel<2>, grid, block, 0, stream, xv, nvec, scales,
-                       static_cast<const uint8_t*>(nullptr), reinterpret_cast<const uint32_t*>(side), yv, mask, qv);
+  if (past_cache(nblocks * 64))
+    launch_mx_fakequant_t<true>(mode, xv, nvec, scales, side, yv, mask, qv, stream);
   else
-    hipLaunchKernelGGL(mx_fakequant_kernel<0>, grid, block, 0, stream, xv, nvec, scales,
-                       static_cast<const uint8_t*>(nullptr), static_cast<const uint32_t*>(nullptr), yv, mask, qv);
+    launch_mx_fakequant_t<false>(mode, xv, nvec, scales, side, yv, mask, qv, stream);
   return hipGetLastError();
 }
 
