@@ -10,7 +10,8 @@
   API: each of several replays, with eager work and synchronizations
   between them, equals the eager results bit for bit (the library issues
   only kernel launches, no memsets or allocations, so the captured graph
-  holds kernel nodes only)."""
+  holds kernel nodes only); on a small site and on one past 256 MiB, whose
+  kernels are the non-temporal instantiations."""
 import sys
 import threading
 
@@ -104,10 +105,11 @@ def test_two_threads_on_their_own_streams(device):
                 assert np.array_equal(got[k], ref[i][k]), (i, rep, k)
 
 
-def test_graph_replays_equal_eager(device):
+@pytest.mark.parametrize("rows,cols", [(1024, 4096), (65537, 2048)], ids=["small", "past-256MiB"])
+def test_graph_replays_equal_eager(device, rows, cols):
     import fp4_rollout_guided_amd as tr
-    _say("case HIP graph capture and replay")
-    xr, xt, g = _site(3, 1024, 4096, device)
+    _say("case HIP graph capture and replay", rows, cols)
+    xr, xt, g = _site(3, rows, cols, device)
     eager = _outputs(tr, xr, device)
     _path(tr, xr, xt, g, eager)
     torch.cuda.synchronize()
