@@ -57,6 +57,11 @@
  *   2-byte alignment, code arrays 8-byte alignment; scale bytes have none.
  * - Aliasing: outputs must not overlap inputs, except exact in-place use
  *   where an entry point allows it.
+ * - Caching: for a tensor larger than 256 MiB (MI355X's memory-side
+ *   last-level cache) the forwards and the STE backward load it and store
+ *   their outputs with the non-temporal hint, and the captures store their
+ *   records with it, so those lines are not left in that cache for the next
+ *   kernel; smaller tensors use plain accesses.  Values are unaffected.
  */
 #ifndef LIBTRACE_TRACE_H
 #define LIBTRACE_TRACE_H
