@@ -4,6 +4,7 @@ C ABI against ``oracle.mx``, bit for bit.  Covers ragged shapes over several
 tiles, every bf16 pattern under every E8M0 scale byte, block maxima over
 every finite bf16 magnitude, tiny elements beside large ones, specials,
 in-place use, and every element of a layer of the deeper-half sweep."""
+import contextlib
 import sys
 
 import numpy as np
@@ -145,10 +146,29 @@ def test_mx_tiny_elements_and_specials(device):
     _same(got, _oracle_mx(xr, xt, g), "mx tiny/specials")
 
 
-def test_mx_in_place(device):
-    """y written over x_train equals y in a separate buffer."""
+@pytest.mark.parametrize("build", ["production", "small-grid"])
+def test_mx_in_place(device, build):
+    """y written over x_train equals y in a separate buffer; also through the
+    small-grid build, which streams every tensor with the non-temporal hint
+    (production does past 256 MiB)."""
     import fp4_rollout_guided_amd as tr
-    _say("case mx in place")
+    _say("case mx in place", build)
+    with _build(tr, build):
+        _test_mx_in_place(tr, device)
+
+
+@contextlib.contextmanager
+def _build(tr, build):
+    saved = tr.lib
+    if build == "small-grid":
+        tr.lib = tr.load_library(tr.SMALLGRID_LIB_PATH)
+    try:
+        yield
+    finally:
+        tr.lib = saved
+
+
+def _test_mx_in_place(tr, device):
     rng = np.random.default_rng(9)
     xr = _bf16_np(rng.standard_normal(64 * 2048))
     xt = _bf16_np(F.bf16_to_f32(xr) * (1 + 0.05 * rng.standard_normal(xr.size)))

@@ -216,11 +216,25 @@ def test_tiny_elements_beside_large_ones(device, ts):
     assert_same(got, want, ctx=f"tiny ts={ts}")
 
 
-def test_in_place_and_guard_bytes(device):
+@pytest.mark.parametrize("build", ["production", "small-grid"])
+def test_in_place_and_guard_bytes(device, build):
     """y written over x_train and grad_in over grad_out give the same bytes
-    as separate buffers; bytes around every output stay untouched."""
+    as separate buffers; bytes around every output stay untouched.  Also
+    through the small-grid build, whose kernels loop over their grids and
+    stream every tensor with the non-temporal hint (production does past
+    256 MiB)."""
     import fp4_rollout_guided_amd as tr
-    _say("case in-place + guards")
+    _say("case in-place + guards", build)
+    saved = tr.lib
+    if build == "small-grid":
+        tr.lib = tr.load_library(tr.SMALLGRID_LIB_PATH)
+    try:
+        _in_place_and_guard_bytes(tr, device)
+    finally:
+        tr.lib = saved
+
+
+def _in_place_and_guard_bytes(tr, device):
     rng = np.random.default_rng(3)
     rows, cols = 300, 2064
     n = rows * cols
