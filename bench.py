@@ -33,7 +33,7 @@ Gelem/s and the fraction of the 8 TB/s HBM peak are reported beside it, with
 the CPU oracle timed on a bounded sample of the same workload and, under
 ``practical_ceiling``, the GB/s of a plain copy, the same copy with
 non-temporal loads and stores, a read-only and a write-only stream on the
-same GPU (``bench_ceiling.hip``).
+same GPU, and of plain copies of 12 to 192 MiB (``bench_ceiling.hip``).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -745,8 +745,9 @@ def practical_ceiling():
     """Copy (plain and non-temporal), read and fill streams over 1 GiB
     (``bench_ceiling.hip``, built into _build/), back to back, after a
     read-only pass and after a 1 GiB write: the practical ceilings for the
-    kernels' access mixes.  Run as a child process after the timed work;
-    None if it is not built."""
+    kernels' access mixes; and plain copies of 12 to 192 MiB
+    (``copy_by_size``), the ceiling of the smaller sites' kernels.  Run as a
+    child process after the timed work; None if it is not built."""
     import subprocess
     exe = os.path.join(ROOT, "_build", "bench_ceiling")
     if not os.path.exists(exe):

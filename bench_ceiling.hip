@@ -4,7 +4,7 @@
 // its loads and stores (as the kernels stream tensors larger than the 256 MB
 // last-level cache), a read-only stream and a write-only fill, each over
 // 1 GiB buffers with one-shot grids, plus the runtime's device-to-device
-// copy.
+// copy, and plain copies of 12 MiB to 192 MiB.
 // Each is timed (median of 15 HIP-event-timed launches) in three settings:
 // back to back, after a read-only pass over another 1 GiB buffer, and after
 // a 1 GiB write to another buffer (whose dirty lines are then written back
@@ -109,6 +109,32 @@ static double median_us(Kind k, int mode, const Buffers& b) {
   return 1e3 * t[t.size() / 2];
 }
 
+// A plain copy of `bytes` (read, and the same written) from b.src to b.dst:
+// median of 15 launches, back to back (mode 0) or each after a read-only pass
+// over the whole 1 GiB of b.other (mode 1).  Small copies show the fixed cost
+// of filling and draining the chip that short kernels pay.
+static double copy_size_us(uint64_t bytes, int mode, const Buffers& b) {
+  const uint64_t n = bytes / 16;
+  hipEvent_t e0, e1;
+  CHECK(hipEventCreate(&e0));
+  CHECK(hipEventCreate(&e1));
+  std::vector<float> t;
+  for (int r = 0; r < 16; ++r) {
+    prepass(mode, b);
+    CHECK(hipEventRecord(e0, 0));
+    hipLaunchKernelGGL(copy_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, 0, b.src, b.dst, n);
+    CHECK(hipEventRecord(e1, 0));
+    CHECK(hipEventSynchronize(e1));
+    float ms = 0.f;
+    CHECK(hipEventElapsedTime(&ms, e0, e1));
+    if (r > 0) t.push_back(ms);
+  }
+  CHECK(hipEventDestroy(e0));
+  CHECK(hipEventDestroy(e1));
+  std::sort(t.begin(), t.end());
+  return 1e3 * t[t.size() / 2];
+}
+
 int main() {
   const uint64_t bytes = 1ull << 30;
   Buffers b;
@@ -137,7 +163,21 @@ int main() {
     }
     printf("}");
   }
-  printf("}\n");
+  // plain copies of 12 MiB to 192 MiB (the sizes of the smaller sites' streams)
+  printf(", \"copy_by_size\": {");
+  const uint64_t mib[] = {12, 24, 48, 96, 192};
+  for (int i = 0; i < 5; ++i) {
+    const uint64_t sz = mib[i] << 20;
+    printf("%s\"%llu_MiB\": {", i ? ", " : "", (unsigned long long)mib[i]);
+    for (int m = 0; m < 2; ++m) {
+      const double us = copy_size_us(sz, m, b);
+      const double gbs = 2.0 * sz / (us * 1e-6) / 1e9;
+      printf("%s\"%s\": {\"us\": %.2f, \"GB_s\": %.1f, \"frac\": %.4f}", m ? ", " : "", modes[m], us, gbs,
+             gbs / 8000.0);
+    }
+    printf("}");
+  }
+  printf("}}\n");
   CHECK(hipFree(b.src));
   CHECK(hipFree(b.dst));
   CHECK(hipFree(b.other));
