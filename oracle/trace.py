@@ -233,8 +233,8 @@ def guided_rule(x, zr, s, valid, c) -> dict:
 
 
 def rne_fwd(x_bits, scale_bytes, ts) -> dict:
-    """Plain round-to-nearest-even fake-quant forward ("standard
-    round-to-nearest", the vanilla-QAT baseline): as ``guided_fwd`` but
+    """Plain round-to-nearest-even fake-quant forward (the usual rounding,
+    the vanilla-QAT baseline the post compares against): as ``guided_fwd`` but
     ``m`` = the E2M1 value nearest to |z|, ties to the even index."""
     x, zr, s, valid = _quotients(x_bits, scale_bytes, ts)
     return rne_rule(x, zr, s, valid)
