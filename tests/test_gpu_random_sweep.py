@@ -10,6 +10,8 @@ Each case draws from its own seed:
   - b low bits;
   - MXFP4 and MXFP8;
   - batches of sites;
+  - the agreement statistics;
+  - the allocation-free tensor scale;
 - a ragged shape of up to a few hundred thousand elements;
 - a value recipe: per-row magnitudes spread over up to 60 decades, heavy
   tails, outlier channels, zero rows, and IEEE specials sprinkled into either
@@ -31,8 +33,9 @@ from oracle import formats as F
 from tests.gpu_util import assert_same, from_np_u16, gpu_path, oracle_path, to_np_u8, to_np_u16
 
 pytestmark = pytest.mark.gpu
-CASES = 96
-FAMILIES = ["path", "path_ts", "grouped", "gathered", "gather", "lowbits", "mx", "mx8", "batch"]
+CASES = 110
+FAMILIES = ["path", "path_ts", "grouped", "gathered", "gather", "lowbits", "mx", "mx8", "batch", "stats",
+            "noalloc"]
 SPECIALS = np.array([np.nan, -np.nan, np.inf, -np.inf, 0.0, -0.0, 1e-40, -1e-42, 3.3e38, -3.3e38, 1.2e-38,
                      6.0, -6.0, 2688.0], dtype=np.float32)
 
@@ -286,6 +289,39 @@ def _run_batch(tr, rng, device, ctx):
                     {"scales": cap["scales"], "bits": cap["bits"], "codes": cap["codes"]}, ctx=f"{ctx} site {i}")
 
 
+def _run_stats(tr, rng, device, ctx):
+    rows, cols = _shape(rng, 16)
+    xr, xt, _ = _pair(rng, rows, cols)
+    n = xr.size
+    ts = np.float32(oracle.tensor_scale(xr))
+    cap = oracle.capture(xr, ts, with_codes=True)
+    roll = oracle.unpack_nibbles(cap["codes"], n).copy()
+    flip = rng.random(n) < rng.choice([0.0, 0.02, 0.5])
+    roll[flip] = rng.integers(0, 16, int(flip.sum()))
+    cbits = (roll & 1) if rng.random() < 0.7 else rng.integers(0, 2, n)
+    codes, bits = oracle.pack_nibbles(roll), oracle.pack_bits(cbits.astype(np.uint8))
+    _say(f"{ctx}: agreement statistics {rows}x{cols}, {int(flip.sum())} rollout codes replaced")
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    got = tr.mismatch_stats(from_np_u16(xt, device, (rows, cols)), dev(cap["scales"]),
+                            dev(np.array([ts], np.float32)), dev(bits), dev(codes))
+    torch.cuda.synchronize()
+    st = oracle.mismatch_stats(xt, cap["scales"], ts, codes, bits)
+    want = st["hist"] + [st["straddle"], st["crossed"], st["recovered"], st["violations"], st["n"]]
+    assert got.cpu().numpy().tolist() == want, ctx
+
+
+def _run_noalloc(tr, rng, device, ctx):
+    sizes = [_shape(rng, 16) for _ in range(2)]
+    sizes.sort(key=lambda rc: -rc[0] * rc[1])      # the second call smaller, as the entry point's callers reuse it
+    _say(f"{ctx}: allocation-free tensor scale on {sizes}")
+    for rows, cols in sizes:
+        x = F.f32_to_bf16_rne(_sprinkle(rng, _f32(rng, rows, cols).reshape(-1)))
+        got = tr.tensor_scale_noalloc(from_np_u16(x, device, (rows, cols)))
+        torch.cuda.synchronize()
+        want = np.float32(oracle.tensor_scale(x))
+        assert got.cpu().numpy().view(np.uint32)[0] == want.view(np.uint32), (ctx, rows, cols)
+
+
 @pytest.mark.parametrize("seed", range(CASES), ids=[f"seed{s}" for s in range(CASES)])
 def test_random_sweep(device, seed):
     import fp4_rollout_guided_amd as tr
@@ -306,5 +342,9 @@ def test_random_sweep(device, seed):
             _run_lowbits(tr, rng, device, ctx)
         elif family in ("mx", "mx8"):
             _run_mx(tr, rng, device, ctx, eight=family == "mx8")
-        else:
+        elif family == "batch":
             _run_batch(tr, rng, device, ctx)
+        elif family == "stats":
+            _run_stats(tr, rng, device, ctx)
+        else:
+            _run_noalloc(tr, rng, device, ctx)
