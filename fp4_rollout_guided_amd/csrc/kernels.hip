@@ -1041,9 +1041,25 @@ __global__ __launch_bounds__(kThreads) void lowbits_fakequant_kernel(const uint4
 // ---------------------------------------------------------------------------
 // STE backward
 // ---------------------------------------------------------------------------
+// The tile of workgroup w among G: the hardware hands workgroup w to XCD
+// w % 8, so in dispatch order each XCD streams every eighth tile.  Within
+// each group of 8 * 256 workgroups this gives XCD x runs of 256 consecutive
+// tiles instead; workgroups past the last whole group keep their own tile.
+// A permutation of [0, G) for every G.
+__device__ __forceinline__ uint32_t xcd_run_tile(uint32_t w, uint32_t G) {
+  constexpr uint32_t kRun = 256, kGroup = 8 * kRun;
+  if (w >= G - G % kGroup) return w;
+  const uint32_t j = w / 8, x = w % 8;
+  return ((j / kRun) * 8 + x) * kRun + j % kRun;
+}
+
 // One 128-bit vector (8 elements, whose mask bits are byte i of the mask)
 // per lane: a lane with one load and one store in flight streams ~5% faster
-// than a lane moving two vectors, for copies as for this kernel.
+// than a lane moving two vectors, for copies as for this kernel.  Tiles go to
+// XCDs in runs (xcd_run_tile): on 20 layers of 262144x2048 in the step order
+// 338-341 us against 346-348 us in dispatch order, with identical outputs.
+// The forwards and the capture keep dispatch order (the same mapping left
+// them level or slower).
 template <bool kNT>
 __global__ __launch_bounds__(kThreads) void ste_bwd_kernel(const uint4* __restrict__ g, uint64_t nblocks,
                                                            const uint16_t* __restrict__ mask16,
@@ -1051,7 +1067,8 @@ __global__ __launch_bounds__(kThreads) void ste_bwd_kernel(const uint4* __restri
   const uint8_t* mask = reinterpret_cast<const uint8_t*>(mask16);
   const uint64_t nvec = 2 * nblocks;
   const uint64_t stride = (uint64_t)gridDim.x * kThreads;
-  for (uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += stride) {
+  const uint32_t tile = xcd_run_tile(blockIdx.x, gridDim.x);
+  for (uint64_t i = (uint64_t)tile * kThreads + threadIdx.x; i < nvec; i += stride) {
     const uint32_t m = mask[i];
     const uint4 v = load_vec<kNT>(&g[i]);
     uint32_t w[4] = {v.x, v.y, v.z, v.w};
