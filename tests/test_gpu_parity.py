@@ -297,3 +297,21 @@ def test_autograd_wrapper(device):
     y.backward(from_np_u16(g, device, (rows, cols)))
     assert np.array_equal(to_np_u16(y.detach()), want["y_g"])
     assert np.array_equal(to_np_u16(x.grad), want["gin"])
+
+
+@pytest.mark.parametrize("tiles", [2047, 2048, 2049, 4096 + 5, 6143])
+def test_ste_bwd_tile_runs(device, tiles):
+    """The STE backward hands tiles (256 vectors of 8 elements) to the XCDs in
+    runs once its grid holds a whole group of 8 x 256 workgroups; a partial
+    last group keeps dispatch order.  Grids just below, at and past whole
+    groups, with a ragged last tile: every element against the oracle."""
+    import fp4_rollout_guided_amd as tr
+    nvec = 256 * tiles - 2                  # 8-element vectors; the last tile is ragged
+    n = 8 * nvec                            # a multiple of 16 (nvec is even)
+    _say("case ste tile runs", tiles, n)
+    rng = np.random.default_rng(tiles)
+    grad = rng.integers(0, 1 << 16, n, dtype=np.uint16)
+    mask = rng.integers(0, 256, n // 8, dtype=np.uint8)
+    gin = tr.ste_bwd(from_np_u16(grad, device, (1, n)), torch.from_numpy(mask).to(device))
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np_u16(gin), oracle.ste_bwd(grad, mask, n)), tiles
